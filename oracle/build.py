@@ -1,0 +1,28 @@
+"""Compile the CPU oracle (oracle.c) into oracle/liboracle.so with gcc.
+
+Test infrastructure: the product library never links or loads the result.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "oracle.c")
+LIBRARY = os.path.join(HERE, "liboracle.so")
+
+
+def build_oracle(verbose: bool = False, extra_flags: tuple = (), output: str = LIBRARY,
+                 source: str = SOURCE) -> str:
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-fPIC", "-shared",
+           *extra_flags, "-o", output + ".tmp", source]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(output + ".tmp", output)
+    return output
+
+
+if __name__ == "__main__":
+    build_oracle(verbose=True, extra_flags=tuple(sys.argv[1:]))

@@ -1,0 +1,358 @@
+/*
+ * CPU oracle of the paged KV-cache write path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
+ * statement of what the write path computes.  Only the test suite, the smoke
+ * check and the CPU-baseline leg of the benchmark may load it.  It shares no
+ * code, header, table or constant generator with the GPU library; the few
+ * numeric conventions both must agree on (the pad id, the flag bits) are
+ * restated here from the interface documentation.
+ *
+ * Sources (pages as published; sections named, not quoted):
+ *  [P1] "Range-addressed KV cache blocks for the vLLM serving engine",
+ *       sections "The Innovation: Range Arithmetic Replaces the Per-Position
+ *       Gather" and "The Coordinate Approach".
+ *  [P2] "Blocktabelle: Abbildung von logischen Token auf physische KV-Blocks",
+ *       sections "Verantwortung", "Entwurfsmotivation", "Datenfluss" and
+ *       "Grenzen und Fehler".
+ *  [P3] "vLLM Block Table Management: From PagedAttention to the V1 KV Cache
+ *       Stack", Deep Dive sections 7 ("Worker-side block table
+ *       materialization") and 8 ("slot_mapping: token -> physical slot").
+ *
+ * Every loop below walks the definition in the order it is stated; nothing
+ * is blocked, fused or reordered.  Integer arithmetic is done in int64.
+ *
+ * Readings where the pages leave a step open (each one is listed with its
+ * reason in the design notes of the repository):
+ *  - a token whose position is negative, or whose logical block lies past
+ *    the blocks its request owns, or past every range, gets the pad id;
+ *  - range descriptors are (start, len, cum) with cum the exclusive prefix
+ *    sum of len; the first range containing the logical block is used;
+ *  - a manager block b expands to kernel blocks b*k .. b*k+k-1, k the ratio
+ *    of the block sizes; table entries past a row's count become block 0;
+ *  - a padded token writes nothing; a slot outside the cache is skipped and
+ *    reported through a flag bit.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_PAD_ID (-1)
+
+/* Return codes of the oracle: 0 = computed; >0 = the input violates a
+ * precondition the oracle checks (the output is then not meaningful). */
+#define ORC_OK 0
+#define ORC_E_ARG 1
+#define ORC_E_QSL 2
+#define ORC_E_RANGES 3
+#define ORC_E_DUPLICATE 4
+
+/* Flag bits reported for recoverable, data-dependent conditions. */
+#define ORC_FLAG_NUM_TOKENS 1u /* query_start_loc[num_reqs] outside [0, max_num_tokens] */
+#define ORC_FLAG_COUNT 2u      /* per-request block or range count outside [0, stride] */
+#define ORC_FLAG_BAD_BLOCK 4u  /* resolved physical block id negative or not representable */
+#define ORC_FLAG_SLOT_OOB 8u   /* slot past the cache: the write is skipped */
+
+static int64_t clamp64(int64_t v, int64_t lo, int64_t hi, uint32_t *flags, uint32_t bit)
+{
+    if (v < lo) { *flags |= bit; return lo; }
+    if (v > hi) { *flags |= bit; return hi; }
+    return v;
+}
+
+/* Number of tokens scheduled this step: the last entry of query_start_loc
+ * ([P2] "Datenfluss": the kernel's token ranges per request). */
+static int64_t num_tokens_of(const int32_t *qsl, int32_t num_reqs, int64_t max_num_tokens,
+                             uint32_t *flags)
+{
+    return clamp64((int64_t)qsl[num_reqs], 0, max_num_tokens, flags, ORC_FLAG_NUM_TOKENS);
+}
+
+static int qsl_ok(const int32_t *qsl, int32_t num_reqs)
+{
+    if (qsl[0] < 0) return 0;
+    for (int32_t r = 0; r < num_reqs; ++r)
+        if (qsl[r + 1] < qsl[r]) return 0;
+    return 1;
+}
+
+/*
+ * Paged slot mapping ([P2] "Entwurfsmotivation", slot_mapping as a kernel;
+ * [P3] section 8): for token t of request r at position p,
+ *   logical block  = p / block_size,  offset = p % block_size,
+ *   physical block = block_table[r][logical block],
+ *   slot           = physical block * block_size + offset,
+ * and every entry from num_tokens up to max_num_tokens is the pad id
+ * ([P2] "Datenfluss": the last program pads the tail for graph replay).
+ * num_blocks_per_req (may be NULL) bounds the valid logical blocks of a row;
+ * NULL means the full row width.
+ */
+int orc_slot_mapping_paged(const int32_t *qsl, int32_t num_reqs, const int64_t *positions,
+                           int64_t max_num_tokens, const int32_t *block_table,
+                           int32_t table_stride, const int32_t *num_blocks_per_req,
+                           int32_t block_size, int64_t *slot_mapping, uint32_t *flags_out)
+{
+    uint32_t flags = 0;
+    if (!qsl || num_reqs < 0 || max_num_tokens < 0 || block_size <= 0 || table_stride < 0 ||
+        (max_num_tokens > 0 && !slot_mapping))
+        return ORC_E_ARG;
+    if (!qsl_ok(qsl, num_reqs)) return ORC_E_QSL;
+
+    for (int64_t t = 0; t < max_num_tokens; ++t) slot_mapping[t] = ORC_PAD_ID;
+    int64_t num_tokens = num_tokens_of(qsl, num_reqs, max_num_tokens, &flags);
+
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        int64_t bound = table_stride;
+        if (num_blocks_per_req)
+            bound = clamp64(num_blocks_per_req[r], 0, table_stride, &flags, ORC_FLAG_COUNT);
+        for (int64_t t = qsl[r]; t < qsl[r + 1] && t < num_tokens; ++t) {
+            int64_t p = positions[t];
+            if (p < 0) continue;                       /* pad id */
+            int64_t logical = p / block_size;
+            int64_t offset = p % block_size;
+            if (logical >= bound) continue;            /* no block owned there: pad id */
+            int64_t physical = block_table[(int64_t)r * table_stride + logical];
+            if (physical < 0) { flags |= ORC_FLAG_BAD_BLOCK; continue; }
+            slot_mapping[t] = physical * block_size + offset;
+        }
+    }
+    if (flags_out) *flags_out |= flags;
+    return ORC_OK;
+}
+
+/*
+ * Range-arithmetic slot mapping ([P1] "The Innovation"): a request's blocks
+ * are contiguous runs; run i covers logical blocks [cum[i], cum[i]+len[i])
+ * and starts at physical block start[i], so
+ *   physical block = start[i] + (logical block - cum[i]).
+ * A position inside no run gets the pad id.  The oracle scans the runs in
+ * order and takes the first that contains the logical block.
+ * Precondition (checked): len[i] >= 1 and cum is the exclusive prefix sum
+ * of len, for the first num_ranges[r] (clamped) entries of every request.
+ */
+int orc_slot_mapping_ranges(const int32_t *qsl, int32_t num_reqs, const int64_t *positions,
+                            int64_t max_num_tokens, const int32_t *range_start,
+                            const int32_t *range_len, const int32_t *range_cum,
+                            const int32_t *num_ranges, int32_t range_stride, int32_t block_size,
+                            int64_t *slot_mapping, uint32_t *flags_out)
+{
+    uint32_t flags = 0;
+    if (!qsl || num_reqs < 0 || max_num_tokens < 0 || block_size <= 0 || range_stride < 0 ||
+        (max_num_tokens > 0 && !slot_mapping))
+        return ORC_E_ARG;
+    if (num_reqs > 0 && (!range_start || !range_len || !range_cum || !num_ranges))
+        return ORC_E_ARG;
+    if (!qsl_ok(qsl, num_reqs)) return ORC_E_QSL;
+
+    /* descriptor precondition */
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        uint32_t dummy = 0;
+        int64_t n = clamp64(num_ranges[r], 0, range_stride, &dummy, ORC_FLAG_COUNT);
+        int64_t expect_cum = 0;
+        for (int64_t i = 0; i < n; ++i) {
+            int64_t k = (int64_t)r * range_stride + i;
+            if (range_len[k] < 1 || range_cum[k] != expect_cum) return ORC_E_RANGES;
+            expect_cum += range_len[k];
+        }
+    }
+
+    for (int64_t t = 0; t < max_num_tokens; ++t) slot_mapping[t] = ORC_PAD_ID;
+    int64_t num_tokens = num_tokens_of(qsl, num_reqs, max_num_tokens, &flags);
+
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        int64_t n = clamp64(num_ranges[r], 0, range_stride, &flags, ORC_FLAG_COUNT);
+        for (int64_t t = qsl[r]; t < qsl[r + 1] && t < num_tokens; ++t) {
+            int64_t p = positions[t];
+            if (p < 0) continue;
+            int64_t logical = p / block_size;
+            int64_t offset = p % block_size;
+            for (int64_t i = 0; i < n; ++i) {
+                int64_t k = (int64_t)r * range_stride + i;
+                int64_t cum = range_cum[k], len = range_len[k];
+                if (cum <= logical && logical < cum + len) {
+                    int64_t physical = (int64_t)range_start[k] + (logical - cum);
+                    if (physical < 0) flags |= ORC_FLAG_BAD_BLOCK;
+                    else slot_mapping[t] = physical * block_size + offset;
+                    break;
+                }
+            }
+        }
+    }
+    if (flags_out) *flags_out |= flags;
+    return ORC_OK;
+}
+
+/* Expansion factor of manager blocks into kernel blocks, or 0 when the
+ * kernel block size does not divide the manager block size ([P2]
+ * "Grenzen und Fehler": such a pair is rejected). */
+static int64_t blocks_per_kv_block(int32_t block_size, int32_t kernel_block_size)
+{
+    if (block_size <= 0 || kernel_block_size <= 0) return 0;
+    if (block_size % kernel_block_size != 0) return 0;
+    return block_size / kernel_block_size;
+}
+
+/* A kernel block id b*k+j must stay a non-negative int32. */
+static int expandable(int64_t id, int64_t k)
+{
+    return id >= 0 && id * k + (k - 1) <= INT32_MAX;
+}
+
+/*
+ * Manager-to-kernel block expansion ([P2] "Entwurfsmotivation" and
+ * "Schluesseldateien"; [P3] section 7): each manager block of a row becomes
+ * k consecutive kernel blocks, k = block_size / kernel_block_size, in order:
+ *   out[r][i*k + j] = in[r][i]*k + j,   0 <= j < k, i < count[r].
+ * Entries of the output row past count[r]*k are block 0 (the null block).
+ * counts may be NULL (every row full).
+ */
+int orc_map_to_kernel_blocks(const int32_t *ids, const int32_t *counts, int32_t rows,
+                             int32_t in_stride, int32_t block_size, int32_t kernel_block_size,
+                             int32_t *out, int32_t out_stride, uint32_t *flags_out)
+{
+    uint32_t flags = 0;
+    int64_t k = blocks_per_kv_block(block_size, kernel_block_size);
+    if (k == 0) return ORC_E_ARG;
+    if (rows < 0 || in_stride < 0 || out_stride < (int64_t)in_stride * k) return ORC_E_ARG;
+    for (int32_t r = 0; r < rows; ++r) {
+        int64_t count = in_stride;
+        if (counts) count = clamp64(counts[r], 0, in_stride, &flags, ORC_FLAG_COUNT);
+        for (int64_t c = 0; c < out_stride; ++c) out[(int64_t)r * out_stride + c] = 0;
+        for (int64_t i = 0; i < count; ++i) {
+            int64_t id = ids[(int64_t)r * in_stride + i];
+            for (int64_t j = 0; j < k; ++j) {
+                int64_t v = 0;
+                if (expandable(id, k)) v = id * k + j;
+                else flags |= ORC_FLAG_BAD_BLOCK;
+                out[(int64_t)r * out_stride + i * k + j] = (int32_t)v;
+            }
+        }
+    }
+    if (flags_out) *flags_out |= flags;
+    return ORC_OK;
+}
+
+/*
+ * The same expansion applied to range descriptors: manager run
+ * (start, len, cum) covers kernel blocks [start*k, (start+len)*k) and
+ * logical kernel blocks [cum*k, (cum+len)*k), so all three fields scale by
+ * k.  num_ranges is copied (clamped to the stride); entries past it are 0.
+ */
+int orc_map_ranges_to_kernel_blocks(const int32_t *start, const int32_t *len, const int32_t *cum,
+                                    const int32_t *num_ranges, int32_t rows, int32_t range_stride,
+                                    int32_t block_size, int32_t kernel_block_size,
+                                    int32_t *out_start, int32_t *out_len, int32_t *out_cum,
+                                    int32_t *out_num_ranges, uint32_t *flags_out)
+{
+    uint32_t flags = 0;
+    int64_t k = blocks_per_kv_block(block_size, kernel_block_size);
+    if (k == 0 || rows < 0 || range_stride < 0) return ORC_E_ARG;
+    for (int32_t r = 0; r < rows; ++r) {
+        int64_t n = clamp64(num_ranges[r], 0, range_stride, &flags, ORC_FLAG_COUNT);
+        out_num_ranges[r] = (int32_t)n;
+        for (int64_t i = 0; i < range_stride; ++i) {
+            int64_t q = (int64_t)r * range_stride + i;
+            int64_t s = 0, l = 0, c = 0;
+            if (i < n) {
+                if (expandable(start[q], k) && expandable(len[q], k) && expandable(cum[q], k)) {
+                    s = (int64_t)start[q] * k;
+                    l = (int64_t)len[q] * k;
+                    c = (int64_t)cum[q] * k;
+                } else {
+                    flags |= ORC_FLAG_BAD_BLOCK;
+                }
+            }
+            out_start[q] = (int32_t)s;
+            out_len[q] = (int32_t)l;
+            out_cum[q] = (int32_t)c;
+        }
+    }
+    if (flags_out) *flags_out |= flags;
+    return ORC_OK;
+}
+
+/*
+ * Coordinate form ([P1] "The Coordinate Approach"):
+ *   n(layer, block, token) = (layer * B + block) * T + token,
+ *   offset = n * bytes_per_token,
+ * B blocks per layer, T tokens per block.
+ */
+int64_t orc_coord_n(int64_t layer, int64_t block, int64_t token, int64_t num_blocks,
+                    int64_t block_size)
+{
+    return (layer * num_blocks + block) * block_size + token;
+}
+
+int64_t orc_coord_offset(int64_t layer, int64_t block, int64_t token, int64_t num_blocks,
+                         int64_t block_size, int64_t bytes_per_token)
+{
+    return orc_coord_n(layer, block, token, num_blocks, block_size) * bytes_per_token;
+}
+
+/*
+ * K/V scatter through slot_mapping ([P2] "Verantwortung": the attention
+ * side reads and writes the cache at each token's slot; [P3] section 8):
+ * for every layer and every token t whose slot s is not the pad id,
+ *   block = s / T, token-in-block = s % T,
+ *   copy the token's K row to the K cache at the coordinate offset of
+ *   (layer, block, token-in-block), and its V row likewise.
+ * A slot at or past B*T is skipped and flagged.  Nothing else is written.
+ *
+ * The caller holds a window of the caches: rows [row_begin, row_begin +
+ * row_count) of the [layers][B][T] row space (k_window/v_window point at
+ * the window's first row), so caches larger than host memory can be
+ * checked piecewise.  Rows outside the window are not touched.
+ * Precondition (checked): no two tokens share a valid slot.
+ */
+static int cmp_i64(const void *a, const void *b)
+{
+    int64_t x = *(const int64_t *)a, y = *(const int64_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* 1 when two tokens carry the same in-cache slot, -1 on allocation failure. */
+static int has_duplicate_slot(const int64_t *slot_mapping, int64_t n, int64_t rows_per_layer)
+{
+    int64_t *v = (int64_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
+    int64_t m = 0;
+    int dup = 0;
+    if (!v) return -1;
+    for (int64_t t = 0; t < n; ++t)
+        if (slot_mapping[t] >= 0 && slot_mapping[t] < rows_per_layer) v[m++] = slot_mapping[t];
+    qsort(v, (size_t)m, sizeof(int64_t), cmp_i64);
+    for (int64_t i = 1; i < m; ++i)
+        if (v[i] == v[i - 1]) { dup = 1; break; }
+    free(v);
+    return dup;
+}
+
+int orc_kv_write(const int64_t *slot_mapping, int64_t max_num_tokens, int32_t num_layers,
+                 const uint8_t *key, const uint8_t *value, int64_t kv_layer_stride,
+                 int64_t kv_token_stride, int64_t num_blocks, int32_t block_size,
+                 int64_t bytes_per_token, uint8_t *k_window, uint8_t *v_window,
+                 int64_t row_begin, int64_t row_count, uint32_t *flags_out)
+{
+    uint32_t flags = 0;
+    if (max_num_tokens < 0 || num_layers < 0 || num_blocks < 0 || block_size <= 0 ||
+        bytes_per_token <= 0 || row_begin < 0 || row_count < 0)
+        return ORC_E_ARG;
+    int64_t rows_per_layer = num_blocks * block_size;
+    if (has_duplicate_slot(slot_mapping, max_num_tokens, rows_per_layer)) return ORC_E_DUPLICATE;
+    for (int64_t layer = 0; layer < num_layers; ++layer) {
+        for (int64_t t = 0; t < max_num_tokens; ++t) {
+            int64_t s = slot_mapping[t];
+            if (s < 0) continue;                         /* padded token: no write */
+            if (s >= rows_per_layer) { flags |= ORC_FLAG_SLOT_OOB; continue; }
+            int64_t block = s / block_size;
+            int64_t token = s % block_size;
+            int64_t n = orc_coord_n(layer, block, token, num_blocks, block_size);
+            if (n < row_begin || n >= row_begin + row_count) continue;
+            int64_t dst = (n - row_begin) * bytes_per_token;
+            int64_t src = layer * kv_layer_stride + t * kv_token_stride;
+            memcpy(k_window + dst, key + src, (size_t)bytes_per_token);
+            memcpy(v_window + dst, value + src, (size_t)bytes_per_token);
+        }
+    }
+    if (flags_out) *flags_out |= flags;
+    return ORC_OK;
+}

@@ -1,0 +1,400 @@
+"""Checks that tie the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` and raises AssertionError
+when the oracle disagrees with:
+  * values the pages print (fixtures under tests/golden/, each cited there);
+  * a token-at-a-time allocation simulation that places every token by
+    counting free slots (no division, no modulo, no table lookup);
+  * enumeration of every slot a request owns, in logical order;
+  * the pages' invariant that range arithmetic and the table gather give the
+    same slot for the same physical layout;
+  * numpy's own row-major indexing (ravel_multi_index, array addresses,
+    fancy-index scatter) for the coordinate form and the K/V copy.
+The same functions are run against deliberately broken builds of the oracle
+(test_oracle_mutants.py) to show that each plausible mistake is caught.
+"""
+from __future__ import annotations
+
+import os
+from typing import Dict, List, Tuple
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+PAD = -1
+
+
+# ---------------------------------------------------------------------------
+# fixture parsing
+# ---------------------------------------------------------------------------
+def _lines(name: str) -> List[List[str]]:
+    out = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for ln in f:
+            ln = ln.strip()
+            if ln and not ln.startswith("#"):
+                out.append(ln.split())
+    return out
+
+
+def _runs_of(row: List[int]) -> List[Tuple[int, int, int]]:
+    """Compress a block row into maximal runs of consecutive ids: (start, len, cum)."""
+    runs: List[Tuple[int, int, int]] = []
+    for j, b in enumerate(row):
+        if runs and runs[-1][0] + runs[-1][1] == b:
+            s, ln, c = runs[-1]
+            runs[-1] = (s, ln + 1, c)
+        else:
+            runs.append((b, 1, j))
+    return runs
+
+
+def _descriptors(rows: List[List[int]], stride: int = 0):
+    runs = [_runs_of(r) for r in rows]
+    stride = max(stride, max((len(r) for r in runs), default=1), 1)
+    R = len(rows)
+    st, ln, cm = (np.zeros((R, stride), np.int32) for _ in range(3))
+    nr = np.zeros(R, np.int32)
+    for i, rr in enumerate(runs):
+        nr[i] = len(rr)
+        for k, (s, l, c) in enumerate(rr):
+            st[i, k], ln[i, k], cm[i, k] = s, l, c
+    return st, ln, cm, nr
+
+
+def _table(rows: List[List[int]], stride: int = 0):
+    stride = max(stride, max((len(r) for r in rows), default=1), 1)
+    t = np.zeros((len(rows), stride), np.int32)
+    for i, r in enumerate(rows):
+        t[i, :len(r)] = r
+    return t, np.array([len(r) for r in rows], np.int32)
+
+
+def _batch(scheduled: List[List[int]], pad_to: int = 0, rng=None):
+    """qsl and positions for requests scheduling the given positions (in order)."""
+    counts = [len(s) for s in scheduled]
+    qsl = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    n = int(qsl[-1])
+    m = max(n, pad_to)
+    pos = np.empty(m, np.int64)
+    pos[:n] = [p for s in scheduled for p in s]
+    if m > n:
+        g = rng if rng is not None else np.random.default_rng(0)
+        pos[n:] = g.integers(-(1 << 20), 1 << 20, size=m - n)
+    return qsl, pos, m
+
+
+def _both(orc, qsl, pos, m, rows, bs, table_stride=0):
+    t, nb = _table(rows, table_stride)
+    st, ln, cm, nr = _descriptors(rows)
+    paged, fp = orc.slot_mapping_paged(qsl, len(rows), pos, m, t, nb, bs)
+    ranges, fr = orc.slot_mapping_ranges(qsl, len(rows), pos, m, st, ln, cm, nr, bs)
+    return paged, ranges, fp, fr
+
+
+# ---------------------------------------------------------------------------
+# pins
+# ---------------------------------------------------------------------------
+def pin_golden_bs16(orc):
+    """Printed slot values for row [7, 1] at block size 16."""
+    bs, row, slots, spans = None, None, {}, []
+    for f in _lines("slot_mapping_bs16.txt"):
+        if f[0] == "block_size":
+            bs = int(f[1])
+        elif f[0] == "row":
+            row = [int(x) for x in f[1:]]
+        elif f[0] == "slot":
+            slots[int(f[1])] = int(f[2])
+        elif f[0] == "block":
+            spans.append((int(f[1]), int(f[2]), int(f[3])))
+    last = max(b for _, b, _ in spans)
+    qsl, pos, m = _batch([list(range(0, last + 1))])
+    paged, ranges, _, _ = _both(orc, qsl, pos, m, [row], bs)
+    for out in (paged, ranges):
+        for p, s in slots.items():
+            assert out[p] == s, (p, out[p], s)
+        for a, b, blk in spans:
+            for p in range(a, b + 1):
+                assert blk * bs <= out[p] < (blk + 1) * bs, (p, out[p], blk)
+        assert len(set(out.tolist())) == len(out)
+
+
+def pin_figure6(orc):
+    """Figure 6 sequence: prompt into blocks 7 and 1, decode into the free slot, then block 3."""
+    bs, steps = None, []
+    for f in _lines("figure6_bs4.txt"):
+        if f[0] == "block_size":
+            bs = int(f[1])
+        elif f[0] == "step":
+            steps.append(([int(x) for x in f[2:]], []))
+        elif f[0] == "place":
+            steps[-1][1].append((int(f[1]), int(f[2]), int(f[3])))
+    for row, places in steps:
+        qsl, pos, m = _batch([[p for p, _, _ in places]], pad_to=len(places) + 3)
+        paged, ranges, _, _ = _both(orc, qsl, pos, m, [row], bs)
+        for out in (paged, ranges):
+            for i, (p, blk, idx) in enumerate(places):
+                assert out[i] == blk * bs + idx, (row, p, out[i], blk, idx)
+            assert (out[len(places):] == PAD).all()
+
+
+def _simulate(rng, lengths: List[int], bs: int, pool: int, run_free_list: bool):
+    """Place tokens one at a time; a request takes a fresh block when its last one is full.
+
+    Returns rows (physical blocks in logical order) and, per request, the
+    (block, index-in-block) of every position.  With run_free_list the free
+    list hands out shuffled runs of consecutive ids (so rows compress into
+    ranges); otherwise single ids in random order.
+    """
+    ids = list(range(1, pool))
+    if run_free_list:
+        runs, i = [], 0
+        while i < len(ids):
+            ln = int(rng.integers(1, 6))
+            runs.append(ids[i:i + ln])
+            i += ln
+        order = rng.permutation(len(runs))
+        free = [b for k in order for b in runs[k]]
+    else:
+        free = [ids[k] for k in rng.permutation(len(ids))]
+    free.reverse()  # pop() from the end == take from the head
+    rows, places = [], []
+    # interleave requests token by token, as continuous batching would
+    fill = [bs] * len(lengths)
+    rows = [[] for _ in lengths]
+    places = [[] for _ in lengths]
+    left = list(lengths)
+    while any(left):
+        for r in range(len(lengths)):
+            if not left[r]:
+                continue
+            if fill[r] == bs:
+                rows[r].append(free.pop())
+                fill[r] = 0
+            places[r].append((rows[r][-1], fill[r]))
+            fill[r] += 1
+            left[r] -= 1
+    return rows, places
+
+
+def pin_fill_simulation(orc, seeds=range(6)):
+    """Slots agree with a token-at-a-time placement for random batches."""
+    for seed in seeds:
+        rng = np.random.default_rng(1000 + seed)
+        bs = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+        n_req = int(rng.integers(1, 6))
+        lengths = [int(rng.integers(1, 70)) for _ in range(n_req)]
+        need = sum(-(-ln // bs) for ln in lengths)
+        rows, places = _simulate(rng, lengths, bs, need + 40, run_free_list=bool(seed % 2))
+        # each request schedules its last n_new positions this step
+        sched, expect = [], []
+        for ln, plc in zip(lengths, places):
+            n_new = int(rng.integers(0, ln + 1))
+            sched.append(list(range(ln - n_new, ln)))
+            expect += [b * bs + i for (b, i) in plc[ln - n_new:]]
+        qsl, pos, m = _batch(sched, pad_to=len(expect) + int(rng.integers(0, 9)), rng=rng)
+        paged, ranges, _, _ = _both(orc, qsl, pos, m, rows, bs,
+                                    table_stride=int(rng.integers(0, 4)) + max(map(len, rows)))
+        n = len(expect)
+        for out in (paged, ranges):
+            assert out[:n].tolist() == expect, (seed, out[:n].tolist(), expect)
+            assert (out[n:] == PAD).all()
+
+
+def pin_enumeration(orc):
+    """Exhaustive tiny layouts: position p owns the p-th slot of the request, in logical order."""
+    rng = np.random.default_rng(7)
+    for bs in (1, 2, 3):
+        for lens in ([1], [2], [1, 1], [2, 1], [1, 2, 1], [2, 2, 2]):
+            for trial in range(3):
+                starts = rng.choice(np.arange(1, 40, 3), size=len(lens), replace=False)
+                row = [int(s) + j for s, ln in zip(starts, lens) for j in range(ln)]
+                owned = [b * bs + i for b in row for i in range(bs)]
+                positions = list(range(-2, len(owned) + bs + 1))
+                qsl, pos, m = _batch([positions])
+                paged, ranges, _, _ = _both(orc, qsl, pos, m, [row], bs)
+                for out in (paged, ranges):
+                    for i, p in enumerate(positions):
+                        want = owned[p] if 0 <= p < len(owned) else PAD
+                        assert out[i] == want, (bs, lens, p, out[i], want)
+
+
+def pin_padding_rules(orc):
+    """Tail, negative positions, unowned blocks, clamped counts and num_tokens."""
+    bs = 4
+    rows = [[5, 6], [9]]
+    # request 0: positions 0..9 (blocks 0,1 owned, 2 not); request 1: -1, 3, 4
+    sched = [list(range(10)), [-1, 3, 4]]
+    qsl, pos, m = _batch(sched, pad_to=20)
+    t, nb = _table(rows, 3)
+    paged, f = orc.slot_mapping_paged(qsl, 2, pos, m, t, nb, bs)
+    want = [20, 21, 22, 23, 24, 25, 26, 27, PAD, PAD, PAD, 39, PAD] + [PAD] * 7
+    assert paged.tolist() == want, paged.tolist()
+    assert f == 0
+    # without per-row counts the whole row width is owned; unfilled entries are block 0
+    paged, _ = orc.slot_mapping_paged(qsl, 2, pos, m, t, None, bs)
+    assert paged[8] == 0 and paged[9] == 1 and paged[13] == PAD
+    # counts beyond the row width are clamped and flagged
+    paged, f = orc.slot_mapping_paged(qsl, 2, pos, m, t, np.array([9, 1], np.int32), bs)
+    assert f & 2 and paged[8] == 0
+    # num_tokens past max_num_tokens is clamped and flagged
+    q2 = qsl.copy()
+    q2[-1] = 25
+    paged, f = orc.slot_mapping_paged(q2, 2, pos, m, t, nb, bs)
+    assert f & 1 and paged[12] == PAD and paged[11] == 39
+    # ranges: same layout, same rules
+    st, ln, cm, nr = _descriptors(rows)
+    ranges, f = orc.slot_mapping_ranges(qsl, 2, pos, m, st, ln, cm, nr, bs)
+    assert ranges.tolist() == want
+    # dummy requests with no tokens and no ranges contribute nothing
+    qd = np.array([0, 3, 3, 3], np.int32)
+    pd = np.array([0, 1, 2, 77, 78], np.int64)
+    td, nbd = _table([[2], [], []], 2)
+    out, _ = orc.slot_mapping_paged(qd, 3, pd, 5, td, nbd, bs)
+    assert out.tolist() == [8, 9, 10, PAD, PAD]
+
+
+def pin_range_equals_gather(orc, workloads):
+    """The pages' invariant: range arithmetic == gather through the materialized table."""
+    for w in workloads:
+        paged, _ = orc.slot_mapping_paged(w.query_start_loc, w.num_reqs, w.positions,
+                                          w.max_num_tokens, w.block_table, w.num_blocks_per_req,
+                                          w.block_size)
+        ranges, _ = orc.slot_mapping_ranges(w.query_start_loc, w.num_reqs, w.positions,
+                                            w.max_num_tokens, w.range_start, w.range_len,
+                                            w.range_cum, w.num_ranges, w.block_size)
+        assert np.array_equal(paged, ranges), w.name
+        n = w.num_tokens
+        assert (paged[n:] == PAD).all()
+        real = paged[:n][paged[:n] >= 0]
+        assert len(np.unique(real)) == len(real), w.name
+
+
+def pin_expansion(orc):
+    """Manager->kernel expansion keeps every token's slot (same memory, finer blocks)."""
+    rng = np.random.default_rng(11)
+    for (bs_m, bs_k) in ((32, 16), (64, 16), (16, 16), (48, 16), (12, 4)):
+        k = bs_m // bs_k
+        lengths = [int(rng.integers(1, 200)) for _ in range(4)]
+        need = sum(-(-ln // bs_m) for ln in lengths)
+        rows, places = _simulate(rng, lengths, bs_m, need + 30, run_free_list=True)
+        sched = [list(range(ln)) for ln in lengths]
+        qsl, pos, m = _batch(sched, pad_to=sum(lengths) + 5)
+        expect = [b * bs_m + i for plc in places for (b, i) in plc]
+        t, nb = _table(rows, max(map(len, rows)) + 2)
+        kt, f = orc.map_to_kernel_blocks(t, nb, bs_m, bs_k)
+        assert f == 0 and kt.shape[1] == t.shape[1] * k
+        # row r, manager block i covers kernel blocks i*k .. i*k+k-1 of the same memory
+        for r, row in enumerate(rows):
+            for i, b in enumerate(row):
+                for j in range(k):
+                    assert kt[r, i * k + j] * bs_k == b * bs_m + j * bs_k
+            assert (kt[r, len(row) * k:] == 0).all()
+        sm, _ = orc.slot_mapping_paged(qsl, len(rows), pos, m, kt, nb * k, bs_k)
+        assert sm[:len(expect)].tolist() == expect
+        st, ln, cm, nr = _descriptors(rows)
+        (ks, kl, kc, kn), f = orc.map_ranges_to_kernel_blocks(st, ln, cm, nr, bs_m, bs_k)
+        assert f == 0 and np.array_equal(kn, nr)
+        sr, _ = orc.slot_mapping_ranges(qsl, len(rows), pos, m, ks, kl, kc, kn, bs_k)
+        assert sr[:len(expect)].tolist() == expect
+        sr32, _ = orc.slot_mapping_ranges(qsl, len(rows), pos, m, st, ln, cm, nr, bs_m)
+        assert np.array_equal(sr32, sr)
+    # a kernel block size that does not divide the manager block size is rejected
+    from oracle import OracleError
+    for bad in ((32, 12), (16, 32), (16, 0)):
+        try:
+            orc.map_to_kernel_blocks(np.ones((1, 2), np.int32), None, *bad)
+        except OracleError:
+            pass
+        else:
+            raise AssertionError(f"expansion {bad} not rejected")
+
+
+def pin_coordinates(orc):
+    """Coordinate form == numpy row-major indexing of [layers][blocks][tokens] rows."""
+    cfg = {f[0]: int(f[1]) for f in _lines("coordinate_layout.txt")}
+    L, B, T, bpt = cfg["layers"], cfg["blocks"], cfg["tokens_per_block"], cfg["bytes_per_token"]
+    rng = np.random.default_rng(3)
+    pts = [(0, 0, 0), (L - 1, B - 1, T - 1), (1, 0, 0), (0, 1, 0), (0, 0, 1)]
+    pts += [tuple(int(v) for v in (rng.integers(L), rng.integers(B), rng.integers(T)))
+            for _ in range(200)]
+    for (l, b, t) in pts:
+        want = int(np.ravel_multi_index((l, b, t), (L, B, T))) * bpt
+        assert orc.coord_offset(l, b, t, B, T, bpt) == want, (l, b, t)
+    # the last row of that layout ends at 128 GiB: offsets need 64-bit integers
+    assert orc.coord_offset(L - 1, B - 1, T - 1, B, T, bpt) + bpt == 128 << 30
+    # element addresses of a real nested array
+    shape = (3, 5, 4, 24)
+    arr = np.zeros(shape, np.uint8)
+    base = arr.ctypes.data
+    for l in range(shape[0]):
+        for b in range(shape[1]):
+            for t in range(shape[2]):
+                addr = arr[l, b, t].ctypes.data - base
+                assert orc.coord_offset(l, b, t, shape[1], shape[2], shape[3]) == addr
+
+
+def expected_caches_numpy(slots: np.ndarray, key: np.ndarray, value: np.ndarray,
+                          num_blocks: int, block_size: int, sentinel: int):
+    """Independent K/V scatter with numpy fancy indexing over [layers, B*T, row]."""
+    L, M, E = key.shape
+    kc = np.full((L, num_blocks * block_size, E), sentinel, key.dtype)
+    vc = np.full_like(kc, sentinel)
+    ok = (slots >= 0) & (slots < num_blocks * block_size)
+    kc[:, slots[ok]] = key[:, ok]
+    vc[:, slots[ok]] = value[:, ok]
+    return kc, vc
+
+
+def pin_kv_write(orc, workloads):
+    """K/V scatter == numpy scatter; windows compose; pads and stray slots write nothing."""
+    from workloads import BF16_SENTINEL
+    for w in workloads:
+        slots, _ = orc.slot_mapping_paged(w.query_start_loc, w.num_reqs, w.positions,
+                                          w.max_num_tokens, w.block_table, w.num_blocks_per_req,
+                                          w.block_size)
+        key, value = w.kv_plane(0), w.kv_plane(1)
+        ek, ev = expected_caches_numpy(slots, key, value, w.num_blocks, w.block_size,
+                                       BF16_SENTINEL)
+        rows = w.num_layers * w.num_blocks * w.block_size
+        kc = np.full((rows, w.row_elems), BF16_SENTINEL, np.uint16)
+        vc = np.full_like(kc, BF16_SENTINEL)
+        f = orc.kv_write(slots, key, value, w.num_blocks, w.block_size, kc, vc)
+        assert f == 0
+        assert np.array_equal(kc, ek.reshape(rows, -1)), w.name
+        assert np.array_equal(vc, ev.reshape(rows, -1)), w.name
+        # piecewise windows give the same bytes
+        kc2 = np.full_like(kc, BF16_SENTINEL)
+        vc2 = np.full_like(kc, BF16_SENTINEL)
+        cuts = np.unique(np.concatenate([[0, rows], np.random.default_rng(5).integers(
+            0, rows, size=7)]))
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            orc.kv_write(slots, key, value, w.num_blocks, w.block_size, kc2[a:b], vc2[a:b],
+                         row_begin=int(a))
+        assert np.array_equal(kc, kc2) and np.array_equal(vc, vc2)
+        # K/V rows of padded tokens (bf16 1.0 everywhere) never reach the cache
+        n = w.num_tokens
+        if n < w.max_num_tokens:
+            marker = key[0, n]
+            assert not (kc == marker).all(axis=1).any()
+    # a slot beyond the cache is skipped and flagged; a pad slot is skipped silently
+    key = np.arange(2 * 3 * 8, dtype=np.uint16).reshape(2, 3, 8)
+    kc = np.zeros((2 * 2 * 2, 8), np.uint16)
+    vc = np.zeros_like(kc)
+    f = orc.kv_write(np.array([3, 4, PAD]), key, key, 2, 2, kc, vc)
+    assert f == 8
+    assert (kc[3] == key[0, 0]).all() and (kc[4 + 3] == key[1, 0]).all()
+    assert (np.delete(kc, [3, 7], axis=0) == 0).all()
+
+
+def all_pins(orc, small, full=()):
+    """Every pin, for the mutation campaign (small inputs only)."""
+    pin_golden_bs16(orc)
+    pin_figure6(orc)
+    pin_fill_simulation(orc)
+    pin_enumeration(orc)
+    pin_padding_rules(orc)
+    pin_range_equals_gather(orc, list(small) + list(full))
+    pin_expansion(orc)
+    pin_coordinates(orc)
+    pin_kv_write(orc, small)

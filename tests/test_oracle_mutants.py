@@ -1,0 +1,85 @@
+"""Plant plausible mistakes in copies of the oracle and check the pins catch each one.
+
+Every mutant is a one-line edit of oracle.c (a dropped term, a wrong sign, a
+transposed index, an off-by-one bound), compiled on the CPU into a temporary
+library and run through the same pin functions in a child process (a broken
+index may crash it, which also counts as caught).
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle.build import SOURCE, build_oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+MUTANTS = {
+    "paged_offset_sign": ("continue; }\n            slot_mapping[t] = physical * block_size + offset;",
+                          "continue; }\n            slot_mapping[t] = physical * block_size - offset;"),
+    "ranges_offset_dropped": ("else slot_mapping[t] = physical * block_size + offset;",
+                              "else slot_mapping[t] = physical * block_size;"),
+    "offset_is_quotient": ("int64_t offset = p % block_size;\n            if (logical >= bound)",
+                           "int64_t offset = p / block_size;\n            if (logical >= bound)"),
+    "bound_off_by_one": ("if (logical >= bound) continue;", "if (logical > bound) continue;"),
+    "table_transposed": ("block_table[(int64_t)r * table_stride + logical]",
+                         "block_table[(int64_t)logical * table_stride + r]"),
+    "range_sign": ("(int64_t)range_start[k] + (logical - cum)",
+                   "(int64_t)range_start[k] + (cum - logical)"),
+    "range_end_inclusive": ("if (cum <= logical && logical < cum + len) {",
+                            "if (cum <= logical && logical <= cum + len) {"),
+    "range_drops_cum": ("(int64_t)range_start[k] + (logical - cum)",
+                        "(int64_t)range_start[k] + logical"),
+    "expansion_drops_factor": ("if (expandable(id, k)) v = id * k + j;",
+                               "if (expandable(id, k)) v = id + j;"),
+    "expansion_tail_not_null": ("for (int64_t c = 0; c < out_stride; ++c) out[(int64_t)r * out_stride + c] = 0;",
+                                "for (int64_t c = 0; c < out_stride; ++c) out[(int64_t)r * out_stride + c] = 1;"),
+    "coord_swaps_B_T": ("return (layer * num_blocks + block) * block_size + token;",
+                        "return (layer * block_size + block) * num_blocks + token;"),
+    "kv_drops_layer_term": ("int64_t src = layer * kv_layer_stride + t * kv_token_stride;",
+                            "int64_t src = t * kv_token_stride;"),
+    "tail_not_padded": ("for (int64_t t = 0; t < max_num_tokens; ++t) slot_mapping[t] = ORC_PAD_ID;\n    int64_t num_tokens = num_tokens_of(qsl, num_reqs, max_num_tokens, &flags);\n\n    for (int32_t r = 0; r < num_reqs; ++r) {\n        int64_t bound",
+                        "for (int64_t t = 0; t < max_num_tokens; ++t) slot_mapping[t] = 0;\n    int64_t num_tokens = num_tokens_of(qsl, num_reqs, max_num_tokens, &flags);\n\n    for (int32_t r = 0; r < num_reqs; ++r) {\n        int64_t bound"),
+    "request_end_inclusive": ("for (int64_t t = qsl[r]; t < qsl[r + 1] && t < num_tokens; ++t) {\n            int64_t p = positions[t];\n            if (p < 0) continue;                       /* pad id */",
+                              "for (int64_t t = qsl[r]; t <= qsl[r + 1] && t < num_tokens; ++t) {\n            int64_t p = positions[t];\n            if (p < 0) continue;                       /* pad id */"),
+    "negative_position_kept": ("if (p < 0) continue;                       /* pad id */",
+                               "if (p < -1) continue;                      /* pad id */"),
+    "pad_rows_written": ("if (s < 0) continue;                         /* padded token: no write */",
+                         "if (s < 0) s = 0;                            /* padded token: no write */"),
+}
+
+CHILD = r"""
+import sys
+sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+import oracle, oracle_pins as P
+from workloads import small_cases
+orc = oracle.Oracle({lib!r})
+small = [w for w in small_cases() if w.name in ("tiny_prefill", "small_bs8", "small_layers",
+         "small_out_of_range", "small_dummy", "small_row256", "small_long_r4")]
+P.all_pins(orc, small)
+print("ALL PINS PASSED")
+"""
+
+
+def test_unmutated_copy_passes(tmp_path):
+    lib = str(tmp_path / "liboracle_copy.so")
+    build_oracle(output=lib)
+    r = subprocess.run([sys.executable, "-c", CHILD.format(root=ROOT, tests=HERE, lib=lib)],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "ALL PINS PASSED" in r.stdout, r.stderr[-2000:]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    src = open(SOURCE).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(old, new))
+    lib = str(tmp_path / "liboracle_mut.so")
+    build_oracle(output=lib, source=str(mutated), extra_flags=("-Wno-error",))
+    r = subprocess.run([sys.executable, "-c", CHILD.format(root=ROOT, tests=HERE, lib=lib)],
+                       capture_output=True, text=True, timeout=300)
+    assert "ALL PINS PASSED" not in r.stdout, f"mutant {name} survived every pin"
