@@ -1,0 +1,234 @@
+/*
+ * kvw.h -- paged KV-cache write path for AMD Instinct MI355X (gfx950).
+ *
+ * The write path turns every scheduled token's position into a physical
+ * cache slot ("slot mapping") and copies the token's K and V rows into the
+ * paged cache at that slot.  Sources (cited by page title and section):
+ *
+ *  [P1] "Range-addressed KV cache blocks for the vLLM serving engine":
+ *       "The Innovation: Range Arithmetic Replaces the Per-Position Gather"
+ *       (the two slot-mapping strategies, pad id for positions outside every
+ *       range) and "The Coordinate Approach" (cache coordinates).
+ *  [P2] "Blocktabelle: Abbildung von logischen Token auf physische
+ *       KV-Blocks": "Verantwortung" (block table shape, slot_mapping),
+ *       "Entwurfsmotivation" (manager/kernel block sizes, the slot-mapping
+ *       kernel), "Datenfluss" (kernel arguments, tail padding for graph
+ *       replay) and "Grenzen und Fehler" (rejected block-size pairs).
+ *  [P3] "vLLM Block Table Management: From PagedAttention to the V1 KV Cache
+ *       Stack": Deep Dive sections 7 (worker-side block table) and 8
+ *       (slot_mapping: token -> physical slot).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array arguments are DEVICE pointers owned by the caller; the
+ *    library allocates no memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *    Every call is asynchronous: it validates host-side scalars, enqueues
+ *    its kernels on `stream` and returns.  No call synchronizes.
+ *  - Launch shapes depend only on host scalars (max_num_tokens, row counts,
+ *    strides, layer count), never on device data, so a call can be captured
+ *    into a HIP graph once and replayed with new device contents.
+ *  - Errors: a non-KVW_OK status means nothing was enqueued, except
+ *    KVW_ERR_HIP after a failed launch; kvw_last_error() then describes it.
+ *    Conditions that depend on device data are never synchronized on: the
+ *    kernels clamp or skip as documented and OR a KVW_FLAG_* bit into
+ *    `*err_flag` (a device int32, may be NULL; never cleared by the library).
+ *  - Token ranges: request r owns tokens [query_start_loc[r],
+ *    query_start_loc[r+1]); num_tokens = query_start_loc[num_reqs] is read on
+ *    the device.  query_start_loc must be non-decreasing (not checked).
+ *  - Pad id: KVW_PAD_ID (-1) marks a token without a slot: tokens at or past
+ *    num_tokens, tokens of no request, negative positions, positions past
+ *    the blocks a request owns ([P3] section 8; [P2] "Datenfluss").
+ */
+#ifndef KVW_H
+#define KVW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVW_ABI_VERSION 1
+#define KVW_PAD_ID (-1)
+/* Largest accepted range_stride (range descriptors per request). */
+#define KVW_MAX_RANGE_STRIDE 65536
+
+typedef enum kvw_status {
+    KVW_OK = 0,
+    KVW_ERR_INVALID_ARG = 1, /* a host-side argument is out of its domain */
+    KVW_ERR_UNSUPPORTED = 2, /* a well-formed request this build does not handle */
+    KVW_ERR_RANGE_CAP = 3,   /* range_stride above KVW_MAX_RANGE_STRIDE */
+    KVW_ERR_HIP = 4          /* the HIP runtime reported an error */
+} kvw_status;
+
+/* Sticky bits OR-ed into *err_flag by the kernels. */
+#define KVW_FLAG_NUM_TOKENS 1 /* query_start_loc[num_reqs] outside [0, max_num_tokens]; clamped */
+#define KVW_FLAG_COUNT 2      /* a per-request block or range count outside [0, stride]; clamped */
+#define KVW_FLAG_BAD_BLOCK 4  /* a resolved physical block id is negative (token gets the pad id),
+                                 or an id cannot be expanded within int32 (written as block 0) */
+#define KVW_FLAG_SLOT_OOB 8   /* a slot at or past num_blocks*block_size: its write is skipped */
+
+/* Slot sources of kvw_kv_write. */
+#define KVW_SLOTS_PRECOMPUTED 0 /* read slot_mapping_in */
+#define KVW_SLOTS_PAGED 1       /* resolve through the block table (fused) */
+#define KVW_SLOTS_RANGES 2      /* resolve through range descriptors (fused) */
+
+/* KVW_ABI_VERSION of the loaded library. */
+int32_t kvw_abi_version(void);
+
+/* Message for the last non-KVW_OK status returned on the calling thread. */
+const char *kvw_last_error(void);
+
+/*
+ * Paged slot mapping ([P2] "Entwurfsmotivation" and "Datenfluss"; [P3]
+ * section 8).  For token t < num_tokens of request r at position p >= 0:
+ *   lb = p / block_size, off = p % block_size,
+ *   slot_mapping[t] = block_table[r][lb] * block_size + off
+ * when lb < num_blocks_per_req[r] (or lb < block_table_stride when
+ * num_blocks_per_req is NULL), else KVW_PAD_ID.  Every t in
+ * [num_tokens, max_num_tokens) is KVW_PAD_ID.
+ *
+ *   query_start_loc    int32[num_reqs + 1]
+ *   positions          int64[max_num_tokens]; entries past num_tokens unread
+ *   block_table        int32[max_num_reqs][block_table_stride], row-major;
+ *                      row r holds request r's physical block ids in
+ *                      logical order
+ *   num_blocks_per_req int32[max_num_reqs] or NULL
+ *   slot_mapping       int64[max_num_tokens] (output)
+ * Flags: KVW_FLAG_NUM_TOKENS, KVW_FLAG_COUNT, KVW_FLAG_BAD_BLOCK.
+ * Errors: KVW_ERR_INVALID_ARG for NULL required pointers, misaligned
+ * pointers, negative sizes, block_size <= 0 or max_num_tokens >= 2^31.
+ */
+kvw_status kvw_slot_mapping_paged(const int32_t *query_start_loc, int32_t num_reqs,
+                                  const int64_t *positions, int64_t max_num_tokens,
+                                  const int32_t *block_table, int32_t block_table_stride,
+                                  const int32_t *num_blocks_per_req, int32_t block_size,
+                                  int64_t *slot_mapping, int32_t *err_flag, void *stream);
+
+/*
+ * Range-arithmetic slot mapping ([P1] "The Innovation").  Request r owns
+ * num_ranges[r] contiguous runs; run i starts at physical block
+ * range_start[r][i], spans range_len[r][i] blocks and covers the logical
+ * blocks [range_cum[r][i], range_cum[r][i] + range_len[r][i]).  For token t
+ * of request r at position p >= 0 with lb = p / block_size:
+ *   slot_mapping[t] = (range_start[r][i] + lb - range_cum[r][i]) * block_size
+ *                     + p % block_size
+ * for the run i containing lb, else KVW_PAD_ID; the tail is padded as in
+ * kvw_slot_mapping_paged.  Precondition (not checked on the device):
+ * range_len >= 1 and range_cum is the exclusive prefix sum of range_len
+ * within each request.  Given the same physical layout, the result equals
+ * kvw_slot_mapping_paged through the materialized table.
+ *
+ *   range_start, range_len, range_cum  int32[max_num_reqs][range_stride]
+ *   num_ranges                         int32[max_num_reqs]
+ * Flags: KVW_FLAG_NUM_TOKENS, KVW_FLAG_COUNT (num_ranges clamped to
+ * [0, range_stride]), KVW_FLAG_BAD_BLOCK.
+ * Errors: as kvw_slot_mapping_paged, plus KVW_ERR_RANGE_CAP when
+ * range_stride > KVW_MAX_RANGE_STRIDE.
+ */
+kvw_status kvw_slot_mapping_ranges(const int32_t *query_start_loc, int32_t num_reqs,
+                                   const int64_t *positions, int64_t max_num_tokens,
+                                   const int32_t *range_start, const int32_t *range_len,
+                                   const int32_t *range_cum, const int32_t *num_ranges,
+                                   int32_t range_stride, int32_t block_size,
+                                   int64_t *slot_mapping, int32_t *err_flag, void *stream);
+
+/*
+ * Manager-to-kernel block expansion ([P2] "Entwurfsmotivation" and
+ * "Grenzen und Fehler"; [P3] section 7).  With k = block_size /
+ * kernel_block_size, each manager block b becomes kernel blocks
+ * b*k .. b*k+k-1 (the same memory at the finer block size):
+ *   out[r][i*k + j] = ids[r][i] * k + j   for i < counts[r], j < k,
+ *   out[r][c] = 0 (the null block)         for c >= counts[r] * k.
+ *   ids    int32[rows][in_stride]; counts int32[rows] or NULL (full rows)
+ *   out    int32[rows][out_stride] (output), out_stride >= in_stride * k
+ * Flags: KVW_FLAG_COUNT, KVW_FLAG_BAD_BLOCK (id < 0 or id*k+k-1 > INT32_MAX:
+ * written as 0).
+ * Errors: KVW_ERR_INVALID_ARG when kernel_block_size does not divide
+ * block_size (or either is <= 0), or out_stride < in_stride * k.
+ */
+kvw_status kvw_map_to_kernel_blocks(const int32_t *ids, const int32_t *counts, int32_t rows,
+                                    int32_t in_stride, int32_t block_size,
+                                    int32_t kernel_block_size, int32_t *out, int32_t out_stride,
+                                    int32_t *err_flag, void *stream);
+
+/*
+ * The same expansion for range descriptors: a manager run (start, len,
+ * cum) is the kernel run (start*k, len*k, cum*k).  out_num_ranges[r] =
+ * num_ranges[r] clamped to [0, range_stride]; descriptor entries past it
+ * are written 0.  All arrays are [rows][range_stride] (num_ranges: [rows]).
+ * Flags and errors as kvw_map_to_kernel_blocks (plus KVW_ERR_RANGE_CAP).
+ */
+kvw_status kvw_map_ranges_to_kernel_blocks(const int32_t *range_start, const int32_t *range_len,
+                                           const int32_t *range_cum, const int32_t *num_ranges,
+                                           int32_t rows, int32_t range_stride, int32_t block_size,
+                                           int32_t kernel_block_size, int32_t *out_start,
+                                           int32_t *out_len, int32_t *out_cum,
+                                           int32_t *out_num_ranges, int32_t *err_flag,
+                                           void *stream);
+
+/*
+ * Arguments of kvw_kv_write.  Byte strides; every pointer of key, value,
+ * k_cache, v_cache and every stride must be a multiple of 16.
+ */
+typedef struct kvw_kv_write_args {
+    int32_t mode;                      /* KVW_SLOTS_* */
+    int32_t num_reqs;                  /* PAGED/RANGES */
+    const int32_t *query_start_loc;    /* PAGED/RANGES: int32[num_reqs + 1] */
+    const int64_t *positions;          /* PAGED/RANGES: int64[max_num_tokens] */
+    int64_t max_num_tokens;            /* token rows of key/value and slot mappings */
+    const int64_t *slot_mapping_in;    /* PRECOMPUTED: int64[max_num_tokens] */
+    int64_t *slot_mapping_out;         /* PAGED/RANGES: int64[max_num_tokens] or NULL */
+    const int32_t *block_table;        /* PAGED: as kvw_slot_mapping_paged */
+    const int32_t *num_blocks_per_req; /* PAGED: or NULL */
+    int32_t block_table_stride;        /* PAGED */
+    int32_t range_stride;              /* RANGES */
+    const int32_t *range_start;        /* RANGES: as kvw_slot_mapping_ranges */
+    const int32_t *range_len;
+    const int32_t *range_cum;
+    const int32_t *num_ranges;
+    int32_t block_size;                /* T: token slots per cache block */
+    int32_t num_layers;                /* L */
+    int64_t num_blocks;                /* B: cache blocks per layer */
+    const void *key;                   /* row of token t, layer l at key + l*kv_layer_stride
+                                          + t*kv_token_stride, bytes_per_token bytes */
+    const void *value;                 /* same layout as key */
+    int64_t kv_layer_stride;
+    int64_t kv_token_stride;
+    void *k_cache;                     /* [L][B][T] rows of bytes_per_token bytes */
+    void *v_cache;                     /* same layout as k_cache */
+    int64_t bytes_per_token;           /* multiple of 16 */
+    int32_t *err_flag;                 /* device int32 or NULL */
+} kvw_kv_write_args;
+
+/* sizeof(kvw_kv_write_args) as compiled into the library. */
+size_t kvw_kv_write_args_size(void);
+
+/*
+ * K/V scatter through the slot mapping, optionally fused with it ([P2]
+ * "Verantwortung": attention writes each token's KV at its slot; [P1] "The
+ * Coordinate Approach": coordinates n(layer, block, token) =
+ * (layer*B + block)*T + token, byte offset n*bytes_per_token).
+ * For every layer l < L and token t < max_num_tokens whose slot s (read
+ * from slot_mapping_in, or resolved as in kvw_slot_mapping_paged /
+ * kvw_slot_mapping_ranges) satisfies 0 <= s < B*T:
+ *   k_cache + n*bytes_per_token <- key row (l, t),  v_cache likewise,
+ *   with n = (l*B + s/T)*T + s%T.
+ * A slot >= B*T is skipped (KVW_FLAG_SLOT_OOB); the pad id writes nothing.
+ * No other cache byte is touched.  In the fused modes the slots are also
+ * stored to slot_mapping_out when it is non-NULL (tail padded).
+ * Precondition: no two tokens share a slot (else the surviving row is
+ * unspecified).
+ * Errors: KVW_ERR_INVALID_ARG for an unknown mode, NULL required pointers,
+ * misalignment, negative sizes, bytes_per_token % 16 != 0, or a cache size
+ * beyond int64; KVW_ERR_RANGE_CAP as kvw_slot_mapping_ranges.
+ */
+kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVW_H */

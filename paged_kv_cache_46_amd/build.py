@@ -1,0 +1,47 @@
+"""Build libkvw.so (the HIP library behind include/kvw.h) for gfx950 with hipcc.
+
+Usage: python -m paged_kv_cache_46_amd.build [extra hipcc flags...]
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SOURCE = os.path.join(PKG, "csrc", "kvw.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIBRARY = os.path.join(PKG, "libkvw.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found: the ROCm toolchain is required to build libkvw.so")
+    return path
+
+
+def build_library(verbose: bool = False, extra_flags: tuple = (), output: str = LIBRARY) -> str:
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Wall", "-Wextra",
+           # never let the compiler form packed fp32 instructions (none are wanted here)
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-I", INCLUDE, *extra_flags, "-o", output + ".tmp", SOURCE]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(ln for ln in r.stderr.splitlines() if noise not in ln)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+    os.replace(output + ".tmp", output)
+    return output
+
+
+if __name__ == "__main__":
+    print(build_library(verbose=True, extra_flags=tuple(sys.argv[1:])))

@@ -1,0 +1,696 @@
+// Paged KV-cache write path for MI355X (gfx950, CDNA4, wave64).
+//
+// Kernels:
+//   slot_mapping_kernel<MODE>  token-parallel slot resolution (paged gather or
+//                              range arithmetic), tail padded with the pad id;
+//   kv_write_kernel<MODE,...>  K/V scatter into the paged cache, optionally
+//                              fused with the slot resolution;
+//   expand_blocks_kernel,
+//   expand_ranges_kernel       manager-to-kernel block expansion.
+// The host functions at the bottom validate host-side scalars and launch on
+// the caller's stream; see include/kvw.h for the contract.
+//
+// Sources: "Range-addressed KV cache blocks for the vLLM serving engine"
+// ("The Innovation", "The Coordinate Approach"); "Blocktabelle: Abbildung
+// von logischen Token auf physische KV-Blocks" ("Entwurfsmotivation",
+// "Datenfluss", "Grenzen und Fehler"); "vLLM Block Table Management"
+// (Deep Dive sections 7 and 8).
+//
+// The path is a memory-bound gather/scatter: no matrix cores are involved.
+// Design notes:
+//  * Token-tiled grids instead of one program per request: a batch mixing
+//    8192-token prefill chunks with single decode tokens keeps every wave
+//    equally loaded.  A token finds its request by binary search over
+//    query_start_loc.
+//  * Each wave resolves the slots of its tile with one token per lane, then
+//    copies the tile's rows: one 2 KiB row (8 heads x 128 bf16) is two
+//    64-lane x 16-byte vector accesses, so every load and store instruction
+//    moves a fully used 1 KiB span.  Several rows are loaded before any is
+//    stored to keep enough bytes in flight per wave.
+//  * All cache addressing is 64-bit: a 32-layer cache plane reaches 32 GiB.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "kvw.h"
+
+#ifndef KVW_TOKENS_PER_WAVE
+#define KVW_TOKENS_PER_WAVE 32
+#endif
+#ifndef KVW_ROWS_IN_FLIGHT
+#define KVW_ROWS_IN_FLIGHT 4
+#endif
+#ifndef KVW_LAYERS_PER_WAVE
+#define KVW_LAYERS_PER_WAVE 4
+#endif
+#ifndef KVW_NT_LOADS
+#define KVW_NT_LOADS 1
+#endif
+#ifndef KVW_NT_STORES
+#define KVW_NT_STORES 1
+#endif
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kBlockThreads = 256;
+constexpr int kWavesPerBlock = kBlockThreads / kWave;
+constexpr int kSliceBytes = kWave * 16;  // one wave-wide 16-byte access
+constexpr int kMaxGridY = 65535;
+
+enum : int { kPrecomputed = KVW_SLOTS_PRECOMPUTED, kPaged = KVW_SLOTS_PAGED, kRanges = KVW_SLOTS_RANGES };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Everything the slot resolution reads.
+struct MapArgs {
+    const int32_t *qsl;
+    const int64_t *positions;
+    const int32_t *block_table;
+    const int32_t *num_blocks_per_req;
+    const int32_t *range_start;
+    const int32_t *range_len;
+    const int32_t *range_cum;
+    const int32_t *num_ranges;
+    const int64_t *slots_in;
+    int64_t *slots_out;
+    int32_t *err_flag;
+    int64_t max_num_tokens;
+    int32_t num_reqs;
+    int32_t table_stride;
+    int32_t range_stride;
+    int32_t block_size;
+};
+
+// Everything the K/V copy touches.
+struct CopyArgs {
+    const uint8_t *key;
+    const uint8_t *value;
+    uint8_t *k_cache;
+    uint8_t *v_cache;
+    int64_t kv_layer_stride;
+    int64_t kv_token_stride;
+    int64_t rows_per_layer;  // B * T
+    int64_t bytes_per_token;
+    int32_t num_layers;
+    int32_t layers_per_wave;
+};
+
+__device__ __forceinline__ void raise_flags(int32_t *err, uint32_t flags)
+{
+    if (err && flags) atomicOr(err, static_cast<int>(flags));
+}
+
+// num_tokens = query_start_loc[num_reqs], clamped to [0, max_num_tokens].
+__device__ __forceinline__ int64_t device_num_tokens(const MapArgs &a, bool report)
+{
+    int64_t n = a.qsl[a.num_reqs];
+    uint32_t f = 0;
+    if (n < 0) { n = 0; f = KVW_FLAG_NUM_TOKENS; }
+    if (n > a.max_num_tokens) { n = a.max_num_tokens; f = KVW_FLAG_NUM_TOKENS; }
+    if (report) raise_flags(a.err_flag, f);
+    return n;
+}
+
+// Largest r in [0, num_reqs) with qsl[r] <= t, or -1.  With a
+// non-decreasing qsl and t < qsl[num_reqs] this is the request owning t
+// (empty requests are skipped because the last equal entry wins).
+__device__ __forceinline__ int32_t find_request(const int32_t *qsl, int32_t num_reqs, int64_t t)
+{
+    if (num_reqs <= 0 || qsl[0] > t) return -1;
+    int32_t lo = 0, hi = num_reqs;
+    while (hi - lo > 1) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (qsl[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ int64_t clamp_count(int32_t c, int32_t stride, uint32_t &flags)
+{
+    if (c < 0) { flags |= KVW_FLAG_COUNT; return 0; }
+    if (c > stride) { flags |= KVW_FLAG_COUNT; return stride; }
+    return c;
+}
+
+// Paged gather: one table load per position.
+__device__ __forceinline__ int64_t paged_block(const MapArgs &a, int32_t r, int64_t lb,
+                                               uint32_t &flags)
+{
+    int64_t bound = a.table_stride;
+    if (a.num_blocks_per_req) bound = clamp_count(a.num_blocks_per_req[r], a.table_stride, flags);
+    if (lb >= bound) return -1;
+    const int32_t b = a.block_table[static_cast<int64_t>(r) * a.table_stride + lb];
+    if (b < 0) { flags |= KVW_FLAG_BAD_BLOCK; return -1; }
+    return b;
+}
+
+// Range arithmetic: the run whose [cum, cum + len) holds lb, found by binary
+// search over the (strictly increasing) cum column of the request.
+__device__ __forceinline__ int64_t range_block(const MapArgs &a, int32_t r, int64_t lb,
+                                               uint32_t &flags)
+{
+    const int64_t n = clamp_count(a.num_ranges[r], a.range_stride, flags);
+    if (n == 0) return -1;
+    const int64_t row = static_cast<int64_t>(r) * a.range_stride;
+    const int32_t *cum = a.range_cum + row;
+    if (lb < cum[0]) return -1;
+    int32_t lo = 0, hi = static_cast<int32_t>(n);
+    while (hi - lo > 1) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (cum[mid] <= lb) lo = mid; else hi = mid;
+    }
+    const int64_t c = cum[lo];
+    if (lb >= c + a.range_len[row + lo]) return -1;
+    const int64_t b = static_cast<int64_t>(a.range_start[row + lo]) + (lb - c);
+    if (b < 0) { flags |= KVW_FLAG_BAD_BLOCK; return -1; }
+    return b;
+}
+
+// Slot of token t (fused modes), or the pad id.
+template <int MODE>
+__device__ __forceinline__ int64_t resolve_slot(const MapArgs &a, int64_t t, int64_t num_tokens,
+                                                uint32_t &flags)
+{
+    if (MODE == kPrecomputed) return a.slots_in[t];
+    if (t >= num_tokens) return KVW_PAD_ID;
+    const int32_t r = find_request(a.qsl, a.num_reqs, t);
+    if (r < 0) return KVW_PAD_ID;
+    const int64_t p = a.positions[t];
+    if (p < 0) return KVW_PAD_ID;
+    const int32_t bs = a.block_size;
+    int64_t lb;
+    int32_t off;
+    if (p <= INT32_MAX) {
+        const uint32_t q = static_cast<uint32_t>(p) / static_cast<uint32_t>(bs);
+        lb = q;
+        off = static_cast<int32_t>(static_cast<uint32_t>(p) - q * static_cast<uint32_t>(bs));
+    } else {
+        lb = p / bs;
+        off = static_cast<int32_t>(p - lb * bs);
+    }
+    const int64_t b = (MODE == kPaged) ? paged_block(a, r, lb, flags) : range_block(a, r, lb, flags);
+    if (b < 0) return KVW_PAD_ID;
+    return b * bs + off;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
+{
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x;
+    if (t >= a.max_num_tokens) return;
+    const int64_t num_tokens = device_num_tokens(a, t == 0);
+    uint32_t flags = 0;
+    a.slots_out[t] = resolve_slot<MODE>(a, t, num_tokens, flags);
+    raise_flags(a.err_flag, flags);
+}
+
+__device__ __forceinline__ int64_t wave_bcast64(int64_t v, int lane)
+{
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), lane);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint64_t>(v) >> 32), lane);
+    return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
+                                static_cast<uint32_t>(lo));
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const uint8_t *p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    else return *reinterpret_cast<const u32x4 *>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(uint8_t *p, u32x4 v)
+{
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+    else *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// One wave owns TPW consecutive tokens and LPW consecutive layers
+// (blockIdx.y).  Lane i < TPW resolves token t0 + i; the copy then walks the
+// tile U rows at a time, each row's slot broadcast from its lane.  CH is the
+// number of 1 KiB slices of a row held per lane (rows longer than CH KiB
+// are walked in segments).
+template <int MODE, int TPW, int U, int CH>
+__global__ __launch_bounds__(kBlockThreads) void kv_write_kernel(MapArgs a, CopyArgs c)
+{
+    static_assert(TPW >= 1 && TPW <= kWave, "one token per lane");
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x / kWave);
+    const int64_t t0 = wave * TPW;
+    if (t0 >= a.max_num_tokens) return;  // whole wave leaves together
+    const int64_t left = a.max_num_tokens - t0;
+    const int ntok = static_cast<int>(left < TPW ? left : TPW);
+    const bool first_layer_group = blockIdx.y == 0;
+
+    uint32_t flags = 0;
+    int64_t slot = KVW_PAD_ID;
+    if (lane < ntok) {
+        const int64_t t = t0 + lane;
+        int64_t num_tokens = 0;
+        if (MODE != kPrecomputed) num_tokens = device_num_tokens(a, first_layer_group && t == 0);
+        slot = resolve_slot<MODE>(a, t, num_tokens, flags);
+        if (MODE != kPrecomputed && a.slots_out && first_layer_group) a.slots_out[t] = slot;
+        if (slot >= c.rows_per_layer) {
+            if (c.num_layers > 0) flags |= KVW_FLAG_SLOT_OOB;
+            slot = KVW_PAD_ID;
+        }
+        if (slot < 0) slot = KVW_PAD_ID;
+    }
+    if (!first_layer_group) flags = 0;  // report each condition from one layer group only
+    raise_flags(a.err_flag, flags);
+
+    const int l_begin = blockIdx.y * c.layers_per_wave;
+    const int l_end = min(c.num_layers, l_begin + c.layers_per_wave);
+    const int64_t bpt = c.bytes_per_token;
+    const int64_t lane_off = static_cast<int64_t>(lane) * 16;
+
+    for (int l = l_begin; l < l_end; ++l) {
+        const uint8_t *ksrc = c.key + l * c.kv_layer_stride + t0 * c.kv_token_stride + lane_off;
+        const uint8_t *vsrc = c.value + l * c.kv_layer_stride + t0 * c.kv_token_stride + lane_off;
+        uint8_t *kdst = c.k_cache + static_cast<int64_t>(l) * c.rows_per_layer * bpt + lane_off;
+        uint8_t *vdst = c.v_cache + static_cast<int64_t>(l) * c.rows_per_layer * bpt + lane_off;
+        for (int k0 = 0; k0 < ntok; k0 += U) {
+            int64_t s[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) s[u] = (k0 + u < ntok) ? wave_bcast64(slot, k0 + u) : -1;
+            for (int64_t seg = 0; seg < bpt; seg += CH * kSliceBytes) {
+                u32x4 kr[U][CH], vr[U][CH];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (s[u] < 0) continue;
+                    const int64_t src = (k0 + u) * c.kv_token_stride + seg;
+#pragma unroll
+                    for (int ch = 0; ch < CH; ++ch) {
+                        if (seg + lane_off + ch * kSliceBytes < bpt) {
+                            kr[u][ch] = load16<KVW_NT_LOADS>(ksrc + src + ch * kSliceBytes);
+                            vr[u][ch] = load16<KVW_NT_LOADS>(vsrc + src + ch * kSliceBytes);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (s[u] < 0) continue;
+                    // coordinate n = (l*B + s/T)*T + s%T = l*B*T + s (the layer base is in kdst)
+                    const int64_t dst = s[u] * bpt + seg;
+#pragma unroll
+                    for (int ch = 0; ch < CH; ++ch) {
+                        if (seg + lane_off + ch * kSliceBytes < bpt) {
+                            store16<KVW_NT_STORES>(kdst + dst + ch * kSliceBytes, kr[u][ch]);
+                            store16<KVW_NT_STORES>(vdst + dst + ch * kSliceBytes, vr[u][ch]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ bool expandable(int64_t id, int64_t k)
+{
+    return id >= 0 && id * k + (k - 1) <= INT32_MAX;
+}
+
+// out[r][q] for q = i*k + j: ids[r][i]*k + j while i < count[r], else 0.
+__global__ __launch_bounds__(kBlockThreads) void expand_blocks_kernel(
+    const int32_t *ids, const int32_t *counts, int32_t rows, int32_t in_stride, int32_t k,
+    int32_t *out, int32_t out_stride, int32_t *err_flag)
+{
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x;
+    if (idx >= static_cast<int64_t>(rows) * out_stride) return;
+    const int32_t r = static_cast<int32_t>(idx / out_stride);
+    const int32_t q = static_cast<int32_t>(idx - static_cast<int64_t>(r) * out_stride);
+    const int32_t i = q / k, j = q - (q / k) * k;
+    uint32_t flags = 0;
+    const int64_t count = counts ? clamp_count(counts[r], in_stride, flags) : in_stride;
+    int32_t v = 0;
+    if (i < count) {
+        const int64_t id = ids[static_cast<int64_t>(r) * in_stride + i];
+        if (expandable(id, k)) v = static_cast<int32_t>(id * k + j);
+        else flags |= KVW_FLAG_BAD_BLOCK;
+    }
+    out[idx] = v;
+    raise_flags(err_flag, flags);
+}
+
+// (start, len, cum) -> (start*k, len*k, cum*k) for i < num_ranges[r]; 0 past it.
+__global__ __launch_bounds__(kBlockThreads) void expand_ranges_kernel(
+    const int32_t *start, const int32_t *len, const int32_t *cum, const int32_t *num_ranges,
+    int32_t rows, int32_t stride, int32_t k, int32_t *o_start, int32_t *o_len, int32_t *o_cum,
+    int32_t *o_num, int32_t *err_flag)
+{
+    const int32_t width = stride > 0 ? stride : 1;
+    const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x;
+    if (idx >= static_cast<int64_t>(rows) * width) return;
+    const int32_t r = static_cast<int32_t>(idx / width);
+    const int32_t i = static_cast<int32_t>(idx - static_cast<int64_t>(r) * width);
+    uint32_t flags = 0;
+    const int64_t n = clamp_count(num_ranges[r], stride, flags);
+    if (i == 0) o_num[r] = static_cast<int32_t>(n);
+    else flags = 0;  // the count is reported once per row
+    if (i < stride) {
+        const int64_t q = static_cast<int64_t>(r) * stride + i;
+        int32_t s = 0, l = 0, c = 0;
+        if (i < n) {
+            if (expandable(start[q], k) && expandable(len[q], k) && expandable(cum[q], k)) {
+                s = start[q] * k;
+                l = len[q] * k;
+                c = cum[q] * k;
+            } else {
+                flags |= KVW_FLAG_BAD_BLOCK;
+            }
+        }
+        o_start[q] = s;
+        o_len[q] = l;
+        o_cum[q] = c;
+    }
+    raise_flags(err_flag, flags);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+thread_local char g_last_error[512] = "";
+
+kvw_status fail(kvw_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+kvw_status launched(const char *what)
+{
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(KVW_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return KVW_OK;
+}
+
+unsigned grid_for(int64_t items, int64_t per_block)
+{
+    return static_cast<unsigned>((items + per_block - 1) / per_block);
+}
+
+#define KVW_REQUIRE(cond, ...)                                 \
+    do {                                                       \
+        if (!(cond)) return fail(KVW_ERR_INVALID_ARG, __VA_ARGS__); \
+    } while (0)
+
+// Checks shared by both slot-mapping calls and the fused write.
+kvw_status check_mapping_common(const char *fn, const int32_t *qsl, int32_t num_reqs,
+                                const int64_t *positions, int64_t max_num_tokens,
+                                int32_t block_size, const int32_t *err_flag)
+{
+    KVW_REQUIRE(max_num_tokens >= 0 && max_num_tokens <= INT32_MAX,
+                "%s: max_num_tokens %lld outside [0, 2^31)", fn, (long long)max_num_tokens);
+    KVW_REQUIRE(num_reqs >= 0, "%s: num_reqs %d is negative", fn, num_reqs);
+    KVW_REQUIRE(block_size > 0, "%s: block_size %d must be positive", fn, block_size);
+    KVW_REQUIRE(!err_flag || aligned(err_flag, 4), "%s: err_flag misaligned", fn);
+    if (max_num_tokens == 0) return KVW_OK;
+    KVW_REQUIRE(qsl && aligned(qsl, 4), "%s: query_start_loc is NULL or misaligned", fn);
+    KVW_REQUIRE(positions && aligned(positions, 8), "%s: positions is NULL or misaligned", fn);
+    return KVW_OK;
+}
+
+kvw_status check_paged(const char *fn, int32_t num_reqs, const int32_t *block_table,
+                       int32_t stride, const int32_t *num_blocks_per_req)
+{
+    KVW_REQUIRE(stride >= 0, "%s: block_table_stride %d is negative", fn, stride);
+    KVW_REQUIRE(!(num_reqs > 0 && stride > 0) || block_table, "%s: block_table is NULL", fn);
+    KVW_REQUIRE(!block_table || aligned(block_table, 4), "%s: block_table misaligned", fn);
+    KVW_REQUIRE(!num_blocks_per_req || aligned(num_blocks_per_req, 4),
+                "%s: num_blocks_per_req misaligned", fn);
+    return KVW_OK;
+}
+
+kvw_status check_ranges(const char *fn, int32_t num_reqs, const int32_t *start, const int32_t *len,
+                        const int32_t *cum, const int32_t *num_ranges, int32_t stride)
+{
+    KVW_REQUIRE(stride >= 0, "%s: range_stride %d is negative", fn, stride);
+    if (stride > KVW_MAX_RANGE_STRIDE)
+        return fail(KVW_ERR_RANGE_CAP, "%s: range_stride %d exceeds the cap of %d", fn, stride,
+                    KVW_MAX_RANGE_STRIDE);
+    if (num_reqs > 0) {
+        KVW_REQUIRE(start && len && cum && num_ranges, "%s: a range descriptor array is NULL", fn);
+        KVW_REQUIRE(aligned(start, 4) && aligned(len, 4) && aligned(cum, 4) && aligned(num_ranges, 4),
+                    "%s: a range descriptor array is misaligned", fn);
+    }
+    return KVW_OK;
+}
+
+MapArgs make_map_args(const int32_t *qsl, int32_t num_reqs, const int64_t *positions,
+                      int64_t max_num_tokens, int32_t block_size, int32_t *err_flag)
+{
+    MapArgs a{};
+    a.qsl = qsl;
+    a.num_reqs = num_reqs;
+    a.positions = positions;
+    a.max_num_tokens = max_num_tokens;
+    a.block_size = block_size;
+    a.err_flag = err_flag;
+    return a;
+}
+
+template <int MODE, int TPW, int U, int CH>
+void launch_kv_write(const MapArgs &a, const CopyArgs &c, int64_t max_num_tokens, int32_t groups,
+                     hipStream_t s)
+{
+    const int64_t waves = (max_num_tokens + TPW - 1) / TPW;
+    const dim3 grid(grid_for(waves, kWavesPerBlock), static_cast<unsigned>(groups));
+    hipLaunchKernelGGL((kv_write_kernel<MODE, TPW, U, CH>), grid, dim3(kBlockThreads), 0, s, a, c);
+}
+
+template <int MODE>
+void dispatch_kv_write(const MapArgs &a, const CopyArgs &c, int64_t max_num_tokens, int32_t groups,
+                       hipStream_t s)
+{
+    constexpr int TPW = KVW_TOKENS_PER_WAVE;
+    constexpr int U = KVW_ROWS_IN_FLIGHT;
+    const int64_t slices = (c.bytes_per_token + kSliceBytes - 1) / kSliceBytes;
+    if (slices <= 1) launch_kv_write<MODE, TPW, U, 1>(a, c, max_num_tokens, groups, s);
+    else if (slices == 2) launch_kv_write<MODE, TPW, U, 2>(a, c, max_num_tokens, groups, s);
+    else if (slices == 3) launch_kv_write<MODE, TPW, U, 3>(a, c, max_num_tokens, groups, s);
+    else launch_kv_write<MODE, TPW, (U > 2 ? U / 2 : 1), 4>(a, c, max_num_tokens, groups, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvw_abi_version(void) { return KVW_ABI_VERSION; }
+
+const char *kvw_last_error(void) { return g_last_error; }
+
+size_t kvw_kv_write_args_size(void) { return sizeof(kvw_kv_write_args); }
+
+kvw_status kvw_slot_mapping_paged(const int32_t *query_start_loc, int32_t num_reqs,
+                                  const int64_t *positions, int64_t max_num_tokens,
+                                  const int32_t *block_table, int32_t block_table_stride,
+                                  const int32_t *num_blocks_per_req, int32_t block_size,
+                                  int64_t *slot_mapping, int32_t *err_flag, void *stream)
+{
+    const char *fn = "kvw_slot_mapping_paged";
+    kvw_status st = check_mapping_common(fn, query_start_loc, num_reqs, positions, max_num_tokens,
+                                         block_size, err_flag);
+    if (st != KVW_OK) return st;
+    if ((st = check_paged(fn, num_reqs, block_table, block_table_stride, num_blocks_per_req)) != KVW_OK)
+        return st;
+    if (max_num_tokens == 0) return KVW_OK;
+    KVW_REQUIRE(slot_mapping && aligned(slot_mapping, 8), "%s: slot_mapping is NULL or misaligned", fn);
+    MapArgs a = make_map_args(query_start_loc, num_reqs, positions, max_num_tokens, block_size, err_flag);
+    a.block_table = block_table;
+    a.table_stride = block_table_stride;
+    a.num_blocks_per_req = num_blocks_per_req;
+    a.slots_out = slot_mapping;
+    hipLaunchKernelGGL(slot_mapping_kernel<kPaged>, dim3(grid_for(max_num_tokens, kBlockThreads)),
+                       dim3(kBlockThreads), 0, reinterpret_cast<hipStream_t>(stream), a);
+    return launched(fn);
+}
+
+kvw_status kvw_slot_mapping_ranges(const int32_t *query_start_loc, int32_t num_reqs,
+                                   const int64_t *positions, int64_t max_num_tokens,
+                                   const int32_t *range_start, const int32_t *range_len,
+                                   const int32_t *range_cum, const int32_t *num_ranges,
+                                   int32_t range_stride, int32_t block_size,
+                                   int64_t *slot_mapping, int32_t *err_flag, void *stream)
+{
+    const char *fn = "kvw_slot_mapping_ranges";
+    kvw_status st = check_mapping_common(fn, query_start_loc, num_reqs, positions, max_num_tokens,
+                                         block_size, err_flag);
+    if (st != KVW_OK) return st;
+    if ((st = check_ranges(fn, num_reqs, range_start, range_len, range_cum, num_ranges,
+                           range_stride)) != KVW_OK)
+        return st;
+    if (max_num_tokens == 0) return KVW_OK;
+    KVW_REQUIRE(slot_mapping && aligned(slot_mapping, 8), "%s: slot_mapping is NULL or misaligned", fn);
+    MapArgs a = make_map_args(query_start_loc, num_reqs, positions, max_num_tokens, block_size, err_flag);
+    a.range_start = range_start;
+    a.range_len = range_len;
+    a.range_cum = range_cum;
+    a.num_ranges = num_ranges;
+    a.range_stride = range_stride;
+    a.slots_out = slot_mapping;
+    hipLaunchKernelGGL(slot_mapping_kernel<kRanges>, dim3(grid_for(max_num_tokens, kBlockThreads)),
+                       dim3(kBlockThreads), 0, reinterpret_cast<hipStream_t>(stream), a);
+    return launched(fn);
+}
+
+kvw_status kvw_map_to_kernel_blocks(const int32_t *ids, const int32_t *counts, int32_t rows,
+                                    int32_t in_stride, int32_t block_size,
+                                    int32_t kernel_block_size, int32_t *out, int32_t out_stride,
+                                    int32_t *err_flag, void *stream)
+{
+    const char *fn = "kvw_map_to_kernel_blocks";
+    KVW_REQUIRE(block_size > 0 && kernel_block_size > 0 && block_size % kernel_block_size == 0,
+                "%s: kernel block size %d does not divide block size %d", fn, kernel_block_size,
+                block_size);
+    const int64_t k = block_size / kernel_block_size;
+    KVW_REQUIRE(rows >= 0 && in_stride >= 0, "%s: negative rows or in_stride", fn);
+    KVW_REQUIRE(out_stride >= static_cast<int64_t>(in_stride) * k,
+                "%s: out_stride %d below in_stride*k = %lld", fn, out_stride,
+                (long long)(in_stride * k));
+    KVW_REQUIRE(!err_flag || aligned(err_flag, 4), "%s: err_flag misaligned", fn);
+    const int64_t total = static_cast<int64_t>(rows) * out_stride;
+    if (total == 0) return KVW_OK;
+    KVW_REQUIRE(total <= INT32_MAX, "%s: rows*out_stride too large", fn);
+    KVW_REQUIRE(out && aligned(out, 4), "%s: out is NULL or misaligned", fn);
+    KVW_REQUIRE(in_stride == 0 || (ids && aligned(ids, 4)), "%s: ids is NULL or misaligned", fn);
+    KVW_REQUIRE(!counts || aligned(counts, 4), "%s: counts misaligned", fn);
+    hipLaunchKernelGGL(expand_blocks_kernel, dim3(grid_for(total, kBlockThreads)), dim3(kBlockThreads),
+                       0, reinterpret_cast<hipStream_t>(stream), ids, counts, rows, in_stride,
+                       static_cast<int32_t>(k), out, out_stride, err_flag);
+    return launched(fn);
+}
+
+kvw_status kvw_map_ranges_to_kernel_blocks(const int32_t *range_start, const int32_t *range_len,
+                                           const int32_t *range_cum, const int32_t *num_ranges,
+                                           int32_t rows, int32_t range_stride, int32_t block_size,
+                                           int32_t kernel_block_size, int32_t *out_start,
+                                           int32_t *out_len, int32_t *out_cum,
+                                           int32_t *out_num_ranges, int32_t *err_flag,
+                                           void *stream)
+{
+    const char *fn = "kvw_map_ranges_to_kernel_blocks";
+    KVW_REQUIRE(block_size > 0 && kernel_block_size > 0 && block_size % kernel_block_size == 0,
+                "%s: kernel block size %d does not divide block size %d", fn, kernel_block_size,
+                block_size);
+    const int32_t k = block_size / kernel_block_size;
+    KVW_REQUIRE(rows >= 0 && range_stride >= 0, "%s: negative rows or range_stride", fn);
+    if (range_stride > KVW_MAX_RANGE_STRIDE)
+        return fail(KVW_ERR_RANGE_CAP, "%s: range_stride %d exceeds the cap of %d", fn, range_stride,
+                    KVW_MAX_RANGE_STRIDE);
+    KVW_REQUIRE(!err_flag || aligned(err_flag, 4), "%s: err_flag misaligned", fn);
+    if (rows == 0) return KVW_OK;
+    const int32_t *ins[] = {range_start, range_len, range_cum};
+    const int32_t *outs[] = {out_start, out_len, out_cum};
+    for (int i = 0; i < 3; ++i) {
+        KVW_REQUIRE(range_stride == 0 || (ins[i] && aligned(ins[i], 4)),
+                    "%s: an input descriptor array is NULL or misaligned", fn);
+        KVW_REQUIRE(range_stride == 0 || (outs[i] && aligned(outs[i], 4)),
+                    "%s: an output descriptor array is NULL or misaligned", fn);
+    }
+    KVW_REQUIRE(num_ranges && aligned(num_ranges, 4) && out_num_ranges && aligned(out_num_ranges, 4),
+                "%s: num_ranges or out_num_ranges is NULL or misaligned", fn);
+    const int64_t total = static_cast<int64_t>(rows) * (range_stride > 0 ? range_stride : 1);
+    KVW_REQUIRE(total <= INT32_MAX, "%s: rows*range_stride too large", fn);
+    hipLaunchKernelGGL(expand_ranges_kernel, dim3(grid_for(total, kBlockThreads)), dim3(kBlockThreads),
+                       0, reinterpret_cast<hipStream_t>(stream), range_start, range_len, range_cum,
+                       num_ranges, rows, range_stride, k, out_start, out_len, out_cum,
+                       out_num_ranges, err_flag);
+    return launched(fn);
+}
+
+kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
+{
+    const char *fn = "kvw_kv_write";
+    KVW_REQUIRE(args, "%s: args is NULL", fn);
+    const kvw_kv_write_args &g = *args;
+    KVW_REQUIRE(g.mode == KVW_SLOTS_PRECOMPUTED || g.mode == KVW_SLOTS_PAGED || g.mode == KVW_SLOTS_RANGES,
+                "%s: unknown mode %d", fn, g.mode);
+    KVW_REQUIRE(g.max_num_tokens >= 0 && g.max_num_tokens <= INT32_MAX,
+                "%s: max_num_tokens %lld outside [0, 2^31)", fn, (long long)g.max_num_tokens);
+    KVW_REQUIRE(g.num_layers >= 0, "%s: num_layers is negative", fn);
+    KVW_REQUIRE(g.num_blocks >= 0, "%s: num_blocks is negative", fn);
+    KVW_REQUIRE(g.block_size > 0, "%s: block_size %d must be positive", fn, g.block_size);
+    KVW_REQUIRE(g.bytes_per_token > 0 && g.bytes_per_token % 16 == 0,
+                "%s: bytes_per_token %lld must be a positive multiple of 16", fn,
+                (long long)g.bytes_per_token);
+    KVW_REQUIRE(g.num_blocks <= INT64_MAX / g.block_size, "%s: num_blocks*block_size overflows", fn);
+    const int64_t rows_per_layer = g.num_blocks * g.block_size;
+    KVW_REQUIRE(g.num_layers == 0 || rows_per_layer <= INT64_MAX / g.num_layers / g.bytes_per_token,
+                "%s: cache size overflows int64", fn);
+    KVW_REQUIRE(!g.err_flag || aligned(g.err_flag, 4), "%s: err_flag misaligned", fn);
+
+    kvw_status st = KVW_OK;
+    if (g.mode == KVW_SLOTS_PAGED || g.mode == KVW_SLOTS_RANGES) {
+        st = check_mapping_common(fn, g.query_start_loc, g.num_reqs, g.positions, g.max_num_tokens,
+                                  g.block_size, g.err_flag);
+        if (st != KVW_OK) return st;
+        st = (g.mode == KVW_SLOTS_PAGED)
+                 ? check_paged(fn, g.num_reqs, g.block_table, g.block_table_stride, g.num_blocks_per_req)
+                 : check_ranges(fn, g.num_reqs, g.range_start, g.range_len, g.range_cum, g.num_ranges,
+                                g.range_stride);
+        if (st != KVW_OK) return st;
+        KVW_REQUIRE(!g.slot_mapping_out || aligned(g.slot_mapping_out, 8),
+                    "%s: slot_mapping_out misaligned", fn);
+    }
+    if (g.max_num_tokens == 0) return KVW_OK;
+    if (g.mode == KVW_SLOTS_PRECOMPUTED)
+        KVW_REQUIRE(g.slot_mapping_in && aligned(g.slot_mapping_in, 8),
+                    "%s: slot_mapping_in is NULL or misaligned", fn);
+    if (g.num_layers > 0) {
+        KVW_REQUIRE(g.key && g.value && g.k_cache && g.v_cache, "%s: a K/V or cache pointer is NULL", fn);
+        KVW_REQUIRE(aligned(g.key, 16) && aligned(g.value, 16) && aligned(g.k_cache, 16) &&
+                        aligned(g.v_cache, 16),
+                    "%s: K/V and cache pointers must be 16-byte aligned", fn);
+        KVW_REQUIRE(g.kv_layer_stride >= 0 && g.kv_token_stride >= 0 && g.kv_layer_stride % 16 == 0 &&
+                        g.kv_token_stride % 16 == 0,
+                    "%s: K/V strides must be non-negative multiples of 16", fn);
+    }
+    if (g.mode == KVW_SLOTS_PRECOMPUTED && g.num_layers == 0) return KVW_OK;
+
+    MapArgs a = make_map_args(g.query_start_loc, g.num_reqs, g.positions, g.max_num_tokens,
+                              g.block_size, g.err_flag);
+    a.block_table = g.block_table;
+    a.table_stride = g.block_table_stride;
+    a.num_blocks_per_req = g.num_blocks_per_req;
+    a.range_start = g.range_start;
+    a.range_len = g.range_len;
+    a.range_cum = g.range_cum;
+    a.num_ranges = g.num_ranges;
+    a.range_stride = g.range_stride;
+    a.slots_in = g.slot_mapping_in;
+    a.slots_out = g.slot_mapping_out;
+
+    CopyArgs c{};
+    c.key = static_cast<const uint8_t *>(g.key);
+    c.value = static_cast<const uint8_t *>(g.value);
+    c.k_cache = static_cast<uint8_t *>(g.k_cache);
+    c.v_cache = static_cast<uint8_t *>(g.v_cache);
+    c.kv_layer_stride = g.kv_layer_stride;
+    c.kv_token_stride = g.kv_token_stride;
+    c.rows_per_layer = rows_per_layer;
+    c.bytes_per_token = g.bytes_per_token;
+    c.num_layers = g.num_layers;
+    c.layers_per_wave = g.num_layers < KVW_LAYERS_PER_WAVE ? (g.num_layers > 0 ? g.num_layers : 1)
+                                                           : KVW_LAYERS_PER_WAVE;
+    if (g.num_layers / c.layers_per_wave >= kMaxGridY)  // keep gridDim.y within its limit
+        c.layers_per_wave = g.num_layers / kMaxGridY + 1;
+    const int32_t groups = g.num_layers > 0 ? (g.num_layers + c.layers_per_wave - 1) / c.layers_per_wave : 1;
+
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (g.mode == KVW_SLOTS_PRECOMPUTED) dispatch_kv_write<kPrecomputed>(a, c, g.max_num_tokens, groups, s);
+    else if (g.mode == KVW_SLOTS_PAGED) dispatch_kv_write<kPaged>(a, c, g.max_num_tokens, groups, s);
+    else dispatch_kv_write<kRanges>(a, c, g.max_num_tokens, groups, s);
+    return launched(fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,305 @@
+"""HIP path vs CPU oracle, element by element, through the C-ABI (needs an MI355X).
+
+Slot ids are compared exactly; cache planes are compared byte for byte
+(the write is a copy: tolerance 0); the sticky flag word must equal the
+oracle's flag bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_46_amd as kvw
+from parity import (DEV, Caches, DeviceInputs, compare_caches, dev, gpu_slots, host, new_flag,
+                    oracle_slots, say)
+import oracle
+from workloads import config, custom, long_context, small_cases
+from workloads.gen import Request
+
+pytestmark = pytest.mark.gpu
+
+SMALL = small_cases()
+MODES = {"precomputed": kvw.KVW_SLOTS_PRECOMPUTED, "paged": kvw.KVW_SLOTS_PAGED,
+         "ranges": kvw.KVW_SLOTS_RANGES}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kvw.library()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_kv_write(w, d, mode, caches, key, value, slots_in=None, block_size=None, num_blocks=None,
+                 over=None):
+    over = over or {}
+    flag = new_flag()
+    sm_out = torch.full((w.max_num_tokens,), 777, dtype=torch.int64, device=DEV)
+    kw = dict(mode=MODES[mode], key=key, value=value, k_cache=caches.k, v_cache=caches.v,
+              num_blocks=num_blocks or w.num_blocks, block_size=block_size or w.block_size,
+              max_num_tokens=w.max_num_tokens, err_flag=flag)
+    if mode == "precomputed":
+        kw["slot_mapping_in"] = dev(slots_in)
+    else:
+        kw.update(query_start_loc=d.qsl, num_reqs=w.num_reqs, positions=d.positions,
+                  slot_mapping_out=sm_out)
+        if mode == "paged":
+            kw.update(block_table=over.get("block_table", d.block_table),
+                      num_blocks_per_req=over.get("nbpr", d.nbpr))
+        else:
+            kw.update(range_start=over.get("rs", d.rs), range_len=over.get("rl", d.rl),
+                      range_cum=over.get("rc", d.rc), num_ranges=over.get("nr", d.nr))
+    kvw.kvw_kv_write(**kw)
+    torch.cuda.synchronize()
+    return host(sm_out), int(flag.item())
+
+
+def check_kv_write(w, mode, **over):
+    say(f"[kv_write] {w.describe()} mode={mode}")
+    d = DeviceInputs(w)
+    variant = "ranges" if mode == "ranges" else "paged"
+    o_slots, o_flags = oracle_slots(w, variant)
+    key_h, value_h = w.kv_plane(0), w.kv_plane(1)
+    key = dev(key_h).view(w.num_layers, w.max_num_tokens, w.num_kv_heads, w.head_dim)
+    value = dev(value_h).view_as(key)
+    caches = Caches(w.num_layers, w.num_blocks, w.block_size, w.row_elems)
+    sm, flags = run_kv_write(w, d, mode, caches, key, value, slots_in=o_slots)
+    if mode != "precomputed":
+        assert np.array_equal(sm, o_slots), f"{w.name}: fused slot_mapping_out differs"
+    else:
+        o_flags = 0
+    c_flags = compare_caches(w, caches, o_slots, key_h, value_h, w.num_blocks, w.block_size)
+    assert flags == o_flags | c_flags
+
+
+# ---------------------------------------------------------------------------
+# slot mapping
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", ["paged", "ranges"])
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_slot_mapping_small(w, variant):
+    say(f"[slots] {w.describe()} {variant}")
+    g, gf = gpu_slots(w, DeviceInputs(w), variant)
+    o, of = oracle_slots(w, variant)
+    assert np.array_equal(g, o)
+    assert gf == of
+
+
+STUDY = ["tiny_prefill", "decode_step", "mixed_chunked", "full_32_layer"]
+
+
+@pytest.mark.parametrize("variant", ["paged", "ranges"])
+@pytest.mark.parametrize("name", STUDY)
+def test_slot_mapping_study(name, variant):
+    w = config(name)
+    say(f"[slots] {w.describe()} {variant}")
+    g, gf = gpu_slots(w, DeviceInputs(w), variant)
+    o, of = oracle_slots(w, variant)
+    assert np.array_equal(g, o) and gf == of == 0
+
+
+@pytest.mark.parametrize("r", [1, 16, 512, 4096])
+def test_long_context_slots_and_expansion(r):
+    """128K context: expansion 32->16 on the GPU, then both variants, against the oracle chain."""
+    w = long_context(r)
+    say(f"[expand+slots] {w.describe()}")
+    orc = oracle.get()
+    d = DeviceInputs(w)
+    k = w.blocks_per_kv_block
+    # block-table expansion
+    kt = torch.full((w.max_num_reqs, w.table_stride * k), -5, dtype=torch.int32, device=DEV)
+    flag = new_flag()
+    kvw.kvw_map_to_kernel_blocks(d.block_table, d.nbpr, w.block_size, w.kernel_block_size, kt, flag)
+    o_kt, of = orc.map_to_kernel_blocks(w.block_table, w.num_blocks_per_req, w.block_size,
+                                        w.kernel_block_size)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(kt), o_kt) and int(flag.item()) == of == 0
+    # range expansion
+    outs = [torch.full_like(d.rs, -5) for _ in range(3)] + [torch.full_like(d.nr, -5)]
+    kvw.kvw_map_ranges_to_kernel_blocks(d.rs, d.rl, d.rc, d.nr, w.block_size, w.kernel_block_size,
+                                        *outs, err_flag=flag)
+    (o_s, o_l, o_c, o_n), of = orc.map_ranges_to_kernel_blocks(
+        w.range_start, w.range_len, w.range_cum, w.num_ranges, w.block_size, w.kernel_block_size)
+    torch.cuda.synchronize()
+    for g_, o_ in zip(outs, (o_s, o_l, o_c, o_n)):
+        assert np.array_equal(host(g_), o_)
+    # slot mapping at kernel block size through the GPU-expanded table and ranges
+    nb_k = d.nbpr * k
+    sm = torch.empty(w.max_num_tokens, dtype=torch.int64, device=DEV)
+    kvw.kvw_slot_mapping_paged(d.qsl, w.num_reqs, d.positions, w.max_num_tokens, kt, nb_k,
+                               w.kernel_block_size, sm, flag)
+    o_paged, _ = orc.slot_mapping_paged(w.query_start_loc, w.num_reqs, w.positions,
+                                        w.max_num_tokens, o_kt, w.num_blocks_per_req * k,
+                                        w.kernel_block_size)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sm), o_paged)
+    kvw.kvw_slot_mapping_ranges(d.qsl, w.num_reqs, d.positions, w.max_num_tokens, *outs,
+                                w.kernel_block_size, sm, flag)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sm), o_paged)
+    # and the manager-unit ranges at block size 32 give the same slots
+    kvw.kvw_slot_mapping_ranges(d.qsl, w.num_reqs, d.positions, w.max_num_tokens, d.rs, d.rl,
+                                d.rc, d.nr, w.block_size, sm, flag)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sm), o_paged)
+    assert int(flag.item()) == 0
+
+
+# ---------------------------------------------------------------------------
+# K/V write
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["precomputed", "paged", "ranges"])
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_kv_write_small(w, mode):
+    check_kv_write(w, mode)
+
+
+@pytest.mark.parametrize("mode", ["paged", "ranges"])
+@pytest.mark.parametrize("name", ["tiny_prefill", "decode_step", "mixed_chunked"])
+def test_kv_write_study(name, mode):
+    check_kv_write(config(name), mode)
+
+
+@pytest.mark.parametrize("variant", ["paged", "ranges_bs32", "ranges_expanded"])
+@pytest.mark.parametrize("r", [1, 4096])
+def test_kv_write_long_context(r, variant):
+    """128K context, fused write of 131,072 tokens into an 8 GiB cache, whole cache compared."""
+    if variant == "paged" and r != 1:
+        pytest.skip("the paged table does not depend on the range count")
+    w = long_context(r)
+    say(f"[kv_write long] {w.describe()} {variant}")
+    orc = oracle.get()
+    d = DeviceInputs(w)
+    k = w.blocks_per_kv_block
+    key_h, value_h = w.kv_plane(0), w.kv_plane(1)
+    key = dev(key_h).view(1, w.max_num_tokens, w.num_kv_heads, w.head_dim)
+    value = dev(value_h).view_as(key)
+    bs_k, nb_k = w.kernel_block_size, w.kernel_num_blocks
+    caches = Caches(1, nb_k, bs_k, w.row_elems)
+    o_slots, _ = orc.slot_mapping_ranges(w.query_start_loc, w.num_reqs, w.positions,
+                                         w.max_num_tokens, w.range_start, w.range_len,
+                                         w.range_cum, w.num_ranges, w.block_size)
+    if variant == "paged":
+        kt = torch.empty((w.max_num_reqs, w.table_stride * k), dtype=torch.int32, device=DEV)
+        kvw.kvw_map_to_kernel_blocks(d.block_table, d.nbpr, w.block_size, bs_k, kt)
+        sm, flags = run_kv_write(w, d, "paged", caches, key, value, block_size=bs_k,
+                                 num_blocks=nb_k, over=dict(block_table=kt, nbpr=d.nbpr * k))
+    elif variant == "ranges_expanded":
+        outs = [torch.empty_like(d.rs) for _ in range(3)] + [torch.empty_like(d.nr)]
+        kvw.kvw_map_ranges_to_kernel_blocks(d.rs, d.rl, d.rc, d.nr, w.block_size, bs_k, *outs)
+        sm, flags = run_kv_write(w, d, "ranges", caches, key, value, block_size=bs_k,
+                                 num_blocks=nb_k,
+                                 over=dict(rs=outs[0], rl=outs[1], rc=outs[2], nr=outs[3]))
+    else:
+        sm, flags = run_kv_write(w, d, "ranges", caches, key, value, block_size=w.block_size,
+                                 num_blocks=w.num_blocks)
+    assert np.array_equal(sm, o_slots) and flags == 0
+    # slots are identical in manager and kernel units, so one oracle pass checks every variant
+    assert compare_caches(w, caches, o_slots, key_h, value_h, nb_k, bs_k) == 0
+
+
+@pytest.mark.parametrize("mode", ["paged", "ranges"])
+def test_kv_write_32_layers(mode):
+    """16,384 tokens x 32 layers in one launch into 2 x 32 GiB cache planes."""
+    check_kv_write(config("full_32_layer"), mode)
+
+
+# ---------------------------------------------------------------------------
+# flags, padding and degenerate sizes
+# ---------------------------------------------------------------------------
+def _flagged_workload():
+    reqs = [Request(100, 40), Request(70, 1), Request(300, 30), Request(20, 20)]
+    w = custom("flagged", 4790, reqs, block_size=16, num_blocks=64, runs=("count", 1, 3),
+               max_num_tokens=120, table_stride=24, range_stride=6)
+    w.num_blocks_per_req[0] = 99      # above the row width: clamped
+    w.num_blocks_per_req[3] = -3      # negative: clamped to 0
+    w.block_table[1, 4] = -7          # negative physical block (request 1 writes logical block 4)
+    w.block_table[2, 16] = 900        # beyond the pool (request 2 writes logical blocks 16..18)
+    # request 1: more ranges than the stride holds; fill the row with valid runs past its blocks
+    n1 = int(w.num_ranges[1])
+    end = int(w.range_cum[1, n1 - 1] + w.range_len[1, n1 - 1])
+    for i in range(n1, w.range_stride):
+        w.range_start[1, i], w.range_len[1, i], w.range_cum[1, i] = 40 + i, 1, end
+        end += 1
+    w.num_ranges[1] = 50
+    w.num_ranges[3] = -1
+    # request 2: the run holding logical block 17 starts below block 0
+    for i in range(int(w.num_ranges[2])):
+        if w.range_cum[2, i] <= 17 < w.range_cum[2, i] + w.range_len[2, i]:
+            w.range_start[2, i] = -100
+    return w
+
+
+@pytest.mark.parametrize("variant", ["paged", "ranges"])
+def test_flags_and_clamps(variant):
+    w = _flagged_workload()
+    d = DeviceInputs(w)
+    g, gf = gpu_slots(w, d, variant)
+    o, of = oracle_slots(w, variant)
+    assert np.array_equal(g, o) and gf == of and of != 0
+    # num_tokens past max_num_tokens
+    q = w.query_start_loc.copy()
+    q[-1] = w.max_num_tokens + 50
+    d.qsl = dev(q)
+    g, gf = gpu_slots(w, d, variant)
+    o, of = oracle_slots(w, variant, qsl=q)
+    assert np.array_equal(g, o) and gf == of and of & kvw.KVW_FLAG_NUM_TOKENS
+
+
+def test_kv_write_out_of_pool_and_bad_slots():
+    w = _flagged_workload()
+    check_kv_write(w, "paged")
+    # precomputed slots beyond the cache and below the pad id write nothing
+    key_h = w.kv_plane(0)
+    rng = np.random.default_rng(4)
+    slots = np.full(w.max_num_tokens, -1, np.int64)
+    rows = w.num_blocks * w.block_size
+    slots[:60] = rng.permutation(rows)[:60]
+    slots[60:70] = rows + np.arange(10)
+    slots[70:75] = -(2 + np.arange(5))
+    key = dev(key_h).view(1, w.max_num_tokens, w.num_kv_heads, w.head_dim)
+    caches = Caches(1, w.num_blocks, w.block_size, w.row_elems)
+    sm, flags = run_kv_write(w, DeviceInputs(w), "precomputed", caches, key, key, slots_in=slots)
+    c_flags = compare_caches(w, caches, slots, key_h, key_h, w.num_blocks, w.block_size)
+    assert flags == c_flags == kvw.KVW_FLAG_SLOT_OOB
+
+
+def test_zero_token_rows_and_zero_layers():
+    w = config("tiny_prefill")
+    d = DeviceInputs(w)
+    out = torch.full((4,), 9, dtype=torch.int64, device=DEV)
+    kvw.kvw_slot_mapping_paged(d.qsl, w.num_reqs, d.positions, 0, d.block_table, d.nbpr, 16, out)
+    torch.cuda.synchronize()
+    assert host(out).tolist() == [9, 9, 9, 9]
+    # fused call with no layers still produces the slot mapping and touches no cache
+    key = torch.zeros((0, w.max_num_tokens, 8, 128), dtype=torch.int16, device=DEV)
+    caches = Caches(1, 4, 16, 1024)
+    sm = torch.full((w.max_num_tokens,), 5, dtype=torch.int64, device=DEV)
+    kvw.kvw_kv_write(mode=kvw.KVW_SLOTS_PAGED, key=key, value=key, k_cache=caches.k,
+                     v_cache=caches.v, num_blocks=w.num_blocks, block_size=16,
+                     max_num_tokens=w.max_num_tokens, query_start_loc=d.qsl,
+                     num_reqs=w.num_reqs, positions=d.positions, block_table=d.block_table,
+                     num_blocks_per_req=d.nbpr, slot_mapping_out=sm)
+    o, _ = oracle_slots(w, "paged")
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sm), o)
+    assert (host(caches.t) == 0x7FC0).all()
+
+
+def test_invalid_arguments_raise():
+    w = config("tiny_prefill")
+    d = DeviceInputs(w)
+    out = torch.empty(w.max_num_tokens, dtype=torch.int64, device=DEV)
+    with pytest.raises(kvw.KvwError) as e:
+        kvw.kvw_slot_mapping_paged(d.qsl, w.num_reqs, d.positions, w.max_num_tokens,
+                                   d.block_table, d.nbpr, 0, out)
+    assert e.value.status == 1
+    kt = torch.empty((4, 64), dtype=torch.int32, device=DEV)
+    with pytest.raises(kvw.KvwError):
+        kvw.kvw_map_to_kernel_blocks(d.block_table, d.nbpr, 32, 12, kt)
+    big = torch.zeros((4, kvw.kvw.KVW_MAX_RANGE_STRIDE + 1), dtype=torch.int32, device=DEV)
+    with pytest.raises(kvw.KvwError) as e:
+        kvw.kvw_slot_mapping_ranges(d.qsl, w.num_reqs, d.positions, w.max_num_tokens, big, big,
+                                    big, d.nr, 16, out)
+    assert e.value.status == 3

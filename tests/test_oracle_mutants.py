@@ -40,8 +40,8 @@ MUTANTS = {
                         "return (layer * block_size + block) * num_blocks + token;"),
     "kv_drops_layer_term": ("int64_t src = layer * kv_layer_stride + t * kv_token_stride;",
                             "int64_t src = t * kv_token_stride;"),
-    "tail_not_padded": ("for (int64_t t = 0; t < max_num_tokens; ++t) slot_mapping[t] = ORC_PAD_ID;\n    int64_t num_tokens = num_tokens_of(qsl, num_reqs, max_num_tokens, &flags);\n\n    for (int32_t r = 0; r < num_reqs; ++r) {\n        int64_t bound",
-                        "for (int64_t t = 0; t < max_num_tokens; ++t) slot_mapping[t] = 0;\n    int64_t num_tokens = num_tokens_of(qsl, num_reqs, max_num_tokens, &flags);\n\n    for (int32_t r = 0; r < num_reqs; ++r) {\n        int64_t bound"),
+    "tail_not_padded": ("/* no token rows: nothing is read */\n    for (int64_t t = 0; t < max_num_tokens; ++t) slot_mapping[t] = ORC_PAD_ID;",
+                        "/* no token rows: nothing is read */\n    for (int64_t t = 0; t < max_num_tokens; ++t) slot_mapping[t] = 0;"),
     "request_end_inclusive": ("for (int64_t t = qsl[r]; t < qsl[r + 1] && t < num_tokens; ++t) {\n            int64_t p = positions[t];\n            if (p < 0) continue;                       /* pad id */",
                               "for (int64_t t = qsl[r]; t <= qsl[r + 1] && t < num_tokens; ++t) {\n            int64_t p = positions[t];\n            if (p < 0) continue;                       /* pad id */"),
     "negative_position_kept": ("if (p < 0) continue;                       /* pad id */",
