@@ -85,7 +85,9 @@ static int qsl_ok(const int32_t *qsl, int32_t num_reqs)
  * and every entry from num_tokens up to max_num_tokens is the pad id
  * ([P2] "Datenfluss": the last program pads the tail for graph replay).
  * num_blocks_per_req (may be NULL) bounds the valid logical blocks of a row;
- * NULL means the full row width.
+ * NULL means the full row width.  A request's count is read (clamped to
+ * [0, table_stride], flagged if outside) for each of its tokens with a
+ * non-negative position.  With max_num_tokens == 0 nothing is read.
  */
 int orc_slot_mapping_paged(const int32_t *qsl, int32_t num_reqs, const int64_t *positions,
                            int64_t max_num_tokens, const int32_t *block_table,
@@ -98,16 +100,17 @@ int orc_slot_mapping_paged(const int32_t *qsl, int32_t num_reqs, const int64_t *
         return ORC_E_ARG;
     if (!qsl_ok(qsl, num_reqs)) return ORC_E_QSL;
 
+    if (max_num_tokens == 0) return ORC_OK;            /* no token rows: nothing is read */
     for (int64_t t = 0; t < max_num_tokens; ++t) slot_mapping[t] = ORC_PAD_ID;
     int64_t num_tokens = num_tokens_of(qsl, num_reqs, max_num_tokens, &flags);
 
     for (int32_t r = 0; r < num_reqs; ++r) {
-        int64_t bound = table_stride;
-        if (num_blocks_per_req)
-            bound = clamp64(num_blocks_per_req[r], 0, table_stride, &flags, ORC_FLAG_COUNT);
         for (int64_t t = qsl[r]; t < qsl[r + 1] && t < num_tokens; ++t) {
             int64_t p = positions[t];
             if (p < 0) continue;                       /* pad id */
+            int64_t bound = table_stride;
+            if (num_blocks_per_req)
+                bound = clamp64(num_blocks_per_req[r], 0, table_stride, &flags, ORC_FLAG_COUNT);
             int64_t logical = p / block_size;
             int64_t offset = p % block_size;
             if (logical >= bound) continue;            /* no block owned there: pad id */
@@ -156,14 +159,15 @@ int orc_slot_mapping_ranges(const int32_t *qsl, int32_t num_reqs, const int64_t 
         }
     }
 
+    if (max_num_tokens == 0) return ORC_OK;
     for (int64_t t = 0; t < max_num_tokens; ++t) slot_mapping[t] = ORC_PAD_ID;
     int64_t num_tokens = num_tokens_of(qsl, num_reqs, max_num_tokens, &flags);
 
     for (int32_t r = 0; r < num_reqs; ++r) {
-        int64_t n = clamp64(num_ranges[r], 0, range_stride, &flags, ORC_FLAG_COUNT);
         for (int64_t t = qsl[r]; t < qsl[r + 1] && t < num_tokens; ++t) {
             int64_t p = positions[t];
             if (p < 0) continue;
+            int64_t n = clamp64(num_ranges[r], 0, range_stride, &flags, ORC_FLAG_COUNT);
             int64_t logical = p / block_size;
             int64_t offset = p % block_size;
             for (int64_t i = 0; i < n; ++i) {
@@ -214,6 +218,7 @@ int orc_map_to_kernel_blocks(const int32_t *ids, const int32_t *counts, int32_t 
     int64_t k = blocks_per_kv_block(block_size, kernel_block_size);
     if (k == 0) return ORC_E_ARG;
     if (rows < 0 || in_stride < 0 || out_stride < (int64_t)in_stride * k) return ORC_E_ARG;
+    if (out_stride == 0) return ORC_OK;                /* empty rows: nothing is read */
     for (int32_t r = 0; r < rows; ++r) {
         int64_t count = in_stride;
         if (counts) count = clamp64(counts[r], 0, in_stride, &flags, ORC_FLAG_COUNT);
