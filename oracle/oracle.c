@@ -22,8 +22,7 @@
  * Every loop below walks the definition in the order it is stated; nothing
  * is blocked, fused or reordered.  Integer arithmetic is done in int64.
  *
- * Readings where the pages leave a step open (each one is listed with its
- * reason in the design notes of the repository):
+ * Readings where the pages leave a step open:
  *  - a token whose position is negative, or whose logical block lies past
  *    the blocks its request owns, or past every range, gets the pad id;
  *  - range descriptors are (start, len, cum) with cum the exclusive prefix
