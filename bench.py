@@ -2,17 +2,21 @@
 
 Default workload: 128K context, 16 requests x 8192-token prefill chunks
 (131,072 tokens written per step), manager block size 32 expanded to kernel
-block size 16, 8 KV heads x 128 bf16, one layer.  A step is the whole hot
-path for one batch: manager->kernel expansion of the variant's mapping
-structure, then the fused slot-map + K/V scatter kernel.
+block size 16, 8 KV heads x 128 bf16, one layer.  Each request's blocks form
+R contiguous runs placed at random (R in 1, 16, 512, 4096; 4096 = every
+manager block on its own).  A step is the whole hot path for one batch:
+manager->kernel expansion of the variant's mapping structure, then the fused
+slot-map + K/V write (kvw_kv_write keeping the slot mapping).
 
-  paged          expand the block table, fused paged write
-  ranges_r{R}    expand the range descriptors (R runs per request), fused range write
+  paged_r{R}     expand the block table, fused paged write
+  ranges_r{R}    expand the range descriptors, fused range write
 
-`value` is the paged variant's tokens/s; every variant is reported under
-"variants".  The roofline entry is for the fused write kernel (the dominant
-kernel), timed with HIP events recorded on the stream it is launched on.
-The CPU baseline times the CPU oracle (test infrastructure) on the same batch.
+`value` is tokens/s of paged_r4096; every variant is reported under
+"variants", with the fused call's time (HIP events on the launch stream)
+and the time of the single-kernel form used when no slot mapping is kept.
+The roofline entry is for kv_scatter_kernel, the dominant kernel, timed
+alone on the headline variant's slots.  The CPU baseline times the CPU
+oracle (test infrastructure) on the same batch.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -30,9 +34,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "tokens/s and HBM GB/s (% of peak) for fused slot-map+KV write, paged vs range"
+# headline: paged gather over the fully fragmented layout (every manager block its own run)
+HEADLINE = "paged_r4096"
 HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_46_amd", "csrc", "kvw.hip")
-COUNTERS = os.path.join(ROOT, "profiles", "kv_write_fused_long_context_counters.json")
+COUNTERS = os.path.join(ROOT, "profiles", "kv_scatter_kernel_long_context_counters.json")
 
 
 def log(*a):
@@ -44,7 +50,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--variants", default="paged,ranges_r1,ranges_r16,ranges_r512,ranges_r4096")
+    p.add_argument("--variants", default=",".join(
+        f"{k}_r{r}" for k in ("paged", "ranges") for r in (1, 16, 512, 4096)))
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timing (e.g. under a profiler)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -105,6 +112,7 @@ def main():
     bs_k, nb_k = base.kernel_block_size, base.kernel_num_blocks
     log(f"[bench] workload {base.describe()} -> kernel bs {bs_k}, {nb_k} kernel blocks")
     t = time.time()
+    # one K/V payload serves every layout variant (same requests and positions)
     key = d(base.kv_layer(0, 0)).view(1, M, H, D)
     value = d(base.kv_layer(1, 0)).view(1, M, H, D)
     log(f"[bench] K/V generated and uploaded in {time.time() - t:.1f}s "
@@ -117,82 +125,115 @@ def main():
     # (4 x bytes_per_token per token per layer) + position read + slot written (8 + 8 B)
     real_tokens = base.num_tokens
     fused_bytes = real_tokens * base.num_layers * 4 * bpt + real_tokens * 16
+    # the scatter kernel alone: K and V rows read and written + slot read (8 B)
+    scatter_bytes = real_tokens * base.num_layers * 4 * bpt + real_tokens * 8
 
-    results = {}
-    for name in variants:
-        if name == "paged":
-            w = base
-            dd = dict(qsl=d(w.query_start_loc), pos=d(w.positions), bt=d(w.block_table),
-                      nb=d(w.num_blocks_per_req))
-            kt = torch.empty((w.max_num_reqs, w.table_stride * k), dtype=torch.int32, device=dev)
-            nb_kernel = dd["nb"] * k
-            expand_bytes = w.block_table.nbytes + w.num_blocks_per_req.nbytes + kt.numel() * 4
-
-            def step(ev=None, w=w, dd=dd, kt=kt, nb_kernel=nb_kernel):
-                kvw.kvw_map_to_kernel_blocks(dd["bt"], dd["nb"], w.block_size, bs_k, kt)
-                if ev is not None:
-                    ev[0].record(stream)
-                kvw.kvw_kv_write(mode=kvw.KVW_SLOTS_PAGED, key=key, value=value,
-                                 k_cache=cache[0], v_cache=cache[1], num_blocks=nb_k,
-                                 block_size=bs_k, query_start_loc=dd["qsl"], num_reqs=w.num_reqs,
-                                 positions=dd["pos"], block_table=kt, num_blocks_per_req=nb_kernel,
-                                 slot_mapping_out=sm_out)
-                if ev is not None:
-                    ev[1].record(stream)
-        elif name.startswith("ranges_r"):
-            r = int(name[len("ranges_r"):])
-            w = long_context(r)
-            dd = dict(qsl=d(w.query_start_loc), pos=d(w.positions), rs=d(w.range_start),
-                      rl=d(w.range_len), rc=d(w.range_cum), nr=d(w.num_ranges))
-            outs = [torch.empty_like(dd["rs"]) for _ in range(3)] + [torch.empty_like(dd["nr"])]
-            expand_bytes = 2 * (3 * w.range_start.nbytes + w.num_ranges.nbytes)
-
-            def step(ev=None, w=w, dd=dd, outs=outs):
-                kvw.kvw_map_ranges_to_kernel_blocks(dd["rs"], dd["rl"], dd["rc"], dd["nr"],
-                                                    w.block_size, bs_k, *outs)
-                if ev is not None:
-                    ev[0].record(stream)
-                kvw.kvw_kv_write(mode=kvw.KVW_SLOTS_RANGES, key=key, value=value,
-                                 k_cache=cache[0], v_cache=cache[1], num_blocks=nb_k,
-                                 block_size=bs_k, query_start_loc=dd["qsl"], num_reqs=w.num_reqs,
-                                 positions=dd["pos"], range_start=outs[0], range_len=outs[1],
-                                 range_cum=outs[2], num_ranges=outs[3], slot_mapping_out=sm_out)
-                if ev is not None:
-                    ev[1].record(stream)
-        else:
-            raise SystemExit(f"unknown variant {name}")
-
-        for _ in range(args.warmup):
-            step()
+    def timed(fn, n_warm, n_steps):
+        for _ in range(n_warm):
+            fn(None)
         torch.cuda.synchronize()
-        events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(args.steps)]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(events[i])
+        for i in range(n_steps):
+            fn(evs[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        kernel_ms = [a.elapsed_time(b) for a, b in events]
-        kavg = statistics.fmean(kernel_ms)
-        ms_step = wall * 1e3 / args.steps
+        return wall * 1e3 / n_steps, [a.elapsed_time(b) for a, b in evs]
+
+    results = {}
+    scatter = None
+    for name in variants:
+        kind, _, r = name.partition("_r")
+        if kind not in ("paged", "ranges") or not r.isdigit():
+            raise SystemExit(f"unknown variant {name}")
+        w = long_context(int(r))
+        qsl, pos = d(w.query_start_loc), d(w.positions)
+        if kind == "paged":
+            bt, nb = d(w.block_table), d(w.num_blocks_per_req)
+            kt = torch.empty((w.max_num_reqs, w.table_stride * k), dtype=torch.int32, device=dev)
+            nb_kernel = nb * k
+            expand_bytes = w.block_table.nbytes + w.num_blocks_per_req.nbytes + kt.numel() * 4
+            mapping = dict(block_table=kt, num_blocks_per_req=nb_kernel)
+
+            def expand(bt=bt, nb=nb, kt=kt, w=w):
+                kvw.kvw_map_to_kernel_blocks(bt, nb, w.block_size, bs_k, kt)
+            mode = kvw.KVW_SLOTS_PAGED
+        else:
+            rs, rl, rc, nr = (d(a) for a in (w.range_start, w.range_len, w.range_cum, w.num_ranges))
+            outs = [torch.empty_like(rs) for _ in range(3)] + [torch.empty_like(nr)]
+            expand_bytes = 2 * (3 * w.range_start.nbytes + w.num_ranges.nbytes)
+            mapping = dict(range_start=outs[0], range_len=outs[1], range_cum=outs[2],
+                           num_ranges=outs[3])
+
+            def expand(rs=rs, rl=rl, rc=rc, nr=nr, outs=outs, w=w):
+                kvw.kvw_map_ranges_to_kernel_blocks(rs, rl, rc, nr, w.block_size, bs_k, *outs)
+            mode = kvw.KVW_SLOTS_RANGES
+
+        def write(slots_out, mode=mode, mapping=mapping, qsl=qsl, pos=pos, w=w):
+            kvw.kvw_kv_write(mode=mode, key=key, value=value, k_cache=cache[0], v_cache=cache[1],
+                             num_blocks=nb_k, block_size=bs_k, query_start_loc=qsl,
+                             num_reqs=w.num_reqs, positions=pos, slot_mapping_out=slots_out,
+                             **mapping)
+
+        def step(ev, expand=expand, write=write):
+            expand()
+            if ev is not None:
+                ev[0].record(stream)
+            write(sm_out)
+            if ev is not None:
+                ev[1].record(stream)
+
+        def single(ev, write=write):
+            if ev is not None:
+                ev[0].record(stream)
+            write(None)
+            if ev is not None:
+                ev[1].record(stream)
+
+        ms_step, call_ms = timed(step, args.warmup, args.steps)
+        _, single_ms = timed(single, args.warmup, args.steps)
+        call_avg = statistics.fmean(call_ms)
+        single_avg = statistics.fmean(single_ms)
         step_bytes = fused_bytes + expand_bytes
         results[name] = {
             "tokens_per_s": real_tokens / (ms_step * 1e-3),
             "ms_per_step": ms_step,
             "step_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
-            "fused_kernel_ms_avg": kavg,
-            "fused_kernel_ms_p10": float(np.percentile(kernel_ms, 10)),
-            "fused_kernel_ms_p90": float(np.percentile(kernel_ms, 90)),
-            "fused_kernel_gbps": fused_bytes / (kavg * 1e-3) / 1e9,
-            "fused_kernel_frac_of_peak": fused_bytes / (kavg * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "ranges_per_request": None if name == "paged" else int(name[len("ranges_r"):]),
+            "fused_call_ms_avg": call_avg,
+            "fused_call_ms_p10": float(np.percentile(call_ms, 10)),
+            "fused_call_ms_p90": float(np.percentile(call_ms, 90)),
+            "fused_call_gbps": fused_bytes / (call_avg * 1e-3) / 1e9,
+            "fused_call_frac_of_peak": fused_bytes / (call_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "single_kernel_ms_avg": single_avg,
+            "single_kernel_frac_of_peak": fused_bytes / (single_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "ranges_per_request": int(r),
         }
-        log(f"[bench] {name:14s} step {ms_step * 1e3:8.1f} us  fused kernel {kavg * 1e3:8.1f} us "
-            f"= {results[name]['fused_kernel_gbps']:7.0f} GB/s "
-            f"({100 * results[name]['fused_kernel_frac_of_peak']:.1f}% of 8 TB/s)  "
+        log(f"[bench] {name:13s} step {ms_step * 1e3:7.1f} us  fused call {call_avg * 1e3:7.1f} us = "
+            f"{results[name]['fused_call_gbps']:5.0f} GB/s "
+            f"({100 * results[name]['fused_call_frac_of_peak']:.1f}%)  single kernel "
+            f"{single_avg * 1e3:7.1f} us ({100 * results[name]['single_kernel_frac_of_peak']:.1f}%)  "
             f"{results[name]['tokens_per_s'] / 1e6:.0f} M tokens/s")
-        del step
+        if name == HEADLINE:
+            # the dominant kernel alone, on the slots the fused call just produced
+            step(None)
+            torch.cuda.synchronize()
+            slots = sm_out.clone()
+
+            def scatter_only(ev, slots=slots):
+                if ev is not None:
+                    ev[0].record(stream)
+                kvw.kvw_kv_write(mode=kvw.KVW_SLOTS_PRECOMPUTED, key=key, value=value,
+                                 k_cache=cache[0], v_cache=cache[1], num_blocks=nb_k,
+                                 block_size=bs_k, slot_mapping_in=slots)
+                if ev is not None:
+                    ev[1].record(stream)
+            _, sc_ms = timed(scatter_only, args.warmup, args.steps)
+            scatter = statistics.fmean(sc_ms)
+            log(f"[bench] kv_scatter_kernel alone ({name} slots): {scatter * 1e3:.1f} us = "
+                f"{scatter_bytes / (scatter * 1e-3) / 1e9:.0f} GB/s")
+        del step, single, write, expand
 
     copy_ceiling = None
     if args.copy_calibration_mib:
@@ -210,27 +251,31 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
-        copy_ceiling = {"bytes_moved": 2 * n, "ms": ms, "gbps": 2 * n / (ms * 1e-3) / 1e9}
+        copy_ceiling = {"what": "torch device-to-device copy_", "bytes_moved": 2 * n, "ms": ms,
+                        "gbps": 2 * n / (ms * 1e-3) / 1e9}
         log(f"[bench] device copy of {args.copy_calibration_mib} MiB: {copy_ceiling['gbps']:.0f} GB/s "
             "(read + write)")
         del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(base, args.cpu_seconds)
+        cpu = cpu_baseline(long_context(int(HEADLINE.partition("_r")[2])), args.cpu_seconds)
 
-    head = results.get("paged") or next(iter(results.values()))
+    head = results.get(HEADLINE) or next(iter(results.values()))
     traffic = counter_traffic()
-    roof = {
-        "bound": "hbm",
-        "achieved": round(head["fused_kernel_gbps"], 1),
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": round(head["fused_kernel_frac_of_peak"], 4),
-        "traffic": traffic,
-        "kernel": "kv_write_kernel (fused paged slot map + K/V scatter)",
-        "algorithmic_bytes_per_launch": fused_bytes,
-    }
+    roof = None
+    if scatter is not None:
+        roof = {
+            "bound": "hbm",
+            "achieved": round(scatter_bytes / (scatter * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(scatter_bytes / (scatter * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "kv_scatter_kernel",
+            "launch_ms_avg": round(scatter, 5),
+            "algorithmic_bytes_per_launch": scatter_bytes,
+        }
     line = {
         "metric": METRIC,
         "value": round(head["tokens_per_s"], 1),
@@ -247,9 +292,12 @@ def main():
         "config": {"workload": "long_context_128k", "requests": base.num_reqs,
                    "tokens_per_step": real_tokens, "context": 131072, "layers": base.num_layers,
                    "manager_block_size": base.block_size, "kernel_block_size": bs_k,
-                   "kv_heads": H, "head_dim": D, "payload": "bf16", "variant": "paged"},
+                   "kv_heads": H, "head_dim": D, "payload": "bf16", "variant": HEADLINE},
         "hbm_gbps": round(head["step_gbps"], 1),
         "hbm_frac_of_peak": round(head["step_gbps"] / HBM_PEAK_GBPS, 4),
+        "fused_call_frac_of_peak": round(head["fused_call_frac_of_peak"], 4),
+        "worst_fused_call_frac_of_peak": round(min(v["fused_call_frac_of_peak"]
+                                                   for v in results.values()), 4),
         "roofline": roof,
         "cpu_baseline": cpu,
         "copy_ceiling": copy_ceiling,

@@ -221,6 +221,11 @@ size_t kvw_kv_write_args_size(void);
  * stored to slot_mapping_out when it is non-NULL (tail padded).
  * Precondition: no two tokens share a slot (else the surviving row is
  * unspecified).
+ * Execution: in the paged and range modes with slot_mapping_out set, the
+ * call enqueues two kernels on `stream`: the slot mapping (written to
+ * slot_mapping_out), then the scatter that reads it; without
+ * slot_mapping_out it enqueues one kernel that does both.  The precomputed
+ * mode enqueues the scatter only.
  * Errors: KVW_ERR_INVALID_ARG for an unknown mode, NULL required pointers,
  * misalignment, negative sizes, bytes_per_token % 16 != 0, or a cache size
  * beyond int64; KVW_ERR_RANGE_CAP as kvw_slot_mapping_ranges.

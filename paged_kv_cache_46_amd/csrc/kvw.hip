@@ -1,14 +1,19 @@
 // Paged KV-cache write path for MI355X (gfx950, CDNA4, wave64).
 //
 // Kernels:
-//   slot_mapping_kernel<MODE>  token-parallel slot resolution (paged gather or
-//                              range arithmetic), tail padded with the pad id;
-//   kv_write_kernel<MODE,...>  K/V scatter into the paged cache, optionally
-//                              fused with the slot resolution;
+//   slot_mapping_kernel<MODE>    one token per lane: paged gather or range
+//                                arithmetic, tail padded with the pad id;
+//   kv_scatter_kernel            one 1 KiB slice of one K or V row per wave,
+//                                slot read from a slot mapping;
+//   kv_write_fused_kernel<MODE>  one wave per token: slot resolution and the
+//                                copy of the token's K and V rows in one pass;
 //   expand_blocks_kernel,
-//   expand_ranges_kernel       manager-to-kernel block expansion.
-// The host functions at the bottom validate host-side scalars and launch on
-// the caller's stream; see include/kvw.h for the contract.
+//   expand_ranges_kernel         manager-to-kernel block expansion.
+// kvw_kv_write in a fused mode runs slot_mapping_kernel then
+// kv_scatter_kernel when the caller keeps the slot mapping (the usual case:
+// attention consumes it), and kv_write_fused_kernel otherwise.  The host
+// functions at the bottom validate host-side scalars and launch on the
+// caller's stream; include/kvw.h holds the contract.
 //
 // Sources: "Range-addressed KV cache blocks for the vLLM serving engine"
 // ("The Innovation", "The Coordinate Approach"); "Blocktabelle: Abbildung
@@ -17,17 +22,13 @@
 // (Deep Dive sections 7 and 8).
 //
 // The path is a memory-bound gather/scatter: no matrix cores are involved.
-// Design notes:
-//  * Token-tiled grids instead of one program per request: a batch mixing
-//    8192-token prefill chunks with single decode tokens keeps every wave
-//    equally loaded.  A token finds its request by binary search over
-//    query_start_loc.
-//  * Each wave resolves the slots of its tile with one token per lane, then
-//    copies the tile's rows: one 2 KiB row (8 heads x 128 bf16) is two
-//    64-lane x 16-byte vector accesses, so every load and store instruction
-//    moves a fully used 1 KiB span.  Several rows are loaded before any is
-//    stored to keep enough bytes in flight per wave.
-//  * All cache addressing is 64-bit: a 32-layer cache plane reaches 32 GiB.
+// Measured on MI355X, HBM throughput of a copy is highest when every wave
+// moves a single 1 KiB span (one 16-byte load and one 16-byte store per
+// lane) and retires: larger per-wave batches, loops and persistent grids
+// all lose 5-30%.  A copy wave therefore cannot afford a dependent chain of
+// metadata loads, which is why the scatter reads ready-made slots and the
+// slot resolution runs one token per lane in its own kernel.  All cache
+// addressing is 64-bit: a 32-layer cache plane reaches 32 GiB.
 
 #include <hip/hip_runtime.h>
 
@@ -37,14 +38,11 @@
 
 #include "kvw.h"
 
-#ifndef KVW_TOKENS_PER_WAVE
-#define KVW_TOKENS_PER_WAVE 32
+#ifndef KVW_SCATTER_WAVES
+#define KVW_SCATTER_WAVES 1
 #endif
-#ifndef KVW_ROWS_IN_FLIGHT
-#define KVW_ROWS_IN_FLIGHT 4
-#endif
-#ifndef KVW_LAYERS_PER_WAVE
-#define KVW_LAYERS_PER_WAVE 4
+#ifndef KVW_FUSED_WAVES
+#define KVW_FUSED_WAVES 1
 #endif
 #ifndef KVW_NT_LOADS
 #define KVW_NT_LOADS 1
@@ -56,10 +54,15 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kBlockThreads = 256;
-constexpr int kWavesPerBlock = kBlockThreads / kWave;
-constexpr int kSliceBytes = kWave * 16;  // one wave-wide 16-byte access
-constexpr int kMaxGridY = 65535;
+constexpr int kBlockThreads = 256;           // slot mapping and expansion kernels
+constexpr int kSliceBytes = kWave * 16;      // one wave-wide 16-byte access
+constexpr int kScatterWaves = KVW_SCATTER_WAVES;
+constexpr int kScatterThreads = kScatterWaves * kWave;
+constexpr int kFusedWaves = KVW_FUSED_WAVES;
+constexpr int kFusedThreads = kFusedWaves * kWave;
+constexpr int kMaxSlicesPerLane = 4;         // rows up to 4 KiB are held in registers whole
+constexpr unsigned kMaxGridX = 0x7fffffffu;
+constexpr unsigned kMaxGridY = 65535u;
 
 enum : int { kPrecomputed = KVW_SLOTS_PRECOMPUTED, kPaged = KVW_SLOTS_PAGED, kRanges = KVW_SLOTS_RANGES };
 
@@ -75,7 +78,6 @@ struct MapArgs {
     const int32_t *range_len;
     const int32_t *range_cum;
     const int32_t *num_ranges;
-    const int64_t *slots_in;
     int64_t *slots_out;
     int32_t *err_flag;
     int64_t max_num_tokens;
@@ -93,10 +95,14 @@ struct CopyArgs {
     uint8_t *v_cache;
     int64_t kv_layer_stride;
     int64_t kv_token_stride;
-    int64_t rows_per_layer;  // B * T
+    int64_t rows_per_layer;   // B * T
     int64_t bytes_per_token;
+    int64_t max_num_tokens;
     int32_t num_layers;
-    int32_t layers_per_wave;
+    int32_t layers_per_wave;  // fused kernel: layers handled by one wave
+    uint32_t slices_per_row;  // ceil(bytes_per_token / 1 KiB)
+    uint32_t items_per_token; // 2 planes x slices_per_row
+    int32_t items_log2;       // log2(items_per_token), or -1 if not a power of two
 };
 
 __device__ __forceinline__ void raise_flags(int32_t *err, uint32_t flags)
@@ -104,14 +110,15 @@ __device__ __forceinline__ void raise_flags(int32_t *err, uint32_t flags)
     if (err && flags) atomicOr(err, static_cast<int>(flags));
 }
 
-// num_tokens = query_start_loc[num_reqs], clamped to [0, max_num_tokens].
-__device__ __forceinline__ int64_t device_num_tokens(const MapArgs &a, bool report)
+// num_tokens = query_start_loc[num_reqs], clamped to [0, max_num_tokens]; a
+// clamp sets KVW_FLAG_NUM_TOKENS in `flags`.  Flags are collected in
+// registers and raised after the metadata loads, so that no store precedes
+// those loads (they may then be scalar loads for a wave-uniform token).
+__device__ __forceinline__ int64_t device_num_tokens(const MapArgs &a, uint32_t &flags)
 {
     int64_t n = a.qsl[a.num_reqs];
-    uint32_t f = 0;
-    if (n < 0) { n = 0; f = KVW_FLAG_NUM_TOKENS; }
-    if (n > a.max_num_tokens) { n = a.max_num_tokens; f = KVW_FLAG_NUM_TOKENS; }
-    if (report) raise_flags(a.err_flag, f);
+    if (n < 0) { n = 0; flags |= KVW_FLAG_NUM_TOKENS; }
+    if (n > a.max_num_tokens) { n = a.max_num_tokens; flags |= KVW_FLAG_NUM_TOKENS; }
     return n;
 }
 
@@ -175,7 +182,6 @@ template <int MODE>
 __device__ __forceinline__ int64_t resolve_slot(const MapArgs &a, int64_t t, int64_t num_tokens,
                                                 uint32_t &flags)
 {
-    if (MODE == kPrecomputed) return a.slots_in[t];
     if (t >= num_tokens) return KVW_PAD_ID;
     const int32_t r = find_request(a.qsl, a.num_reqs, t);
     if (r < 0) return KVW_PAD_ID;
@@ -202,18 +208,10 @@ __global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
 {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x;
     if (t >= a.max_num_tokens) return;
-    const int64_t num_tokens = device_num_tokens(a, t == 0);
-    uint32_t flags = 0;
+    uint32_t nt_flag = 0, flags = 0;
+    const int64_t num_tokens = device_num_tokens(a, nt_flag);
     a.slots_out[t] = resolve_slot<MODE>(a, t, num_tokens, flags);
-    raise_flags(a.err_flag, flags);
-}
-
-__device__ __forceinline__ int64_t wave_bcast64(int64_t v, int lane)
-{
-    const int lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), lane);
-    const int hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint64_t>(v) >> 32), lane);
-    return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) |
-                                static_cast<uint32_t>(lo));
+    raise_flags(a.err_flag, flags | (t == 0 ? nt_flag : 0u));
 }
 
 template <bool NT>
@@ -230,80 +228,109 @@ __device__ __forceinline__ void store16(uint8_t *p, u32x4 v)
     else *reinterpret_cast<u32x4 *>(p) = v;
 }
 
-// One wave owns TPW consecutive tokens and LPW consecutive layers
-// (blockIdx.y).  Lane i < TPW resolves token t0 + i; the copy then walks the
-// tile U rows at a time, each row's slot broadcast from its lane.  CH is the
-// number of 1 KiB slices of a row held per lane (rows longer than CH KiB
-// are walked in segments).
-template <int MODE, int TPW, int U, int CH>
-__global__ __launch_bounds__(kBlockThreads) void kv_write_kernel(MapArgs a, CopyArgs c)
+// One wave per (layer, token, plane, 1 KiB slice) item.  The token is
+// wave-uniform; its slot is one scalar load, issued together with the
+// 16-byte data load of each lane; the store follows and the wave retires.
+// Items are ordered layer-major (blockIdx.y), then token, plane, slice, so
+// consecutive waves stream through consecutive K/V rows and, for tokens of
+// one block, consecutive cache slots.
+__global__ __launch_bounds__(kScatterThreads) void kv_scatter_kernel(const int64_t *slots,
+                                                                     CopyArgs c, int32_t *err_flag)
 {
-    static_assert(TPW >= 1 && TPW <= kWave, "one token per lane");
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x / kWave);
-    const int64_t t0 = wave * TPW;
-    if (t0 >= a.max_num_tokens) return;  // whole wave leaves together
-    const int64_t left = a.max_num_tokens - t0;
-    const int ntok = static_cast<int>(left < TPW ? left : TPW);
-    const bool first_layer_group = blockIdx.y == 0;
-
-    uint32_t flags = 0;
-    int64_t slot = KVW_PAD_ID;
-    if (lane < ntok) {
-        const int64_t t = t0 + lane;
-        int64_t num_tokens = 0;
-        if (MODE != kPrecomputed) num_tokens = device_num_tokens(a, first_layer_group && t == 0);
-        slot = resolve_slot<MODE>(a, t, num_tokens, flags);
-        if (MODE != kPrecomputed && a.slots_out && first_layer_group) a.slots_out[t] = slot;
-        if (slot >= c.rows_per_layer) {
-            if (c.num_layers > 0) flags |= KVW_FLAG_SLOT_OOB;
-            slot = KVW_PAD_ID;
-        }
-        if (slot < 0) slot = KVW_PAD_ID;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint64_t item = static_cast<uint64_t>(blockIdx.x) * kScatterWaves + wave;
+    uint64_t t64;
+    uint32_t r;
+    if (c.items_log2 >= 0) {
+        t64 = item >> c.items_log2;
+        r = static_cast<uint32_t>(item & ((1u << c.items_log2) - 1));
+    } else {
+        t64 = item / c.items_per_token;
+        r = static_cast<uint32_t>(item - t64 * c.items_per_token);
     }
-    if (!first_layer_group) flags = 0;  // report each condition from one layer group only
-    raise_flags(a.err_flag, flags);
+    if (t64 >= static_cast<uint64_t>(c.max_num_tokens)) return;
+    const int64_t t = static_cast<int64_t>(t64);
+    const uint32_t plane = r >= c.slices_per_row ? 1u : 0u;
+    const uint32_t slice = r - plane * c.slices_per_row;
+    const int64_t off = static_cast<int64_t>(slice) * kSliceBytes + static_cast<int64_t>(lane) * 16;
+    const int64_t slot = slots[t];
+    if (slot >= c.rows_per_layer) {  // beyond the cache: skipped, reported once per token
+        if (blockIdx.y == 0 && r == 0 && lane == 0) raise_flags(err_flag, KVW_FLAG_SLOT_OOB);
+        return;
+    }
+    if (slot < 0 || off >= c.bytes_per_token) return;
+    const uint8_t *src = (plane ? c.value : c.key) + t * c.kv_token_stride + off;
+    uint8_t *dst = (plane ? c.v_cache : c.k_cache) + slot * c.bytes_per_token + off;
+    // coordinate n = (l*B + slot/T)*T + slot%T = l*B*T + slot
+    for (int64_t l = blockIdx.y; l < c.num_layers; l += gridDim.y)
+        store16<KVW_NT_STORES>(dst + l * c.rows_per_layer * c.bytes_per_token,
+                               load16<KVW_NT_LOADS>(src + l * c.kv_layer_stride));
+}
 
-    const int l_begin = blockIdx.y * c.layers_per_wave;
-    const int l_end = min(c.num_layers, l_begin + c.layers_per_wave);
+// One wave per token and layer group (blockIdx.y): the wave first issues the
+// loads of the token's K and V rows for the group's first layer, then
+// resolves the slot with scalar loads (the token is wave-uniform) while they
+// are in flight, then stores.  Rows longer than CH KiB are copied in
+// further CH KiB segments once the slot is known.
+template <int MODE, int CH>
+__global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a, CopyArgs c)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * kFusedWaves +
+                      __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (t >= a.max_num_tokens) return;  // whole wave: this kernel has no barrier
+    const int l0 = blockIdx.y * c.layers_per_wave;
+    const int l1 = min(c.num_layers, l0 + c.layers_per_wave);
     const int64_t bpt = c.bytes_per_token;
     const int64_t lane_off = static_cast<int64_t>(lane) * 16;
+    const uint8_t *ksrc = c.key + t * c.kv_token_stride + lane_off;
+    const uint8_t *vsrc = c.value + t * c.kv_token_stride + lane_off;
 
-    for (int l = l_begin; l < l_end; ++l) {
-        const uint8_t *ksrc = c.key + l * c.kv_layer_stride + t0 * c.kv_token_stride + lane_off;
-        const uint8_t *vsrc = c.value + l * c.kv_layer_stride + t0 * c.kv_token_stride + lane_off;
-        uint8_t *kdst = c.k_cache + static_cast<int64_t>(l) * c.rows_per_layer * bpt + lane_off;
-        uint8_t *vdst = c.v_cache + static_cast<int64_t>(l) * c.rows_per_layer * bpt + lane_off;
-        for (int k0 = 0; k0 < ntok; k0 += U) {
-            int64_t s[U];
+    uint32_t flags = 0;
+    const int64_t num_tokens = device_num_tokens(a, flags);
+    if (t != 0) flags = 0;
+    const bool real = t < num_tokens;  // rows of padded tokens are not read
+    u32x4 kr[CH], vr[CH];
+    if (real && l0 < l1) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) s[u] = (k0 + u < ntok) ? wave_bcast64(slot, k0 + u) : -1;
-            for (int64_t seg = 0; seg < bpt; seg += CH * kSliceBytes) {
-                u32x4 kr[U][CH], vr[U][CH];
+        for (int ch = 0; ch < CH; ++ch) {
+            if (lane_off + ch * kSliceBytes < bpt) {
+                kr[ch] = load16<KVW_NT_LOADS>(ksrc + l0 * c.kv_layer_stride + ch * kSliceBytes);
+                vr[ch] = load16<KVW_NT_LOADS>(vsrc + l0 * c.kv_layer_stride + ch * kSliceBytes);
+            }
+        }
+    }
+    int64_t slot = resolve_slot<MODE>(a, t, num_tokens, flags);
+    const bool first_group = blockIdx.y == 0;
+    if (first_group && lane == 0 && a.slots_out) a.slots_out[t] = slot;
+    if (slot >= c.rows_per_layer) {
+        if (c.num_layers > 0) flags |= KVW_FLAG_SLOT_OOB;
+        slot = KVW_PAD_ID;
+    }
+    if (first_group && lane == 0) raise_flags(a.err_flag, flags);
+    if (slot < 0 || !real) return;
+
+    uint8_t *kdst = c.k_cache + slot * bpt + lane_off;
+    uint8_t *vdst = c.v_cache + slot * bpt + lane_off;
+    for (int l = l0; l < l1; ++l) {
+        const int64_t src_l = l * c.kv_layer_stride;
+        const int64_t dst_l = static_cast<int64_t>(l) * c.rows_per_layer * bpt;  // l*B*T rows
+        for (int64_t seg = 0; seg < bpt; seg += CH * kSliceBytes) {
+            if (l != l0 || seg != 0) {
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if (s[u] < 0) continue;
-                    const int64_t src = (k0 + u) * c.kv_token_stride + seg;
-#pragma unroll
-                    for (int ch = 0; ch < CH; ++ch) {
-                        if (seg + lane_off + ch * kSliceBytes < bpt) {
-                            kr[u][ch] = load16<KVW_NT_LOADS>(ksrc + src + ch * kSliceBytes);
-                            vr[u][ch] = load16<KVW_NT_LOADS>(vsrc + src + ch * kSliceBytes);
-                        }
+                for (int ch = 0; ch < CH; ++ch) {
+                    if (seg + lane_off + ch * kSliceBytes < bpt) {
+                        kr[ch] = load16<KVW_NT_LOADS>(ksrc + src_l + seg + ch * kSliceBytes);
+                        vr[ch] = load16<KVW_NT_LOADS>(vsrc + src_l + seg + ch * kSliceBytes);
                     }
                 }
+            }
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if (s[u] < 0) continue;
-                    // coordinate n = (l*B + s/T)*T + s%T = l*B*T + s (the layer base is in kdst)
-                    const int64_t dst = s[u] * bpt + seg;
-#pragma unroll
-                    for (int ch = 0; ch < CH; ++ch) {
-                        if (seg + lane_off + ch * kSliceBytes < bpt) {
-                            store16<KVW_NT_STORES>(kdst + dst + ch * kSliceBytes, kr[u][ch]);
-                            store16<KVW_NT_STORES>(vdst + dst + ch * kSliceBytes, vr[u][ch]);
-                        }
-                    }
+            for (int ch = 0; ch < CH; ++ch) {
+                if (seg + lane_off + ch * kSliceBytes < bpt) {
+                    store16<KVW_NT_STORES>(kdst + dst_l + seg + ch * kSliceBytes, kr[ch]);
+                    store16<KVW_NT_STORES>(vdst + dst_l + seg + ch * kSliceBytes, vr[ch]);
                 }
             }
         }
@@ -399,8 +426,8 @@ unsigned grid_for(int64_t items, int64_t per_block)
     return static_cast<unsigned>((items + per_block - 1) / per_block);
 }
 
-#define KVW_REQUIRE(cond, ...)                                 \
-    do {                                                       \
+#define KVW_REQUIRE(cond, ...)                                      \
+    do {                                                            \
         if (!(cond)) return fail(KVW_ERR_INVALID_ARG, __VA_ARGS__); \
     } while (0)
 
@@ -459,26 +486,24 @@ MapArgs make_map_args(const int32_t *qsl, int32_t num_reqs, const int64_t *posit
     return a;
 }
 
-template <int MODE, int TPW, int U, int CH>
-void launch_kv_write(const MapArgs &a, const CopyArgs &c, int64_t max_num_tokens, int32_t groups,
-                     hipStream_t s)
+void launch_slot_mapping(int mode, const MapArgs &a, hipStream_t s)
 {
-    const int64_t waves = (max_num_tokens + TPW - 1) / TPW;
-    const dim3 grid(grid_for(waves, kWavesPerBlock), static_cast<unsigned>(groups));
-    hipLaunchKernelGGL((kv_write_kernel<MODE, TPW, U, CH>), grid, dim3(kBlockThreads), 0, s, a, c);
+    const dim3 grid(grid_for(a.max_num_tokens, kBlockThreads));
+    if (mode == kPaged) hipLaunchKernelGGL(slot_mapping_kernel<kPaged>, grid, dim3(kBlockThreads), 0, s, a);
+    else hipLaunchKernelGGL(slot_mapping_kernel<kRanges>, grid, dim3(kBlockThreads), 0, s, a);
 }
 
 template <int MODE>
-void dispatch_kv_write(const MapArgs &a, const CopyArgs &c, int64_t max_num_tokens, int32_t groups,
-                       hipStream_t s)
+void launch_fused(const MapArgs &a, const CopyArgs &c, unsigned groups, hipStream_t s)
 {
-    constexpr int TPW = KVW_TOKENS_PER_WAVE;
-    constexpr int U = KVW_ROWS_IN_FLIGHT;
-    const int64_t slices = (c.bytes_per_token + kSliceBytes - 1) / kSliceBytes;
-    if (slices <= 1) launch_kv_write<MODE, TPW, U, 1>(a, c, max_num_tokens, groups, s);
-    else if (slices == 2) launch_kv_write<MODE, TPW, U, 2>(a, c, max_num_tokens, groups, s);
-    else if (slices == 3) launch_kv_write<MODE, TPW, U, 3>(a, c, max_num_tokens, groups, s);
-    else launch_kv_write<MODE, TPW, (U > 2 ? U / 2 : 1), 4>(a, c, max_num_tokens, groups, s);
+    const dim3 grid(grid_for(a.max_num_tokens, kFusedWaves), groups);
+    const dim3 block(kFusedThreads);
+    switch (c.slices_per_row) {
+    case 1: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 1>), grid, block, 0, s, a, c); break;
+    case 2: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 2>), grid, block, 0, s, a, c); break;
+    case 3: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 3>), grid, block, 0, s, a, c); break;
+    default: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, kMaxSlicesPerLane>), grid, block, 0, s, a, c);
+    }
 }
 
 }  // namespace
@@ -510,8 +535,7 @@ kvw_status kvw_slot_mapping_paged(const int32_t *query_start_loc, int32_t num_re
     a.table_stride = block_table_stride;
     a.num_blocks_per_req = num_blocks_per_req;
     a.slots_out = slot_mapping;
-    hipLaunchKernelGGL(slot_mapping_kernel<kPaged>, dim3(grid_for(max_num_tokens, kBlockThreads)),
-                       dim3(kBlockThreads), 0, reinterpret_cast<hipStream_t>(stream), a);
+    launch_slot_mapping(kPaged, a, reinterpret_cast<hipStream_t>(stream));
     return launched(fn);
 }
 
@@ -538,8 +562,7 @@ kvw_status kvw_slot_mapping_ranges(const int32_t *query_start_loc, int32_t num_r
     a.num_ranges = num_ranges;
     a.range_stride = range_stride;
     a.slots_out = slot_mapping;
-    hipLaunchKernelGGL(slot_mapping_kernel<kRanges>, dim3(grid_for(max_num_tokens, kBlockThreads)),
-                       dim3(kBlockThreads), 0, reinterpret_cast<hipStream_t>(stream), a);
+    launch_slot_mapping(kRanges, a, reinterpret_cast<hipStream_t>(stream));
     return launched(fn);
 }
 
@@ -630,7 +653,8 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
     KVW_REQUIRE(!g.err_flag || aligned(g.err_flag, 4), "%s: err_flag misaligned", fn);
 
     kvw_status st = KVW_OK;
-    if (g.mode == KVW_SLOTS_PAGED || g.mode == KVW_SLOTS_RANGES) {
+    const bool fused = g.mode != KVW_SLOTS_PRECOMPUTED;
+    if (fused) {
         st = check_mapping_common(fn, g.query_start_loc, g.num_reqs, g.positions, g.max_num_tokens,
                                   g.block_size, g.err_flag);
         if (st != KVW_OK) return st;
@@ -643,7 +667,7 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
                     "%s: slot_mapping_out misaligned", fn);
     }
     if (g.max_num_tokens == 0) return KVW_OK;
-    if (g.mode == KVW_SLOTS_PRECOMPUTED)
+    if (!fused)
         KVW_REQUIRE(g.slot_mapping_in && aligned(g.slot_mapping_in, 8),
                     "%s: slot_mapping_in is NULL or misaligned", fn);
     if (g.num_layers > 0) {
@@ -655,7 +679,29 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
                         g.kv_token_stride % 16 == 0,
                     "%s: K/V strides must be non-negative multiples of 16", fn);
     }
-    if (g.mode == KVW_SLOTS_PRECOMPUTED && g.num_layers == 0) return KVW_OK;
+
+    CopyArgs c{};
+    c.key = static_cast<const uint8_t *>(g.key);
+    c.value = static_cast<const uint8_t *>(g.value);
+    c.k_cache = static_cast<uint8_t *>(g.k_cache);
+    c.v_cache = static_cast<uint8_t *>(g.v_cache);
+    c.kv_layer_stride = g.kv_layer_stride;
+    c.kv_token_stride = g.kv_token_stride;
+    c.rows_per_layer = rows_per_layer;
+    c.bytes_per_token = g.bytes_per_token;
+    c.max_num_tokens = g.max_num_tokens;
+    c.num_layers = g.num_layers;
+    c.layers_per_wave = 1;
+    c.slices_per_row = static_cast<uint32_t>((g.bytes_per_token + kSliceBytes - 1) / kSliceBytes);
+    c.items_per_token = 2 * c.slices_per_row;
+    c.items_log2 = -1;
+    for (int b = 0; b < 31; ++b)
+        if (c.items_per_token == (1u << b)) c.items_log2 = b;
+    const unsigned layer_grid =
+        g.num_layers < 1 ? 1u : (static_cast<unsigned>(g.num_layers) < kMaxGridY ? g.num_layers : kMaxGridY);
+    const int64_t scatter_blocks =
+        (g.max_num_tokens * static_cast<int64_t>(c.items_per_token) + kScatterWaves - 1) / kScatterWaves;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
     MapArgs a = make_map_args(g.query_start_loc, g.num_reqs, g.positions, g.max_num_tokens,
                               g.block_size, g.err_flag);
@@ -667,29 +713,30 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
     a.range_cum = g.range_cum;
     a.num_ranges = g.num_ranges;
     a.range_stride = g.range_stride;
-    a.slots_in = g.slot_mapping_in;
     a.slots_out = g.slot_mapping_out;
 
-    CopyArgs c{};
-    c.key = static_cast<const uint8_t *>(g.key);
-    c.value = static_cast<const uint8_t *>(g.value);
-    c.k_cache = static_cast<uint8_t *>(g.k_cache);
-    c.v_cache = static_cast<uint8_t *>(g.v_cache);
-    c.kv_layer_stride = g.kv_layer_stride;
-    c.kv_token_stride = g.kv_token_stride;
-    c.rows_per_layer = rows_per_layer;
-    c.bytes_per_token = g.bytes_per_token;
-    c.num_layers = g.num_layers;
-    c.layers_per_wave = g.num_layers < KVW_LAYERS_PER_WAVE ? (g.num_layers > 0 ? g.num_layers : 1)
-                                                           : KVW_LAYERS_PER_WAVE;
-    if (g.num_layers / c.layers_per_wave >= kMaxGridY)  // keep gridDim.y within its limit
-        c.layers_per_wave = g.num_layers / kMaxGridY + 1;
-    const int32_t groups = g.num_layers > 0 ? (g.num_layers + c.layers_per_wave - 1) / c.layers_per_wave : 1;
-
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (g.mode == KVW_SLOTS_PRECOMPUTED) dispatch_kv_write<kPrecomputed>(a, c, g.max_num_tokens, groups, s);
-    else if (g.mode == KVW_SLOTS_PAGED) dispatch_kv_write<kPaged>(a, c, g.max_num_tokens, groups, s);
-    else dispatch_kv_write<kRanges>(a, c, g.max_num_tokens, groups, s);
+    const bool two_pass = !fused || g.slot_mapping_out != nullptr;
+    if (two_pass && g.num_layers > 0 && scatter_blocks > static_cast<int64_t>(kMaxGridX))
+        return fail(KVW_ERR_UNSUPPORTED, "%s: %lld token rows of %lld bytes exceed one launch", fn,
+                    (long long)g.max_num_tokens, (long long)g.bytes_per_token);
+    if (two_pass) {
+        // slots (unless given), then the slice-granular scatter that reads them
+        if (fused) {
+            launch_slot_mapping(g.mode, a, s);
+            if (kvw_status e = launched(fn); e != KVW_OK) return e;
+        }
+        if (g.num_layers == 0) return KVW_OK;
+        const int64_t *slots = fused ? g.slot_mapping_out : g.slot_mapping_in;
+        hipLaunchKernelGGL(kv_scatter_kernel, dim3(static_cast<unsigned>(scatter_blocks), layer_grid),
+                           dim3(kScatterThreads), 0, s, slots, c, g.err_flag);
+        return launched(fn);
+    }
+    // fused mode without a slot-mapping output: one kernel, one wave per token
+    if (g.num_layers > static_cast<int32_t>(kMaxGridY)) c.layers_per_wave = g.num_layers / kMaxGridY + 1;
+    const unsigned groups =
+        g.num_layers < 1 ? 1u : static_cast<unsigned>((g.num_layers + c.layers_per_wave - 1) / c.layers_per_wave);
+    if (g.mode == KVW_SLOTS_PAGED) launch_fused<kPaged>(a, c, groups, s);
+    else launch_fused<kRanges>(a, c, groups, s);
     return launched(fn);
 }
 

@@ -20,6 +20,8 @@ pytestmark = pytest.mark.gpu
 SMALL = small_cases()
 MODES = {"precomputed": kvw.KVW_SLOTS_PRECOMPUTED, "paged": kvw.KVW_SLOTS_PAGED,
          "ranges": kvw.KVW_SLOTS_RANGES}
+# fused modes run as two kernels when the slot mapping is kept, as one kernel otherwise
+WRITE_MODES = ["precomputed", "paged", "ranges", "paged-noslots", "ranges-noslots"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -33,7 +35,10 @@ def _gpu():
 
 def run_kv_write(w, d, mode, caches, key, value, slots_in=None, block_size=None, num_blocks=None,
                  over=None):
+    """Returns (slot_mapping_out or None, flags)."""
     over = over or {}
+    keep = not mode.endswith("-noslots")
+    mode = mode.replace("-noslots", "")
     flag = new_flag()
     sm_out = torch.full((w.max_num_tokens,), 777, dtype=torch.int64, device=DEV)
     kw = dict(mode=MODES[mode], key=key, value=value, k_cache=caches.k, v_cache=caches.v,
@@ -43,7 +48,7 @@ def run_kv_write(w, d, mode, caches, key, value, slots_in=None, block_size=None,
         kw["slot_mapping_in"] = dev(slots_in)
     else:
         kw.update(query_start_loc=d.qsl, num_reqs=w.num_reqs, positions=d.positions,
-                  slot_mapping_out=sm_out)
+                  slot_mapping_out=sm_out if keep else None)
         if mode == "paged":
             kw.update(block_table=over.get("block_table", d.block_table),
                       num_blocks_per_req=over.get("nbpr", d.nbpr))
@@ -52,23 +57,23 @@ def run_kv_write(w, d, mode, caches, key, value, slots_in=None, block_size=None,
                       range_cum=over.get("rc", d.rc), num_ranges=over.get("nr", d.nr))
     kvw.kvw_kv_write(**kw)
     torch.cuda.synchronize()
-    return host(sm_out), int(flag.item())
+    return (host(sm_out) if keep else None), int(flag.item())
 
 
 def check_kv_write(w, mode, **over):
     say(f"[kv_write] {w.describe()} mode={mode}")
     d = DeviceInputs(w)
-    variant = "ranges" if mode == "ranges" else "paged"
+    variant = "ranges" if mode.startswith("ranges") else "paged"
     o_slots, o_flags = oracle_slots(w, variant)
     key_h, value_h = w.kv_plane(0), w.kv_plane(1)
     key = dev(key_h).view(w.num_layers, w.max_num_tokens, w.num_kv_heads, w.head_dim)
     value = dev(value_h).view_as(key)
     caches = Caches(w.num_layers, w.num_blocks, w.block_size, w.row_elems)
     sm, flags = run_kv_write(w, d, mode, caches, key, value, slots_in=o_slots)
-    if mode != "precomputed":
-        assert np.array_equal(sm, o_slots), f"{w.name}: fused slot_mapping_out differs"
-    else:
+    if mode == "precomputed":
         o_flags = 0
+    elif sm is not None:
+        assert np.array_equal(sm, o_slots), f"{w.name}: fused slot_mapping_out differs"
     c_flags = compare_caches(w, caches, o_slots, key_h, value_h, w.num_blocks, w.block_size)
     assert flags == o_flags | c_flags
 
@@ -149,21 +154,22 @@ def test_long_context_slots_and_expansion(r):
 # ---------------------------------------------------------------------------
 # K/V write
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("mode", ["precomputed", "paged", "ranges"])
+@pytest.mark.parametrize("mode", WRITE_MODES)
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
 def test_kv_write_small(w, mode):
     check_kv_write(w, mode)
 
 
-@pytest.mark.parametrize("mode", ["paged", "ranges"])
+@pytest.mark.parametrize("mode", WRITE_MODES[1:])
 @pytest.mark.parametrize("name", ["tiny_prefill", "decode_step", "mixed_chunked"])
 def test_kv_write_study(name, mode):
     check_kv_write(config(name), mode)
 
 
+@pytest.mark.parametrize("keep_slots", [True, False], ids=["slots", "noslots"])
 @pytest.mark.parametrize("variant", ["paged", "ranges_bs32", "ranges_expanded"])
 @pytest.mark.parametrize("r", [1, 4096])
-def test_kv_write_long_context(r, variant):
+def test_kv_write_long_context(r, variant, keep_slots):
     """128K context, fused write of 131,072 tokens into an 8 GiB cache, whole cache compared."""
     if variant == "paged" and r != 1:
         pytest.skip("the paged table does not depend on the range count")
@@ -176,6 +182,7 @@ def test_kv_write_long_context(r, variant):
     key = dev(key_h).view(1, w.max_num_tokens, w.num_kv_heads, w.head_dim)
     value = dev(value_h).view_as(key)
     bs_k, nb_k = w.kernel_block_size, w.kernel_num_blocks
+    suffix = "" if keep_slots else "-noslots"
     caches = Caches(1, nb_k, bs_k, w.row_elems)
     o_slots, _ = orc.slot_mapping_ranges(w.query_start_loc, w.num_reqs, w.positions,
                                          w.max_num_tokens, w.range_start, w.range_len,
@@ -183,23 +190,23 @@ def test_kv_write_long_context(r, variant):
     if variant == "paged":
         kt = torch.empty((w.max_num_reqs, w.table_stride * k), dtype=torch.int32, device=DEV)
         kvw.kvw_map_to_kernel_blocks(d.block_table, d.nbpr, w.block_size, bs_k, kt)
-        sm, flags = run_kv_write(w, d, "paged", caches, key, value, block_size=bs_k,
+        sm, flags = run_kv_write(w, d, "paged" + suffix, caches, key, value, block_size=bs_k,
                                  num_blocks=nb_k, over=dict(block_table=kt, nbpr=d.nbpr * k))
     elif variant == "ranges_expanded":
         outs = [torch.empty_like(d.rs) for _ in range(3)] + [torch.empty_like(d.nr)]
         kvw.kvw_map_ranges_to_kernel_blocks(d.rs, d.rl, d.rc, d.nr, w.block_size, bs_k, *outs)
-        sm, flags = run_kv_write(w, d, "ranges", caches, key, value, block_size=bs_k,
+        sm, flags = run_kv_write(w, d, "ranges" + suffix, caches, key, value, block_size=bs_k,
                                  num_blocks=nb_k,
                                  over=dict(rs=outs[0], rl=outs[1], rc=outs[2], nr=outs[3]))
     else:
-        sm, flags = run_kv_write(w, d, "ranges", caches, key, value, block_size=w.block_size,
-                                 num_blocks=w.num_blocks)
-    assert np.array_equal(sm, o_slots) and flags == 0
+        sm, flags = run_kv_write(w, d, "ranges" + suffix, caches, key, value,
+                                 block_size=w.block_size, num_blocks=w.num_blocks)
+    assert (sm is None or np.array_equal(sm, o_slots)) and flags == 0
     # slots are identical in manager and kernel units, so one oracle pass checks every variant
     assert compare_caches(w, caches, o_slots, key_h, value_h, nb_k, bs_k) == 0
 
 
-@pytest.mark.parametrize("mode", ["paged", "ranges"])
+@pytest.mark.parametrize("mode", WRITE_MODES[1:])
 def test_kv_write_32_layers(mode):
     """16,384 tokens x 32 layers in one launch into 2 x 32 GiB cache planes."""
     check_kv_write(config("full_32_layer"), mode)
@@ -247,9 +254,13 @@ def test_flags_and_clamps(variant):
     assert np.array_equal(g, o) and gf == of and of & kvw.KVW_FLAG_NUM_TOKENS
 
 
+@pytest.mark.parametrize("mode", ["paged", "paged-noslots", "ranges", "ranges-noslots"])
+def test_kv_write_flagged(mode):
+    check_kv_write(_flagged_workload(), mode)
+
+
 def test_kv_write_out_of_pool_and_bad_slots():
     w = _flagged_workload()
-    check_kv_write(w, "paged")
     # precomputed slots beyond the cache and below the pad id write nothing
     key_h = w.kv_plane(0)
     rng = np.random.default_rng(4)
