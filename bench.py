@@ -5,15 +5,17 @@ Default workload: 128K context, 16 requests x 8192-token prefill chunks
 block size 16, 8 KV heads x 128 bf16, one layer.  Each request's blocks form
 R contiguous runs placed at random (R in 1, 16, 512, 4096; 4096 = every
 manager block on its own).  A step is the whole hot path for one batch:
-manager->kernel expansion of the variant's mapping structure, then the fused
-slot-map + K/V write (kvw_kv_write keeping the slot mapping).
+manager->kernel expansion of the variant's mapping structure (on a second
+stream: the write does not need it, slot ids being the same at either block
+size) and the fused slot-map + K/V write (kvw_kv_write keeping the slot
+mapping, automatic kernel schedule).
 
   paged_r{R}     expand the block table, fused paged write
   ranges_r{R}    expand the range descriptors, fused range write
 
 `value` is tokens/s of paged_r4096; every variant is reported under
 "variants", with the fused call's time (HIP events on the launch stream)
-and the time of the single-kernel form used when no slot mapping is kept.
+and the time of the one-kernel schedule.
 The roofline entry is for kv_scatter_kernel, the dominant kernel, timed
 alone on the headline variant's slots.  The CPU baseline times the CPU
 oracle (test infrastructure) on the same batch.
@@ -56,6 +58,12 @@ def parse():
                    help="skip the CPU oracle timing (e.g. under a profiler)")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="approximate CPU time budget of the oracle baseline")
+    p.add_argument("--workload", default="long_context",
+                   choices=["long_context", "tiny_prefill", "decode_step", "mixed_chunked",
+                            "full_32_layer"],
+                   help="long_context (default) is the 128K study above; the others time the\n"
+                        "fused write (paged and ranges) on that config, flushing L2 and MALL\n"
+                        "before every step; ms_per_step is then the fused call's event time")
     p.add_argument("--copy-calibration-mib", type=int, default=512,
                    help="size of the plain device copy timed as the practical ceiling "
                         "(read + write of this many MiB); 0 to skip")
@@ -99,6 +107,9 @@ def main():
     kvw.library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload != "long_context":
+        bench_config(args)
+        return
 
     def d(a):
         a = np.ascontiguousarray(a)
@@ -144,51 +155,56 @@ def main():
 
     results = {}
     scatter = None
+    side = torch.cuda.Stream()  # default priority, like every stream here
     for name in variants:
         kind, _, r = name.partition("_r")
         if kind not in ("paged", "ranges") or not r.isdigit():
             raise SystemExit(f"unknown variant {name}")
         w = long_context(int(r))
         qsl, pos = d(w.query_start_loc), d(w.positions)
+        # Slot ids do not change under manager->kernel expansion (same memory at a finer
+        # block size), so the write takes the manager-unit mapping and the expansion, whose
+        # output only the attention side reads, runs on a second stream alongside it.
         if kind == "paged":
             bt, nb = d(w.block_table), d(w.num_blocks_per_req)
             kt = torch.empty((w.max_num_reqs, w.table_stride * k), dtype=torch.int32, device=dev)
-            nb_kernel = nb * k
             expand_bytes = w.block_table.nbytes + w.num_blocks_per_req.nbytes + kt.numel() * 4
-            mapping = dict(block_table=kt, num_blocks_per_req=nb_kernel)
+            mapping = dict(block_table=bt, num_blocks_per_req=nb)
 
             def expand(bt=bt, nb=nb, kt=kt, w=w):
-                kvw.kvw_map_to_kernel_blocks(bt, nb, w.block_size, bs_k, kt)
+                kvw.kvw_map_to_kernel_blocks(bt, nb, w.block_size, bs_k, kt, stream=side)
             mode = kvw.KVW_SLOTS_PAGED
         else:
             rs, rl, rc, nr = (d(a) for a in (w.range_start, w.range_len, w.range_cum, w.num_ranges))
             outs = [torch.empty_like(rs) for _ in range(3)] + [torch.empty_like(nr)]
             expand_bytes = 2 * (3 * w.range_start.nbytes + w.num_ranges.nbytes)
-            mapping = dict(range_start=outs[0], range_len=outs[1], range_cum=outs[2],
-                           num_ranges=outs[3])
+            mapping = dict(range_start=rs, range_len=rl, range_cum=rc, num_ranges=nr)
 
             def expand(rs=rs, rl=rl, rc=rc, nr=nr, outs=outs, w=w):
-                kvw.kvw_map_ranges_to_kernel_blocks(rs, rl, rc, nr, w.block_size, bs_k, *outs)
+                kvw.kvw_map_ranges_to_kernel_blocks(rs, rl, rc, nr, w.block_size, bs_k, *outs,
+                                                    stream=side)
             mode = kvw.KVW_SLOTS_RANGES
 
-        def write(slots_out, mode=mode, mapping=mapping, qsl=qsl, pos=pos, w=w):
+        def write(schedule, mode=mode, mapping=mapping, qsl=qsl, pos=pos, w=w):
             kvw.kvw_kv_write(mode=mode, key=key, value=value, k_cache=cache[0], v_cache=cache[1],
-                             num_blocks=nb_k, block_size=bs_k, query_start_loc=qsl,
-                             num_reqs=w.num_reqs, positions=pos, slot_mapping_out=slots_out,
-                             **mapping)
+                             num_blocks=w.num_blocks, block_size=w.block_size,
+                             query_start_loc=qsl, num_reqs=w.num_reqs, positions=pos,
+                             slot_mapping_out=sm_out, schedule=schedule, **mapping)
 
         def step(ev, expand=expand, write=write):
+            side.wait_stream(stream)
             expand()
             if ev is not None:
                 ev[0].record(stream)
-            write(sm_out)
+            write(kvw.KVW_SCHEDULE_AUTO)
             if ev is not None:
                 ev[1].record(stream)
+            stream.wait_stream(side)
 
         def single(ev, write=write):
             if ev is not None:
                 ev[0].record(stream)
-            write(None)
+            write(kvw.KVW_SCHEDULE_ONE_KERNEL)
             if ev is not None:
                 ev[1].record(stream)
 
@@ -221,12 +237,12 @@ def main():
             torch.cuda.synchronize()
             slots = sm_out.clone()
 
-            def scatter_only(ev, slots=slots):
+            def scatter_only(ev, slots=slots, w=w):
                 if ev is not None:
                     ev[0].record(stream)
                 kvw.kvw_kv_write(mode=kvw.KVW_SLOTS_PRECOMPUTED, key=key, value=value,
-                                 k_cache=cache[0], v_cache=cache[1], num_blocks=nb_k,
-                                 block_size=bs_k, slot_mapping_in=slots)
+                                 k_cache=cache[0], v_cache=cache[1], num_blocks=w.num_blocks,
+                                 block_size=w.block_size, slot_mapping_in=slots)
                 if ev is not None:
                     ev[1].record(stream)
             _, sc_ms = timed(scatter_only, args.warmup, args.steps)
@@ -303,6 +319,91 @@ def main():
         "copy_ceiling": copy_ceiling,
         "variants": {k_: {kk: (round(vv, 6) if isinstance(vv, float) else vv)
                           for kk, vv in v.items()} for k_, v in results.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_config(args):
+    """Fused write (paged, ranges) on one of the other study configs."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_46_amd as kvw
+    from workloads import BF16_SENTINEL, config
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def d(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    w = config(args.workload)
+    L, M, H, D = w.num_layers, w.max_num_tokens, w.num_kv_heads, w.head_dim
+    log(f"[bench] workload {w.describe()}")
+    t = time.time()
+    key = d(w.kv_plane(0)).view(L, M, H, D)
+    value = d(w.kv_plane(1)).view(L, M, H, D)
+    log(f"[bench] K/V generated and uploaded in {time.time() - t:.1f}s")
+    rows = L * w.num_blocks * w.block_size
+    cache = torch.full((2, rows, H * D), BF16_SENTINEL, dtype=torch.int16, device=dev)
+    sm_out = torch.empty(M, dtype=torch.int64, device=dev)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)  # evicts L2 and MALL
+    qsl, pos = d(w.query_start_loc), d(w.positions)
+    maps = {
+        "paged": (kvw.KVW_SLOTS_PAGED, dict(block_table=d(w.block_table),
+                                            num_blocks_per_req=d(w.num_blocks_per_req))),
+        "ranges": (kvw.KVW_SLOTS_RANGES, dict(range_start=d(w.range_start),
+                                              range_len=d(w.range_len), range_cum=d(w.range_cum),
+                                              num_ranges=d(w.num_ranges))),
+    }
+    real = w.num_tokens
+    fused_bytes = real * L * 4 * w.bytes_per_token + real * 16
+    results = {}
+    schedules = (("", kvw.KVW_SCHEDULE_AUTO), ("_two_kernels", kvw.KVW_SCHEDULE_TWO_KERNELS),
+                 ("_one_kernel", kvw.KVW_SCHEDULE_ONE_KERNEL))
+    for name, (mode, mapping) in maps.items():
+        for suffix, schedule in schedules:
+            def call(mode=mode, mapping=mapping, schedule=schedule):
+                kvw.kvw_kv_write(mode=mode, key=key, value=value, k_cache=cache[0],
+                                 v_cache=cache[1], num_blocks=w.num_blocks,
+                                 block_size=w.block_size, query_start_loc=qsl,
+                                 num_reqs=w.num_reqs, positions=pos, slot_mapping_out=sm_out,
+                                 schedule=schedule, **mapping)
+            for _ in range(args.warmup):
+                call()
+            times = []
+            for i in range(args.steps):
+                scratch.fill_(i & 0xFF)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                call()
+                e1.record(stream)
+                e1.synchronize()
+                times.append(e0.elapsed_time(e1))
+            ms = statistics.fmean(times)
+            key_ = name + suffix
+            results[key_] = {"ms_avg": ms, "ms_p10": float(np.percentile(times, 10)),
+                             "ms_p90": float(np.percentile(times, 90)),
+                             "tokens_per_s": real / (ms * 1e-3),
+                             "gbps": fused_bytes / (ms * 1e-3) / 1e9,
+                             "frac_of_peak": fused_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+            r = results[key_]
+            log(f"[bench] {key_:20s} {ms * 1e3:8.1f} us  {r['gbps']:6.0f} GB/s "
+                f"({100 * r['frac_of_peak']:.1f}%)  {r['tokens_per_s'] / 1e6:.2f} M tokens/s")
+    head = results["paged"]
+    line = {
+        "metric": METRIC, "value": round(head["tokens_per_s"], 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(head["ms_avg"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int64", "data": "synthetic",
+        "config": {"workload": w.name, "requests": w.num_reqs, "tokens_per_step": real,
+                   "max_num_tokens": M, "layers": L, "block_size": w.block_size,
+                   "num_blocks": w.num_blocks, "kv_heads": H, "head_dim": D, "payload": "bf16",
+                   "variant": "paged", "timing": "fused call, HIP events, L2/MALL flushed"},
+        "hbm_gbps": round(head["gbps"], 1), "hbm_frac_of_peak": round(head["frac_of_peak"], 4),
+        "algorithmic_bytes_per_step": fused_bytes,
+        "variants": {k_: {kk: round(vv, 6) for kk, vv in v.items()} for k_, v in results.items()},
     }
     print(json.dumps(line), flush=True)
 

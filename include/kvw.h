@@ -75,6 +75,13 @@ typedef enum kvw_status {
 #define KVW_SLOTS_PAGED 1       /* resolve through the block table (fused) */
 #define KVW_SLOTS_RANGES 2      /* resolve through range descriptors (fused) */
 
+/* Kernel schedules of kvw_kv_write in the paged and range modes. */
+#define KVW_SCHEDULE_AUTO 0        /* two kernels for large writes when slot_mapping_out is set */
+#define KVW_SCHEDULE_TWO_KERNELS 1 /* slot mapping kernel, then the scatter (needs slot_mapping_out) */
+#define KVW_SCHEDULE_ONE_KERNEL 2  /* one kernel resolves each token's slot and copies its rows */
+/* AUTO picks two kernels from this many token rows (max_num_tokens * num_layers) up. */
+#define KVW_TWO_KERNEL_MIN_ROWS 32768
+
 /* KVW_ABI_VERSION of the loaded library. */
 int32_t kvw_abi_version(void);
 
@@ -201,6 +208,7 @@ typedef struct kvw_kv_write_args {
     void *v_cache;                     /* same layout as k_cache */
     int64_t bytes_per_token;           /* multiple of 16 */
     int32_t *err_flag;                 /* device int32 or NULL */
+    int32_t schedule;                  /* KVW_SCHEDULE_*; ignored in the precomputed mode */
 } kvw_kv_write_args;
 
 /* sizeof(kvw_kv_write_args) as compiled into the library. */
@@ -221,14 +229,18 @@ size_t kvw_kv_write_args_size(void);
  * stored to slot_mapping_out when it is non-NULL (tail padded).
  * Precondition: no two tokens share a slot (else the surviving row is
  * unspecified).
- * Execution: in the paged and range modes with slot_mapping_out set, the
- * call enqueues two kernels on `stream`: the slot mapping (written to
- * slot_mapping_out), then the scatter that reads it; without
- * slot_mapping_out it enqueues one kernel that does both.  The precomputed
- * mode enqueues the scatter only.
- * Errors: KVW_ERR_INVALID_ARG for an unknown mode, NULL required pointers,
- * misalignment, negative sizes, bytes_per_token % 16 != 0, or a cache size
- * beyond int64; KVW_ERR_RANGE_CAP as kvw_slot_mapping_ranges.
+ * Execution: the precomputed mode enqueues one scatter kernel.  In the
+ * paged and range modes the call enqueues either two kernels on `stream`
+ * (the slot mapping, written to slot_mapping_out, then the scatter that
+ * reads it) or one kernel that resolves each token's slot and copies its
+ * rows (and stores slot_mapping_out if set).  KVW_SCHEDULE_AUTO takes two
+ * kernels when slot_mapping_out is set and max_num_tokens * num_layers >=
+ * KVW_TWO_KERNEL_MIN_ROWS (measured crossover on MI355X), one otherwise.
+ * Results are identical either way.
+ * Errors: KVW_ERR_INVALID_ARG for an unknown mode or schedule,
+ * KVW_SCHEDULE_TWO_KERNELS without slot_mapping_out, NULL required
+ * pointers, misalignment, negative sizes, bytes_per_token % 16 != 0, or a
+ * cache size beyond int64; KVW_ERR_RANGE_CAP as kvw_slot_mapping_ranges.
  */
 kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream);
 

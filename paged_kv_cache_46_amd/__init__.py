@@ -9,6 +9,9 @@ from .kvw import (  # noqa: F401
     KVW_FLAG_NUM_TOKENS,
     KVW_FLAG_SLOT_OOB,
     KVW_PAD_ID,
+    KVW_SCHEDULE_AUTO,
+    KVW_SCHEDULE_ONE_KERNEL,
+    KVW_SCHEDULE_TWO_KERNELS,
     KVW_SLOTS_PAGED,
     KVW_SLOTS_PRECOMPUTED,
     KVW_SLOTS_RANGES,

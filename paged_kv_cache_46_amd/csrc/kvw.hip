@@ -10,8 +10,9 @@
 //   expand_blocks_kernel,
 //   expand_ranges_kernel         manager-to-kernel block expansion.
 // kvw_kv_write in a fused mode runs slot_mapping_kernel then
-// kv_scatter_kernel when the caller keeps the slot mapping (the usual case:
-// attention consumes it), and kv_write_fused_kernel otherwise.  The host
+// kv_scatter_kernel for large writes whose slot mapping the caller keeps
+// (the usual case: attention consumes it), and kv_write_fused_kernel
+// otherwise (small writes pay less for one launch than for two).  The host
 // functions at the bottom validate host-side scalars and launch on the
 // caller's stream; include/kvw.h holds the contract.
 //
@@ -665,6 +666,11 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
         if (st != KVW_OK) return st;
         KVW_REQUIRE(!g.slot_mapping_out || aligned(g.slot_mapping_out, 8),
                     "%s: slot_mapping_out misaligned", fn);
+        KVW_REQUIRE(g.schedule == KVW_SCHEDULE_AUTO || g.schedule == KVW_SCHEDULE_TWO_KERNELS ||
+                        g.schedule == KVW_SCHEDULE_ONE_KERNEL,
+                    "%s: unknown schedule %d", fn, g.schedule);
+        KVW_REQUIRE(g.schedule != KVW_SCHEDULE_TWO_KERNELS || g.slot_mapping_out,
+                    "%s: the two-kernel schedule needs slot_mapping_out", fn);
     }
     if (g.max_num_tokens == 0) return KVW_OK;
     if (!fused)
@@ -715,7 +721,11 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
     a.range_stride = g.range_stride;
     a.slots_out = g.slot_mapping_out;
 
-    const bool two_pass = !fused || g.slot_mapping_out != nullptr;
+    const bool two_pass =
+        !fused || (g.slot_mapping_out != nullptr &&
+                   (g.schedule == KVW_SCHEDULE_TWO_KERNELS ||
+                    (g.schedule == KVW_SCHEDULE_AUTO &&
+                     g.max_num_tokens * static_cast<int64_t>(g.num_layers) >= KVW_TWO_KERNEL_MIN_ROWS)));
     if (two_pass && g.num_layers > 0 && scatter_blocks > static_cast<int64_t>(kMaxGridX))
         return fail(KVW_ERR_UNSUPPORTED, "%s: %lld token rows of %lld bytes exceed one launch", fn,
                     (long long)g.max_num_tokens, (long long)g.bytes_per_token);

@@ -21,6 +21,8 @@ KVW_MAX_RANGE_STRIDE = 65536
 KVW_OK, KVW_ERR_INVALID_ARG, KVW_ERR_UNSUPPORTED, KVW_ERR_RANGE_CAP, KVW_ERR_HIP = range(5)
 KVW_FLAG_NUM_TOKENS, KVW_FLAG_COUNT, KVW_FLAG_BAD_BLOCK, KVW_FLAG_SLOT_OOB = 1, 2, 4, 8
 KVW_SLOTS_PRECOMPUTED, KVW_SLOTS_PAGED, KVW_SLOTS_RANGES = 0, 1, 2
+KVW_SCHEDULE_AUTO, KVW_SCHEDULE_TWO_KERNELS, KVW_SCHEDULE_ONE_KERNEL = 0, 1, 2
+KVW_TWO_KERNEL_MIN_ROWS = 32768
 
 
 class KvwError(RuntimeError):
@@ -43,7 +45,7 @@ class kvw_kv_write_args(ctypes.Structure):
         ("block_size", _I32), ("num_layers", _I32), ("num_blocks", _I64),
         ("key", _P), ("value", _P), ("kv_layer_stride", _I64), ("kv_token_stride", _I64),
         ("k_cache", _P), ("v_cache", _P), ("bytes_per_token", _I64),
-        ("err_flag", _P),
+        ("err_flag", _P), ("schedule", _I32),
     ]
 
 
@@ -164,7 +166,7 @@ def kvw_kv_write(*, mode, key, value, k_cache, v_cache, num_blocks, block_size,
                  max_num_tokens=None, slot_mapping_in=None, slot_mapping_out=None,
                  query_start_loc=None, num_reqs=0, positions=None, block_table=None,
                  num_blocks_per_req=None, range_start=None, range_len=None, range_cum=None,
-                 num_ranges=None, err_flag=None, stream=None):
+                 num_ranges=None, err_flag=None, schedule=KVW_SCHEDULE_AUTO, stream=None):
     """K/V scatter into the paged cache, optionally fused with the slot mapping.
 
     key, value: [num_layers, max_num_tokens, H, D] (or [max_num_tokens, H, D]) tensors of a
@@ -205,6 +207,7 @@ def kvw_kv_write(*, mode, key, value, k_cache, v_cache, num_blocks, block_size,
     a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
     a.bytes_per_token = bpt
     a.err_flag = _dev(err_flag, torch.int32, "err_flag", optional=True)
+    a.schedule = int(schedule)
     if mode == KVW_SLOTS_PRECOMPUTED:
         a.slot_mapping_in = _dev(slot_mapping_in, torch.int64, "slot_mapping_in")
     else:

@@ -122,6 +122,10 @@ def test_kv_write_validation(lib):
     assert f(ctypes.byref(_args(block_size=-16)), None) == INVALID
     assert f(ctypes.byref(_args(mode=kvw.KVW_SLOTS_RANGES, range_stride=1 << 20)), None) == RANGE_CAP
     assert f(ctypes.byref(_args(mode=kvw.KVW_SLOTS_PRECOMPUTED, slot_mapping_in=None)), None) == INVALID
+    assert f(ctypes.byref(_args(schedule=3)), None) == INVALID
+    assert "schedule" in _err(lib)
+    assert f(ctypes.byref(_args(schedule=kvw.KVW_SCHEDULE_TWO_KERNELS, slot_mapping_out=None)),
+             None) == INVALID
     assert f(ctypes.byref(_args(max_num_tokens=0)), None) == OK
 
 

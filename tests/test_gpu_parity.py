@@ -20,8 +20,12 @@ pytestmark = pytest.mark.gpu
 SMALL = small_cases()
 MODES = {"precomputed": kvw.KVW_SLOTS_PRECOMPUTED, "paged": kvw.KVW_SLOTS_PAGED,
          "ranges": kvw.KVW_SLOTS_RANGES}
-# fused modes run as two kernels when the slot mapping is kept, as one kernel otherwise
-WRITE_MODES = ["precomputed", "paged", "ranges", "paged-noslots", "ranges-noslots"]
+# fused modes: automatic schedule, forced two-kernel and one-kernel schedules (slot mapping
+# kept), and no slot-mapping output (always one kernel)
+WRITE_MODES = ["precomputed", "paged", "ranges", "paged-two", "ranges-two", "paged-one",
+               "ranges-one", "paged-noslots", "ranges-noslots"]
+SCHEDULES = {"": kvw.KVW_SCHEDULE_AUTO, "two": kvw.KVW_SCHEDULE_TWO_KERNELS,
+             "one": kvw.KVW_SCHEDULE_ONE_KERNEL, "noslots": kvw.KVW_SCHEDULE_AUTO}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -37,13 +41,13 @@ def run_kv_write(w, d, mode, caches, key, value, slots_in=None, block_size=None,
                  over=None):
     """Returns (slot_mapping_out or None, flags)."""
     over = over or {}
-    keep = not mode.endswith("-noslots")
-    mode = mode.replace("-noslots", "")
+    mode, _, sched = mode.partition("-")
+    keep = sched != "noslots"
     flag = new_flag()
     sm_out = torch.full((w.max_num_tokens,), 777, dtype=torch.int64, device=DEV)
     kw = dict(mode=MODES[mode], key=key, value=value, k_cache=caches.k, v_cache=caches.v,
               num_blocks=num_blocks or w.num_blocks, block_size=block_size or w.block_size,
-              max_num_tokens=w.max_num_tokens, err_flag=flag)
+              max_num_tokens=w.max_num_tokens, err_flag=flag, schedule=SCHEDULES[sched])
     if mode == "precomputed":
         kw["slot_mapping_in"] = dev(slots_in)
     else:
@@ -206,7 +210,7 @@ def test_kv_write_long_context(r, variant, keep_slots):
     assert compare_caches(w, caches, o_slots, key_h, value_h, nb_k, bs_k) == 0
 
 
-@pytest.mark.parametrize("mode", WRITE_MODES[1:])
+@pytest.mark.parametrize("mode", ["paged", "ranges", "paged-noslots", "ranges-noslots"])
 def test_kv_write_32_layers(mode):
     """16,384 tokens x 32 layers in one launch into 2 x 32 GiB cache planes."""
     check_kv_write(config("full_32_layer"), mode)
@@ -254,7 +258,7 @@ def test_flags_and_clamps(variant):
     assert np.array_equal(g, o) and gf == of and of & kvw.KVW_FLAG_NUM_TOKENS
 
 
-@pytest.mark.parametrize("mode", ["paged", "paged-noslots", "ranges", "ranges-noslots"])
+@pytest.mark.parametrize("mode", WRITE_MODES[1:])
 def test_kv_write_flagged(mode):
     check_kv_write(_flagged_workload(), mode)
 
