@@ -5,10 +5,10 @@ Default workload: 128K context, 16 requests x 8192-token prefill chunks
 block size 16, 8 KV heads x 128 bf16, one layer.  Each request's blocks form
 R contiguous runs placed at random (R in 1, 16, 512, 4096; 4096 = every
 manager block on its own).  A step is the whole hot path for one batch:
-manager->kernel expansion of the variant's mapping structure (on a second
-stream: the write does not need it, slot ids being the same at either block
-size) and the fused slot-map + K/V write (kvw_kv_write keeping the slot
-mapping, automatic kernel schedule).
+manager->kernel expansion of the variant's mapping structure, then the fused
+slot-map + K/V write (kvw_kv_write keeping the slot mapping, automatic
+kernel schedule) on the manager-unit mapping: slot ids are the same at
+either block size, so the write does not wait on the expanded table.
 
   paged_r{R}     expand the block table, fused paged write
   ranges_r{R}    expand the range descriptors, fused range write
@@ -155,7 +155,6 @@ def main():
 
     results = {}
     scatter = None
-    side = torch.cuda.Stream()  # default priority, like every stream here
     for name in variants:
         kind, _, r = name.partition("_r")
         if kind not in ("paged", "ranges") or not r.isdigit():
@@ -163,8 +162,9 @@ def main():
         w = long_context(int(r))
         qsl, pos = d(w.query_start_loc), d(w.positions)
         # Slot ids do not change under manager->kernel expansion (same memory at a finer
-        # block size), so the write takes the manager-unit mapping and the expansion, whose
-        # output only the attention side reads, runs on a second stream alongside it.
+        # block size), so the write takes the manager-unit mapping; the expansion's output is
+        # for the attention side.  (Running the expansion on a second stream was measured
+        # slower: the cross-stream waits cost more than the 4 us kernel they would hide.)
         if kind == "paged":
             bt, nb = d(w.block_table), d(w.num_blocks_per_req)
             kt = torch.empty((w.max_num_reqs, w.table_stride * k), dtype=torch.int32, device=dev)
@@ -172,7 +172,7 @@ def main():
             mapping = dict(block_table=bt, num_blocks_per_req=nb)
 
             def expand(bt=bt, nb=nb, kt=kt, w=w):
-                kvw.kvw_map_to_kernel_blocks(bt, nb, w.block_size, bs_k, kt, stream=side)
+                kvw.kvw_map_to_kernel_blocks(bt, nb, w.block_size, bs_k, kt)
             mode = kvw.KVW_SLOTS_PAGED
         else:
             rs, rl, rc, nr = (d(a) for a in (w.range_start, w.range_len, w.range_cum, w.num_ranges))
@@ -181,8 +181,7 @@ def main():
             mapping = dict(range_start=rs, range_len=rl, range_cum=rc, num_ranges=nr)
 
             def expand(rs=rs, rl=rl, rc=rc, nr=nr, outs=outs, w=w):
-                kvw.kvw_map_ranges_to_kernel_blocks(rs, rl, rc, nr, w.block_size, bs_k, *outs,
-                                                    stream=side)
+                kvw.kvw_map_ranges_to_kernel_blocks(rs, rl, rc, nr, w.block_size, bs_k, *outs)
             mode = kvw.KVW_SLOTS_RANGES
 
         def write(schedule, mode=mode, mapping=mapping, qsl=qsl, pos=pos, w=w):
@@ -192,14 +191,12 @@ def main():
                              slot_mapping_out=sm_out, schedule=schedule, **mapping)
 
         def step(ev, expand=expand, write=write):
-            side.wait_stream(stream)
             expand()
             if ev is not None:
                 ev[0].record(stream)
             write(kvw.KVW_SCHEDULE_AUTO)
             if ev is not None:
                 ev[1].record(stream)
-            stream.wait_stream(side)
 
         def single(ev, write=write):
             if ev is not None:

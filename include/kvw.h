@@ -80,7 +80,7 @@ typedef enum kvw_status {
 #define KVW_SCHEDULE_TWO_KERNELS 1 /* slot mapping kernel, then the scatter (needs slot_mapping_out) */
 #define KVW_SCHEDULE_ONE_KERNEL 2  /* one kernel resolves each token's slot and copies its rows */
 /* AUTO picks two kernels from this many token rows (max_num_tokens * num_layers) up. */
-#define KVW_TWO_KERNEL_MIN_ROWS 32768
+#define KVW_TWO_KERNEL_MIN_ROWS 65536
 
 /* KVW_ABI_VERSION of the loaded library. */
 int32_t kvw_abi_version(void);

@@ -5,8 +5,8 @@
 //                                arithmetic, tail padded with the pad id;
 //   kv_scatter_kernel            one 1 KiB slice of one K or V row per wave,
 //                                slot read from a slot mapping;
-//   kv_write_fused_kernel<MODE>  one wave per token: slot resolution and the
-//                                copy of the token's K and V rows in one pass;
+//   kv_write_fused_kernel<MODE>  one wave per token and plane: slot resolution
+//                                and the copy of the token's row in one pass;
 //   expand_blocks_kernel,
 //   expand_ranges_kernel         manager-to-kernel block expansion.
 // kvw_kv_write in a fused mode runs slot_mapping_kernel then
@@ -48,6 +48,7 @@
 #ifndef KVW_NT_LOADS
 #define KVW_NT_LOADS 1
 #endif
+
 #ifndef KVW_NT_STORES
 #define KVW_NT_STORES 1
 #endif
@@ -204,14 +205,152 @@ __device__ __forceinline__ int64_t resolve_slot(const MapArgs &a, int64_t t, int
     return b * bs + off;
 }
 
+// ---- wavefront-level search (slot mapping kernel) ---------------------------
+// The 64 lanes of a wave hold 64 evenly spaced entries of a sorted array (one
+// vector load) and each lane ranks its own key among them with a 6-step
+// ds_bpermute search, which touches no memory.  A second load of the window
+// that holds every lane's answer finishes the search, so two dependent loads
+// replace the ~log2(n) of a per-lane binary search: the request of a token is
+// found in query_start_loc this way, and the run of a position in range_cum
+// (the range descriptors are loaded once for the consecutive positions of a
+// wave, not once per position).
+
+// Number of lanes whose sample is <= x; samples are non-decreasing over the
+// lanes and lanes without a sample hold INT64_MAX.  Every lane runs every
+// shuffle (a permute that reads an inactive lane gets no defined value).
+__device__ __forceinline__ int wave_rank(int64_t sample, int64_t x)
+{
+    const bool all = __shfl(sample, kWave - 1) <= x;
+    int cnt = 0;
+#pragma unroll
+    for (int b = kWave / 2; b >= 1; b >>= 1) {
+        const int64_t probe = __shfl(sample, cnt + b - 1);
+        cnt += probe <= x ? b : 0;
+    }
+    return all ? kWave : cnt;
+}
+
+__device__ __forceinline__ int32_t wave_min(int32_t v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ int32_t wave_max(int32_t v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Largest i in [0, n) with v[i] <= x (this lane's key), or -1; v sorted.
+// Every lane of the wave calls it with the same v and n; lanes with
+// part == false get -1 and do not shape the search.  When the lanes' answers
+// lie too far apart for one 128-entry window, each lane finishes with a
+// binary search inside its own 1/64 bucket.
+__device__ int32_t wave_upper_index(const int32_t *v, int32_t n, int64_t x, bool part)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    if (n <= 0) return -1;
+    int32_t lo = 0, len = n;
+    if (len > 2 * kWave) {
+        const int32_t step = (len + kWave - 1) / kWave;
+        const int32_t idx = lane * step;
+        const int cnt = wave_rank(idx < len ? static_cast<int64_t>(v[idx]) : INT64_MAX, x);
+        int32_t b_lo = INT32_MAX, b_hi = INT32_MIN;  // this lane's bucket [b_lo, b_hi)
+        if (part && cnt > 0) {
+            b_lo = (cnt - 1) * step;
+            b_hi = min(cnt * step, len);
+        }
+        const int32_t u_lo = wave_min(b_lo), u_hi = wave_max(b_hi);
+        if (u_lo == INT32_MAX) return -1;  // no taking-part lane has an answer
+        if (u_hi - u_lo > 2 * kWave) {
+            if (!part || cnt == 0) return -1;
+            int32_t a = b_lo, h = b_hi;  // v[a] <= x
+            while (h - a > 1) {
+                const int32_t mid = (a + h) >> 1;
+                if (v[mid] <= x) a = mid; else h = mid;
+            }
+            return a;
+        }
+        lo = u_lo;
+        len = u_hi - u_lo;
+    }
+    // window of at most 128 entries: two samples per lane, loaded together
+    const int64_t s0 = lane < len ? static_cast<int64_t>(v[lo + lane]) : INT64_MAX;
+    const int64_t s1 = lane + kWave < len ? static_cast<int64_t>(v[lo + kWave + lane]) : INT64_MAX;
+    int cnt = wave_rank(s0, x);
+    const int cnt1 = wave_rank(s1, x);
+    if (cnt == kWave) cnt += cnt1;
+    return (part && cnt > 0) ? lo + cnt - 1 : -1;
+}
+
+// Block of lb in run i of request r (i from a search of range_cum), or -1.
+__device__ __forceinline__ int64_t range_block_at(const MapArgs &a, int32_t r, int32_t i, int64_t lb,
+                                                  uint32_t &flags)
+{
+    if (i < 0) return -1;
+    const int64_t row = static_cast<int64_t>(r) * a.range_stride;
+    const int64_t c = a.range_cum[row + i];
+    if (lb < c || lb >= c + a.range_len[row + i]) return -1;
+    const int64_t b = static_cast<int64_t>(a.range_start[row + i]) + (lb - c);
+    if (b < 0) { flags |= KVW_FLAG_BAD_BLOCK; return -1; }
+    return b;
+}
+
+// One token per lane; the wave finds its tokens' requests (and, for ranges,
+// the runs of the tokens of its first request) with wavefront searches.
 template <int MODE>
 __global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
 {
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x;
-    if (t >= a.max_num_tokens) return;
+    const bool in = t < a.max_num_tokens;  // every lane stays for the wave-wide searches
     uint32_t nt_flag = 0, flags = 0;
     const int64_t num_tokens = device_num_tokens(a, nt_flag);
-    a.slots_out[t] = resolve_slot<MODE>(a, t, num_tokens, flags);
+    const bool real = in && t < num_tokens;
+    const int64_t p = real ? a.positions[t] : -1;
+    const int32_t r = wave_upper_index(a.qsl, a.num_reqs, t, real);
+    const bool ok = real && r >= 0 && p >= 0;
+    const int32_t bs = a.block_size;
+    int64_t lb = 0;
+    int32_t off = 0;
+    if (ok) {
+        if (p <= INT32_MAX) {
+            const uint32_t q = static_cast<uint32_t>(p) / static_cast<uint32_t>(bs);
+            lb = q;
+            off = static_cast<int32_t>(static_cast<uint32_t>(p) - q * static_cast<uint32_t>(bs));
+        } else {
+            lb = p / bs;
+            off = static_cast<int32_t>(p - lb * bs);
+        }
+    }
+    int64_t b = -1;
+    if (MODE == kPaged) {
+        if (ok) b = paged_block(a, r, lb, flags);
+    } else {
+        // lanes of the wave's first request search its range_cum row together
+        const uint64_t oks = __ballot(ok);
+        const int32_t leader = oks ? __shfl(r, __builtin_ctzll(oks)) : -1;
+        int32_t n_lead = 0;
+        if (leader >= 0) {
+            uint32_t unused = 0;
+            n_lead = static_cast<int32_t>(clamp_count(a.num_ranges[leader], a.range_stride, unused));
+        }
+        const bool coop = ok && r == leader;
+        const int32_t i = wave_upper_index(a.range_cum + static_cast<int64_t>(leader < 0 ? 0 : leader) *
+                                                             a.range_stride,
+                                           n_lead, lb, coop);
+        if (ok) {
+            if (coop) {
+                clamp_count(a.num_ranges[r], a.range_stride, flags);  // the count's flag, per token
+                b = range_block_at(a, r, i, lb, flags);
+            } else {
+                b = range_block(a, r, lb, flags);
+            }
+        }
+    }
+    if (in) a.slots_out[t] = b < 0 ? KVW_PAD_ID : b * bs + off;
     raise_flags(a.err_flag, flags | (t == 0 ? nt_flag : 0u));
 }
 
@@ -269,71 +408,64 @@ __global__ __launch_bounds__(kScatterThreads) void kv_scatter_kernel(const int64
                                load16<KVW_NT_LOADS>(src + l * c.kv_layer_stride));
 }
 
-// One wave per token and layer group (blockIdx.y): the wave first issues the
-// loads of the token's K and V rows for the group's first layer, then
-// resolves the slot with scalar loads (the token is wave-uniform) while they
-// are in flight, then stores.  Rows longer than CH KiB are copied in
-// further CH KiB segments once the slot is known.
+// One wave per (token, plane) and layer group (blockIdx.y): the wave first
+// issues the loads of the token's K or V row for the group's first layer,
+// then resolves the slot with scalar loads (the token is wave-uniform) while
+// they are in flight, then stores.  The two planes go to two waves because a
+// wave that moves 2 KiB keeps more transfers in flight per byte than one that
+// moves 4 KiB; the plane-0 wave reports the slot and the flags.  Rows longer
+// than CH KiB are copied in further CH KiB segments once the slot is known.
 template <int MODE, int CH>
 __global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a, CopyArgs c)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * kFusedWaves +
-                      __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * kFusedWaves +
+                         __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t t = item >> 1;
+    const int plane = static_cast<int>(item & 1);
     if (t >= a.max_num_tokens) return;  // whole wave: this kernel has no barrier
     const int l0 = blockIdx.y * c.layers_per_wave;
     const int l1 = min(c.num_layers, l0 + c.layers_per_wave);
     const int64_t bpt = c.bytes_per_token;
     const int64_t lane_off = static_cast<int64_t>(lane) * 16;
-    const uint8_t *ksrc = c.key + t * c.kv_token_stride + lane_off;
-    const uint8_t *vsrc = c.value + t * c.kv_token_stride + lane_off;
+    const uint8_t *src = (plane ? c.value : c.key) + t * c.kv_token_stride + lane_off;
 
     uint32_t flags = 0;
     const int64_t num_tokens = device_num_tokens(a, flags);
     if (t != 0) flags = 0;
     const bool real = t < num_tokens;  // rows of padded tokens are not read
-    u32x4 kr[CH], vr[CH];
+    u32x4 row[CH];
     if (real && l0 < l1) {
 #pragma unroll
-        for (int ch = 0; ch < CH; ++ch) {
-            if (lane_off + ch * kSliceBytes < bpt) {
-                kr[ch] = load16<KVW_NT_LOADS>(ksrc + l0 * c.kv_layer_stride + ch * kSliceBytes);
-                vr[ch] = load16<KVW_NT_LOADS>(vsrc + l0 * c.kv_layer_stride + ch * kSliceBytes);
-            }
-        }
+        for (int ch = 0; ch < CH; ++ch)
+            if (lane_off + ch * kSliceBytes < bpt)
+                row[ch] = load16<KVW_NT_LOADS>(src + l0 * c.kv_layer_stride + ch * kSliceBytes);
     }
     int64_t slot = resolve_slot<MODE>(a, t, num_tokens, flags);
-    const bool first_group = blockIdx.y == 0;
-    if (first_group && lane == 0 && a.slots_out) a.slots_out[t] = slot;
+    const bool report = blockIdx.y == 0 && plane == 0;
+    if (report && lane == 0 && a.slots_out) a.slots_out[t] = slot;
     if (slot >= c.rows_per_layer) {
         if (c.num_layers > 0) flags |= KVW_FLAG_SLOT_OOB;
         slot = KVW_PAD_ID;
     }
-    if (first_group && lane == 0) raise_flags(a.err_flag, flags);
+    if (report && lane == 0) raise_flags(a.err_flag, flags);
     if (slot < 0 || !real) return;
 
-    uint8_t *kdst = c.k_cache + slot * bpt + lane_off;
-    uint8_t *vdst = c.v_cache + slot * bpt + lane_off;
+    uint8_t *dst = (plane ? c.v_cache : c.k_cache) + slot * bpt + lane_off;
     for (int l = l0; l < l1; ++l) {
         const int64_t src_l = l * c.kv_layer_stride;
         const int64_t dst_l = static_cast<int64_t>(l) * c.rows_per_layer * bpt;  // l*B*T rows
         for (int64_t seg = 0; seg < bpt; seg += CH * kSliceBytes) {
             if (l != l0 || seg != 0) {
 #pragma unroll
-                for (int ch = 0; ch < CH; ++ch) {
-                    if (seg + lane_off + ch * kSliceBytes < bpt) {
-                        kr[ch] = load16<KVW_NT_LOADS>(ksrc + src_l + seg + ch * kSliceBytes);
-                        vr[ch] = load16<KVW_NT_LOADS>(vsrc + src_l + seg + ch * kSliceBytes);
-                    }
-                }
+                for (int ch = 0; ch < CH; ++ch)
+                    if (seg + lane_off + ch * kSliceBytes < bpt)
+                        row[ch] = load16<KVW_NT_LOADS>(src + src_l + seg + ch * kSliceBytes);
             }
 #pragma unroll
-            for (int ch = 0; ch < CH; ++ch) {
-                if (seg + lane_off + ch * kSliceBytes < bpt) {
-                    store16<KVW_NT_STORES>(kdst + dst_l + seg + ch * kSliceBytes, kr[ch]);
-                    store16<KVW_NT_STORES>(vdst + dst_l + seg + ch * kSliceBytes, vr[ch]);
-                }
-            }
+            for (int ch = 0; ch < CH; ++ch)
+                if (seg + lane_off + ch * kSliceBytes < bpt)
+                    store16<KVW_NT_STORES>(dst + dst_l + seg + ch * kSliceBytes, row[ch]);
         }
     }
 }
@@ -497,7 +629,7 @@ void launch_slot_mapping(int mode, const MapArgs &a, hipStream_t s)
 template <int MODE>
 void launch_fused(const MapArgs &a, const CopyArgs &c, unsigned groups, hipStream_t s)
 {
-    const dim3 grid(grid_for(a.max_num_tokens, kFusedWaves), groups);
+    const dim3 grid(grid_for(2 * a.max_num_tokens, kFusedWaves), groups);  // two planes per token
     const dim3 block(kFusedThreads);
     switch (c.slices_per_row) {
     case 1: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 1>), grid, block, 0, s, a, c); break;
