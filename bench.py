@@ -388,6 +388,31 @@ def bench_config(args):
             r = results[key_]
             log(f"[bench] {key_:20s} {ms * 1e3:8.1f} us  {r['gbps']:6.0f} GB/s "
                 f"({100 * r['frac_of_peak']:.1f}%)  {r['tokens_per_s'] / 1e6:.2f} M tokens/s")
+    # the slot mapping alone (latency-bound: reported in tokens/s)
+    for name, (mode, mapping) in maps.items():
+        def smap(name=name, mapping=mapping):
+            if name == "paged":
+                kvw.kvw_slot_mapping_paged(qsl, w.num_reqs, pos, M, mapping["block_table"],
+                                           mapping["num_blocks_per_req"], w.block_size, sm_out)
+            else:
+                kvw.kvw_slot_mapping_ranges(qsl, w.num_reqs, pos, M, mapping["range_start"],
+                                            mapping["range_len"], mapping["range_cum"],
+                                            mapping["num_ranges"], w.block_size, sm_out)
+        for _ in range(args.warmup):
+            smap()
+        times = []
+        for i in range(args.steps):
+            scratch.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            smap()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = statistics.fmean(times)
+        results[f"slot_mapping_{name}"] = {"ms_avg": ms, "tokens_per_s": real / (ms * 1e-3)}
+        log(f"[bench] slot_mapping_{name:8s} {ms * 1e3:8.1f} us  "
+            f"{real / (ms * 1e-3) / 1e6:.1f} M tokens/s")
     head = results["paged"]
     line = {
         "metric": METRIC, "value": round(head["tokens_per_s"], 1), "unit": "tokens/s",
