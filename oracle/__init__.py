@@ -57,6 +57,8 @@ class Oracle:
         lib.orc_map_to_kernel_blocks.argtypes = [_P, _P, _I32, _I32, _I32, _I32, _P, _I32, _P]
         lib.orc_map_ranges_to_kernel_blocks.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                                         _P, _P, _P, _P, _P]
+        lib.orc_ranges_to_block_table.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P,
+                                                  _I32, _P, _P]
         lib.orc_coord_n.argtypes = [_I64] * 5
         lib.orc_coord_n.restype = _I64
         lib.orc_coord_offset.argtypes = [_I64] * 6
@@ -65,7 +67,7 @@ class Oracle:
                                      _I64, _I64, _P]
         for f in (lib.orc_slot_mapping_paged, lib.orc_slot_mapping_ranges,
                   lib.orc_map_to_kernel_blocks, lib.orc_map_ranges_to_kernel_blocks,
-                  lib.orc_kv_write):
+                  lib.orc_ranges_to_block_table, lib.orc_kv_write):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -139,6 +141,22 @@ class Oracle:
                                                       ctypes.byref(flags))
         self._check(rc, "map_ranges_to_kernel_blocks")
         return (o_s, o_l, o_c, o_n), flags.value
+
+    def ranges_to_block_table(self, range_start, range_len, range_cum, num_ranges,
+                              block_size: int, kernel_block_size: int, out_stride: int
+                              ) -> Tuple[np.ndarray, np.ndarray, int]:
+        """Block table [rows][out_stride] (kernel block ids) and per-row counts."""
+        rs, rl, rc_ = (_c(a, np.int32) for a in (range_start, range_len, range_cum))
+        nr = _c(num_ranges, np.int32)
+        rows, stride = rs.shape
+        out = np.empty((rows, out_stride), dtype=np.int32)
+        counts = np.empty(rows, dtype=np.int32)
+        flags = ctypes.c_uint32(0)
+        rc = self.lib.orc_ranges_to_block_table(_ptr(rs), _ptr(rl), _ptr(rc_), _ptr(nr), rows,
+                                                stride, block_size, kernel_block_size, _ptr(out),
+                                                out_stride, _ptr(counts), ctypes.byref(flags))
+        self._check(rc, "ranges_to_block_table")
+        return out, counts, flags.value
 
     # -- coordinate form ---------------------------------------------------
     def coord_n(self, layer, block, token, num_blocks, block_size) -> int:

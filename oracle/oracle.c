@@ -11,7 +11,7 @@
  * Sources (pages as published; sections named, not quoted):
  *  [P1] "Range-addressed KV cache blocks for the vLLM serving engine",
  *       sections "The Innovation: Range Arithmetic Replaces the Per-Position
- *       Gather" and "The Coordinate Approach".
+ *       Gather", "The Coordinate Approach", "Measured Results" and "Status".
  *  [P2] "Blocktabelle: Abbildung von logischen Token auf physische KV-Blocks",
  *       sections "Verantwortung", "Entwurfsmotivation", "Datenfluss" and
  *       "Grenzen und Fehler".
@@ -270,6 +270,73 @@ int orc_map_ranges_to_kernel_blocks(const int32_t *start, const int32_t *len, co
             out_len[q] = (int32_t)l;
             out_cum[q] = (int32_t)c;
         }
+    }
+    if (flags_out) *flags_out |= flags;
+    return ORC_OK;
+}
+
+/*
+ * Block table filled from range descriptors ([P1] "Status", GPU level: a
+ * range-expansion kernel that writes the attention side's block table
+ * straight from the range tables, in place of the per-step copy of a staged
+ * table).  The row of a request is its runs laid end to end -- the same
+ * relation that makes the range arithmetic and the gather give one slot
+ * ([P1] "Measured Results", slot-mapping structural model) -- with the manager-to-kernel
+ * expansion of [P3] section 7 applied on the way:
+ *   run i (start, len) contributes blocks start, start+1, ..., start+len-1;
+ *   block b contributes kernel blocks b*k, b*k+1, ..., b*k+k-1;
+ *   out[r][q] = the q-th id of that list for q < min(length, out_stride),
+ *   out[r][q] = 0 (the null block) for the rest of the row.
+ * counts_out[r] (may be NULL) = min(length, out_stride); a list longer than
+ * the row sets COUNT.  A stored entry whose block is negative or whose
+ * kernel id does not fit an int32 is 0 and sets BAD_BLOCK (entries past
+ * out_stride are not examined).
+ * Precondition (checked): as for orc_slot_mapping_ranges.
+ */
+int orc_ranges_to_block_table(const int32_t *start, const int32_t *len, const int32_t *cum,
+                              const int32_t *num_ranges, int32_t rows, int32_t range_stride,
+                              int32_t block_size, int32_t kernel_block_size, int32_t *out,
+                              int32_t out_stride, int32_t *counts_out, uint32_t *flags_out)
+{
+    uint32_t flags = 0;
+    int64_t k = blocks_per_kv_block(block_size, kernel_block_size);
+    if (k == 0 || rows < 0 || range_stride < 0 || out_stride < 0) return ORC_E_ARG;
+    if (rows > 0 && (!num_ranges || (range_stride > 0 && (!start || !len || !cum)) ||
+                     (out_stride > 0 && !out)))
+        return ORC_E_ARG;
+
+    for (int32_t r = 0; r < rows; ++r) {
+        uint32_t dummy = 0;
+        int64_t n = clamp64(num_ranges[r], 0, range_stride, &dummy, ORC_FLAG_COUNT);
+        int64_t expect_cum = 0;
+        for (int64_t i = 0; i < n; ++i) {
+            int64_t q = (int64_t)r * range_stride + i;
+            if (len[q] < 1 || cum[q] != expect_cum) return ORC_E_RANGES;
+            expect_cum += len[q];
+        }
+    }
+
+    for (int32_t r = 0; r < rows; ++r) {
+        int32_t *row = out + (int64_t)r * out_stride;
+        int64_t n = clamp64(num_ranges[r], 0, range_stride, &flags, ORC_FLAG_COUNT);
+        for (int64_t q = 0; q < out_stride; ++q) row[q] = 0;
+        int64_t length = 0; /* ids in the list so far */
+        for (int64_t i = 0; i < n; ++i) {
+            int64_t d = (int64_t)r * range_stride + i;
+            for (int64_t b = start[d]; b < (int64_t)start[d] + len[d]; ++b) {
+                for (int64_t j = 0; j < k; ++j) {
+                    if (length >= out_stride) break; /* stored entries only */
+                    if (expandable(b, k)) row[length] = (int32_t)(b * k + j);
+                    else flags |= ORC_FLAG_BAD_BLOCK;
+                    ++length;
+                }
+                if (length >= out_stride) break;
+            }
+        }
+        int64_t full = 0; /* the whole list's length */
+        for (int64_t i = 0; i < n; ++i) full += (int64_t)len[(int64_t)r * range_stride + i] * k;
+        if (full > out_stride) flags |= ORC_FLAG_COUNT;
+        if (counts_out) counts_out[r] = (int32_t)(full < out_stride ? full : out_stride);
     }
     if (flags_out) *flags_out |= flags;
     return ORC_OK;

@@ -7,7 +7,8 @@ when the oracle disagrees with:
     counting free slots (no division, no modulo, no table lookup);
   * enumeration of every slot a request owns, in logical order;
   * the pages' invariant that range arithmetic and the table gather give the
-    same slot for the same physical layout;
+    same slot for the same physical layout, and that a table filled from the
+    runs is the runs laid end to end;
   * numpy's own row-major indexing (ravel_multi_index, array addresses,
     fancy-index scatter) for the coordinate form and the K/V copy.
 The same functions are run against deliberately broken builds of the oracle
@@ -310,6 +311,76 @@ def pin_expansion(orc):
             raise AssertionError(f"expansion {bad} not rejected")
 
 
+def pin_table_fill(orc, workloads=()):
+    """Block table filled from range descriptors == the request's runs laid end to end.
+
+    The printed rows ([7, 1] at block size 16, the Figure 6 rows) come back
+    from their descriptors; rows of the token-at-a-time simulation round-trip
+    through run compression (``_runs_of``, written independently above); at a
+    finer kernel block size, entry q of a row names the same memory as manager
+    block q // k; the filled table drives the gather to the slots the
+    simulation placed; truncation, clamped counts and unrepresentable ids are
+    flagged; and every generated workload's own table is reproduced.
+    """
+    from oracle import FLAG_BAD_BLOCK, FLAG_COUNT
+    printed = [[int(x) for x in f[1:]] for f in _lines("slot_mapping_bs16.txt") if f[0] == "row"]
+    printed += [[int(x) for x in f[2:]] for f in _lines("figure6_bs4.txt") if f[0] == "step"]
+    assert [7, 1] in printed and [7, 1, 3] in printed
+    for row in printed:
+        st, ln, cm, nr = _descriptors([row])
+        out, cnt, f = orc.ranges_to_block_table(st, ln, cm, nr, 1, 1, len(row) + 3)
+        assert out[0].tolist() == row + [0, 0, 0] and cnt.tolist() == [len(row)] and f == 0, row
+
+    rng = np.random.default_rng(23)
+    for trial in range(12):
+        bs_m, bs_k = [(16, 16), (32, 16), (64, 16), (12, 4), (4, 1), (3, 3)][trial % 6]
+        k = bs_m // bs_k
+        lengths = [int(rng.integers(1, 90)) for _ in range(int(rng.integers(1, 5)))]
+        need = sum(-(-ln // bs_m) for ln in lengths)
+        rows, places = _simulate(rng, lengths, bs_m, need + 30, run_free_list=trial % 2 == 0)
+        st, ln, cm, nr = _descriptors(rows, stride=int(rng.integers(0, 3)))
+        width = max(map(len, rows)) * k + int(rng.integers(0, 5))
+        out, cnt, f = orc.ranges_to_block_table(st, ln, cm, nr, bs_m, bs_k, width)
+        assert f == 0 and out.shape == (len(rows), width)
+        for r, row in enumerate(rows):
+            assert cnt[r] == len(row) * k
+            for q in range(len(row) * k):
+                assert out[r, q] * bs_k == row[q // k] * bs_m + (q % k) * bs_k, (trial, r, q)
+            assert (out[r, len(row) * k:] == 0).all()
+        qsl, pos, m = _batch([list(range(n)) for n in lengths], pad_to=sum(lengths) + 4, rng=rng)
+        expect = [b * bs_m + i for plc in places for (b, i) in plc]
+        sm, _ = orc.slot_mapping_paged(qsl, len(rows), pos, m, out, cnt, bs_k)
+        assert sm[:len(expect)].tolist() == expect and (sm[len(expect):] == PAD).all(), trial
+
+    # runs (5, 3) and (9, 2) at k = 2: ten kernel ids, of which a 4-wide row keeps four
+    st, ln, cm, nr = _descriptors([[5, 6, 7, 9, 10]])
+    out, cnt, f = orc.ranges_to_block_table(st, ln, cm, nr, 2, 1, 4)
+    assert out.tolist() == [[10, 11, 12, 13]] and cnt.tolist() == [4] and f == FLAG_COUNT
+    out, cnt, f = orc.ranges_to_block_table(st, ln, cm, nr, 2, 1, 12)
+    assert out.tolist() == [[10, 11, 12, 13, 14, 15, 18, 19, 20, 21, 0, 0]] and cnt.tolist() == [10]
+    assert f == 0
+    # a count outside [0, range_stride] is clamped and flagged
+    out, cnt, f = orc.ranges_to_block_table(st, ln, cm, np.array([7], np.int32), 1, 1, 6)
+    assert out.tolist() == [[5, 6, 7, 9, 10, 0]] and cnt.tolist() == [5] and f == FLAG_COUNT
+    out, cnt, f = orc.ranges_to_block_table(st, ln, cm, np.array([-1], np.int32), 1, 1, 3)
+    assert out.tolist() == [[0, 0, 0]] and cnt.tolist() == [0] and f == FLAG_COUNT
+    # negative ids and ids whose kernel id leaves int32 become the null block
+    big = (1 << 31) // 2 - 1  # big*2 + 1 == INT32_MAX: representable; big + 1 is not
+    st = np.array([[-3, big]], np.int32)
+    ln = np.array([[2, 2]], np.int32)
+    cm = np.array([[0, 2]], np.int32)
+    out, cnt, f = orc.ranges_to_block_table(st, ln, cm, np.array([2], np.int32), 2, 1, 8)
+    assert out.tolist() == [[0, 0, 0, 0, 2 * big, 2 * big + 1, 0, 0]] and cnt.tolist() == [8]
+    assert f == FLAG_BAD_BLOCK
+
+    for w in workloads:
+        out, cnt, f = orc.ranges_to_block_table(w.range_start, w.range_len, w.range_cum,
+                                                w.num_ranges, w.block_size, w.block_size,
+                                                w.table_stride)
+        assert f == 0 and np.array_equal(out, w.block_table), w.name
+        assert np.array_equal(cnt, w.num_blocks_per_req), w.name
+
+
 def pin_coordinates(orc):
     """Coordinate form == numpy row-major indexing of [layers][blocks][tokens] rows."""
     cfg = {f[0]: int(f[1]) for f in _lines("coordinate_layout.txt")}
@@ -396,5 +467,6 @@ def all_pins(orc, small, full=()):
     pin_padding_rules(orc)
     pin_range_equals_gather(orc, list(small) + list(full))
     pin_expansion(orc)
+    pin_table_fill(orc, small)
     pin_coordinates(orc)
     pin_kv_write(orc, small)

@@ -36,6 +36,16 @@ MUTANTS = {
                                "if (expandable(id, k)) v = id + j;"),
     "expansion_tail_not_null": ("for (int64_t c = 0; c < out_stride; ++c) out[(int64_t)r * out_stride + c] = 0;",
                                 "for (int64_t c = 0; c < out_stride; ++c) out[(int64_t)r * out_stride + c] = 1;"),
+    "fill_drops_factor": ("if (expandable(b, k)) row[length] = (int32_t)(b * k + j);",
+                          "if (expandable(b, k)) row[length] = (int32_t)(b + j);"),
+    "fill_drops_sub_block": ("if (expandable(b, k)) row[length] = (int32_t)(b * k + j);",
+                             "if (expandable(b, k)) row[length] = (int32_t)(b * k);"),
+    "fill_run_end_inclusive": ("for (int64_t b = start[d]; b < (int64_t)start[d] + len[d]; ++b) {",
+                               "for (int64_t b = start[d]; b <= (int64_t)start[d] + len[d]; ++b) {"),
+    "fill_tail_not_null": ("for (int64_t q = 0; q < out_stride; ++q) row[q] = 0;",
+                           "for (int64_t q = 0; q < out_stride; ++q) row[q] = 1;"),
+    "fill_count_unclamped": ("counts_out[r] = (int32_t)(full < out_stride ? full : out_stride);",
+                             "counts_out[r] = (int32_t)full;"),
     "coord_swaps_B_T": ("return (layer * num_blocks + block) * block_size + token;",
                         "return (layer * block_size + block) * num_blocks + token;"),
     "kv_drops_layer_term": ("int64_t src = layer * kv_layer_stride + t * kv_token_stride;",

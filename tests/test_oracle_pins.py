@@ -75,6 +75,23 @@ def test_expansion(orc):
     P.pin_expansion(orc)
 
 
+def test_table_fill(orc, small):
+    P.pin_table_fill(orc, small + [config(n) for n in ("tiny_prefill", "decode_step",
+                                                       "mixed_chunked")])
+
+
+@pytest.mark.parametrize("r", [1, 4096])
+def test_table_fill_long_context(orc, r):
+    """128K context: manager runs filled at kernel block size == the expanded manager table."""
+    w = long_context(r)
+    k = w.blocks_per_kv_block
+    kt, _ = orc.map_to_kernel_blocks(w.block_table, w.num_blocks_per_req, w.block_size,
+                                     w.kernel_block_size)
+    out, cnt, f = orc.ranges_to_block_table(w.range_start, w.range_len, w.range_cum, w.num_ranges,
+                                            w.block_size, w.kernel_block_size, w.table_stride * k)
+    assert f == 0 and np.array_equal(out, kt) and np.array_equal(cnt, w.num_blocks_per_req * k)
+
+
 def test_coordinate_form(orc):
     P.pin_coordinates(orc)
 
