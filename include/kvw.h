@@ -8,7 +8,8 @@
  *  [P1] "Range-addressed KV cache blocks for the vLLM serving engine":
  *       "The Innovation: Range Arithmetic Replaces the Per-Position Gather"
  *       (the two slot-mapping strategies, pad id for positions outside every
- *       range) and "The Coordinate Approach" (cache coordinates).
+ *       range), "The Coordinate Approach" (cache coordinates) and "Status"
+ *       (the block table filled from the range tables).
  *  [P2] "Blocktabelle: Abbildung von logischen Token auf physische
  *       KV-Blocks": "Verantwortung" (block table shape, slot_mapping),
  *       "Entwurfsmotivation" (manager/kernel block sizes, the slot-mapping
@@ -175,6 +176,45 @@ kvw_status kvw_map_ranges_to_kernel_blocks(const int32_t *range_start, const int
                                            int32_t *out_len, int32_t *out_cum,
                                            int32_t *out_num_ranges, int32_t *err_flag,
                                            void *stream);
+
+/*
+ * The attention side's block table filled straight from the range
+ * descriptors, with no staged table to copy ([P1] "Status": the
+ * range-expansion kernel in place of the per-step materialization copy).
+ * A row is its request's runs laid end to end, each manager block b
+ * expanded to kernel blocks b*k .. b*k+k-1 (k = block_size /
+ * kernel_block_size; k = 1 gives the table at the manager block size):
+ *   block_table[r][q] = (start[i] + q/k - cum[i]) * k + q%k
+ *                       for the run i with cum[i] <= q/k < cum[i] + len[i],
+ *   block_table[r][q] = 0 (the null block) past the last run.
+ *   num_blocks_per_req[r] = min((cum[n-1] + len[n-1]) * k, block_table_stride),
+ *                       n = num_ranges[r] clamped (0 when n = 0).
+ * With the same descriptors, kvw_slot_mapping_paged on this table (and
+ * count) gives the slots kvw_slot_mapping_ranges gives at the manager block
+ * size, and kvw_slot_mapping_paged at kernel_block_size does too.
+ *   range_start, range_len, range_cum  int32[rows][range_stride] (input, as
+ *                                      kvw_slot_mapping_ranges, manager units)
+ *   num_ranges                         int32[rows] (input)
+ *   block_table                        int32[rows][block_table_stride] (output,
+ *                                      every entry written)
+ *   num_blocks_per_req                 int32[rows] (output) or NULL
+ * Flags: KVW_FLAG_COUNT (num_ranges outside [0, range_stride], or more
+ * kernel blocks than block_table_stride: the row keeps the first ones),
+ * KVW_FLAG_BAD_BLOCK (a stored entry whose block is negative or whose
+ * kernel id exceeds INT32_MAX: written as 0).
+ * Errors: KVW_ERR_INVALID_ARG when kernel_block_size does not divide
+ * block_size (or either is <= 0), for negative sizes, NULL or misaligned
+ * required arrays; KVW_ERR_RANGE_CAP when range_stride >
+ * KVW_MAX_RANGE_STRIDE.  Under the descriptor precondition of
+ * kvw_slot_mapping_ranges; inputs that break it give in-bounds but
+ * unspecified table contents.
+ */
+kvw_status kvw_ranges_to_block_table(const int32_t *range_start, const int32_t *range_len,
+                                     const int32_t *range_cum, const int32_t *num_ranges,
+                                     int32_t rows, int32_t range_stride, int32_t block_size,
+                                     int32_t kernel_block_size, int32_t *block_table,
+                                     int32_t block_table_stride, int32_t *num_blocks_per_req,
+                                     int32_t *err_flag, void *stream);
 
 /*
  * Arguments of kvw_kv_write.  Byte strides; every pointer of key, value,

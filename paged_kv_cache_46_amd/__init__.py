@@ -19,6 +19,7 @@ from .kvw import (  # noqa: F401
     kvw_kv_write,
     kvw_map_ranges_to_kernel_blocks,
     kvw_map_to_kernel_blocks,
+    kvw_ranges_to_block_table,
     kvw_slot_mapping_paged,
     kvw_slot_mapping_ranges,
     library,

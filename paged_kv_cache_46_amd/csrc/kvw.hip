@@ -8,7 +8,9 @@
 //   kv_write_fused_kernel<MODE>  one wave per token and plane: slot resolution
 //                                and the copy of the token's row in one pass;
 //   expand_blocks_kernel,
-//   expand_ranges_kernel         manager-to-kernel block expansion.
+//   expand_ranges_kernel         manager-to-kernel block expansion;
+//   fill_table_kernel            the attention side's block table filled
+//                                straight from the range descriptors.
 // kvw_kv_write in a fused mode runs slot_mapping_kernel then
 // kv_scatter_kernel for large writes whose slot mapping the caller keeps
 // (the usual case: attention consumes it), and kv_write_fused_kernel
@@ -17,9 +19,10 @@
 // caller's stream; include/kvw.h holds the contract.
 //
 // Sources: "Range-addressed KV cache blocks for the vLLM serving engine"
-// ("The Innovation", "The Coordinate Approach"); "Blocktabelle: Abbildung
-// von logischen Token auf physische KV-Blocks" ("Entwurfsmotivation",
-// "Datenfluss", "Grenzen und Fehler"); "vLLM Block Table Management"
+// ("The Innovation", "The Coordinate Approach", and "Status" on filling the
+// block table from the range tables); "Blocktabelle: Abbildung von logischen
+// Token auf physische KV-Blocks" ("Entwurfsmotivation", "Datenfluss",
+// "Grenzen und Fehler"); "vLLM Block Table Management"
 // (Deep Dive sections 7 and 8).
 //
 // The path is a memory-bound gather/scatter: no matrix cores are involved.
@@ -531,6 +534,53 @@ __global__ __launch_bounds__(kBlockThreads) void expand_ranges_kernel(
     raise_flags(err_flag, flags);
 }
 
+// Block table filled from range descriptors: entry q of row r is kernel block
+// j = q % k of the manager block at logical index q / k, i.e. of
+// start[i] + (q / k - cum[i]) for the run i holding it; 0 past the runs.
+// One entry per lane; the blocks of a workgroup lie in one row (blockIdx.y),
+// so the consecutive logical blocks of a wave (at most 64, each run at least
+// one block long) fall in at most 64 consecutive runs, found with one
+// wavefront search of the row's cum column.  Lane 0 of each row writes the
+// count, (cum[n-1] + len[n-1]) * k clamped to the row width, which under the
+// descriptor precondition is the total length of the runs.
+__global__ __launch_bounds__(kBlockThreads) void fill_table_kernel(
+    const int32_t *start, const int32_t *len, const int32_t *cum, const int32_t *num_ranges,
+    int32_t rows, int32_t range_stride, int32_t k, int32_t *out, int32_t out_stride,
+    int32_t *counts_out, int32_t *err_flag)
+{
+    const int64_t q = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x;
+    const bool in = q < out_stride;
+    const uint32_t uq = static_cast<uint32_t>(in ? q : 0);
+    const uint32_t lb32 = uq / static_cast<uint32_t>(k);
+    const int64_t lb = lb32;
+    const int32_t j = static_cast<int32_t>(uq - lb32 * static_cast<uint32_t>(k));
+    for (int32_t r = blockIdx.y; r < rows; r += gridDim.y) {  // uniform over the workgroup
+        uint32_t flags = 0, count_flags = 0;
+        const int64_t row = static_cast<int64_t>(r) * range_stride;
+        const int32_t n = static_cast<int32_t>(clamp_count(num_ranges[r], range_stride, count_flags));
+        const int32_t i = wave_upper_index(cum + row, n, lb, in);
+        int32_t v = 0;
+        if (in && i >= 0) {
+            const int64_t c = cum[row + i];
+            if (lb >= c && lb < c + len[row + i]) {
+                const int64_t b = static_cast<int64_t>(start[row + i]) + (lb - c);
+                if (expandable(b, k)) v = static_cast<int32_t>(b * k + j);
+                else flags |= KVW_FLAG_BAD_BLOCK;
+            }
+        }
+        if (in) out[static_cast<int64_t>(r) * out_stride + q] = v;
+        if (q == 0) {
+            int64_t total = 0;
+            if (n > 0) total = (static_cast<int64_t>(cum[row + n - 1]) + len[row + n - 1]) * k;
+            if (total < 0) total = 0;
+            if (total > out_stride) count_flags |= KVW_FLAG_COUNT;
+            if (counts_out) counts_out[r] = static_cast<int32_t>(total < out_stride ? total : out_stride);
+            flags |= count_flags;
+        }
+        raise_flags(err_flag, flags);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -761,6 +811,44 @@ kvw_status kvw_map_ranges_to_kernel_blocks(const int32_t *range_start, const int
                        0, reinterpret_cast<hipStream_t>(stream), range_start, range_len, range_cum,
                        num_ranges, rows, range_stride, k, out_start, out_len, out_cum,
                        out_num_ranges, err_flag);
+    return launched(fn);
+}
+
+kvw_status kvw_ranges_to_block_table(const int32_t *range_start, const int32_t *range_len,
+                                     const int32_t *range_cum, const int32_t *num_ranges,
+                                     int32_t rows, int32_t range_stride, int32_t block_size,
+                                     int32_t kernel_block_size, int32_t *block_table,
+                                     int32_t block_table_stride, int32_t *num_blocks_per_req,
+                                     int32_t *err_flag, void *stream)
+{
+    const char *fn = "kvw_ranges_to_block_table";
+    KVW_REQUIRE(block_size > 0 && kernel_block_size > 0 && block_size % kernel_block_size == 0,
+                "%s: kernel block size %d does not divide block size %d", fn, kernel_block_size,
+                block_size);
+    const int32_t k = block_size / kernel_block_size;
+    KVW_REQUIRE(rows >= 0 && range_stride >= 0 && block_table_stride >= 0,
+                "%s: negative rows, range_stride or block_table_stride", fn);
+    if (range_stride > KVW_MAX_RANGE_STRIDE)
+        return fail(KVW_ERR_RANGE_CAP, "%s: range_stride %d exceeds the cap of %d", fn, range_stride,
+                    KVW_MAX_RANGE_STRIDE);
+    KVW_REQUIRE(!err_flag || aligned(err_flag, 4), "%s: err_flag misaligned", fn);
+    if (rows == 0) return KVW_OK;
+    KVW_REQUIRE(num_ranges && aligned(num_ranges, 4), "%s: num_ranges is NULL or misaligned", fn);
+    const int32_t *ins[] = {range_start, range_len, range_cum};
+    for (const int32_t *p : ins)
+        KVW_REQUIRE(range_stride == 0 || (p && aligned(p, 4)),
+                    "%s: a range descriptor array is NULL or misaligned", fn);
+    KVW_REQUIRE(block_table_stride == 0 || (block_table && aligned(block_table, 4)),
+                "%s: block_table is NULL or misaligned", fn);
+    KVW_REQUIRE(!num_blocks_per_req || aligned(num_blocks_per_req, 4),
+                "%s: num_blocks_per_req misaligned", fn);
+    // at least one workgroup per row: its first lane writes the count and the row's flags
+    const dim3 grid(block_table_stride > 0 ? grid_for(block_table_stride, kBlockThreads) : 1u,
+                    static_cast<unsigned>(rows) < kMaxGridY ? static_cast<unsigned>(rows) : kMaxGridY);
+    hipLaunchKernelGGL(fill_table_kernel, grid, dim3(kBlockThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), range_start, range_len, range_cum,
+                       num_ranges, rows, range_stride, k, block_table, block_table_stride,
+                       num_blocks_per_req, err_flag);
     return launched(fn);
 }
 

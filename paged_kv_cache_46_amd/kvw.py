@@ -67,6 +67,8 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
         "kvw_map_to_kernel_blocks": [_P, _P, _I32, _I32, _I32, _I32, _P, _I32, _P, _P],
         "kvw_map_ranges_to_kernel_blocks": [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P,
                                             _P, _P, _P],
+        "kvw_ranges_to_block_table": [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _I32, _P, _P,
+                                      _P],
         "kvw_kv_write": [ctypes.POINTER(kvw_kv_write_args), _P],
     }
     for name, argtypes in sigs.items():
@@ -159,6 +161,20 @@ def kvw_map_ranges_to_kernel_blocks(range_start, range_len, range_cum, num_range
         int(kernel_block_size), _dev(out_start, torch.int32, "out_start"),
         _dev(out_len, torch.int32, "out_len"), _dev(out_cum, torch.int32, "out_cum"),
         _dev(out_num_ranges, torch.int32, "out_num_ranges"),
+        _dev(err_flag, torch.int32, "err_flag", optional=True), _stream(stream)))
+
+
+def kvw_ranges_to_block_table(range_start, range_len, range_cum, num_ranges, block_size,
+                              kernel_block_size, block_table, num_blocks_per_req=None,
+                              err_flag=None, stream=None):
+    """Fill block_table [rows][stride] (kernel block ids) from the range descriptors."""
+    _check(library().kvw_ranges_to_block_table(
+        _dev(range_start, torch.int32, "range_start"), _dev(range_len, torch.int32, "range_len"),
+        _dev(range_cum, torch.int32, "range_cum"), _dev(num_ranges, torch.int32, "num_ranges"),
+        int(range_start.shape[0]), int(range_start.shape[1]), int(block_size),
+        int(kernel_block_size), _dev(block_table, torch.int32, "block_table"),
+        int(block_table.shape[1]),
+        _dev(num_blocks_per_req, torch.int32, "num_blocks_per_req", optional=True),
         _dev(err_flag, torch.int32, "err_flag", optional=True), _stream(stream)))
 
 

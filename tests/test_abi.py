@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("kvw_slot_mapping_paged", "kvw_slot_mapping_ranges",
-                     "kvw_map_to_kernel_blocks", "kvw_kv_write"):
+                     "kvw_map_to_kernel_blocks", "kvw_ranges_to_block_table", "kvw_kv_write"):
         assert required in names
 
 
@@ -93,6 +93,25 @@ def test_expansion_validation(lib):
     g = lib.kvw_map_ranges_to_kernel_blocks
     assert g(P, P, P, P, 2, 4, 32, 12, P, P, P, P, None, None) == INVALID
     assert g(P, P, P, P, 2, 70000, 32, 16, P, P, P, P, None, None) == RANGE_CAP
+
+
+def test_table_fill_validation(lib):
+    f = lib.kvw_ranges_to_block_table
+    # start, len, cum, num_ranges, rows, range_stride, bs, kernel bs, table, table stride,
+    # counts, err_flag, stream
+    assert f(P, P, P, P, 2, 4, 32, 12, P, 16, None, None, None) == INVALID  # does not divide
+    assert "does not divide" in _err(lib)
+    assert f(P, P, P, P, 2, 4, 32, 0, P, 16, None, None, None) == INVALID
+    assert f(P, P, P, P, 2, 70000, 32, 16, P, 16, None, None, None) == RANGE_CAP
+    assert f(P, P, P, None, 2, 4, 32, 16, P, 16, None, None, None) == INVALID  # num_ranges
+    assert f(None, P, P, P, 2, 4, 32, 16, P, 16, None, None, None) == INVALID
+    assert f(P, P, P + 2, P, 2, 4, 32, 16, P, 16, None, None, None) == INVALID  # misaligned cum
+    assert f(P, P, P, P, 2, 4, 32, 16, None, 16, None, None, None) == INVALID  # table missing
+    assert f(P, P, P, P, 2, 4, 32, 16, P, -1, None, None, None) == INVALID
+    assert f(P, P, P, P, -1, 4, 32, 16, P, 16, None, None, None) == INVALID
+    assert f(P, P, P, P, 2, 4, 32, 16, P, 16, P + 1, None, None) == INVALID  # counts misaligned
+    assert f(P, P, P, P, 2, 4, 32, 16, P, 16, None, P + 3, None) == INVALID  # err_flag misaligned
+    assert f(P, P, P, P, 0, 4, 32, 16, P, 16, None, None, None) == OK        # no rows
 
 
 def _args(**kw):

@@ -14,5 +14,6 @@ from .gen import (  # noqa: F401
     config,
     custom,
     long_context,
+    range_tables,
     small_cases,
 )

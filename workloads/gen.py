@@ -474,3 +474,30 @@ def small_cases() -> List[Workload]:
     cases[-1].name = "small_layers"
     del rng
     return cases
+
+
+def range_tables(seed: int, runs_per_row: Sequence[int], *, max_len: int = 3,
+                 max_start: int = 1 << 20, range_stride: Optional[int] = None):
+    """Bare range descriptors (start, len, cum, num_ranges) for the table fill.
+
+    Row r holds runs_per_row[r] runs with lengths drawn from [1, max_len] and
+    starts drawn from [0, max_start); cum is the running count of blocks
+    before each run (the descriptor precondition).  Runs may overlap: a
+    table fill does not need unique blocks.  Entries past a row's count are 0.
+    """
+    rng = np.random.Generator(np.random.PCG64([seed, 3]))
+    rows = len(runs_per_row)
+    stride = range_stride if range_stride is not None else max(1, max(runs_per_row, default=1))
+    start = np.zeros((rows, stride), np.int32)
+    length = np.zeros((rows, stride), np.int32)
+    cum = np.zeros((rows, stride), np.int32)
+    num = np.zeros(rows, np.int32)
+    for r, n in enumerate(runs_per_row):
+        if n > stride:
+            raise ValueError("range_stride too small")
+        ln = rng.integers(1, max_len + 1, size=n)
+        start[r, :n] = rng.integers(0, max_start, size=n)
+        length[r, :n] = ln
+        cum[r, :n] = np.concatenate([[0], np.cumsum(ln)[:-1]]) if n else []
+        num[r] = n
+    return start, length, cum, num
