@@ -8,10 +8,16 @@ manager block on its own).  A step is the whole hot path for one batch:
 manager->kernel expansion of the variant's mapping structure, then the fused
 slot-map + K/V write (kvw_kv_write keeping the slot mapping, automatic
 kernel schedule) on the manager-unit mapping: slot ids are the same at
-either block size, so the write does not wait on the expanded table.
+either block size, so the write does not wait on the expanded table.  Both
+variants hand the attention side the same kernel-unit block table:
 
-  paged_r{R}     expand the block table, fused paged write
-  ranges_r{R}    expand the range descriptors, fused range write
+  paged_r{R}     expand the manager block table, fused paged write
+  ranges_r{R}    fill the block table straight from the range descriptors,
+                 fused range write
+
+The table-producing kernel of each variant is also timed alone, next to a
+plain device copy of the finished table (the per-step copy of a staged
+table that the fill replaces).
 
 `value` is tokens/s of paged_r4096; every variant is reported under
 "variants", with the fused call's time (HIP events on the launch stream)
@@ -176,12 +182,15 @@ def main():
             mode = kvw.KVW_SLOTS_PAGED
         else:
             rs, rl, rc, nr = (d(a) for a in (w.range_start, w.range_len, w.range_cum, w.num_ranges))
-            outs = [torch.empty_like(rs) for _ in range(3)] + [torch.empty_like(nr)]
-            expand_bytes = 2 * (3 * w.range_start.nbytes + w.num_ranges.nbytes)
+            kt = torch.empty((w.max_num_reqs, w.table_stride * k), dtype=torch.int32, device=dev)
+            kn = torch.empty_like(nr)
+            # descriptors read (12 B per run in use + the count) + table and counts written
+            expand_bytes = (12 * int(w.num_ranges.sum()) + w.num_ranges.nbytes + kt.numel() * 4
+                            + kn.numel() * 4)
             mapping = dict(range_start=rs, range_len=rl, range_cum=rc, num_ranges=nr)
 
-            def expand(rs=rs, rl=rl, rc=rc, nr=nr, outs=outs, w=w):
-                kvw.kvw_map_ranges_to_kernel_blocks(rs, rl, rc, nr, w.block_size, bs_k, *outs)
+            def expand(rs=rs, rl=rl, rc=rc, nr=nr, kt=kt, kn=kn, w=w):
+                kvw.kvw_ranges_to_block_table(rs, rl, rc, nr, w.block_size, bs_k, kt, kn)
             mode = kvw.KVW_SLOTS_RANGES
 
         def write(schedule, mode=mode, mapping=mapping, qsl=qsl, pos=pos, w=w):
@@ -205,10 +214,30 @@ def main():
             if ev is not None:
                 ev[1].record(stream)
 
+        def table_only(ev, expand=expand):
+            if ev is not None:
+                ev[0].record(stream)
+            expand()
+            if ev is not None:
+                ev[1].record(stream)
+
+        def table_copy(ev, kt=kt):
+            # a plain device copy of the finished table: what a staged table costs per step
+            if ev is not None:
+                ev[0].record(stream)
+            table_dst.copy_(kt)
+            if ev is not None:
+                ev[1].record(stream)
+
+        table_dst = torch.empty_like(kt)
         ms_step, call_ms = timed(step, args.warmup, args.steps)
         _, single_ms = timed(single, args.warmup, args.steps)
+        _, table_ms = timed(table_only, args.warmup, args.steps)
+        _, copy_ms = timed(table_copy, args.warmup, args.steps)
         call_avg = statistics.fmean(call_ms)
         single_avg = statistics.fmean(single_ms)
+        table_avg = statistics.fmean(table_ms)
+        copy_avg = statistics.fmean(copy_ms)
         step_bytes = fused_bytes + expand_bytes
         results[name] = {
             "tokens_per_s": real_tokens / (ms_step * 1e-3),
@@ -222,12 +251,20 @@ def main():
             "single_kernel_ms_avg": single_avg,
             "single_kernel_frac_of_peak": fused_bytes / (single_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS,
             "ranges_per_request": int(r),
+            "table_kernel": "expand_blocks_kernel" if kind == "paged" else "fill_table_kernel",
+            "table_ms_avg": table_avg,
+            "table_bytes": expand_bytes,
+            "table_gbps": expand_bytes / (table_avg * 1e-3) / 1e9,
+            "table_copy_ms_avg": copy_avg,
         }
         log(f"[bench] {name:13s} step {ms_step * 1e3:7.1f} us  fused call {call_avg * 1e3:7.1f} us = "
             f"{results[name]['fused_call_gbps']:5.0f} GB/s "
             f"({100 * results[name]['fused_call_frac_of_peak']:.1f}%)  single kernel "
             f"{single_avg * 1e3:7.1f} us ({100 * results[name]['single_kernel_frac_of_peak']:.1f}%)  "
             f"{results[name]['tokens_per_s'] / 1e6:.0f} M tokens/s")
+        log(f"[bench] {name:13s} {results[name]['table_kernel']} {table_avg * 1e3:6.2f} us "
+            f"({expand_bytes / 1e6:.2f} MB, {results[name]['table_gbps']:.0f} GB/s); "
+            f"device copy of the finished table {copy_avg * 1e3:6.2f} us")
         if name == HEADLINE:
             # the dominant kernel alone, on the slots the fused call just produced
             step(None)
@@ -246,7 +283,7 @@ def main():
             scatter = statistics.fmean(sc_ms)
             log(f"[bench] kv_scatter_kernel alone ({name} slots): {scatter * 1e3:.1f} us = "
                 f"{scatter_bytes / (scatter * 1e-3) / 1e9:.0f} GB/s")
-        del step, single, write, expand
+        del step, single, write, expand, table_only, table_copy, table_dst
 
     copy_ceiling = None
     if args.copy_calibration_mib:
