@@ -54,6 +54,10 @@ class Oracle:
         lib.orc_slot_mapping_paged.argtypes = [_P, _I32, _P, _I64, _P, _I32, _P, _I32, _P, _P]
         lib.orc_slot_mapping_ranges.argtypes = [_P, _I32, _P, _I64, _P, _P, _P, _P, _I32, _I32,
                                                 _P, _P]
+        lib.orc_slot_mapping_paged_cp.argtypes = [_P, _I32, _P, _I64, _P, _I32, _P, _I32, _I32,
+                                                  _I32, _I32, _P, _P]
+        lib.orc_slot_mapping_ranges_cp.argtypes = [_P, _I32, _P, _I64, _P, _P, _P, _P, _I32, _I32,
+                                                   _I32, _I32, _I32, _P, _P]
         lib.orc_map_to_kernel_blocks.argtypes = [_P, _P, _I32, _I32, _I32, _I32, _P, _I32, _P]
         lib.orc_map_ranges_to_kernel_blocks.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                                         _P, _P, _P, _P, _P]
@@ -66,6 +70,7 @@ class Oracle:
         lib.orc_kv_write.argtypes = [_P, _I64, _I32, _P, _P, _I64, _I64, _I64, _I32, _I64, _P, _P,
                                      _I64, _I64, _P]
         for f in (lib.orc_slot_mapping_paged, lib.orc_slot_mapping_ranges,
+                  lib.orc_slot_mapping_paged_cp, lib.orc_slot_mapping_ranges_cp,
                   lib.orc_map_to_kernel_blocks, lib.orc_map_ranges_to_kernel_blocks,
                   lib.orc_ranges_to_block_table, lib.orc_kv_write):
             f.restype = ctypes.c_int
@@ -108,6 +113,43 @@ class Oracle:
                                               rs.shape[1], block_size, _ptr(out),
                                               ctypes.byref(flags))
         self._check(rc, "slot_mapping_ranges")
+        return out, flags.value
+
+    # -- context-parallel slot mapping ---------------------------------------
+    def slot_mapping_paged_cp(self, query_start_loc, num_reqs: int, positions,
+                              max_num_tokens: int, block_table, num_blocks_per_req,
+                              block_size: int, cp_world_size: int, cp_rank: int,
+                              cp_interleave_size: int) -> Tuple[np.ndarray, int]:
+        qsl = _c(query_start_loc, np.int32)
+        pos = _c(positions, np.int64)
+        bt = _c(block_table, np.int32)
+        nb = None if num_blocks_per_req is None else _c(num_blocks_per_req, np.int32)
+        out = np.empty(max_num_tokens, dtype=np.int64)
+        flags = ctypes.c_uint32(0)
+        stride = bt.shape[1] if bt.ndim == 2 else 0
+        rc = self.lib.orc_slot_mapping_paged_cp(_ptr(qsl), num_reqs, _ptr(pos), max_num_tokens,
+                                                _ptr(bt), stride, _ptr(nb), block_size,
+                                                cp_world_size, cp_rank, cp_interleave_size,
+                                                _ptr(out), ctypes.byref(flags))
+        self._check(rc, "slot_mapping_paged_cp")
+        return out, flags.value
+
+    def slot_mapping_ranges_cp(self, query_start_loc, num_reqs: int, positions,
+                               max_num_tokens: int, range_start, range_len, range_cum,
+                               num_ranges, block_size: int, cp_world_size: int, cp_rank: int,
+                               cp_interleave_size: int) -> Tuple[np.ndarray, int]:
+        qsl = _c(query_start_loc, np.int32)
+        pos = _c(positions, np.int64)
+        rs, rl, rc_ = (_c(a, np.int32) for a in (range_start, range_len, range_cum))
+        nr = _c(num_ranges, np.int32)
+        out = np.empty(max_num_tokens, dtype=np.int64)
+        flags = ctypes.c_uint32(0)
+        rc = self.lib.orc_slot_mapping_ranges_cp(_ptr(qsl), num_reqs, _ptr(pos), max_num_tokens,
+                                                 _ptr(rs), _ptr(rl), _ptr(rc_), _ptr(nr),
+                                                 rs.shape[1], block_size, cp_world_size, cp_rank,
+                                                 cp_interleave_size, _ptr(out),
+                                                 ctypes.byref(flags))
+        self._check(rc, "slot_mapping_ranges_cp")
         return out, flags.value
 
     # -- manager -> kernel block expansion --------------------------------

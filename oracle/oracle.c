@@ -16,8 +16,9 @@
  *       sections "Verantwortung", "Entwurfsmotivation", "Datenfluss" and
  *       "Grenzen und Fehler".
  *  [P3] "vLLM Block Table Management: From PagedAttention to the V1 KV Cache
- *       Stack", Deep Dive sections 7 ("Worker-side block table
- *       materialization") and 8 ("slot_mapping: token -> physical slot").
+ *       Stack", "Symbol Map" (the block_size row) and Deep Dive sections 7
+ *       ("Worker-side block table materialization") and 8 ("slot_mapping:
+ *       token -> physical slot").
  *
  * Every loop below walks the definition in the order it is stated; nothing
  * is blocked, fused or reordered.  Integer arithmetic is done in int64.
@@ -169,6 +170,134 @@ int orc_slot_mapping_ranges(const int32_t *qsl, int32_t num_reqs, const int64_t 
             int64_t n = clamp64(num_ranges[r], 0, range_stride, &flags, ORC_FLAG_COUNT);
             int64_t logical = p / block_size;
             int64_t offset = p % block_size;
+            for (int64_t i = 0; i < n; ++i) {
+                int64_t k = (int64_t)r * range_stride + i;
+                int64_t cum = range_cum[k], len = range_len[k];
+                if (cum <= logical && logical < cum + len) {
+                    int64_t physical = (int64_t)range_start[k] + (logical - cum);
+                    if (physical < 0) flags |= ORC_FLAG_BAD_BLOCK;
+                    else slot_mapping[t] = physical * block_size + offset;
+                    break;
+                }
+            }
+        }
+    }
+    if (flags_out) *flags_out |= flags;
+    return ORC_OK;
+}
+
+/*
+ * Context-parallel slot mapping ([P2] "Entwurfsmotivation", DCP/PCP
+ * interleaving: with context parallelism the kernel writes real slots only
+ * for the positions of its own rank and the pad id for every other token;
+ * [P3] "Symbol Map", the block_size row: context parallelism multiplies the
+ * block size the attention groups see).  The pages name the three
+ * parameters -- world size W, rank, interleave size I -- but not the
+ * placement.  The reading taken is the plainest that fits both statements:
+ *  - the W ranks deal a request's positions among themselves in chunks of I
+ *    consecutive positions, round robin: position p is held by rank
+ *    (p / I) % W;
+ *  - a table entry names a virtual block of block_size*W positions, kept as
+ *    one block of block_size slots on every rank under the same id, and each
+ *    rank fills its block with its own positions in order.
+ * For position p of this rank, with span = block_size*W and o = p % span:
+ *   logical block = p / span,
+ *   offset        = (o / (I*W)) * I + o % I   (this rank's positions before
+ *                                              p in the virtual block),
+ *   slot          = block_table[r][logical block] * block_size + offset.
+ * A token of another rank is the pad id and reads nothing.  I must divide
+ * block_size (so a rank's share of a virtual block is whole chunks and fits
+ * its block); W = 1 is orc_slot_mapping_paged.  Other rules as there.
+ */
+static int cp_args_ok(int32_t block_size, int32_t world, int32_t rank, int32_t interleave)
+{
+    return world >= 1 && rank >= 0 && rank < world && interleave >= 1 &&
+           block_size % interleave == 0;
+}
+
+int orc_slot_mapping_paged_cp(const int32_t *qsl, int32_t num_reqs, const int64_t *positions,
+                              int64_t max_num_tokens, const int32_t *block_table,
+                              int32_t table_stride, const int32_t *num_blocks_per_req,
+                              int32_t block_size, int32_t cp_world_size, int32_t cp_rank,
+                              int32_t cp_interleave_size, int64_t *slot_mapping,
+                              uint32_t *flags_out)
+{
+    uint32_t flags = 0;
+    if (!qsl || num_reqs < 0 || max_num_tokens < 0 || block_size <= 0 || table_stride < 0 ||
+        (max_num_tokens > 0 && !slot_mapping))
+        return ORC_E_ARG;
+    if (!cp_args_ok(block_size, cp_world_size, cp_rank, cp_interleave_size)) return ORC_E_ARG;
+    if (!qsl_ok(qsl, num_reqs)) return ORC_E_QSL;
+
+    if (max_num_tokens == 0) return ORC_OK;
+    for (int64_t t = 0; t < max_num_tokens; ++t) slot_mapping[t] = ORC_PAD_ID;
+    int64_t num_tokens = num_tokens_of(qsl, num_reqs, max_num_tokens, &flags);
+    int64_t W = cp_world_size, I = cp_interleave_size, span = (int64_t)block_size * W;
+
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        for (int64_t t = qsl[r]; t < qsl[r + 1] && t < num_tokens; ++t) {
+            int64_t p = positions[t];
+            if (p < 0) continue;
+            if ((p / I) % W != cp_rank) continue;      /* another rank's position */
+            int64_t bound = table_stride;
+            if (num_blocks_per_req)
+                bound = clamp64(num_blocks_per_req[r], 0, table_stride, &flags, ORC_FLAG_COUNT);
+            int64_t logical = p / span;
+            int64_t o = p % span;
+            int64_t offset = (o / (I * W)) * I + o % I;
+            if (logical >= bound) continue;
+            int64_t physical = block_table[(int64_t)r * table_stride + logical];
+            if (physical < 0) { flags |= ORC_FLAG_BAD_BLOCK; continue; }
+            slot_mapping[t] = physical * block_size + offset;
+        }
+    }
+    if (flags_out) *flags_out |= flags;
+    return ORC_OK;
+}
+
+/* The same placement through range descriptors (runs of virtual blocks);
+ * W = 1 is orc_slot_mapping_ranges, whose precondition applies. */
+int orc_slot_mapping_ranges_cp(const int32_t *qsl, int32_t num_reqs, const int64_t *positions,
+                               int64_t max_num_tokens, const int32_t *range_start,
+                               const int32_t *range_len, const int32_t *range_cum,
+                               const int32_t *num_ranges, int32_t range_stride,
+                               int32_t block_size, int32_t cp_world_size, int32_t cp_rank,
+                               int32_t cp_interleave_size, int64_t *slot_mapping,
+                               uint32_t *flags_out)
+{
+    uint32_t flags = 0;
+    if (!qsl || num_reqs < 0 || max_num_tokens < 0 || block_size <= 0 || range_stride < 0 ||
+        (max_num_tokens > 0 && !slot_mapping))
+        return ORC_E_ARG;
+    if (num_reqs > 0 && (!range_start || !range_len || !range_cum || !num_ranges))
+        return ORC_E_ARG;
+    if (!cp_args_ok(block_size, cp_world_size, cp_rank, cp_interleave_size)) return ORC_E_ARG;
+    if (!qsl_ok(qsl, num_reqs)) return ORC_E_QSL;
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        uint32_t dummy = 0;
+        int64_t n = clamp64(num_ranges[r], 0, range_stride, &dummy, ORC_FLAG_COUNT);
+        int64_t expect_cum = 0;
+        for (int64_t i = 0; i < n; ++i) {
+            int64_t k = (int64_t)r * range_stride + i;
+            if (range_len[k] < 1 || range_cum[k] != expect_cum) return ORC_E_RANGES;
+            expect_cum += range_len[k];
+        }
+    }
+
+    if (max_num_tokens == 0) return ORC_OK;
+    for (int64_t t = 0; t < max_num_tokens; ++t) slot_mapping[t] = ORC_PAD_ID;
+    int64_t num_tokens = num_tokens_of(qsl, num_reqs, max_num_tokens, &flags);
+    int64_t W = cp_world_size, I = cp_interleave_size, span = (int64_t)block_size * W;
+
+    for (int32_t r = 0; r < num_reqs; ++r) {
+        for (int64_t t = qsl[r]; t < qsl[r + 1] && t < num_tokens; ++t) {
+            int64_t p = positions[t];
+            if (p < 0) continue;
+            if ((p / I) % W != cp_rank) continue;      /* another rank's position */
+            int64_t n = clamp64(num_ranges[r], 0, range_stride, &flags, ORC_FLAG_COUNT);
+            int64_t logical = p / span;
+            int64_t o = p % span;
+            int64_t offset = (o / (I * W)) * I + o % I;
             for (int64_t i = 0; i < n; ++i) {
                 int64_t k = (int64_t)r * range_stride + i;
                 int64_t cum = range_cum[k], len = range_len[k];

@@ -9,6 +9,7 @@ when the oracle disagrees with:
   * the pages' invariant that range arithmetic and the table gather give the
     same slot for the same physical layout, and that a table filled from the
     runs is the runs laid end to end;
+  * a dealing simulation (no division) of the context-parallel placement;
   * numpy's own row-major indexing (ravel_multi_index, array addresses,
     fancy-index scatter) for the coordinate form and the K/V copy.
 The same functions are run against deliberately broken builds of the oracle
@@ -381,6 +382,105 @@ def pin_table_fill(orc, workloads=()):
         assert np.array_equal(cnt, w.num_blocks_per_req), w.name
 
 
+def _deal(rows: List[List[int]], lengths: List[int], bs: int, world: int, interleave: int):
+    """Context parallelism by dealing, with no division: each request's positions are dealt to
+    the ranks in turn, `interleave` at a time; a virtual block of bs*world positions is one
+    table entry, and each rank takes the next free slot of its own copy of that block.
+    Returns, per request, the (rank, slot) of every position (slot None past the row)."""
+    out = []
+    for row, n in zip(rows, lengths):
+        placed = []
+        rank, dealt, v, in_v = 0, 0, 0, 0
+        fill = [0] * world
+        for _ in range(n):
+            if v < len(row):
+                placed.append((rank, row[v] * bs + fill[rank]))
+            else:
+                placed.append((rank, None))
+            fill[rank] += 1
+            dealt += 1
+            if dealt == interleave:
+                dealt, rank = 0, (rank + 1) % world
+            in_v += 1
+            if in_v == bs * world:
+                in_v, v, fill = 0, v + 1, [0] * world
+        out.append(placed)
+    return out
+
+
+def pin_context_parallel(orc, workloads=()):
+    """Context-parallel slot mapping (a reading: the pages name the parameters, not the layout).
+
+    Each rank's slots equal a dealing simulation; over the ranks every position is held exactly
+    once and every (rank, slot) is distinct; ranges and the gather agree on every rank; W = 1
+    is the plain mapping for any interleave size; invalid parameters are rejected."""
+    from oracle import OracleError
+    rng = np.random.default_rng(31)
+    for trial in range(16):
+        bs = [4, 8, 16, 6, 2, 12][trial % 6]
+        world = [2, 3, 4, 8][trial % 4]
+        interleave = int(rng.choice([i for i in range(1, bs + 1) if bs % i == 0]))
+        lengths = [int(rng.integers(1, 4 * bs * world)) for _ in range(int(rng.integers(1, 5)))]
+        vbs = bs * world
+        rows, _ = _simulate(rng, lengths, vbs, sum(-(-n // vbs) for n in lengths) + 20,
+                            run_free_list=trial % 2 == 0)
+        rows = [r[:len(r) - int(rng.integers(0, 2))] or r for r in rows]  # some rows end early
+        dealt = _deal(rows, lengths, bs, world, interleave)
+        sched, want = [], []
+        for n, plc in zip(lengths, dealt):
+            k = int(rng.integers(1, n + 1))
+            sched.append(list(range(n - k, n)))
+            want.append(plc[n - k:])
+        qsl, pos, m = _batch(sched, pad_to=sum(map(len, sched)) + 3, rng=rng)
+        t_, nb = _table(rows)
+        st, ln, cm, nr = _descriptors(rows)
+        seen = set()
+        held = np.zeros(m, np.int64)
+        for rank in range(world):
+            paged, fp = orc.slot_mapping_paged_cp(qsl, len(rows), pos, m, t_, nb, bs, world, rank,
+                                                  interleave)
+            ranges, fr = orc.slot_mapping_ranges_cp(qsl, len(rows), pos, m, st, ln, cm, nr, bs,
+                                                    world, rank, interleave)
+            assert np.array_equal(paged, ranges) and fp == fr == 0, (trial, rank)
+            flat = [x for plc in want for x in plc]
+            for i, (owner, slot) in enumerate(flat):
+                expect = slot if owner == rank and slot is not None else PAD
+                assert paged[i] == expect, (trial, rank, i, paged[i], expect)
+            assert (paged[len(flat):] == PAD).all()
+            for i in np.nonzero(paged >= 0)[0]:
+                assert (rank, int(paged[i])) not in seen
+                seen.add((rank, int(paged[i])))
+                held[i] += 1
+        n_real = sum(1 for plc in want for (_, s) in plc if s is not None)
+        assert held.sum() == n_real and held.max(initial=0) <= 1
+
+    for w in workloads:
+        plain, _ = orc.slot_mapping_paged(w.query_start_loc, w.num_reqs, w.positions,
+                                          w.max_num_tokens, w.block_table, w.num_blocks_per_req,
+                                          w.block_size)
+        for interleave in [i for i in (1, 2, w.block_size) if w.block_size % i == 0]:
+            cp, _ = orc.slot_mapping_paged_cp(w.query_start_loc, w.num_reqs, w.positions,
+                                              w.max_num_tokens, w.block_table,
+                                              w.num_blocks_per_req, w.block_size, 1, 0,
+                                              interleave)
+            assert np.array_equal(cp, plain), (w.name, interleave)
+            cr, _ = orc.slot_mapping_ranges_cp(w.query_start_loc, w.num_reqs, w.positions,
+                                               w.max_num_tokens, w.range_start, w.range_len,
+                                               w.range_cum, w.num_ranges, w.block_size, 1, 0,
+                                               interleave)
+            assert np.array_equal(cr, plain), (w.name, interleave)
+
+    qsl, pos, m = _batch([list(range(20))])
+    t_, nb = _table([[3, 5]])
+    for bad in ((16, 2, 2, 1), (16, 2, -1, 1), (16, 0, 0, 1), (16, 2, 0, 3), (16, 2, 0, 0),
+                (16, 2, 0, 32)):
+        try:
+            orc.slot_mapping_paged_cp(qsl, 1, pos, m, t_, nb, *bad)
+        except OracleError:
+            continue
+        raise AssertionError(f"context-parallel parameters {bad} not rejected")
+
+
 def pin_coordinates(orc):
     """Coordinate form == numpy row-major indexing of [layers][blocks][tokens] rows."""
     cfg = {f[0]: int(f[1]) for f in _lines("coordinate_layout.txt")}
@@ -468,5 +568,6 @@ def all_pins(orc, small, full=()):
     pin_range_equals_gather(orc, list(small) + list(full))
     pin_expansion(orc)
     pin_table_fill(orc, small)
+    pin_context_parallel(orc, small)
     pin_coordinates(orc)
     pin_kv_write(orc, small)

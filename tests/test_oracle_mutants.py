@@ -17,21 +17,22 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 
 MUTANTS = {
-    "paged_offset_sign": ("continue; }\n            slot_mapping[t] = physical * block_size + offset;",
-                          "continue; }\n            slot_mapping[t] = physical * block_size - offset;"),
-    "ranges_offset_dropped": ("else slot_mapping[t] = physical * block_size + offset;",
-                              "else slot_mapping[t] = physical * block_size;"),
+    "paged_offset_sign": ("if (logical >= bound) continue;            /* no block owned there: pad id */\n            int64_t physical = block_table[(int64_t)r * table_stride + logical];\n            if (physical < 0) { flags |= ORC_FLAG_BAD_BLOCK; continue; }\n            slot_mapping[t] = physical * block_size + offset;",
+                          "if (logical >= bound) continue;            /* no block owned there: pad id */\n            int64_t physical = block_table[(int64_t)r * table_stride + logical];\n            if (physical < 0) { flags |= ORC_FLAG_BAD_BLOCK; continue; }\n            slot_mapping[t] = physical * block_size - offset;"),
+    "ranges_offset_dropped": ("if (physical < 0) flags |= ORC_FLAG_BAD_BLOCK;\n                    else slot_mapping[t] = physical * block_size + offset;\n                    break;\n                }\n            }\n        }\n    }\n    if (flags_out) *flags_out |= flags;\n    return ORC_OK;\n}\n\n/*\n * Context-parallel",
+                              "if (physical < 0) flags |= ORC_FLAG_BAD_BLOCK;\n                    else slot_mapping[t] = physical * block_size;\n                    break;\n                }\n            }\n        }\n    }\n    if (flags_out) *flags_out |= flags;\n    return ORC_OK;\n}\n\n/*\n * Context-parallel"),
     "offset_is_quotient": ("int64_t offset = p % block_size;\n            if (logical >= bound)",
                            "int64_t offset = p / block_size;\n            if (logical >= bound)"),
-    "bound_off_by_one": ("if (logical >= bound) continue;", "if (logical > bound) continue;"),
-    "table_transposed": ("block_table[(int64_t)r * table_stride + logical]",
-                         "block_table[(int64_t)logical * table_stride + r]"),
-    "range_sign": ("(int64_t)range_start[k] + (logical - cum)",
-                   "(int64_t)range_start[k] + (cum - logical)"),
-    "range_end_inclusive": ("if (cum <= logical && logical < cum + len) {",
-                            "if (cum <= logical && logical <= cum + len) {"),
-    "range_drops_cum": ("(int64_t)range_start[k] + (logical - cum)",
-                        "(int64_t)range_start[k] + logical"),
+    "bound_off_by_one": ("if (logical >= bound) continue;            /* no block owned there: pad id */",
+                         "if (logical > bound) continue;             /* no block owned there: pad id */"),
+    "table_transposed": ("/* no block owned there: pad id */\n            int64_t physical = block_table[(int64_t)r * table_stride + logical];",
+                         "/* no block owned there: pad id */\n            int64_t physical = block_table[(int64_t)logical * table_stride + r];"),
+    "range_sign": ("int64_t offset = p % block_size;\n            for (int64_t i = 0; i < n; ++i) {\n                int64_t k = (int64_t)r * range_stride + i;\n                int64_t cum = range_cum[k], len = range_len[k];\n                if (cum <= logical && logical < cum + len) {\n                    int64_t physical = (int64_t)range_start[k] + (logical - cum);",
+                   "int64_t offset = p % block_size;\n            for (int64_t i = 0; i < n; ++i) {\n                int64_t k = (int64_t)r * range_stride + i;\n                int64_t cum = range_cum[k], len = range_len[k];\n                if (cum <= logical && logical < cum + len) {\n                    int64_t physical = (int64_t)range_start[k] + (cum - logical);"),
+    "range_end_inclusive": ("int64_t offset = p % block_size;\n            for (int64_t i = 0; i < n; ++i) {\n                int64_t k = (int64_t)r * range_stride + i;\n                int64_t cum = range_cum[k], len = range_len[k];\n                if (cum <= logical && logical < cum + len) {",
+                            "int64_t offset = p % block_size;\n            for (int64_t i = 0; i < n; ++i) {\n                int64_t k = (int64_t)r * range_stride + i;\n                int64_t cum = range_cum[k], len = range_len[k];\n                if (cum <= logical && logical <= cum + len) {"),
+    "range_drops_cum": ("int64_t offset = p % block_size;\n            for (int64_t i = 0; i < n; ++i) {\n                int64_t k = (int64_t)r * range_stride + i;\n                int64_t cum = range_cum[k], len = range_len[k];\n                if (cum <= logical && logical < cum + len) {\n                    int64_t physical = (int64_t)range_start[k] + (logical - cum);",
+                        "int64_t offset = p % block_size;\n            for (int64_t i = 0; i < n; ++i) {\n                int64_t k = (int64_t)r * range_stride + i;\n                int64_t cum = range_cum[k], len = range_len[k];\n                if (cum <= logical && logical < cum + len) {\n                    int64_t physical = (int64_t)range_start[k] + logical;"),
     "expansion_drops_factor": ("if (expandable(id, k)) v = id * k + j;",
                                "if (expandable(id, k)) v = id + j;"),
     "expansion_tail_not_null": ("for (int64_t c = 0; c < out_stride; ++c) out[(int64_t)r * out_stride + c] = 0;",
@@ -46,6 +47,14 @@ MUTANTS = {
                            "for (int64_t q = 0; q < out_stride; ++q) row[q] = 1;"),
     "fill_count_unclamped": ("counts_out[r] = (int32_t)(full < out_stride ? full : out_stride);",
                              "counts_out[r] = (int32_t)full;"),
+    "cp_owner_uses_remainder": ("if ((p / I) % W != cp_rank) continue;      /* another rank's position */\n            int64_t bound",
+                                "if ((p % I) % W != cp_rank) continue;      /* another rank's position */\n            int64_t bound"),
+    "cp_offset_drops_chunk": ("int64_t offset = (o / (I * W)) * I + o % I;\n            if (logical >= bound) continue;",
+                              "int64_t offset = o % I;\n            if (logical >= bound) continue;"),
+    "cp_block_not_widened": ("int64_t logical = p / span;\n            int64_t o = p % span;\n            int64_t offset = (o / (I * W)) * I + o % I;\n            if (logical >= bound)",
+                             "int64_t logical = p / block_size;\n            int64_t o = p % span;\n            int64_t offset = (o / (I * W)) * I + o % I;\n            if (logical >= bound)"),
+    "cp_ranges_offset_global": ("int64_t offset = (o / (I * W)) * I + o % I;\n            for (int64_t i = 0; i < n; ++i) {",
+                                "int64_t offset = o;\n            for (int64_t i = 0; i < n; ++i) {"),
     "coord_swaps_B_T": ("return (layer * num_blocks + block) * block_size + token;",
                         "return (layer * block_size + block) * num_blocks + token;"),
     "kv_drops_layer_term": ("int64_t src = layer * kv_layer_stride + t * kv_token_stride;",

@@ -92,6 +92,10 @@ def test_table_fill_long_context(orc, r):
     assert f == 0 and np.array_equal(out, kt) and np.array_equal(cnt, w.num_blocks_per_req * k)
 
 
+def test_context_parallel(orc, small):
+    P.pin_context_parallel(orc, small)
+
+
 def test_coordinate_form(orc):
     P.pin_coordinates(orc)
 
