@@ -39,7 +39,26 @@
  *    the device.  query_start_loc must be non-decreasing (not checked).
  *  - Pad id: KVW_PAD_ID (-1) marks a token without a slot: tokens at or past
  *    num_tokens, tokens of no request, negative positions, positions past
- *    the blocks a request owns ([P3] section 8; [P2] "Datenfluss").
+ *    the blocks a request owns ([P3] section 8; [P2] "Datenfluss"), and
+ *    with context parallelism the positions another rank holds.
+ *  - Context parallelism ([P2] "Entwurfsmotivation": the slot-mapping kernel
+ *    of a context-parallel rank gives real slots only to that rank's
+ *    positions; [P3] "Symbol Map": context parallelism multiplies the block
+ *    size the attention groups see).  The slot-mapping calls and the fused
+ *    write take cp_world_size W, cp_rank and cp_interleave_size I.  The ranks
+ *    deal a request's positions in chunks of I consecutive positions, round
+ *    robin (position p is held by rank (p / I) % W); a block-table entry, or
+ *    a run's block, names a virtual block of block_size*W positions, stored as
+ *    one block of block_size slots on every rank under the same id, each rank
+ *    filling it with its own positions in order.  For p held by this rank,
+ *    with o = p % (block_size*W):
+ *      lb   = p / (block_size*W),
+ *      slot = block(lb) * block_size + (o / (I*W)) * I + o % I;
+ *    every other token gets KVW_PAD_ID and reads no table entry or run.
+ *    W = 0 or 1 is the plain mapping.  For W >= 1: 0 <= cp_rank < W,
+ *    I >= 1 divides block_size, block_size*W <= INT32_MAX, else
+ *    KVW_ERR_INVALID_ARG.  The pages give the three parameters but not the
+ *    placement: this is the plainest placement with both properties.
  */
 #ifndef KVW_H
 #define KVW_H
@@ -51,7 +70,7 @@
 extern "C" {
 #endif
 
-#define KVW_ABI_VERSION 1
+#define KVW_ABI_VERSION 2
 #define KVW_PAD_ID (-1)
 /* Largest accepted range_stride (range descriptors per request). */
 #define KVW_MAX_RANGE_STRIDE 65536
@@ -113,7 +132,9 @@ kvw_status kvw_slot_mapping_paged(const int32_t *query_start_loc, int32_t num_re
                                   const int64_t *positions, int64_t max_num_tokens,
                                   const int32_t *block_table, int32_t block_table_stride,
                                   const int32_t *num_blocks_per_req, int32_t block_size,
-                                  int64_t *slot_mapping, int32_t *err_flag, void *stream);
+                                  int32_t cp_world_size, int32_t cp_rank,
+                                  int32_t cp_interleave_size, int64_t *slot_mapping,
+                                  int32_t *err_flag, void *stream);
 
 /*
  * Range-arithmetic slot mapping ([P1] "The Innovation").  Request r owns
@@ -141,7 +162,9 @@ kvw_status kvw_slot_mapping_ranges(const int32_t *query_start_loc, int32_t num_r
                                    const int32_t *range_start, const int32_t *range_len,
                                    const int32_t *range_cum, const int32_t *num_ranges,
                                    int32_t range_stride, int32_t block_size,
-                                   int64_t *slot_mapping, int32_t *err_flag, void *stream);
+                                   int32_t cp_world_size, int32_t cp_rank,
+                                   int32_t cp_interleave_size, int64_t *slot_mapping,
+                                   int32_t *err_flag, void *stream);
 
 /*
  * Manager-to-kernel block expansion ([P2] "Entwurfsmotivation" and
@@ -249,6 +272,9 @@ typedef struct kvw_kv_write_args {
     int64_t bytes_per_token;           /* multiple of 16 */
     int32_t *err_flag;                 /* device int32 or NULL */
     int32_t schedule;                  /* KVW_SCHEDULE_*; ignored in the precomputed mode */
+    int32_t cp_world_size;             /* PAGED/RANGES: context parallelism (0 = none); the */
+    int32_t cp_rank;                   /* cache holds this rank's blocks of block_size slots */
+    int32_t cp_interleave_size;
 } kvw_kv_write_args;
 
 /* sizeof(kvw_kv_write_args) as compiled into the library. */

@@ -90,6 +90,9 @@ struct MapArgs {
     int32_t table_stride;
     int32_t range_stride;
     int32_t block_size;
+    int32_t cp_world;       // context-parallel ranks (<= 1: none)
+    int32_t cp_rank;
+    int32_t cp_interleave;  // positions per dealt chunk; divides block_size
 };
 
 // Everything the K/V copy touches.
@@ -148,6 +151,48 @@ __device__ __forceinline__ int64_t clamp_count(int32_t c, int32_t stride, uint32
     return c;
 }
 
+// Logical block lb and in-block offset off of position p >= 0 on this rank.
+// Without context parallelism lb = p / bs and off = p % bs.  With W ranks
+// and interleave I the ranks deal positions in chunks of I, round robin; a
+// table entry covers a virtual block of bs*W positions, of which each rank
+// keeps its own, in order, in its block of bs slots:
+//   owner = (p / I) % W,  lb = p / (bs*W),  o = p % (bs*W),
+//   off = (o / (I*W)) * I + o % I.
+// Returns false when another rank holds p.  bs*W fits an int32 (host check).
+__device__ __forceinline__ bool locate(const MapArgs &a, int64_t p, int64_t &lb, int32_t &off)
+{
+    const uint32_t bs = static_cast<uint32_t>(a.block_size);
+    if (a.cp_world <= 1) {
+        if (p <= INT32_MAX) {
+            const uint32_t q = static_cast<uint32_t>(p) / bs;
+            lb = q;
+            off = static_cast<int32_t>(static_cast<uint32_t>(p) - q * bs);
+        } else {
+            lb = p / a.block_size;
+            off = static_cast<int32_t>(p - lb * a.block_size);
+        }
+        return true;
+    }
+    const int64_t w = a.cp_world, il = a.cp_interleave, span = static_cast<int64_t>(bs) * w;
+    int64_t o;
+    if (p <= INT32_MAX) {
+        const uint32_t up = static_cast<uint32_t>(p);
+        if ((up / static_cast<uint32_t>(il)) % static_cast<uint32_t>(w) !=
+            static_cast<uint32_t>(a.cp_rank))
+            return false;
+        const uint32_t q = up / static_cast<uint32_t>(span);
+        lb = q;
+        o = up - q * static_cast<uint32_t>(span);
+    } else {
+        if ((p / il) % w != a.cp_rank) return false;
+        lb = p / span;
+        o = p - lb * span;
+    }
+    const uint32_t uo = static_cast<uint32_t>(o), ui = static_cast<uint32_t>(il);
+    off = static_cast<int32_t>((uo / (ui * static_cast<uint32_t>(w))) * ui + uo % ui);
+    return true;
+}
+
 // Paged gather: one table load per position.
 __device__ __forceinline__ int64_t paged_block(const MapArgs &a, int32_t r, int64_t lb,
                                                uint32_t &flags)
@@ -195,14 +240,7 @@ __device__ __forceinline__ int64_t resolve_slot(const MapArgs &a, int64_t t, int
     const int32_t bs = a.block_size;
     int64_t lb;
     int32_t off;
-    if (p <= INT32_MAX) {
-        const uint32_t q = static_cast<uint32_t>(p) / static_cast<uint32_t>(bs);
-        lb = q;
-        off = static_cast<int32_t>(static_cast<uint32_t>(p) - q * static_cast<uint32_t>(bs));
-    } else {
-        lb = p / bs;
-        off = static_cast<int32_t>(p - lb * bs);
-    }
+    if (!locate(a, p, lb, off)) return KVW_PAD_ID;  // another context-parallel rank's token
     const int64_t b = (MODE == kPaged) ? paged_block(a, r, lb, flags) : range_block(a, r, lb, flags);
     if (b < 0) return KVW_PAD_ID;
     return b * bs + off;
@@ -314,20 +352,11 @@ __global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
     const bool real = in && t < num_tokens;
     const int64_t p = real ? a.positions[t] : -1;
     const int32_t r = wave_upper_index(a.qsl, a.num_reqs, t, real);
-    const bool ok = real && r >= 0 && p >= 0;
     const int32_t bs = a.block_size;
     int64_t lb = 0;
     int32_t off = 0;
-    if (ok) {
-        if (p <= INT32_MAX) {
-            const uint32_t q = static_cast<uint32_t>(p) / static_cast<uint32_t>(bs);
-            lb = q;
-            off = static_cast<int32_t>(static_cast<uint32_t>(p) - q * static_cast<uint32_t>(bs));
-        } else {
-            lb = p / bs;
-            off = static_cast<int32_t>(p - lb * bs);
-        }
-    }
+    // a token of another context-parallel rank is padding and reads nothing more
+    const bool ok = real && r >= 0 && p >= 0 && locate(a, p, lb, off);
     int64_t b = -1;
     if (MODE == kPaged) {
         if (ok) b = paged_block(a, r, lb, flags);
@@ -656,8 +685,24 @@ kvw_status check_ranges(const char *fn, int32_t num_reqs, const int32_t *start, 
     return KVW_OK;
 }
 
+// Context-parallel parameters: world 0 means none; from 1 up the rank must lie
+// in [0, world) and the interleave size divide block_size.
+kvw_status check_cp(const char *fn, int32_t block_size, int32_t world, int32_t rank,
+                    int32_t interleave)
+{
+    KVW_REQUIRE(world >= 0, "%s: cp_world_size %d is negative", fn, world);
+    if (world == 0) return KVW_OK;
+    KVW_REQUIRE(rank >= 0 && rank < world, "%s: cp_rank %d outside [0, %d)", fn, rank, world);
+    KVW_REQUIRE(interleave >= 1 && block_size % interleave == 0,
+                "%s: cp_interleave_size %d does not divide block_size %d", fn, interleave, block_size);
+    KVW_REQUIRE(static_cast<int64_t>(block_size) * world <= INT32_MAX,
+                "%s: block_size * cp_world_size overflows int32", fn);
+    return KVW_OK;
+}
+
 MapArgs make_map_args(const int32_t *qsl, int32_t num_reqs, const int64_t *positions,
-                      int64_t max_num_tokens, int32_t block_size, int32_t *err_flag)
+                      int64_t max_num_tokens, int32_t block_size, int32_t cp_world,
+                      int32_t cp_rank, int32_t cp_interleave, int32_t *err_flag)
 {
     MapArgs a{};
     a.qsl = qsl;
@@ -665,6 +710,9 @@ MapArgs make_map_args(const int32_t *qsl, int32_t num_reqs, const int64_t *posit
     a.positions = positions;
     a.max_num_tokens = max_num_tokens;
     a.block_size = block_size;
+    a.cp_world = cp_world > 1 ? cp_world : 1;
+    a.cp_rank = cp_world > 1 ? cp_rank : 0;
+    a.cp_interleave = cp_world > 1 ? cp_interleave : 1;
     a.err_flag = err_flag;
     return a;
 }
@@ -703,17 +751,22 @@ kvw_status kvw_slot_mapping_paged(const int32_t *query_start_loc, int32_t num_re
                                   const int64_t *positions, int64_t max_num_tokens,
                                   const int32_t *block_table, int32_t block_table_stride,
                                   const int32_t *num_blocks_per_req, int32_t block_size,
-                                  int64_t *slot_mapping, int32_t *err_flag, void *stream)
+                                  int32_t cp_world_size, int32_t cp_rank,
+                                  int32_t cp_interleave_size, int64_t *slot_mapping,
+                                  int32_t *err_flag, void *stream)
 {
     const char *fn = "kvw_slot_mapping_paged";
     kvw_status st = check_mapping_common(fn, query_start_loc, num_reqs, positions, max_num_tokens,
                                          block_size, err_flag);
     if (st != KVW_OK) return st;
+    if ((st = check_cp(fn, block_size, cp_world_size, cp_rank, cp_interleave_size)) != KVW_OK)
+        return st;
     if ((st = check_paged(fn, num_reqs, block_table, block_table_stride, num_blocks_per_req)) != KVW_OK)
         return st;
     if (max_num_tokens == 0) return KVW_OK;
     KVW_REQUIRE(slot_mapping && aligned(slot_mapping, 8), "%s: slot_mapping is NULL or misaligned", fn);
-    MapArgs a = make_map_args(query_start_loc, num_reqs, positions, max_num_tokens, block_size, err_flag);
+    MapArgs a = make_map_args(query_start_loc, num_reqs, positions, max_num_tokens, block_size,
+                              cp_world_size, cp_rank, cp_interleave_size, err_flag);
     a.block_table = block_table;
     a.table_stride = block_table_stride;
     a.num_blocks_per_req = num_blocks_per_req;
@@ -727,18 +780,23 @@ kvw_status kvw_slot_mapping_ranges(const int32_t *query_start_loc, int32_t num_r
                                    const int32_t *range_start, const int32_t *range_len,
                                    const int32_t *range_cum, const int32_t *num_ranges,
                                    int32_t range_stride, int32_t block_size,
-                                   int64_t *slot_mapping, int32_t *err_flag, void *stream)
+                                   int32_t cp_world_size, int32_t cp_rank,
+                                   int32_t cp_interleave_size, int64_t *slot_mapping,
+                                   int32_t *err_flag, void *stream)
 {
     const char *fn = "kvw_slot_mapping_ranges";
     kvw_status st = check_mapping_common(fn, query_start_loc, num_reqs, positions, max_num_tokens,
                                          block_size, err_flag);
     if (st != KVW_OK) return st;
+    if ((st = check_cp(fn, block_size, cp_world_size, cp_rank, cp_interleave_size)) != KVW_OK)
+        return st;
     if ((st = check_ranges(fn, num_reqs, range_start, range_len, range_cum, num_ranges,
                            range_stride)) != KVW_OK)
         return st;
     if (max_num_tokens == 0) return KVW_OK;
     KVW_REQUIRE(slot_mapping && aligned(slot_mapping, 8), "%s: slot_mapping is NULL or misaligned", fn);
-    MapArgs a = make_map_args(query_start_loc, num_reqs, positions, max_num_tokens, block_size, err_flag);
+    MapArgs a = make_map_args(query_start_loc, num_reqs, positions, max_num_tokens, block_size,
+                              cp_world_size, cp_rank, cp_interleave_size, err_flag);
     a.range_start = range_start;
     a.range_len = range_len;
     a.range_cum = range_cum;
@@ -884,6 +942,8 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
                  : check_ranges(fn, g.num_reqs, g.range_start, g.range_len, g.range_cum, g.num_ranges,
                                 g.range_stride);
         if (st != KVW_OK) return st;
+        st = check_cp(fn, g.block_size, g.cp_world_size, g.cp_rank, g.cp_interleave_size);
+        if (st != KVW_OK) return st;
         KVW_REQUIRE(!g.slot_mapping_out || aligned(g.slot_mapping_out, 8),
                     "%s: slot_mapping_out misaligned", fn);
         KVW_REQUIRE(g.schedule == KVW_SCHEDULE_AUTO || g.schedule == KVW_SCHEDULE_TWO_KERNELS ||
@@ -930,7 +990,8 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
     MapArgs a = make_map_args(g.query_start_loc, g.num_reqs, g.positions, g.max_num_tokens,
-                              g.block_size, g.err_flag);
+                              g.block_size, fused ? g.cp_world_size : 0, g.cp_rank,
+                              g.cp_interleave_size, g.err_flag);
     a.block_table = g.block_table;
     a.table_stride = g.block_table_stride;
     a.num_blocks_per_req = g.num_blocks_per_req;

@@ -15,7 +15,7 @@ import torch
 
 from .build import LIBRARY
 
-KVW_ABI_VERSION = 1
+KVW_ABI_VERSION = 2
 KVW_PAD_ID = -1
 KVW_MAX_RANGE_STRIDE = 65536
 KVW_OK, KVW_ERR_INVALID_ARG, KVW_ERR_UNSUPPORTED, KVW_ERR_RANGE_CAP, KVW_ERR_HIP = range(5)
@@ -46,6 +46,7 @@ class kvw_kv_write_args(ctypes.Structure):
         ("key", _P), ("value", _P), ("kv_layer_stride", _I64), ("kv_token_stride", _I64),
         ("k_cache", _P), ("v_cache", _P), ("bytes_per_token", _I64),
         ("err_flag", _P), ("schedule", _I32),
+        ("cp_world_size", _I32), ("cp_rank", _I32), ("cp_interleave_size", _I32),
     ]
 
 
@@ -62,8 +63,10 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
                            " (or __graft_entry__.build()); there is no fallback path")
     lib = ctypes.CDLL(path)
     sigs = {
-        "kvw_slot_mapping_paged": [_P, _I32, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P],
-        "kvw_slot_mapping_ranges": [_P, _I32, _P, _I64, _P, _P, _P, _P, _I32, _I32, _P, _P, _P],
+        "kvw_slot_mapping_paged": [_P, _I32, _P, _I64, _P, _I32, _P, _I32, _I32, _I32, _I32, _P,
+                                   _P, _P],
+        "kvw_slot_mapping_ranges": [_P, _I32, _P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
+                                    _I32, _P, _P, _P],
         "kvw_map_to_kernel_blocks": [_P, _P, _I32, _I32, _I32, _I32, _P, _I32, _P, _P],
         "kvw_map_ranges_to_kernel_blocks": [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P,
                                             _P, _P, _P],
@@ -116,27 +119,32 @@ def _stride(t: Optional[torch.Tensor]) -> int:
 
 def kvw_slot_mapping_paged(query_start_loc, num_reqs, positions, max_num_tokens, block_table,
                            num_blocks_per_req, block_size, slot_mapping, err_flag=None,
-                           stream=None):
-    """slot_mapping[t] = block_table[r][p // bs] * bs + p % bs (see include/kvw.h)."""
+                           stream=None, *, cp_world_size=1, cp_rank=0, cp_interleave_size=1):
+    """slot_mapping[t] = block_table[r][p // bs] * bs + p % bs (see include/kvw.h); with
+    cp_world_size > 1 only this context-parallel rank's positions get slots."""
     _check(library().kvw_slot_mapping_paged(
         _dev(query_start_loc, torch.int32, "query_start_loc"), int(num_reqs),
         _dev(positions, torch.int64, "positions"), int(max_num_tokens),
         _dev(block_table, torch.int32, "block_table", optional=True), _stride(block_table),
         _dev(num_blocks_per_req, torch.int32, "num_blocks_per_req", optional=True),
-        int(block_size), _dev(slot_mapping, torch.int64, "slot_mapping"),
+        int(block_size), int(cp_world_size), int(cp_rank), int(cp_interleave_size),
+        _dev(slot_mapping, torch.int64, "slot_mapping"),
         _dev(err_flag, torch.int32, "err_flag", optional=True), _stream(stream)))
 
 
 def kvw_slot_mapping_ranges(query_start_loc, num_reqs, positions, max_num_tokens, range_start,
                             range_len, range_cum, num_ranges, block_size, slot_mapping,
-                            err_flag=None, stream=None):
-    """slot = (start + lb - cum) * bs + p % bs for the run holding lb (see include/kvw.h)."""
+                            err_flag=None, stream=None, *, cp_world_size=1, cp_rank=0,
+                            cp_interleave_size=1):
+    """slot = (start + lb - cum) * bs + p % bs for the run holding lb (see include/kvw.h); with
+    cp_world_size > 1 only this context-parallel rank's positions get slots."""
     _check(library().kvw_slot_mapping_ranges(
         _dev(query_start_loc, torch.int32, "query_start_loc"), int(num_reqs),
         _dev(positions, torch.int64, "positions"), int(max_num_tokens),
         _dev(range_start, torch.int32, "range_start"), _dev(range_len, torch.int32, "range_len"),
         _dev(range_cum, torch.int32, "range_cum"), _dev(num_ranges, torch.int32, "num_ranges"),
-        _stride(range_start), int(block_size), _dev(slot_mapping, torch.int64, "slot_mapping"),
+        _stride(range_start), int(block_size), int(cp_world_size), int(cp_rank),
+        int(cp_interleave_size), _dev(slot_mapping, torch.int64, "slot_mapping"),
         _dev(err_flag, torch.int32, "err_flag", optional=True), _stream(stream)))
 
 
@@ -182,12 +190,15 @@ def kvw_kv_write(*, mode, key, value, k_cache, v_cache, num_blocks, block_size,
                  max_num_tokens=None, slot_mapping_in=None, slot_mapping_out=None,
                  query_start_loc=None, num_reqs=0, positions=None, block_table=None,
                  num_blocks_per_req=None, range_start=None, range_len=None, range_cum=None,
-                 num_ranges=None, err_flag=None, schedule=KVW_SCHEDULE_AUTO, stream=None):
+                 num_ranges=None, err_flag=None, schedule=KVW_SCHEDULE_AUTO, stream=None,
+                 cp_world_size=1, cp_rank=0, cp_interleave_size=1):
     """K/V scatter into the paged cache, optionally fused with the slot mapping.
 
     key, value: [num_layers, max_num_tokens, H, D] (or [max_num_tokens, H, D]) tensors of a
     2-byte dtype; their row stride gives bytes_per_token.  k_cache, v_cache: any contiguous
-    tensors holding num_layers * num_blocks * block_size such rows.
+    tensors holding num_layers * num_blocks * block_size such rows.  With cp_world_size > 1
+    the caches are this context-parallel rank's (block_size slots per block) and only its
+    positions are written.
     """
     for name, t in (("key", key), ("value", value)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
@@ -224,6 +235,8 @@ def kvw_kv_write(*, mode, key, value, k_cache, v_cache, num_blocks, block_size,
     a.bytes_per_token = bpt
     a.err_flag = _dev(err_flag, torch.int32, "err_flag", optional=True)
     a.schedule = int(schedule)
+    a.cp_world_size, a.cp_rank = int(cp_world_size), int(cp_rank)
+    a.cp_interleave_size = int(cp_interleave_size)
     if mode == KVW_SLOTS_PRECOMPUTED:
         a.slot_mapping_in = _dev(slot_mapping_in, torch.int64, "slot_mapping_in")
     else:

@@ -64,22 +64,36 @@ def _err(lib):
 
 def test_slot_mapping_validation(lib):
     f = lib.kvw_slot_mapping_paged
-    assert f(P, 4, P, 512, P, 16, P, 0, P, None, None) == INVALID   # block_size 0
+    NO_CP = (1, 0, 1)
+    assert f(P, 4, P, 512, P, 16, P, 0, *NO_CP, P, None, None) == INVALID   # block_size 0
     assert "block_size" in _err(lib)
-    assert f(P, 4, P, -1, P, 16, P, 16, P, None, None) == INVALID   # negative token rows
-    assert f(P, 4, P, 1 << 31, P, 16, P, 16, P, None, None) == INVALID
-    assert f(P, -1, P, 512, P, 16, P, 16, P, None, None) == INVALID
-    assert f(None, 4, P, 512, P, 16, P, 16, P, None, None) == INVALID
-    assert f(P, 4, P + 4, 512, P, 16, P, 16, P, None, None) == INVALID  # misaligned int64
-    assert f(P, 4, P, 512, None, 16, P, 16, P, None, None) == INVALID   # table missing
-    assert f(P, 4, P, 512, P, -2, P, 16, P, None, None) == INVALID
-    assert f(P, 4, P, 512, P, 16, P, 16, None, None, None) == INVALID  # output missing
-    assert f(P, 4, P, 512, P, 16, P, 16, P, P + 2, None) == INVALID   # misaligned err_flag
-    assert f(P, 4, P, 0, P, 16, P, 16, None, None, None) == OK        # nothing to do
+    assert f(P, 4, P, -1, P, 16, P, 16, *NO_CP, P, None, None) == INVALID   # negative token rows
+    assert f(P, 4, P, 1 << 31, P, 16, P, 16, *NO_CP, P, None, None) == INVALID
+    assert f(P, -1, P, 512, P, 16, P, 16, *NO_CP, P, None, None) == INVALID
+    assert f(None, 4, P, 512, P, 16, P, 16, *NO_CP, P, None, None) == INVALID
+    assert f(P, 4, P + 4, 512, P, 16, P, 16, *NO_CP, P, None, None) == INVALID  # misaligned int64
+    assert f(P, 4, P, 512, None, 16, P, 16, *NO_CP, P, None, None) == INVALID   # table missing
+    assert f(P, 4, P, 512, P, -2, P, 16, *NO_CP, P, None, None) == INVALID
+    assert f(P, 4, P, 512, P, 16, P, 16, *NO_CP, None, None, None) == INVALID  # output missing
+    assert f(P, 4, P, 512, P, 16, P, 16, *NO_CP, P, P + 2, None) == INVALID   # misaligned err_flag
+    assert f(P, 4, P, 0, P, 16, P, 16, *NO_CP, None, None, None) == OK        # nothing to do
     g = lib.kvw_slot_mapping_ranges
-    assert g(P, 4, P, 512, P, P, P, P, 65537, 16, P, None, None) == RANGE_CAP
-    assert g(P, 4, P, 512, None, P, P, P, 8, 16, P, None, None) == INVALID
-    assert g(P, 4, P, 512, P, P, P, P, -1, 16, P, None, None) == INVALID
+    assert g(P, 4, P, 512, P, P, P, P, 65537, 16, *NO_CP, P, None, None) == RANGE_CAP
+    assert g(P, 4, P, 512, None, P, P, P, 8, 16, *NO_CP, P, None, None) == INVALID
+    assert g(P, 4, P, 512, P, P, P, P, -1, 16, *NO_CP, P, None, None) == INVALID
+
+
+def test_context_parallel_validation(lib):
+    f = lib.kvw_slot_mapping_paged
+    for cp, what in (((-1, 0, 1), "negative"), ((2, 2, 1), "cp_rank"), ((2, -1, 1), "cp_rank"),
+                     ((2, 0, 3), "divide"), ((2, 0, 0), "divide"), ((1, 1, 1), "cp_rank"),
+                     ((1 << 28, 0, 1), "overflows")):
+        assert f(P, 4, P, 512, P, 16, P, 16, *cp, P, None, None) == INVALID, cp
+        assert what in _err(lib), (cp, _err(lib))
+        assert lib.kvw_slot_mapping_ranges(P, 4, P, 512, P, P, P, P, 8, 16, *cp, P, None,
+                                           None) == INVALID
+    for cp in ((0, 5, 0), (1, 0, 1), (4, 3, 16), (8, 0, 2)):   # world 0: rank and interleave unused
+        assert f(P, 4, P, 0, P, 16, P, 16, *cp, None, None, None) == OK, cp
 
 
 def test_expansion_validation(lib):
@@ -145,6 +159,8 @@ def test_kv_write_validation(lib):
     assert "schedule" in _err(lib)
     assert f(ctypes.byref(_args(schedule=kvw.KVW_SCHEDULE_TWO_KERNELS, slot_mapping_out=None)),
              None) == INVALID
+    assert f(ctypes.byref(_args(cp_world_size=2, cp_rank=2)), None) == INVALID
+    assert f(ctypes.byref(_args(cp_world_size=2, cp_interleave_size=5)), None) == INVALID
     assert f(ctypes.byref(_args(max_num_tokens=0)), None) == OK
 
 
