@@ -17,7 +17,11 @@ variants hand the attention side the same kernel-unit block table:
 
 The table-producing kernel of each variant is also timed alone, next to a
 plain device copy of the finished table (the per-step copy of a staged
-table that the fill replaces).
+table that the fill replaces).  On the headline layout, the fused write is
+also timed per context-parallel rank (two ranks, interleave 1 and 16): each
+rank writes its share of the batch into its own cache.  And per
+tensor-parallel rank (TP = 2, 4, 8 over the 8 KV heads): rows of 2048/TP
+bytes, every token.
 
 `value` is tokens/s of paged_r4096; every variant is reported under
 "variants", with the fused call's time (HIP events on the launch stream)
@@ -285,6 +289,80 @@ def main():
                 f"{scatter_bytes / (scatter * 1e-3) / 1e9:.0f} GB/s")
         del step, single, write, expand, table_only, table_copy, table_dst
 
+    # Context parallelism on the headline layout: the manager's 32-token blocks are the virtual
+    # blocks of two ranks holding 16-slot blocks each; every rank writes its share of the batch
+    # into its own cache (here a view of the same allocation), one rank after the other.
+    cp = None
+    if HEADLINE in results:
+        w = long_context(int(HEADLINE.partition("_r")[2]))
+        qsl, pos = d(w.query_start_loc), d(w.positions)
+        bt, nb = d(w.block_table), d(w.num_blocks_per_req)
+        world, bs_r = 2, w.block_size // 2
+        rows = w.num_blocks * bs_r
+        cp = {}
+        for inter in (1, bs_r):
+            for rank in range(world):
+                def cp_call(ev, inter=inter, rank=rank):
+                    if ev is not None:
+                        ev[0].record(stream)
+                    kvw.kvw_kv_write(mode=kvw.KVW_SLOTS_PAGED, key=key, value=value,
+                                     k_cache=cache[0, :rows], v_cache=cache[1, :rows],
+                                     num_blocks=w.num_blocks, block_size=bs_r,
+                                     query_start_loc=qsl, num_reqs=w.num_reqs, positions=pos,
+                                     block_table=bt, num_blocks_per_req=nb,
+                                     slot_mapping_out=sm_out, cp_world_size=world, cp_rank=rank,
+                                     cp_interleave_size=inter)
+                    if ev is not None:
+                        ev[1].record(stream)
+                _, cp_ms = timed(cp_call, args.warmup, args.steps)
+                held = int((sm_out >= 0).sum().item())  # this rank's tokens, from its own output
+                avg = statistics.fmean(cp_ms)
+                rank_bytes = held * base.num_layers * 4 * bpt + M * 16
+                cp[f"W{world}_I{inter}_rank{rank}"] = {
+                    "tokens": held, "fused_call_ms_avg": round(avg, 6),
+                    "gbps": round(rank_bytes / (avg * 1e-3) / 1e9, 1),
+                    "frac_of_peak": round(rank_bytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+                log(f"[bench] context parallel W={world} I={inter:2d} rank {rank}: {held} tokens, "
+                    f"fused call {avg * 1e3:6.1f} us = {cp[f'W{world}_I{inter}_rank{rank}']['gbps']:.0f}"
+                    f" GB/s")
+        del cp_call
+
+    # Tensor parallelism over KV heads: a rank writes 8/TP heads of every token, so its rows
+    # shrink to 2048/TP bytes; same slots, same layout, one rank's share measured.
+    tp = None
+    if HEADLINE in results:
+        tp = {}
+        w = long_context(int(HEADLINE.partition("_r")[2]))
+        qsl, pos = d(w.query_start_loc), d(w.positions)
+        bt, nb = d(w.block_table), d(w.num_blocks_per_req)
+        for tpn in (2, 4, 8):
+            h = H // tpn
+            k_r = key[:, :, :h, :].contiguous()
+            v_r = value[:, :, :h, :].contiguous()
+            rows = w.num_blocks * w.block_size
+            k_c = cache[0].view(-1)[:rows * h * D].view(rows, h * D)
+            v_c = cache[1].view(-1)[:rows * h * D].view(rows, h * D)
+
+            def tp_call(ev, k_r=k_r, v_r=v_r, k_c=k_c, v_c=v_c):
+                if ev is not None:
+                    ev[0].record(stream)
+                kvw.kvw_kv_write(mode=kvw.KVW_SLOTS_PAGED, key=k_r, value=v_r, k_cache=k_c,
+                                 v_cache=v_c, num_blocks=w.num_blocks, block_size=w.block_size,
+                                 query_start_loc=qsl, num_reqs=w.num_reqs, positions=pos,
+                                 block_table=bt, num_blocks_per_req=nb, slot_mapping_out=sm_out)
+                if ev is not None:
+                    ev[1].record(stream)
+            _, tp_ms = timed(tp_call, args.warmup, args.steps)
+            avg = statistics.fmean(tp_ms)
+            rank_bytes = real_tokens * base.num_layers * 4 * (bpt // tpn) + real_tokens * 16
+            tp[f"TP{tpn}"] = {"bytes_per_token": bpt // tpn, "fused_call_ms_avg": round(avg, 6),
+                              "gbps": round(rank_bytes / (avg * 1e-3) / 1e9, 1),
+                              "frac_of_peak": round(rank_bytes / (avg * 1e-3) / 1e9
+                                                    / HBM_PEAK_GBPS, 4)}
+            log(f"[bench] tensor parallel TP={tpn} ({bpt // tpn} B rows): fused call "
+                f"{avg * 1e3:6.1f} us = {tp[f'TP{tpn}']['gbps']:.0f} GB/s")
+            del tp_call, k_r, v_r
+
     copy_ceiling = None
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -351,6 +429,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "copy_ceiling": copy_ceiling,
+        "context_parallel": cp,
+        "tensor_parallel": tp,
         "variants": {k_: {kk: (round(vv, 6) if isinstance(vv, float) else vv)
                           for kk, vv in v.items()} for k_, v in results.items()},
     }
