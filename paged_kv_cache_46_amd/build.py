@@ -1,4 +1,5 @@
-"""Build libkvw.so (the HIP library behind include/kvw.h) for gfx950 with hipcc.
+"""Build libkvw.so (the HIP library behind include/kvw.h and include/kvw_alloc.h) for gfx950
+with hipcc.
 
 Usage: python -m paged_kv_cache_46_amd.build [extra hipcc flags...]
 """
@@ -12,6 +13,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCE = os.path.join(PKG, "csrc", "kvw.hip")
+SOURCES = (SOURCE, os.path.join(PKG, "csrc", "range_alloc.cpp"))
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libkvw.so")
 ARCH = "gfx950"
@@ -29,7 +31,7 @@ def build_library(verbose: bool = False, extra_flags: tuple = (), output: str = 
            "-Wall", "-Wextra",
            # never let the compiler form packed fp32 instructions (none are wanted here)
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", INCLUDE, *extra_flags, "-o", output + ".tmp", SOURCE]
+           "-I", INCLUDE, *extra_flags, "-o", output + ".tmp", *SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

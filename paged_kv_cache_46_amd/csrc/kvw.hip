@@ -41,6 +41,7 @@
 #include <cstdio>
 
 #include "kvw.h"
+#include "kvw_error.h"
 
 #ifndef KVW_SCATTER_WAVES
 #define KVW_SCATTER_WAVES 1
@@ -55,6 +56,25 @@
 #ifndef KVW_NT_STORES
 #define KVW_NT_STORES 1
 #endif
+
+namespace kvw_detail {
+
+namespace {
+thread_local char g_last_error[512] = "";
+}
+
+kvw_status fail(kvw_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+const char *last_error() { return g_last_error; }
+
+}  // namespace kvw_detail
 
 namespace {
 
@@ -613,16 +633,7 @@ __global__ __launch_bounds__(kBlockThreads) void fill_table_kernel(
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-thread_local char g_last_error[512] = "";
-
-kvw_status fail(kvw_status st, const char *fmt, ...)
-{
-    va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
-    va_end(ap);
-    return st;
-}
+using kvw_detail::fail;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -743,7 +754,7 @@ extern "C" {
 
 int32_t kvw_abi_version(void) { return KVW_ABI_VERSION; }
 
-const char *kvw_last_error(void) { return g_last_error; }
+const char *kvw_last_error(void) { return kvw_detail::last_error(); }
 
 size_t kvw_kv_write_args_size(void) { return sizeof(kvw_kv_write_args); }
 

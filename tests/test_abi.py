@@ -15,14 +15,18 @@ from paged_kv_cache_46_amd.build import LIBRARY
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvw.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 OK, INVALID, UNSUPPORTED, RANGE_CAP, HIP = range(5)
 P = 0x10000  # an aligned, never dereferenced stand-in for a device pointer
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvw_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(kvw_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -35,7 +39,9 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("kvw_slot_mapping_paged", "kvw_slot_mapping_ranges",
-                     "kvw_map_to_kernel_blocks", "kvw_ranges_to_block_table", "kvw_kv_write"):
+                     "kvw_map_to_kernel_blocks", "kvw_ranges_to_block_table", "kvw_kv_write",
+                     "kvw_alloc_create", "kvw_alloc_extend", "kvw_alloc_ranges",
+                     "kvw_coord_offset"):
         assert required in names
 
 
