@@ -385,6 +385,8 @@ def main():
             "(read + write)")
         del src, dst
 
+    host_alloc = host_allocator()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(long_context(int(HEADLINE.partition("_r")[2])), args.cpu_seconds)
@@ -431,6 +433,7 @@ def main():
         "copy_ceiling": copy_ceiling,
         "context_parallel": cp,
         "tensor_parallel": tp,
+        "host_allocator": host_alloc,
         "variants": {k_: {kk: (round(vv, 6) if isinstance(vv, float) else vv)
                           for kk, vv in v.items()} for k_, v in results.items()},
     }
@@ -545,6 +548,41 @@ def bench_config(args):
         "variants": {k_: {kk: round(vv, 6) for kk, vv in v.items()} for k_, v in results.items()},
     }
     print(json.dumps(line), flush=True)
+
+
+# Host figures of the same scenarios published on "Range-addressed KV cache blocks for the vLLM
+# serving engine" ("Measured Results"), measured there on an Apple arm64 host: context, not a target.
+PUBLISHED_HOST_NS = {"map/offset single": 1.85, "map/offset decode walk": 1.85,
+                     "map/offset context walk 4k": 1.71, "alloc/allocate release": 66.6,
+                     "alloc/grow in place": 25.8, "alloc/prefix acquire release": 4.3,
+                     "alloc/evict cache only": 71.6}
+
+
+def host_allocator():
+    """Run the native host benchmark of the range allocator (paged_kv_cache_46_amd/bench_alloc)."""
+    import platform
+    import subprocess
+
+    from paged_kv_cache_46_amd.build import BENCH_ALLOC
+    if not os.path.exists(BENCH_ALLOC):
+        log("[bench] bench_alloc not built; host allocator figures skipped")
+        return None
+    r = subprocess.run([BENCH_ALLOC, "200000", "20"], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        log(f"[bench] bench_alloc failed: {r.stderr[-500:]}")
+        return None
+    out = {}
+    for ln in r.stdout.splitlines():
+        d = json.loads(ln)
+        name = d.pop("scenario")
+        d["published_ns"] = PUBLISHED_HOST_NS.get(name)
+        out[name] = d
+        log(f"[bench] host {name:30s} {d['mean_ns']:8.2f} +- {d['stddev_ns']:.2f} {d['unit']}"
+            f"  (published {d['published_ns']})")
+    cpu = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo")
+                if ln.startswith("model name")), platform.processor())
+    return {"cpu": cpu, "harness": "iterations x rounds, one warmup call per round, steady clock",
+            "scenarios": out}
 
 
 def cpu_baseline(w, budget_s):

@@ -16,6 +16,8 @@ SOURCE = os.path.join(PKG, "csrc", "kvw.hip")
 SOURCES = (SOURCE, os.path.join(PKG, "csrc", "range_alloc.cpp"))
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libkvw.so")
+BENCH_SOURCE = os.path.join(PKG, "csrc", "bench_alloc.cpp")
+BENCH_ALLOC = os.path.join(PKG, "bench_alloc")
 ARCH = "gfx950"
 
 
@@ -45,5 +47,24 @@ def build_library(verbose: bool = False, extra_flags: tuple = (), output: str = 
     return output
 
 
+def build_bench_alloc(verbose: bool = False, library: str = LIBRARY,
+                      output: str = BENCH_ALLOC) -> str:
+    """The host benchmark of the range allocator: a native executable linked to libkvw.so."""
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        raise RuntimeError("no host C++ compiler to build bench_alloc")
+    cmd = [cxx, "-O2", "-std=c++17", "-Wall", "-Wextra", "-Werror", "-I", INCLUDE, BENCH_SOURCE,
+           "-L", os.path.dirname(library), "-lkvw", "-Wl,-rpath,$ORIGIN",
+           "-Wl,-rpath-link,/opt/rocm/lib", "-o", output + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"bench_alloc build failed ({r.returncode}):\n{r.stderr}")
+    os.replace(output + ".tmp", output)
+    return output
+
+
 if __name__ == "__main__":
     print(build_library(verbose=True, extra_flags=tuple(sys.argv[1:])))
+    print(build_bench_alloc(verbose=True))

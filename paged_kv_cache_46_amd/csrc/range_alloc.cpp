@@ -47,6 +47,7 @@ struct Extent {
 struct kvw_alloc {
     int64_t num_blocks = 0;
     int32_t align = 1;
+    int32_t align_log2 = -1;  // log2(align) when align is a power of two
     int32_t c0 = 0;        // first usable chunk
     int32_t nchunks = 0;   // usable chunks end here
     int32_t max_rows = 0;
@@ -62,25 +63,43 @@ struct kvw_alloc {
     int64_t cache_only_chunks = 0;
 
     // -- free space --------------------------------------------------------
+    // The running maximum stays in a register and only the sibling is loaded,
+    // so no level waits on the store made at the level below.
     void set_leaf(int32_t c, int32_t v)
     {
         run_len[c] = v;
         int32_t i = c + leaves;
         tree[i] = v;
-        for (i >>= 1; i >= 1; i >>= 1) {
-            const int32_t m = std::max(tree[2 * i], tree[2 * i + 1]);
+        int32_t m = v;
+        while (i > 1) {
+            m = std::max(m, tree[i ^ 1]);
+            i >>= 1;
             if (tree[i] == m) break;
             tree[i] = m;
         }
     }
 
-    // Leftmost run start with at least k free chunks, or -1.
+    // Leftmost run start with at least k free chunks, or -1.  The descent is
+    // branch-free: the left/right choice is data-dependent and would mispredict.
     int32_t first_fit(int64_t k) const
     {
         if (tree[1] < k) return -1;
         int32_t i = 1;
-        while (i < leaves) i = tree[2 * i] >= k ? 2 * i : 2 * i + 1;
+        while (i < leaves) i = 2 * i + static_cast<int32_t>(tree[2 * i] < k);
         return i - leaves;
+    }
+
+    // Blocks -> chunks; false when n is not a multiple of the alignment.
+    bool to_chunks(int64_t n, int64_t &k) const
+    {
+        if (align_log2 >= 0) {
+            if (n & (static_cast<int64_t>(align) - 1)) return false;
+            k = n >> align_log2;
+            return true;
+        }
+        if (n % align) return false;
+        k = n / align;
+        return true;
     }
 
     // Allocate the first k chunks of the free run starting at s.
@@ -224,6 +243,8 @@ kvw_status kvw_alloc_create(int64_t num_blocks, int32_t alignment, int64_t first
         auto *a = new kvw_alloc();
         a->num_blocks = num_blocks;
         a->align = alignment;
+        if ((alignment & (alignment - 1)) == 0)
+            a->align_log2 = __builtin_ctz(static_cast<unsigned>(alignment));
         a->nchunks = static_cast<int32_t>(num_blocks / alignment);
         a->c0 = static_cast<int32_t>(std::min<int64_t>((first_block + alignment - 1) / alignment,
                                                        a->nchunks));
@@ -255,11 +276,11 @@ kvw_status kvw_alloc_extend(kvw_alloc *a, int32_t row, int64_t num_blocks)
 {
     const char *fn = "kvw_alloc_extend";
     if (!row_ok(a, row)) return fail(KVW_ERR_INVALID_ARG, "%s: no allocator or row %d", fn, row);
-    if (num_blocks < 0 || num_blocks % a->align)
+    int64_t k;
+    if (num_blocks < 0 || !a->to_chunks(num_blocks, k))
         return fail(KVW_ERR_INVALID_ARG, "%s: %lld blocks is not a non-negative multiple of %d",
                     fn, (long long)num_blocks, a->align);
-    if (num_blocks == 0) return KVW_OK;
-    const int64_t k = num_blocks / a->align;
+    if (k == 0) return KVW_OK;
     if (a->free_chunks < k) {
         if (a->free_chunks + a->cache_only_chunks < k)
             return fail(KVW_ERR_NO_SPACE, "%s: %lld blocks wanted, %lld free and %lld evictable",
@@ -522,16 +543,19 @@ kvw_status kvw_coord_offset(int64_t layer, int64_t block, int64_t token, int64_t
                             int64_t num_blocks, int64_t block_size, int64_t bytes_per_token,
                             int64_t *offset)
 {
-    if (!offset || num_layers < 0 || num_blocks < 0 || block_size < 0 || bytes_per_token < 0 ||
-        layer < 0 || layer >= num_layers || block < 0 || block >= num_blocks || token < 0 ||
-        token >= block_size)
+    // unsigned compares reject negative coordinates too; each size is below
+    // 2^63, so the 128-bit product below cannot wrap
+    if (!offset || bytes_per_token < 0 || static_cast<uint64_t>(layer) >= static_cast<uint64_t>(num_layers) ||
+        static_cast<uint64_t>(block) >= static_cast<uint64_t>(num_blocks) ||
+        static_cast<uint64_t>(token) >= static_cast<uint64_t>(block_size))
         return fail(KVW_ERR_INVALID_ARG, "kvw_coord_offset: coordinate out of range");
-    int64_t n;
-    if (__builtin_mul_overflow(layer, num_blocks, &n) || __builtin_add_overflow(n, block, &n) ||
-        __builtin_mul_overflow(n, block_size, &n) || __builtin_add_overflow(n, token, &n) ||
-        __builtin_mul_overflow(n, bytes_per_token, &n))
+    using u128 = unsigned __int128;
+    const u128 n = ((static_cast<u128>(layer) * static_cast<uint64_t>(num_blocks) +
+                     static_cast<uint64_t>(block)) * static_cast<uint64_t>(block_size) +
+                    static_cast<uint64_t>(token)) * static_cast<uint64_t>(bytes_per_token);
+    if (n > static_cast<u128>(INT64_MAX))
         return fail(KVW_ERR_UNSUPPORTED, "kvw_coord_offset: offset overflows int64");
-    *offset = n;
+    *offset = static_cast<int64_t>(n);
     return KVW_OK;
 }
 
