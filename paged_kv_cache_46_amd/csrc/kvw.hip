@@ -3,8 +3,11 @@
 // Kernels:
 //   slot_mapping_kernel<MODE>    one token per lane: paged gather or range
 //                                arithmetic, tail padded with the pad id;
-//   kv_scatter_kernel            one 1 KiB slice of one K or V row per wave,
-//                                slot read from a slot mapping;
+//   kv_scatter_kernel<TPW>       one 1 KiB slice of one K or V row per wave
+//                                (of TPW consecutive tokens under context
+//                                parallelism), slot read from a slot mapping;
+//   kv_scatter_small_kernel      rows under 1 KiB: one plane of several
+//                                consecutive tokens per wave;
 //   kv_write_fused_kernel<MODE>  one wave per token and plane: slot resolution
 //                                and the copy of the token's row in one pass;
 //   expand_blocks_kernel,
@@ -131,6 +134,8 @@ struct CopyArgs {
     uint32_t slices_per_row;  // ceil(bytes_per_token / 1 KiB)
     uint32_t items_per_token; // 2 planes x slices_per_row
     int32_t items_log2;       // log2(items_per_token), or -1 if not a power of two
+    uint32_t lanes_per_row;   // rows under 1 KiB: bytes_per_token / 16 lanes per row
+    uint32_t rows_per_wave;   // rows under 1 KiB: 64 / lanes_per_row tokens per wave
 };
 
 __device__ __forceinline__ void raise_flags(int32_t *err, uint32_t flags)
@@ -426,35 +431,74 @@ __device__ __forceinline__ void store16(uint8_t *p, u32x4 v)
 // Items are ordered layer-major (blockIdx.y), then token, plane, slice, so
 // consecutive waves stream through consecutive K/V rows and, for tokens of
 // one block, consecutive cache slots.
+// TPW > 1 (context parallelism, where most neighbouring tokens of a rank's
+// batch are another rank's): one wave takes the same slice of TPW consecutive
+// tokens and skips the padded ones, so far fewer waves start only to exit.
+template <int TPW>
 __global__ __launch_bounds__(kScatterThreads) void kv_scatter_kernel(const int64_t *slots,
                                                                      CopyArgs c, int32_t *err_flag)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint64_t item = static_cast<uint64_t>(blockIdx.x) * kScatterWaves + wave;
-    uint64_t t64;
+    uint64_t g64;
     uint32_t r;
     if (c.items_log2 >= 0) {
-        t64 = item >> c.items_log2;
+        g64 = item >> c.items_log2;
         r = static_cast<uint32_t>(item & ((1u << c.items_log2) - 1));
     } else {
-        t64 = item / c.items_per_token;
-        r = static_cast<uint32_t>(item - t64 * c.items_per_token);
+        g64 = item / c.items_per_token;
+        r = static_cast<uint32_t>(item - g64 * c.items_per_token);
     }
-    if (t64 >= static_cast<uint64_t>(c.max_num_tokens)) return;
-    const int64_t t = static_cast<int64_t>(t64);
     const uint32_t plane = r >= c.slices_per_row ? 1u : 0u;
     const uint32_t slice = r - plane * c.slices_per_row;
     const int64_t off = static_cast<int64_t>(slice) * kSliceBytes + static_cast<int64_t>(lane) * 16;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+        const uint64_t t64 = g64 * TPW + j;
+        if (t64 >= static_cast<uint64_t>(c.max_num_tokens)) return;
+        const int64_t t = static_cast<int64_t>(t64);
+        const int64_t slot = slots[t];
+        if (slot >= c.rows_per_layer) {  // beyond the cache: skipped, reported once per token
+            if (blockIdx.y == 0 && r == 0 && lane == 0) raise_flags(err_flag, KVW_FLAG_SLOT_OOB);
+            continue;
+        }
+        if (slot < 0 || off >= c.bytes_per_token) continue;
+        const uint8_t *src = (plane ? c.value : c.key) + t * c.kv_token_stride + off;
+        uint8_t *dst = (plane ? c.v_cache : c.k_cache) + slot * c.bytes_per_token + off;
+        // coordinate n = (l*B + slot/T)*T + slot%T = l*B*T + slot
+        for (int64_t l = blockIdx.y; l < c.num_layers; l += gridDim.y)
+            store16<KVW_NT_STORES>(dst + l * c.rows_per_layer * c.bytes_per_token,
+                                   load16<KVW_NT_LOADS>(src + l * c.kv_layer_stride));
+    }
+}
+
+// Rows shorter than a wave's 1 KiB: one wave copies one plane of up to
+// rows_per_wave consecutive tokens (lane group g of lanes_per_row lanes takes
+// token t0 + g), so a wave still moves up to 1 KiB; each lane reads its own
+// token's slot.
+__global__ __launch_bounds__(kScatterThreads) void kv_scatter_small_kernel(const int64_t *slots,
+                                                                           CopyArgs c,
+                                                                           int32_t *err_flag)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint64_t item = static_cast<uint64_t>(blockIdx.x) * kScatterWaves + wave;
+    const uint32_t plane = static_cast<uint32_t>(item & 1);
+    const uint32_t g = static_cast<uint32_t>(lane) / c.lanes_per_row;
+    if (g >= c.rows_per_wave) return;
+    const uint64_t t64 = (item >> 1) * c.rows_per_wave + g;
+    if (t64 >= static_cast<uint64_t>(c.max_num_tokens)) return;
+    const int64_t t = static_cast<int64_t>(t64);
+    const int64_t off = static_cast<int64_t>(static_cast<uint32_t>(lane) - g * c.lanes_per_row) * 16;
     const int64_t slot = slots[t];
     if (slot >= c.rows_per_layer) {  // beyond the cache: skipped, reported once per token
-        if (blockIdx.y == 0 && r == 0 && lane == 0) raise_flags(err_flag, KVW_FLAG_SLOT_OOB);
+        if (blockIdx.y == 0 && plane == 0 && off == 0) raise_flags(err_flag, KVW_FLAG_SLOT_OOB);
         return;
     }
-    if (slot < 0 || off >= c.bytes_per_token) return;
+    if (slot < 0) return;
     const uint8_t *src = (plane ? c.value : c.key) + t * c.kv_token_stride + off;
     uint8_t *dst = (plane ? c.v_cache : c.k_cache) + slot * c.bytes_per_token + off;
-    // coordinate n = (l*B + slot/T)*T + slot%T = l*B*T + slot
     for (int64_t l = blockIdx.y; l < c.num_layers; l += gridDim.y)
         store16<KVW_NT_STORES>(dst + l * c.rows_per_layer * c.bytes_per_token,
                                load16<KVW_NT_LOADS>(src + l * c.kv_layer_stride));
@@ -996,8 +1040,21 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
         if (c.items_per_token == (1u << b)) c.items_log2 = b;
     const unsigned layer_grid =
         g.num_layers < 1 ? 1u : (static_cast<unsigned>(g.num_layers) < kMaxGridY ? g.num_layers : kMaxGridY);
-    const int64_t scatter_blocks =
-        (g.max_num_tokens * static_cast<int64_t>(c.items_per_token) + kScatterWaves - 1) / kScatterWaves;
+    // Scatter shape.  Rows under 1 KiB: a wave copies one plane of several
+    // tokens.  Context parallelism: a wave takes one slice of up to four
+    // consecutive tokens, most of which may be another rank's.
+    const bool small_rows = g.bytes_per_token < kSliceBytes;
+    const int32_t cp = fused && g.cp_world_size > 1 ? g.cp_world_size : 1;
+    const int tpw = small_rows ? 1 : (cp >= 4 ? 4 : (cp >= 2 ? 2 : 1));
+    int64_t scatter_waves;
+    if (small_rows) {
+        c.lanes_per_row = static_cast<uint32_t>(g.bytes_per_token / 16);
+        c.rows_per_wave = static_cast<uint32_t>(kWave) / c.lanes_per_row;
+        scatter_waves = 2 * ((g.max_num_tokens + c.rows_per_wave - 1) / c.rows_per_wave);
+    } else {
+        scatter_waves = (g.max_num_tokens + tpw - 1) / tpw * static_cast<int64_t>(c.items_per_token);
+    }
+    const int64_t scatter_blocks = (scatter_waves + kScatterWaves - 1) / kScatterWaves;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
     MapArgs a = make_map_args(g.query_start_loc, g.num_reqs, g.positions, g.max_num_tokens,
@@ -1029,8 +1086,19 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
         }
         if (g.num_layers == 0) return KVW_OK;
         const int64_t *slots = fused ? g.slot_mapping_out : g.slot_mapping_in;
-        hipLaunchKernelGGL(kv_scatter_kernel, dim3(static_cast<unsigned>(scatter_blocks), layer_grid),
-                           dim3(kScatterThreads), 0, s, slots, c, g.err_flag);
+        const dim3 grid(static_cast<unsigned>(scatter_blocks), layer_grid);
+        if (small_rows)
+            hipLaunchKernelGGL(kv_scatter_small_kernel, grid, dim3(kScatterThreads), 0, s, slots, c,
+                               g.err_flag);
+        else if (tpw == 4)
+            hipLaunchKernelGGL(kv_scatter_kernel<4>, grid, dim3(kScatterThreads), 0, s, slots, c,
+                               g.err_flag);
+        else if (tpw == 2)
+            hipLaunchKernelGGL(kv_scatter_kernel<2>, grid, dim3(kScatterThreads), 0, s, slots, c,
+                               g.err_flag);
+        else
+            hipLaunchKernelGGL(kv_scatter_kernel<1>, grid, dim3(kScatterThreads), 0, s, slots, c,
+                               g.err_flag);
         return launched(fn);
     }
     // fused mode without a slot-mapping output: one kernel, one wave per token

@@ -164,6 +164,28 @@ def test_kv_write_small(w, mode):
     check_kv_write(w, mode)
 
 
+def _row_width_workload(heads, head_dim):
+    r = np.random.default_rng(4730 + heads * 131 + head_dim)
+    reqs = [Request(int(r.integers(1, 3000)) + 700, int(r.integers(300, 700))) for _ in range(5)]
+    reqs += [Request(int(r.integers(1, 3000)), 1) for _ in range(40)]
+    n = sum(q.n_new for q in reqs)
+    return custom(f"rows_{heads * head_dim * 2}B", 4730 + heads, reqs, block_size=16,
+                  num_blocks=9000, runs=("count", 1, 5), num_kv_heads=heads, head_dim=head_dim,
+                  num_layers=2, max_num_tokens=n + 29)
+
+
+# rows of 48 B (21 tokens per wave), 512 B (2 per wave), 1008 B (one per wave, 63 lanes),
+# 1040 B (just over one slice), 2048 B: the packed and the slice-granular scatter
+ROW_WIDTHS = [(1, 24), (2, 128), (63, 8), (65, 8), (8, 128)]
+
+
+@pytest.mark.parametrize("mode", ["precomputed", "paged-two", "ranges-two", "paged-one",
+                                  "paged-noslots"])
+@pytest.mark.parametrize("shape", ROW_WIDTHS, ids=lambda s: f"{s[0] * s[1] * 2}B")
+def test_kv_write_row_widths(shape, mode):
+    check_kv_write(_row_width_workload(*shape), mode)
+
+
 @pytest.mark.parametrize("mode", WRITE_MODES[1:])
 @pytest.mark.parametrize("name", ["tiny_prefill", "decode_step", "mixed_chunked"])
 def test_kv_write_study(name, mode):
