@@ -58,7 +58,8 @@ class Oracle:
                                                   _I32, _I32, _P, _P]
         lib.orc_slot_mapping_ranges_cp.argtypes = [_P, _I32, _P, _I64, _P, _P, _P, _P, _I32, _I32,
                                                    _I32, _I32, _I32, _P, _P]
-        lib.orc_map_to_kernel_blocks.argtypes = [_P, _P, _I32, _I32, _I32, _I32, _P, _I32, _P]
+        lib.orc_map_to_kernel_blocks.argtypes = [_P, _P, _I32, _I32, _I32, _I32, _P, _I32, _P,
+                                                 _P]
         lib.orc_map_ranges_to_kernel_blocks.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                                         _P, _P, _P, _P, _P]
         lib.orc_ranges_to_block_table.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P,
@@ -154,7 +155,8 @@ class Oracle:
 
     # -- manager -> kernel block expansion --------------------------------
     def map_to_kernel_blocks(self, ids, counts, block_size: int, kernel_block_size: int,
-                             out_stride: Optional[int] = None) -> Tuple[np.ndarray, int]:
+                             out_stride: Optional[int] = None, with_counts: bool = False):
+        """(table, flags), or (table, counts, flags) with with_counts."""
         a = _c(ids, np.int32)
         cnt = None if counts is None else _c(counts, np.int32)
         rows, in_stride = a.shape
@@ -162,11 +164,14 @@ class Oracle:
         if out_stride is None:
             out_stride = in_stride * max(k, 1)
         out = np.empty((rows, out_stride), dtype=np.int32)
+        counts_out = np.empty(rows, dtype=np.int32)
         flags = ctypes.c_uint32(0)
         rc = self.lib.orc_map_to_kernel_blocks(_ptr(a), _ptr(cnt), rows, in_stride, block_size,
                                                kernel_block_size, _ptr(out), out_stride,
-                                               ctypes.byref(flags))
+                                               _ptr(counts_out), ctypes.byref(flags))
         self._check(rc, "map_to_kernel_blocks")
+        if with_counts:
+            return out, counts_out, flags.value
         return out, flags.value
 
     def map_ranges_to_kernel_blocks(self, range_start, range_len, range_cum, num_ranges,

@@ -336,11 +336,13 @@ static int expandable(int64_t id, int64_t k)
  * k consecutive kernel blocks, k = block_size / kernel_block_size, in order:
  *   out[r][i*k + j] = in[r][i]*k + j,   0 <= j < k, i < count[r].
  * Entries of the output row past count[r]*k are block 0 (the null block).
- * counts may be NULL (every row full).
+ * counts may be NULL (every row full).  counts_out (may be NULL) receives
+ * each row's kernel-block count, count[r]*k.
  */
 int orc_map_to_kernel_blocks(const int32_t *ids, const int32_t *counts, int32_t rows,
                              int32_t in_stride, int32_t block_size, int32_t kernel_block_size,
-                             int32_t *out, int32_t out_stride, uint32_t *flags_out)
+                             int32_t *out, int32_t out_stride, int32_t *counts_out,
+                             uint32_t *flags_out)
 {
     uint32_t flags = 0;
     int64_t k = blocks_per_kv_block(block_size, kernel_block_size);
@@ -351,6 +353,7 @@ int orc_map_to_kernel_blocks(const int32_t *ids, const int32_t *counts, int32_t 
         int64_t count = in_stride;
         if (counts) count = clamp64(counts[r], 0, in_stride, &flags, ORC_FLAG_COUNT);
         for (int64_t c = 0; c < out_stride; ++c) out[(int64_t)r * out_stride + c] = 0;
+        if (counts_out) counts_out[r] = (int32_t)(count * k);
         for (int64_t i = 0; i < count; ++i) {
             int64_t id = ids[(int64_t)r * in_stride + i];
             for (int64_t j = 0; j < k; ++j) {

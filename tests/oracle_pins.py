@@ -284,8 +284,9 @@ def pin_expansion(orc):
         qsl, pos, m = _batch(sched, pad_to=sum(lengths) + 5)
         expect = [b * bs_m + i for plc in places for (b, i) in plc]
         t, nb = _table(rows, max(map(len, rows)) + 2)
-        kt, f = orc.map_to_kernel_blocks(t, nb, bs_m, bs_k)
+        kt, kc, f = orc.map_to_kernel_blocks(t, nb, bs_m, bs_k, with_counts=True)
         assert f == 0 and kt.shape[1] == t.shape[1] * k
+        assert kc.tolist() == [len(row) * k for row in rows]
         # row r, manager block i covers kernel blocks i*k .. i*k+k-1 of the same memory
         for r, row in enumerate(rows):
             for i, b in enumerate(row):

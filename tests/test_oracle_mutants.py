@@ -55,6 +55,8 @@ MUTANTS = {
                              "int64_t logical = p / block_size;\n            int64_t o = p % span;\n            int64_t offset = (o / (I * W)) * I + o % I;\n            if (logical >= bound)"),
     "cp_ranges_offset_global": ("int64_t offset = (o / (I * W)) * I + o % I;\n            for (int64_t i = 0; i < n; ++i) {",
                                 "int64_t offset = o;\n            for (int64_t i = 0; i < n; ++i) {"),
+    "expansion_counts_unscaled": ("if (counts_out) counts_out[r] = (int32_t)(count * k);",
+                                  "if (counts_out) counts_out[r] = (int32_t)count;"),
     "coord_swaps_B_T": ("return (layer * num_blocks + block) * block_size + token;",
                         "return (layer * block_size + block) * num_blocks + token;"),
     "kv_drops_layer_term": ("int64_t src = layer * kv_layer_stride + t * kv_token_stride;",
