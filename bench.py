@@ -8,16 +8,18 @@ manager block on its own).  A step is the whole hot path for one batch:
 manager->kernel expansion of the variant's mapping structure, then the fused
 slot-map + K/V write (kvw_kv_write keeping the slot mapping, automatic
 kernel schedule) on the manager-unit mapping: slot ids are the same at
-either block size, so the write does not wait on the expanded table.  Both
-variants hand the attention side the same kernel-unit block table:
+either block size.  Both variants hand the attention side the same
+kernel-unit block table, written by extra workgroups of the slot-mapping
+launch (kvw_kv_write's table_out), so a step is two launches:
 
-  paged_r{R}     expand the manager block table, fused paged write
-  ranges_r{R}    fill the block table straight from the range descriptors,
+  paged_r{R}     manager block table expanded, fused paged write
+  ranges_r{R}    block table filled straight from the range descriptors,
                  fused range write
 
-The table-producing kernel of each variant is also timed alone, next to a
-plain device copy of the finished table (the per-step copy of a staged
-table that the fill replaces).  On the headline layout, the fused write is
+"fused call" times the write without the table.  The table-producing kernel
+of each variant is also timed alone (as its own call), next to a plain
+device copy of the finished table (the per-step copy of a staged table that
+the fill replaces).  On the headline layout, the fused write is
 also timed per context-parallel rank (two ranks, interleave 1 and 16): each
 rank writes its share of the batch into its own cache.  And per
 tensor-parallel rank (TP = 2, 4, 8 over the 8 KV heads): rows of 2048/TP
@@ -178,11 +180,13 @@ def main():
         if kind == "paged":
             bt, nb = d(w.block_table), d(w.num_blocks_per_req)
             kt = torch.empty((w.max_num_reqs, w.table_stride * k), dtype=torch.int32, device=dev)
-            expand_bytes = w.block_table.nbytes + w.num_blocks_per_req.nbytes + kt.numel() * 4
+            kn = torch.empty_like(nb)
+            expand_bytes = (w.block_table.nbytes + w.num_blocks_per_req.nbytes + kt.numel() * 4
+                            + kn.numel() * 4)
             mapping = dict(block_table=bt, num_blocks_per_req=nb)
 
             def expand(bt=bt, nb=nb, kt=kt, w=w):
-                kvw.kvw_map_to_kernel_blocks(bt, nb, w.block_size, bs_k, kt)
+                kvw.kvw_map_to_kernel_blocks(bt, nb, w.block_size, bs_k, kt)  # no counts here
             mode = kvw.KVW_SLOTS_PAGED
         else:
             rs, rl, rc, nr = (d(a) for a in (w.range_start, w.range_len, w.range_cum, w.num_ranges))
@@ -197,14 +201,23 @@ def main():
                 kvw.kvw_ranges_to_block_table(rs, rl, rc, nr, w.block_size, bs_k, kt, kn)
             mode = kvw.KVW_SLOTS_RANGES
 
-        def write(schedule, mode=mode, mapping=mapping, qsl=qsl, pos=pos, w=w):
+        def write(schedule, table=False, mode=mode, mapping=mapping, qsl=qsl, pos=pos, w=w,
+                  kt=kt, kn=kn):
+            extra = dict(table_out=kt, table_counts_out=kn, table_block_size=bs_k) if table else {}
             kvw.kvw_kv_write(mode=mode, key=key, value=value, k_cache=cache[0], v_cache=cache[1],
                              num_blocks=w.num_blocks, block_size=w.block_size,
                              query_start_loc=qsl, num_reqs=w.num_reqs, positions=pos,
-                             slot_mapping_out=sm_out, schedule=schedule, **mapping)
+                             slot_mapping_out=sm_out, schedule=schedule, **mapping, **extra)
 
-        def step(ev, expand=expand, write=write):
-            expand()
+        def step(ev, write=write):
+            # the whole step: slots + attention-side table in one launch, then the scatter
+            if ev is not None:
+                ev[0].record(stream)
+            write(kvw.KVW_SCHEDULE_AUTO, table=True)
+            if ev is not None:
+                ev[1].record(stream)
+
+        def fused_call(ev, write=write):
             if ev is not None:
                 ev[0].record(stream)
             write(kvw.KVW_SCHEDULE_AUTO)
@@ -234,7 +247,8 @@ def main():
                 ev[1].record(stream)
 
         table_dst = torch.empty_like(kt)
-        ms_step, call_ms = timed(step, args.warmup, args.steps)
+        ms_step, step_ev_ms = timed(step, args.warmup, args.steps)
+        _, call_ms = timed(fused_call, args.warmup, args.steps)
         _, single_ms = timed(single, args.warmup, args.steps)
         _, table_ms = timed(table_only, args.warmup, args.steps)
         _, copy_ms = timed(table_copy, args.warmup, args.steps)
@@ -246,6 +260,7 @@ def main():
         results[name] = {
             "tokens_per_s": real_tokens / (ms_step * 1e-3),
             "ms_per_step": ms_step,
+            "step_event_ms_avg": statistics.fmean(step_ev_ms),
             "step_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
             "fused_call_ms_avg": call_avg,
             "fused_call_ms_p10": float(np.percentile(call_ms, 10)),
@@ -287,7 +302,7 @@ def main():
             scatter = statistics.fmean(sc_ms)
             log(f"[bench] kv_scatter_kernel alone ({name} slots): {scatter * 1e3:.1f} us = "
                 f"{scatter_bytes / (scatter * 1e-3) / 1e9:.0f} GB/s")
-        del step, single, write, expand, table_only, table_copy, table_dst
+        del step, fused_call, single, write, expand, table_only, table_copy, table_dst
 
     # Context parallelism on the headline layout: the manager's 32-token blocks are the virtual
     # blocks of two ranks holding 16-slot blocks each; every rank writes its share of the batch
@@ -402,7 +417,7 @@ def main():
             "unit": "GB/s",
             "frac": round(scatter_bytes / (scatter * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "kernel": "kv_scatter_kernel",
+            "kernel": "kv_scatter_kernel<1>",
             "launch_ms_avg": round(scatter, 5),
             "algorithmic_bytes_per_launch": scatter_bytes,
         }

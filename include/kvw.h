@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define KVW_ABI_VERSION 2
+#define KVW_ABI_VERSION 3
 #define KVW_PAD_ID (-1)
 /* Largest accepted range_stride (range descriptors per request). */
 #define KVW_MAX_RANGE_STRIDE 65536
@@ -277,6 +277,18 @@ typedef struct kvw_kv_write_args {
     int32_t cp_world_size;             /* PAGED/RANGES: context parallelism (0 = none); the */
     int32_t cp_rank;                   /* cache holds this rank's blocks of block_size slots */
     int32_t cp_interleave_size;
+    /* PAGED/RANGES, optional: the attention side's block table for the same
+     * step, at table_block_size (which divides block_size; k = block_size /
+     * table_block_size).  PAGED: block_table expanded as kvw_map_to_kernel_blocks
+     * does; RANGES: filled from the runs as kvw_ranges_to_block_table does.
+     * Rows: num_reqs.  table_counts_out (or NULL) receives each row's kernel-block
+     * count.  With the two-kernel schedule the table is written by the same
+     * launch as the slot mapping (one launch fewer than a separate call); with
+     * one kernel, by a launch before it; with max_num_tokens == 0, alone. */
+    int32_t *table_out;                /* int32[num_reqs][table_out_stride] or NULL */
+    int32_t *table_counts_out;         /* int32[num_reqs] or NULL */
+    int32_t table_out_stride;          /* > 0; PAGED: >= block_table_stride * k */
+    int32_t table_block_size;
 } kvw_kv_write_args;
 
 /* sizeof(kvw_kv_write_args) as compiled into the library. */

@@ -116,6 +116,15 @@ struct MapArgs {
     int32_t cp_world;       // context-parallel ranks (<= 1: none)
     int32_t cp_rank;
     int32_t cp_interleave;  // positions per dealt chunk; divides block_size
+    // Optional attention-side block table, written by extra workgroups of the
+    // slot-mapping launch (blockIdx.x >= slot_blocks): the block table expanded
+    // (paged) or filled from the runs (ranges) at table_k kernel blocks per block.
+    int32_t *table_out;
+    int32_t *table_counts_out;
+    int32_t table_out_stride;
+    int32_t table_k;
+    uint32_t slot_blocks;           // workgroups of the slot-mapping role
+    uint32_t table_blocks_per_row;  // ranges: workgroups per table row
 };
 
 // Everything the K/V copy touches.
@@ -365,11 +374,109 @@ __device__ __forceinline__ int64_t range_block_at(const MapArgs &a, int32_t r, i
     return b;
 }
 
+__device__ __forceinline__ bool expandable(int64_t id, int64_t k)
+{
+    return id >= 0 && id * k + (k - 1) <= INT32_MAX;
+}
+
+// Entry q of row r of a kernel-unit table expanded from a manager table
+// ([P2] "Entwurfsmotivation"; [P3] section 7): ids[r][i]*k + j for q = i*k + j
+// while i < count[r], else 0 (the null block).  With counts_out, entry 0 of a
+// row also writes the row's kernel-block count, count[r] * k.
+__device__ __forceinline__ void expand_entry(const int32_t *ids, const int32_t *counts,
+                                             int32_t in_stride, int32_t k, int32_t *out,
+                                             int32_t out_stride, int32_t *counts_out, int32_t r,
+                                             int32_t q, uint32_t &flags)
+{
+    const int32_t i = q / k, j = q - (q / k) * k;
+    const int64_t count = counts ? clamp_count(counts[r], in_stride, flags) : in_stride;
+    int32_t v = 0;
+    if (i < count) {
+        const int64_t id = ids[static_cast<int64_t>(r) * in_stride + i];
+        if (expandable(id, k)) v = static_cast<int32_t>(id * k + j);
+        else flags |= KVW_FLAG_BAD_BLOCK;
+    }
+    out[static_cast<int64_t>(r) * out_stride + q] = v;
+    if (counts_out && q == 0) counts_out[r] = static_cast<int32_t>(count * k);
+}
+
+// Entry q (one per lane; r uniform over the wave, every lane calls) of row r
+// of a block table filled from range descriptors ([P1] "Status"): kernel
+// block j = q % k of the manager block at logical index q / k, i.e. of
+// start[i] + (q / k - cum[i]) for the run i holding it; 0 past the runs.  The
+// consecutive logical blocks of a wave (at most 64, each run at least one
+// block long) fall in at most 64 consecutive runs, found with one wavefront
+// search of the row's cum column.  Entry 0 writes the count,
+// (cum[n-1] + len[n-1]) * k clamped to the row width, which under the
+// descriptor precondition is the total length of the runs.
+__device__ __forceinline__ void fill_table_row(const int32_t *start, const int32_t *len,
+                                               const int32_t *cum, const int32_t *num_ranges,
+                                               int32_t range_stride, int32_t k, int32_t *out,
+                                               int32_t out_stride, int32_t *counts_out, int32_t r,
+                                               int64_t q, uint32_t &flags)
+{
+    const bool in = q < out_stride;
+    const uint32_t uq = static_cast<uint32_t>(in ? q : 0);
+    const uint32_t lb32 = uq / static_cast<uint32_t>(k);
+    const int64_t lb = lb32;
+    const int32_t j = static_cast<int32_t>(uq - lb32 * static_cast<uint32_t>(k));
+    uint32_t count_flags = 0;
+    const int64_t row = static_cast<int64_t>(r) * range_stride;
+    const int32_t n = static_cast<int32_t>(clamp_count(num_ranges[r], range_stride, count_flags));
+    const int32_t i = wave_upper_index(cum + row, n, lb, in);
+    int32_t v = 0;
+    if (in && i >= 0) {
+        const int64_t c = cum[row + i];
+        if (lb >= c && lb < c + len[row + i]) {
+            const int64_t b = static_cast<int64_t>(start[row + i]) + (lb - c);
+            if (expandable(b, k)) v = static_cast<int32_t>(b * k + j);
+            else flags |= KVW_FLAG_BAD_BLOCK;
+        }
+    }
+    if (in) out[static_cast<int64_t>(r) * out_stride + q] = v;
+    if (q == 0) {
+        int64_t total = 0;
+        if (n > 0) total = (static_cast<int64_t>(cum[row + n - 1]) + len[row + n - 1]) * k;
+        if (total < 0) total = 0;
+        if (total > out_stride) count_flags |= KVW_FLAG_COUNT;
+        if (counts_out) counts_out[r] = static_cast<int32_t>(total < out_stride ? total : out_stride);
+        flags |= count_flags;
+    }
+}
+
+// The table role of a slot-mapping launch: workgroup tb of the workgroups
+// past the slot-mapping ones.
+template <int MODE>
+__device__ __forceinline__ void table_role(const MapArgs &a, uint32_t tb)
+{
+    uint32_t flags = 0;
+    if (MODE == kPaged) {
+        const int64_t idx = static_cast<int64_t>(tb) * kBlockThreads + threadIdx.x;
+        if (idx < static_cast<int64_t>(a.num_reqs) * a.table_out_stride) {
+            const int32_t r = static_cast<int32_t>(idx / a.table_out_stride);
+            const int32_t q = static_cast<int32_t>(idx - static_cast<int64_t>(r) * a.table_out_stride);
+            expand_entry(a.block_table, a.num_blocks_per_req, a.table_stride, a.table_k, a.table_out,
+                         a.table_out_stride, a.table_counts_out, r, q, flags);
+        }
+    } else {
+        const int32_t r = static_cast<int32_t>(tb / a.table_blocks_per_row);
+        const int64_t q = static_cast<int64_t>(tb - static_cast<uint32_t>(r) * a.table_blocks_per_row) *
+                              kBlockThreads + threadIdx.x;
+        fill_table_row(a.range_start, a.range_len, a.range_cum, a.num_ranges, a.range_stride,
+                       a.table_k, a.table_out, a.table_out_stride, a.table_counts_out, r, q, flags);
+    }
+    raise_flags(a.err_flag, flags);
+}
+
 // One token per lane; the wave finds its tokens' requests (and, for ranges,
 // the runs of the tokens of its first request) with wavefront searches.
 template <int MODE>
 __global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
 {
+    if (blockIdx.x >= a.slot_blocks) {  // uniform over the workgroup; no barriers below
+        table_role<MODE>(a, blockIdx.x - a.slot_blocks);
+        return;
+    }
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x;
     const bool in = t < a.max_num_tokens;  // every lane stays for the wave-wide searches
     uint32_t nt_flag = 0, flags = 0;
@@ -566,30 +673,17 @@ __global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a
     }
 }
 
-__device__ __forceinline__ bool expandable(int64_t id, int64_t k)
-{
-    return id >= 0 && id * k + (k - 1) <= INT32_MAX;
-}
-
 // out[r][q] for q = i*k + j: ids[r][i]*k + j while i < count[r], else 0.
 __global__ __launch_bounds__(kBlockThreads) void expand_blocks_kernel(
     const int32_t *ids, const int32_t *counts, int32_t rows, int32_t in_stride, int32_t k,
-    int32_t *out, int32_t out_stride, int32_t *err_flag)
+    int32_t *out, int32_t out_stride, int32_t *counts_out, int32_t *err_flag)
 {
     const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x;
     if (idx >= static_cast<int64_t>(rows) * out_stride) return;
     const int32_t r = static_cast<int32_t>(idx / out_stride);
     const int32_t q = static_cast<int32_t>(idx - static_cast<int64_t>(r) * out_stride);
-    const int32_t i = q / k, j = q - (q / k) * k;
     uint32_t flags = 0;
-    const int64_t count = counts ? clamp_count(counts[r], in_stride, flags) : in_stride;
-    int32_t v = 0;
-    if (i < count) {
-        const int64_t id = ids[static_cast<int64_t>(r) * in_stride + i];
-        if (expandable(id, k)) v = static_cast<int32_t>(id * k + j);
-        else flags |= KVW_FLAG_BAD_BLOCK;
-    }
-    out[idx] = v;
+    expand_entry(ids, counts, in_stride, k, out, out_stride, counts_out, r, q, flags);
     raise_flags(err_flag, flags);
 }
 
@@ -627,49 +721,18 @@ __global__ __launch_bounds__(kBlockThreads) void expand_ranges_kernel(
     raise_flags(err_flag, flags);
 }
 
-// Block table filled from range descriptors: entry q of row r is kernel block
-// j = q % k of the manager block at logical index q / k, i.e. of
-// start[i] + (q / k - cum[i]) for the run i holding it; 0 past the runs.
-// One entry per lane; the blocks of a workgroup lie in one row (blockIdx.y),
-// so the consecutive logical blocks of a wave (at most 64, each run at least
-// one block long) fall in at most 64 consecutive runs, found with one
-// wavefront search of the row's cum column.  Lane 0 of each row writes the
-// count, (cum[n-1] + len[n-1]) * k clamped to the row width, which under the
-// descriptor precondition is the total length of the runs.
+// Block table filled from range descriptors (see fill_table_row); the
+// workgroups of a launch column share one row, looped over blockIdx.y.
 __global__ __launch_bounds__(kBlockThreads) void fill_table_kernel(
     const int32_t *start, const int32_t *len, const int32_t *cum, const int32_t *num_ranges,
     int32_t rows, int32_t range_stride, int32_t k, int32_t *out, int32_t out_stride,
     int32_t *counts_out, int32_t *err_flag)
 {
     const int64_t q = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x;
-    const bool in = q < out_stride;
-    const uint32_t uq = static_cast<uint32_t>(in ? q : 0);
-    const uint32_t lb32 = uq / static_cast<uint32_t>(k);
-    const int64_t lb = lb32;
-    const int32_t j = static_cast<int32_t>(uq - lb32 * static_cast<uint32_t>(k));
     for (int32_t r = blockIdx.y; r < rows; r += gridDim.y) {  // uniform over the workgroup
-        uint32_t flags = 0, count_flags = 0;
-        const int64_t row = static_cast<int64_t>(r) * range_stride;
-        const int32_t n = static_cast<int32_t>(clamp_count(num_ranges[r], range_stride, count_flags));
-        const int32_t i = wave_upper_index(cum + row, n, lb, in);
-        int32_t v = 0;
-        if (in && i >= 0) {
-            const int64_t c = cum[row + i];
-            if (lb >= c && lb < c + len[row + i]) {
-                const int64_t b = static_cast<int64_t>(start[row + i]) + (lb - c);
-                if (expandable(b, k)) v = static_cast<int32_t>(b * k + j);
-                else flags |= KVW_FLAG_BAD_BLOCK;
-            }
-        }
-        if (in) out[static_cast<int64_t>(r) * out_stride + q] = v;
-        if (q == 0) {
-            int64_t total = 0;
-            if (n > 0) total = (static_cast<int64_t>(cum[row + n - 1]) + len[row + n - 1]) * k;
-            if (total < 0) total = 0;
-            if (total > out_stride) count_flags |= KVW_FLAG_COUNT;
-            if (counts_out) counts_out[r] = static_cast<int32_t>(total < out_stride ? total : out_stride);
-            flags |= count_flags;
-        }
+        uint32_t flags = 0;
+        fill_table_row(start, len, cum, num_ranges, range_stride, k, out, out_stride, counts_out,
+                       r, q, flags);
         raise_flags(err_flag, flags);
     }
 }
@@ -772,11 +835,43 @@ MapArgs make_map_args(const int32_t *qsl, int32_t num_reqs, const int64_t *posit
     return a;
 }
 
-void launch_slot_mapping(int mode, const MapArgs &a, hipStream_t s)
+// Workgroups that write the optional attention-side table next to the slots.
+unsigned table_blocks(int mode, const MapArgs &a, uint32_t *per_row)
 {
-    const dim3 grid(grid_for(a.max_num_tokens, kBlockThreads));
+    *per_row = 0;
+    if (!a.table_out || a.num_reqs == 0) return 0;
+    if (mode == kPaged) return grid_for(static_cast<int64_t>(a.num_reqs) * a.table_out_stride, kBlockThreads);
+    *per_row = a.table_out_stride > 0 ? grid_for(a.table_out_stride, kBlockThreads) : 1u;
+    return *per_row * static_cast<unsigned>(a.num_reqs);
+}
+
+void launch_slot_mapping(int mode, const MapArgs &args, hipStream_t s)
+{
+    MapArgs a = args;
+    a.slot_blocks = grid_for(a.max_num_tokens, kBlockThreads);
+    const dim3 grid(a.slot_blocks + table_blocks(mode, a, &a.table_blocks_per_row));
     if (mode == kPaged) hipLaunchKernelGGL(slot_mapping_kernel<kPaged>, grid, dim3(kBlockThreads), 0, s, a);
     else hipLaunchKernelGGL(slot_mapping_kernel<kRanges>, grid, dim3(kBlockThreads), 0, s, a);
+}
+
+// The attention-side table on its own (the one-kernel schedule has no
+// slot-mapping launch to ride on).
+void launch_table(int mode, const MapArgs &a, hipStream_t s)
+{
+    uint32_t per_row;
+    const unsigned blocks = table_blocks(mode, a, &per_row);
+    if (!blocks) return;
+    if (mode == kPaged) {
+        hipLaunchKernelGGL(expand_blocks_kernel, dim3(blocks), dim3(kBlockThreads), 0, s, a.block_table,
+                           a.num_blocks_per_req, a.num_reqs, a.table_stride, a.table_k, a.table_out,
+                           a.table_out_stride, a.table_counts_out, a.err_flag);
+    } else {
+        const unsigned rows = static_cast<unsigned>(a.num_reqs) < kMaxGridY ? a.num_reqs : kMaxGridY;
+        hipLaunchKernelGGL(fill_table_kernel, dim3(per_row, rows), dim3(kBlockThreads), 0, s,
+                           a.range_start, a.range_len, a.range_cum, a.num_ranges, a.num_reqs,
+                           a.range_stride, a.table_k, a.table_out, a.table_out_stride,
+                           a.table_counts_out, a.err_flag);
+    }
 }
 
 template <int MODE>
@@ -885,7 +980,7 @@ kvw_status kvw_map_to_kernel_blocks(const int32_t *ids, const int32_t *counts, i
     KVW_REQUIRE(!counts || aligned(counts, 4), "%s: counts misaligned", fn);
     hipLaunchKernelGGL(expand_blocks_kernel, dim3(grid_for(total, kBlockThreads)), dim3(kBlockThreads),
                        0, reinterpret_cast<hipStream_t>(stream), ids, counts, rows, in_stride,
-                       static_cast<int32_t>(k), out, out_stride, err_flag);
+                       static_cast<int32_t>(k), out, out_stride, nullptr, err_flag);
     return launched(fn);
 }
 
@@ -1006,8 +1101,44 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
                     "%s: unknown schedule %d", fn, g.schedule);
         KVW_REQUIRE(g.schedule != KVW_SCHEDULE_TWO_KERNELS || g.slot_mapping_out,
                     "%s: the two-kernel schedule needs slot_mapping_out", fn);
+        if (g.table_out) {
+            KVW_REQUIRE(aligned(g.table_out, 4) && (!g.table_counts_out || aligned(g.table_counts_out, 4)),
+                        "%s: table_out or table_counts_out misaligned", fn);
+            KVW_REQUIRE(g.table_block_size > 0 && g.block_size % g.table_block_size == 0,
+                        "%s: table_block_size %d does not divide block_size %d", fn,
+                        g.table_block_size, g.block_size);
+            KVW_REQUIRE(g.table_out_stride > 0, "%s: table_out_stride must be positive", fn);
+            KVW_REQUIRE(g.mode != KVW_SLOTS_PAGED ||
+                            g.table_out_stride >= static_cast<int64_t>(g.block_table_stride) *
+                                                      (g.block_size / g.table_block_size),
+                        "%s: table_out_stride below block_table_stride * k", fn);
+            KVW_REQUIRE(static_cast<int64_t>(g.num_reqs) * g.table_out_stride <= INT32_MAX,
+                        "%s: num_reqs * table_out_stride too large", fn);
+        }
+    } else {
+        KVW_REQUIRE(!g.table_out, "%s: table_out needs the paged or range mode", fn);
     }
-    if (g.max_num_tokens == 0) return KVW_OK;
+    if (g.max_num_tokens == 0) {  // no token rows; the attention-side table is still written
+        if (fused && g.table_out) {
+            MapArgs t = make_map_args(g.query_start_loc, g.num_reqs, g.positions, 0, g.block_size, 0,
+                                      0, 0, g.err_flag);
+            t.block_table = g.block_table;
+            t.table_stride = g.block_table_stride;
+            t.num_blocks_per_req = g.num_blocks_per_req;
+            t.range_start = g.range_start;
+            t.range_len = g.range_len;
+            t.range_cum = g.range_cum;
+            t.num_ranges = g.num_ranges;
+            t.range_stride = g.range_stride;
+            t.table_out = g.table_out;
+            t.table_counts_out = g.table_counts_out;
+            t.table_out_stride = g.table_out_stride;
+            t.table_k = g.block_size / g.table_block_size;
+            launch_table(g.mode, t, reinterpret_cast<hipStream_t>(stream));
+            return launched(fn);
+        }
+        return KVW_OK;
+    }
     if (!fused)
         KVW_REQUIRE(g.slot_mapping_in && aligned(g.slot_mapping_in, 8),
                     "%s: slot_mapping_in is NULL or misaligned", fn);
@@ -1069,6 +1200,12 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
     a.num_ranges = g.num_ranges;
     a.range_stride = g.range_stride;
     a.slots_out = g.slot_mapping_out;
+    if (fused && g.table_out) {
+        a.table_out = g.table_out;
+        a.table_counts_out = g.table_counts_out;
+        a.table_out_stride = g.table_out_stride;
+        a.table_k = g.block_size / g.table_block_size;
+    }
 
     const bool two_pass =
         !fused || (g.slot_mapping_out != nullptr &&
@@ -1102,6 +1239,8 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
         return launched(fn);
     }
     // fused mode without a slot-mapping output: one kernel, one wave per token
+    // (after the attention-side table, if asked for, in a launch of its own)
+    launch_table(g.mode, a, s);
     if (g.num_layers > static_cast<int32_t>(kMaxGridY)) c.layers_per_wave = g.num_layers / kMaxGridY + 1;
     const unsigned groups =
         g.num_layers < 1 ? 1u : static_cast<unsigned>((g.num_layers + c.layers_per_wave - 1) / c.layers_per_wave);

@@ -15,7 +15,7 @@ import torch
 
 from .build import LIBRARY
 
-KVW_ABI_VERSION = 2
+KVW_ABI_VERSION = 3
 KVW_PAD_ID = -1
 KVW_MAX_RANGE_STRIDE = 65536
 KVW_OK, KVW_ERR_INVALID_ARG, KVW_ERR_UNSUPPORTED, KVW_ERR_RANGE_CAP, KVW_ERR_HIP = range(5)
@@ -47,6 +47,8 @@ class kvw_kv_write_args(ctypes.Structure):
         ("k_cache", _P), ("v_cache", _P), ("bytes_per_token", _I64),
         ("err_flag", _P), ("schedule", _I32),
         ("cp_world_size", _I32), ("cp_rank", _I32), ("cp_interleave_size", _I32),
+        ("table_out", _P), ("table_counts_out", _P), ("table_out_stride", _I32),
+        ("table_block_size", _I32),
     ]
 
 
@@ -191,14 +193,16 @@ def kvw_kv_write(*, mode, key, value, k_cache, v_cache, num_blocks, block_size,
                  query_start_loc=None, num_reqs=0, positions=None, block_table=None,
                  num_blocks_per_req=None, range_start=None, range_len=None, range_cum=None,
                  num_ranges=None, err_flag=None, schedule=KVW_SCHEDULE_AUTO, stream=None,
-                 cp_world_size=1, cp_rank=0, cp_interleave_size=1):
+                 cp_world_size=1, cp_rank=0, cp_interleave_size=1, table_out=None,
+                 table_counts_out=None, table_block_size=None):
     """K/V scatter into the paged cache, optionally fused with the slot mapping.
 
     key, value: [num_layers, max_num_tokens, H, D] (or [max_num_tokens, H, D]) tensors of a
     2-byte dtype; their row stride gives bytes_per_token.  k_cache, v_cache: any contiguous
     tensors holding num_layers * num_blocks * block_size such rows.  With cp_world_size > 1
     the caches are this context-parallel rank's (block_size slots per block) and only its
-    positions are written.
+    positions are written.  table_out (optional, [num_reqs, stride] int32) receives the
+    attention side's block table at table_block_size, made in the same launch as the slots.
     """
     for name, t in (("key", key), ("value", value)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
@@ -237,6 +241,11 @@ def kvw_kv_write(*, mode, key, value, k_cache, v_cache, num_blocks, block_size,
     a.schedule = int(schedule)
     a.cp_world_size, a.cp_rank = int(cp_world_size), int(cp_rank)
     a.cp_interleave_size = int(cp_interleave_size)
+    if table_out is not None:
+        a.table_out = _dev(table_out, torch.int32, "table_out")
+        a.table_out_stride = _stride(table_out)
+        a.table_counts_out = _dev(table_counts_out, torch.int32, "table_counts_out", optional=True)
+        a.table_block_size = int(table_block_size if table_block_size is not None else block_size)
     if mode == KVW_SLOTS_PRECOMPUTED:
         a.slot_mapping_in = _dev(slot_mapping_in, torch.int64, "slot_mapping_in")
     else:

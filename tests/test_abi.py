@@ -167,6 +167,16 @@ def test_kv_write_validation(lib):
              None) == INVALID
     assert f(ctypes.byref(_args(cp_world_size=2, cp_rank=2)), None) == INVALID
     assert f(ctypes.byref(_args(cp_world_size=2, cp_interleave_size=5)), None) == INVALID
+    assert f(ctypes.byref(_args(table_out=P, table_out_stride=32, table_block_size=5)),
+             None) == INVALID                                   # does not divide block_size
+    assert f(ctypes.byref(_args(table_out=P, table_out_stride=31, table_block_size=8)),
+             None) == INVALID                                   # below block_table_stride * k
+    assert f(ctypes.byref(_args(table_out=P, table_out_stride=0, table_block_size=8)),
+             None) == INVALID
+    assert f(ctypes.byref(_args(table_out=P + 2, table_out_stride=32, table_block_size=8)),
+             None) == INVALID                                   # misaligned
+    assert f(ctypes.byref(_args(mode=kvw.KVW_SLOTS_PRECOMPUTED, table_out=P, table_out_stride=32,
+                                table_block_size=8)), None) == INVALID
     assert f(ctypes.byref(_args(max_num_tokens=0)), None) == OK
 
 

@@ -5,13 +5,15 @@ count, strides, layer count), so one captured graph serves every batch that
 fits those sizes; the tail of the slot mapping and the rows of dummy requests
 must come out as the pad id on every replay ("Blocktabelle" page,
 "Datenfluss": the tail is padded so graph replay sees stable values).
-Each replay is checked against the CPU oracle; caches are re-filled eagerly
-between replays (no fill inside the graph).
+The captured call also writes the attention side's block table at block
+size 8.  Each replay is checked against the CPU oracle; caches are re-filled
+eagerly between replays (no fill inside the graph).
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import paged_kv_cache_46_amd as kvw
 from parity import DEV, Caches, compare_caches, dev, host, new_flag, oracle_slots, say
 from workloads import custom
@@ -51,6 +53,9 @@ def test_graph_replay_matches_oracle(variant, keep_slots):
     value = torch.empty_like(key)
     caches = Caches(LAYERS, POOL, 16, w0.row_elems)
     sm = torch.full((M,), 31, dtype=torch.int64, device=DEV)
+    # the attention side's table at block size 8, written by the same launches
+    table = torch.full((MAX_REQS, STRIDE * 2), -5, dtype=torch.int32, device=DEV)
+    counts = torch.full((MAX_REQS,), -5, dtype=torch.int32, device=DEV)
     flag = new_flag()
     mode = kvw.KVW_SLOTS_PAGED if variant == "paged" else kvw.KVW_SLOTS_RANGES
     mapping = (dict(block_table=static["block_table"],
@@ -65,6 +70,8 @@ def test_graph_replay_matches_oracle(variant, keep_slots):
         value.copy_(dev(w.kv_plane(1)).view_as(value))
         caches.t.fill_(0x7FC0)
         sm.fill_(31)
+        table.fill_(-5)
+        counts.fill_(-5)
         flag.zero_()
 
     def call():
@@ -72,7 +79,8 @@ def test_graph_replay_matches_oracle(variant, keep_slots):
                          num_blocks=POOL, block_size=16, max_num_tokens=M,
                          query_start_loc=static["query_start_loc"], num_reqs=MAX_REQS,
                          positions=static["positions"],
-                         slot_mapping_out=sm if keep_slots else None, err_flag=flag, **mapping)
+                         slot_mapping_out=sm if keep_slots else None, err_flag=flag,
+                         table_out=table, table_counts_out=counts, table_block_size=8, **mapping)
 
     load(w0)
     side = torch.cuda.Stream()
@@ -97,4 +105,12 @@ def test_graph_replay_matches_oracle(variant, keep_slots):
             assert np.array_equal(host(sm), o_slots)
             assert (host(sm)[w.num_tokens:] == -1).all()
         c_flags = compare_caches(w, caches, o_slots, w.kv_plane(0), w.kv_plane(1), POOL, 16)
-        assert int(flag.item()) == o_flags | c_flags == 0
+        orc = oracle.get()
+        if variant == "paged":
+            o_t, o_c, t_flags = orc.map_to_kernel_blocks(w.block_table, w.num_blocks_per_req, 16, 8,
+                                                         with_counts=True)
+        else:
+            o_t, o_c, t_flags = orc.ranges_to_block_table(w.range_start, w.range_len, w.range_cum,
+                                                          w.num_ranges, 16, 8, STRIDE * 2)
+        assert np.array_equal(host(table), o_t) and np.array_equal(host(counts), o_c)
+        assert int(flag.item()) == o_flags | c_flags | t_flags == 0

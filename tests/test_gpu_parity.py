@@ -156,6 +156,108 @@ def test_long_context_slots_and_expansion(r):
 
 
 # ---------------------------------------------------------------------------
+# K/V write with the attention-side table made in the same launch
+# ---------------------------------------------------------------------------
+def check_kv_write_with_table(w, mode, k, pad=3):
+    """Fused write that also returns the kernel-unit block table: slots, caches, table, counts."""
+    say(f"[kv_write+table] {w.describe()} mode={mode} k={k}")
+    variant, _, sched = mode.partition("-")
+    orc = oracle.get()
+    d = DeviceInputs(w)
+    o_slots, o_flags = oracle_slots(w, variant)
+    kbs = w.block_size // k
+    width = w.table_stride * k + pad
+    if variant == "paged":
+        o_table, o_counts, t_flags = orc.map_to_kernel_blocks(
+            w.block_table, w.num_blocks_per_req, w.block_size, kbs, width, with_counts=True)
+    else:
+        o_table, o_counts, t_flags = orc.ranges_to_block_table(
+            w.range_start, w.range_len, w.range_cum, w.num_ranges, w.block_size, kbs, width)
+    key_h, value_h = w.kv_plane(0), w.kv_plane(1)
+    key = dev(key_h).view(w.num_layers, w.max_num_tokens, w.num_kv_heads, w.head_dim)
+    value = dev(value_h).view_as(key)
+    caches = Caches(w.num_layers, w.num_blocks, w.block_size, w.row_elems)
+    table = torch.full((w.num_reqs, width), -5, dtype=torch.int32, device=DEV)
+    counts = torch.full((w.num_reqs,), -5, dtype=torch.int32, device=DEV)
+    flag = new_flag()
+    sm = torch.full((w.max_num_tokens,), 777, dtype=torch.int64, device=DEV)
+    kw = dict(query_start_loc=d.qsl, num_reqs=w.num_reqs, positions=d.positions,
+              slot_mapping_out=None if sched == "noslots" else sm)
+    if variant == "paged":
+        kw.update(mode=kvw.KVW_SLOTS_PAGED, block_table=d.block_table, num_blocks_per_req=d.nbpr)
+    else:
+        kw.update(mode=kvw.KVW_SLOTS_RANGES, range_start=d.rs, range_len=d.rl, range_cum=d.rc,
+                  num_ranges=d.nr)
+    kvw.kvw_kv_write(key=key, value=value, k_cache=caches.k, v_cache=caches.v,
+                     num_blocks=w.num_blocks, block_size=w.block_size,
+                     max_num_tokens=w.max_num_tokens, err_flag=flag, schedule=SCHEDULES[sched],
+                     table_out=table, table_counts_out=counts, table_block_size=kbs, **kw)
+    torch.cuda.synchronize()
+    bad = np.argwhere(host(table) != o_table)
+    assert len(bad) == 0, f"{len(bad)} table entries differ, first {bad[:4].tolist()}"
+    assert np.array_equal(host(counts), o_counts)
+    if sched != "noslots":
+        assert np.array_equal(host(sm), o_slots)
+    c_flags = compare_caches(w, caches, o_slots, key_h, value_h, w.num_blocks, w.block_size)
+    assert int(flag.item()) == o_flags | t_flags | c_flags
+
+
+TABLE_MODES = ["paged", "ranges", "paged-two", "ranges-two", "paged-one", "ranges-one",
+               "paged-noslots", "ranges-noslots"]
+
+
+@pytest.mark.parametrize("mode", TABLE_MODES)
+@pytest.mark.parametrize("w", [w for w in SMALL if w.name in (
+    "tiny_prefill", "small_mixed_l3", "small_bs8", "small_bs64", "small_oversub", "small_dummy",
+    "small_out_of_range", "small_empty")], ids=lambda w: w.name)
+def test_kv_write_with_table(w, mode):
+    check_kv_write_with_table(w, mode, k=2 if w.block_size % 2 == 0 else 1)
+
+
+@pytest.mark.parametrize("mode", ["paged", "ranges", "paged-noslots"])
+@pytest.mark.parametrize("r", [1, 4096])
+def test_kv_write_with_table_long_context(r, mode):
+    """128K: the step's kernel-unit table (32 -> 16) written by the slot-mapping launch."""
+    check_kv_write_with_table(long_context(r), mode, k=2, pad=0)
+
+
+@pytest.mark.parametrize("mode", ["paged-two", "ranges-two", "paged-one", "ranges-one"])
+def test_kv_write_with_table_flagged(mode):
+    check_kv_write_with_table(_flagged_workload(), mode, k=2)
+
+
+def test_kv_write_table_without_token_rows():
+    """max_num_tokens == 0: nothing is copied, the table is still written."""
+    w = config("tiny_prefill")
+    d = DeviceInputs(w)
+    orc = oracle.get()
+    key = torch.zeros((1, 0, w.num_kv_heads, w.head_dim), dtype=torch.int16, device=DEV)
+    caches = Caches(1, 4, w.block_size, w.row_elems)
+    for variant in ("paged", "ranges"):
+        table = torch.full((w.num_reqs, w.table_stride * 2), -5, dtype=torch.int32, device=DEV)
+        counts = torch.full((w.num_reqs,), -5, dtype=torch.int32, device=DEV)
+        mapping = (dict(mode=kvw.KVW_SLOTS_PAGED, block_table=d.block_table,
+                        num_blocks_per_req=d.nbpr) if variant == "paged" else
+                   dict(mode=kvw.KVW_SLOTS_RANGES, range_start=d.rs, range_len=d.rl,
+                        range_cum=d.rc, num_ranges=d.nr))
+        kvw.kvw_kv_write(key=key, value=key, k_cache=caches.k, v_cache=caches.v, num_blocks=4,
+                         block_size=w.block_size, max_num_tokens=0, query_start_loc=d.qsl,
+                         num_reqs=w.num_reqs, positions=d.positions, table_out=table,
+                         table_counts_out=counts, table_block_size=w.block_size // 2, **mapping)
+        torch.cuda.synchronize()
+        if variant == "paged":
+            o_t, o_c, _ = orc.map_to_kernel_blocks(w.block_table, w.num_blocks_per_req,
+                                                   w.block_size, w.block_size // 2,
+                                                   with_counts=True)
+        else:
+            o_t, o_c, _ = orc.ranges_to_block_table(w.range_start, w.range_len, w.range_cum,
+                                                    w.num_ranges, w.block_size,
+                                                    w.block_size // 2, w.table_stride * 2)
+        assert np.array_equal(host(table), o_t) and np.array_equal(host(counts), o_c)
+    assert (host(caches.t) == 0x7FC0).all()
+
+
+# ---------------------------------------------------------------------------
 # K/V write
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("mode", WRITE_MODES)
