@@ -152,17 +152,23 @@ def main():
     scatter_bytes = real_tokens * base.num_layers * 4 * bpt + real_tokens * 8
 
     def timed(fn, n_warm, n_steps):
+        """Wall ms per call over n_steps bare calls (between two synchronizations), then the
+        per-call HIP-event times of a second, instrumented pass of n_steps calls (the event
+        records cost the stream a few microseconds, so they stay out of the wall time)."""
         for _ in range(n_warm):
             fn(None)
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_steps):
+            fn(None)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n_steps)]
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for i in range(n_steps):
             fn(evs[i])
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         return wall * 1e3 / n_steps, [a.elapsed_time(b) for a, b in evs]
 
     results = {}
