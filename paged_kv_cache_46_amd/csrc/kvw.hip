@@ -39,7 +39,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <cstdarg>
 #include <cstdint>
 #include <cstdio>
 
@@ -59,25 +58,6 @@
 #ifndef KVW_NT_STORES
 #define KVW_NT_STORES 1
 #endif
-
-namespace kvw_detail {
-
-namespace {
-thread_local char g_last_error[512] = "";
-}
-
-kvw_status fail(kvw_status st, const char *fmt, ...)
-{
-    va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
-    va_end(ap);
-    return st;
-}
-
-const char *last_error() { return g_last_error; }
-
-}  // namespace kvw_detail
 
 namespace {
 
@@ -892,8 +872,6 @@ void launch_fused(const MapArgs &a, const CopyArgs &c, unsigned groups, hipStrea
 extern "C" {
 
 int32_t kvw_abi_version(void) { return KVW_ABI_VERSION; }
-
-const char *kvw_last_error(void) { return kvw_detail::last_error(); }
 
 size_t kvw_kv_write_args_size(void) { return sizeof(kvw_kv_write_args); }
 
