@@ -64,6 +64,9 @@ class Oracle:
                                                         _P, _P, _P, _P, _P]
         lib.orc_ranges_to_block_table.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P,
                                                   _I32, _P, _P]
+        lib.orc_decode_attention.argtypes = [_P, _P, _P, _I64, _P, _P, _P, _I32, _I32, _I32,
+                                             _I32, ctypes.c_double, _P]
+        lib.orc_decode_attention.restype = ctypes.c_int
         lib.orc_coord_n.argtypes = [_I64] * 5
         lib.orc_coord_n.restype = _I64
         lib.orc_coord_offset.argtypes = [_I64] * 6
@@ -204,6 +207,29 @@ class Oracle:
                                                 out_stride, _ptr(counts), ctypes.byref(flags))
         self._check(rc, "ranges_to_block_table")
         return out, counts, flags.value
+
+    # -- decode attention over the paged cache -------------------------------
+    def decode_attention(self, q, k_cache, v_cache, slots_per_req, reqs, num_q_heads: int,
+                         num_kv_heads: int, scale: float) -> np.ndarray:
+        """out[i][h][d] (float64) for requests reqs[i]; slots_per_req[i] lists the slots of
+        positions 0, 1, ... of that request.  q: uint16 [R][Hq][D]; caches: uint16
+        [rows][Hkv][D] (bf16 bit patterns)."""
+        qq = _c(q, np.uint16)
+        kc = _c(k_cache, np.uint16)
+        vc = _c(v_cache, np.uint16)
+        head_dim = qq.shape[-1]
+        rows = kc.shape[0]
+        slots = np.ascontiguousarray(np.concatenate([np.asarray(s, np.int64) for s in
+                                                     slots_per_req] or [np.zeros(0, np.int64)]))
+        begin = np.zeros(len(slots_per_req) + 1, np.int64)
+        begin[1:] = np.cumsum([len(s) for s in slots_per_req])
+        rq = _c(reqs, np.int32)
+        out = np.zeros((len(rq), num_q_heads, head_dim), np.float64)
+        rc = self.lib.orc_decode_attention(_ptr(qq), _ptr(kc), _ptr(vc), rows, _ptr(slots),
+                                           _ptr(begin), _ptr(rq), len(rq), num_q_heads,
+                                           num_kv_heads, head_dim, float(scale), _ptr(out))
+        self._check(rc, "decode_attention")
+        return out
 
     # -- coordinate form ---------------------------------------------------
     def coord_n(self, layer, block, token, num_blocks, block_size) -> int:

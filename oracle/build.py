@@ -16,7 +16,7 @@ LIBRARY = os.path.join(HERE, "liboracle.so")
 def build_oracle(verbose: bool = False, extra_flags: tuple = (), output: str = LIBRARY,
                  source: str = SOURCE) -> str:
     cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-Werror", "-fPIC", "-shared",
-           *extra_flags, "-o", output + ".tmp", source]
+           *extra_flags, "-o", output + ".tmp", source, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -10,8 +10,9 @@
  *
  * Sources (pages as published; sections named, not quoted):
  *  [P1] "Range-addressed KV cache blocks for the vLLM serving engine",
- *       sections "The Innovation: Range Arithmetic Replaces the Per-Position
- *       Gather", "The Coordinate Approach", "Measured Results" and "Status".
+ *       sections "The block-table access pattern", "The Innovation: Range
+ *       Arithmetic Replaces the Per-Position Gather", "The Coordinate
+ *       Approach", "The Direction", "Measured Results" and "Status".
  *  [P2] "Blocktabelle: Abbildung von logischen Token auf physische KV-Blocks",
  *       sections "Verantwortung", "Entwurfsmotivation", "Datenfluss" and
  *       "Grenzen und Fehler".
@@ -33,6 +34,7 @@
  *  - a padded token writes nothing; a slot outside the cache is skipped and
  *    reported through a flag bit.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -471,6 +473,87 @@ int orc_ranges_to_block_table(const int32_t *start, const int32_t *len, const in
         if (counts_out) counts_out[r] = (int32_t)(full < out_stride ? full : out_stride);
     }
     if (flags_out) *flags_out |= flags;
+    return ORC_OK;
+}
+
+/* bf16 bit pattern -> double: the 16 bits are the high half of a float32, so
+ * the widening is exact. */
+static double bf16_value(uint16_t bits)
+{
+    uint32_t w = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+/* scale * (q . k) over one head's head_dim entries */
+static double attention_score(const uint16_t *qh, const uint16_t *kr, int32_t head_dim,
+                              double scale)
+{
+    double sc = 0.0;
+    for (int32_t d = 0; d < head_dim; ++d) sc += bf16_value(qh[d]) * bf16_value(kr[d]);
+    return sc * scale;
+}
+
+/*
+ * Decode attention over the paged cache: the read path, where the attention
+ * kernels resolve each position's block again ([P1] "The block-table access
+ * pattern", block-table lookup per position; "The Direction", M7: range
+ * arithmetic in the attention kernels).  The attention itself is the standard
+ * scaled dot product, which the pages do not restate: for selected request
+ * i (request id reqs[i]), its context slots slots[begin[i] .. begin[i+1]) (one
+ * per position 0, 1, ..., in order; a slot < 0 holds no token and is skipped),
+ * query head h and key/value head g = h / (num_q_heads / num_kv_heads):
+ *   s_j = scale * sum_d q[reqs[i]][h][d] * K[slot_j][g][d]
+ *   w_j = exp(s_j - max s) / sum_j' exp(s_j' - max s)
+ *   out[i][h][d] = sum_j w_j * V[slot_j][g][d]
+ * in double precision (bf16 inputs widened exactly); no token gives 0.
+ * Cache rows: [cache_rows][num_kv_heads][head_dim] bf16.
+ */
+int orc_decode_attention(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                         int64_t cache_rows, const int64_t *slots, const int64_t *begin,
+                         const int32_t *reqs, int32_t num_sel, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, double scale, double *out)
+{
+    if (num_sel < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        num_q_heads % num_kv_heads != 0 || cache_rows < 0)
+        return ORC_E_ARG;
+    int64_t group = num_q_heads / num_kv_heads;
+    for (int32_t i = 0; i < num_sel; ++i) {
+        for (int64_t j = begin[i]; j < begin[i + 1]; ++j)
+            if (slots[j] >= cache_rows) return ORC_E_ARG;
+        for (int32_t h = 0; h < num_q_heads; ++h) {
+            int64_t g = h / group;
+            const uint16_t *qh = q + ((int64_t)reqs[i] * num_q_heads + h) * head_dim;
+            double *o = out + ((int64_t)i * num_q_heads + h) * head_dim;
+            for (int32_t d = 0; d < head_dim; ++d) o[d] = 0.0;
+            /* scores and their maximum */
+            double smax = -1.0 / 0.0;
+            int64_t n = 0;
+            for (int64_t j = begin[i]; j < begin[i + 1]; ++j) {
+                if (slots[j] < 0) continue;
+                const uint16_t *kr = k_cache + (slots[j] * num_kv_heads + g) * head_dim;
+                double sc = attention_score(qh, kr, head_dim, scale);
+                if (sc > smax) smax = sc;
+                ++n;
+            }
+            if (n == 0) continue;
+            /* normalizer, then the weighted sum of value rows */
+            double denom = 0.0;
+            for (int64_t j = begin[i]; j < begin[i + 1]; ++j) {
+                if (slots[j] < 0) continue;
+                const uint16_t *kr = k_cache + (slots[j] * num_kv_heads + g) * head_dim;
+                denom += exp(attention_score(qh, kr, head_dim, scale) - smax);
+            }
+            for (int64_t j = begin[i]; j < begin[i + 1]; ++j) {
+                if (slots[j] < 0) continue;
+                const uint16_t *kr = k_cache + (slots[j] * num_kv_heads + g) * head_dim;
+                const uint16_t *vr = v_cache + (slots[j] * num_kv_heads + g) * head_dim;
+                double w = exp(attention_score(qh, kr, head_dim, scale) - smax) / denom;
+                for (int32_t d = 0; d < head_dim; ++d) o[d] += w * bf16_value(vr[d]);
+            }
+        }
+    }
     return ORC_OK;
 }
 

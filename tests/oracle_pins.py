@@ -10,6 +10,8 @@ when the oracle disagrees with:
     same slot for the same physical layout, and that a table filled from the
     runs is the runs laid end to end;
   * a dealing simulation (no division) of the context-parallel placement;
+  * closed forms of decode attention (one token, zero query, the two-token logistic
+    weights, a dominant score, constant value rows per head, linearity, placement);
   * numpy's own row-major indexing (ravel_multi_index, array addresses,
     fancy-index scatter) for the coordinate form and the K/V copy.
 The same functions are run against deliberately broken builds of the oracle
@@ -482,6 +484,82 @@ def pin_context_parallel(orc, workloads=()):
         raise AssertionError(f"context-parallel parameters {bad} not rejected")
 
 
+def _bf16(x):
+    """float -> bf16 bit pattern, rounding to nearest even (exact for the small integers and
+    halves used below)."""
+    b = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _bf16_value(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def pin_attention(orc):
+    """Decode attention: closed forms and invariants, none of them a restatement of the loops."""
+    rng = np.random.default_rng(41)
+    hq, hkv, d = 8, 2, 16
+    group = hq // hkv
+    rows = 40
+    q = _bf16(rng.standard_normal((3, hq, d)))
+    k = _bf16(rng.standard_normal((rows, hkv, d)))
+    v = _bf16(rng.standard_normal((rows, hkv, d)))
+    scale = 1.0 / np.sqrt(d)
+    vv = _bf16_value(v)
+    # one token: its value row, exactly, for every head
+    out = orc.decode_attention(q, k, v, [[7]], [1], hq, hkv, scale)
+    for h in range(hq):
+        assert np.array_equal(out[0, h], vv[7, h // group])
+    # no token: zeros
+    assert not orc.decode_attention(q, k, v, [[]], [1], hq, hkv, scale).any()
+    # zero query: uniform weights, the mean of the value rows
+    qz = np.zeros_like(q)
+    sl = [3, 9, 11, 20, 21, 33]
+    out = orc.decode_attention(qz, k, v, [sl], [0], hq, hkv, scale)
+    for h in range(hq):
+        assert np.allclose(out[0, h], vv[sl, h // group].mean(axis=0), rtol=0, atol=1e-13)
+    # two tokens with one-hot keys: weights are the logistic function of the score gap
+    q2 = np.zeros_like(q)
+    q2[:, :, 0] = _bf16(2.0)
+    k2 = np.zeros_like(k)
+    k2[5, :, 0] = _bf16(1.0)      # key of the second position: score 2 * scale, first: 0
+    out = orc.decode_attention(q2, k2, v, [[4, 5]], [2], hq, hkv, scale)
+    w1 = 1.0 / (1.0 + np.exp(-2.0 * scale))
+    for h in range(hq):
+        g = h // group
+        assert np.allclose(out[0, h], w1 * vv[5, g] + (1 - w1) * vv[4, g], rtol=0, atol=1e-13)
+    # one dominant score (exp(1000) overflows unless the maximum is subtracted first)
+    q3 = np.zeros_like(q)
+    q3[:, :, 0] = _bf16(1000.0)
+    out = orc.decode_attention(q3, k2, v, [[1, 2, 5, 8]], [0], hq, hkv, 1.0)
+    for h in range(hq):
+        assert np.allclose(out[0, h], vv[5, h // group], rtol=0, atol=1e-13)
+    # grouped heads: value rows constant per kv head give that head's constant
+    vc = np.zeros_like(v)
+    for g in range(hkv):
+        vc[:, g, :] = _bf16(float(g + 1))
+    out = orc.decode_attention(q, k, vc, [sl], [2], hq, hkv, scale)
+    for h in range(hq):
+        assert np.allclose(out[0, h], h // group + 1, rtol=0, atol=1e-13)
+    # doubling every value doubles the output (2 v is exact in bf16)
+    v2 = _bf16(2.0 * vv)
+    a = orc.decode_attention(q, k, v, [sl], [1], hq, hkv, scale)
+    b = orc.decode_attention(q, k, v2, [sl], [1], hq, hkv, scale)
+    assert np.allclose(b, 2 * a, rtol=0, atol=1e-12)
+    # physical placement does not matter: the same logical rows at other slots
+    perm = rng.permutation(rows)
+    kp, vp = np.empty_like(k), np.empty_like(v)
+    kp[perm], vp[perm] = k, v            # row j moves to slot perm[j]
+    a = orc.decode_attention(q, k, v, [sl, sl[::-1]], [0, 1], hq, hkv, scale)
+    b = orc.decode_attention(q, kp, vp, [list(perm[sl]), list(perm[sl[::-1]])], [0, 1], hq,
+                             hkv, scale)
+    assert np.array_equal(a, b)
+    # a slot of -1 holds no token
+    c = orc.decode_attention(q, k, v, [[3, -1, 9, 11, -1, 20, 21, 33]], [0], hq, hkv, scale)
+    e = orc.decode_attention(q, k, v, [sl], [0], hq, hkv, scale)
+    assert np.array_equal(c, e)
+
+
 def pin_coordinates(orc):
     """Coordinate form == numpy row-major indexing of [layers][blocks][tokens] rows."""
     cfg = {f[0]: int(f[1]) for f in _lines("coordinate_layout.txt")}
@@ -571,4 +649,5 @@ def all_pins(orc, small, full=()):
     pin_table_fill(orc, small)
     pin_context_parallel(orc, small)
     pin_coordinates(orc)
+    pin_attention(orc)
     pin_kv_write(orc, small)

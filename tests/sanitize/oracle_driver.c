@@ -27,6 +27,9 @@ int orc_ranges_to_block_table(const int32_t *, const int32_t *, const int32_t *,
                               int32_t, int32_t, int32_t, int32_t, int32_t *, int32_t, int32_t *,
                               uint32_t *);
 int64_t orc_coord_offset(int64_t, int64_t, int64_t, int64_t, int64_t, int64_t);
+int orc_decode_attention(const uint16_t *, const uint16_t *, const uint16_t *, int64_t,
+                         const int64_t *, const int64_t *, const int32_t *, int32_t, int32_t,
+                         int32_t, int32_t, double, double *);
 int orc_kv_write(const int64_t *, int64_t, int32_t, const uint8_t *, const uint8_t *, int64_t,
                  int64_t, int64_t, int32_t, int64_t, uint8_t *, uint8_t *, int64_t, int64_t,
                  uint32_t *);
@@ -84,6 +87,22 @@ int main(void)
         CALL(orc_kv_write(ws, m, 2, key, val, (int64_t)M * ROW, ROW, NB, BS, ROW, kc, vc, 0,
                      2 * NB * BS, &flags));
         (void)orc_coord_offset(below(4), below(NB), below(BS), NB, BS, 2048);
+        /* decode attention: 4 q heads over 2 kv heads of 8 dims; cache rows reinterpret kc */
+        {
+            static uint16_t qa[R * 4 * 8];
+            static double oa[R * 4 * 8];
+            int64_t aslots[M], begin[R + 1];
+            int32_t sel[R];
+            for (int i = 0; i < R * 4 * 8; ++i) qa[i] = (uint16_t)(0x3C00 + below(0x800));
+            begin[0] = 0;
+            for (int r = 0; r < R; ++r) {
+                sel[r] = r;
+                begin[r + 1] = begin[r] + below(M / R);
+                for (int64_t j = begin[r]; j < begin[r + 1]; ++j) aslots[j] = below(100) - 2;
+            }
+            CALL(orc_decode_attention(qa, (const uint16_t *)kc, (const uint16_t *)vc, 100, aslots,
+                                      begin, sel, R, 4, 2, 8, 0.35, oa));
+        }
     }
     if (ok * 10 < calls * 9) {  /* nearly every call must get past its argument checks */
         fprintf(stderr, "only %ld of %ld calls succeeded\n", ok, calls);

@@ -57,6 +57,14 @@ MUTANTS = {
                                 "int64_t offset = o;\n            for (int64_t i = 0; i < n; ++i) {"),
     "expansion_counts_unscaled": ("if (counts_out) counts_out[r] = (int32_t)(count * k);",
                                   "if (counts_out) counts_out[r] = (int32_t)count;"),
+    "attention_drops_scale": ("    return sc * scale;\n}", "    return sc;\n}"),
+    "attention_heads_interleaved": ("            int64_t g = h / group;", "            int64_t g = h % num_kv_heads;"),
+    "attention_no_max_shift": ("denom += exp(attention_score(qh, kr, head_dim, scale) - smax);",
+                               "denom += exp(attention_score(qh, kr, head_dim, scale));"),
+    "attention_unnormalized": ("double w = exp(attention_score(qh, kr, head_dim, scale) - smax) / denom;",
+                               "double w = exp(attention_score(qh, kr, head_dim, scale) - smax);"),
+    "attention_keys_as_values": ("for (int32_t d = 0; d < head_dim; ++d) o[d] += w * bf16_value(vr[d]);",
+                                 "for (int32_t d = 0; d < head_dim; ++d) o[d] += w * bf16_value(kr[d]);"),
     "coord_swaps_B_T": ("return (layer * num_blocks + block) * block_size + token;",
                         "return (layer * block_size + block) * num_blocks + token;"),
     "kv_drops_layer_term": ("int64_t src = layer * kv_layer_stride + t * kv_token_stride;",

@@ -96,6 +96,10 @@ def test_context_parallel(orc, small):
     P.pin_context_parallel(orc, small)
 
 
+def test_decode_attention(orc):
+    P.pin_attention(orc)
+
+
 def test_coordinate_form(orc):
     P.pin_coordinates(orc)
 

@@ -23,7 +23,7 @@ def build_and_run(tmp_path, compiler, std, sources, includes=()):
     if cc is None:
         pytest.skip(f"{compiler} not available")
     exe = str(tmp_path / "driver")
-    cmd = [cc, std, *SAN, *[f"-I{i}" for i in includes], *sources, "-o", exe]
+    cmd = [cc, std, *SAN, *[f"-I{i}" for i in includes], *sources, "-o", exe, "-lm"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0 and "asan" in r.stderr.lower():
         pytest.skip("sanitizer runtime not available")
