@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define KVW_ABI_VERSION 3
+#define KVW_ABI_VERSION 4
 #define KVW_PAD_ID (-1)
 /* Largest accepted range_stride (range descriptors per request). */
 #define KVW_MAX_RANGE_STRIDE 65536
@@ -323,6 +323,68 @@ size_t kvw_kv_write_args_size(void);
  * cache size beyond int64; KVW_ERR_RANGE_CAP as kvw_slot_mapping_ranges.
  */
 kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream);
+
+/*
+ * Decode attention over the paged cache: the read path, where each position's
+ * block is resolved again ([P1] "The block-table access pattern"; "The
+ * Direction", M7: range arithmetic in the attention kernels).  One query token
+ * per request; request r attends its positions 0 .. context_lens[r]-1, whose
+ * slots follow the slot-mapping definitions above (PAGED: block table; RANGES:
+ * range descriptors); a position without a block (pad id) is skipped.  For
+ * query head h and key/value head g = h / (num_q_heads / num_kv_heads):
+ *   out[r][h] = sum_j softmax_j(scale * q[r][h] . K[slot_j][g]) * V[slot_j][g]
+ * computed in fp32 from bf16 inputs; no position gives 0.  Each position's
+ * slot is resolved once per 256-position chunk and staged in LDS for all
+ * heads; chunks are combined in a second launch through `workspace`.
+ *   q                  bf16 [num_reqs][num_q_heads][head_dim], 16-byte aligned
+ *   context_lens       int32 [num_reqs] (device); clamped to [0, max_context]
+ *                      with KVW_FLAG_COUNT
+ *   max_context        host bound on the context lengths; sets the grid, so a
+ *                      graph captured once serves any lengths up to it
+ *   k_cache, v_cache   bf16 [num_blocks * block_size][num_kv_heads][head_dim]
+ *                      (one layer, the K/V write's layout), 16-byte aligned
+ *   out                fp32 [num_reqs][num_q_heads][head_dim]
+ *   workspace          device memory of kvw_decode_workspace_size(...) bytes
+ * Supported: head_dim 128; num_kv_heads 1..16; num_q_heads <= 32;
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}; else KVW_ERR_UNSUPPORTED.  Flags: KVW_FLAG_COUNT,
+ * KVW_FLAG_BAD_BLOCK, KVW_FLAG_SLOT_OOB (slot past the cache: skipped).
+ */
+typedef struct kvw_decode_args {
+    int32_t mode;                      /* KVW_SLOTS_PAGED or KVW_SLOTS_RANGES */
+    int32_t num_reqs;
+    const void *q;
+    const int32_t *context_lens;
+    int32_t max_context;
+    int32_t block_size;
+    const int32_t *block_table;        /* PAGED: as kvw_slot_mapping_paged */
+    const int32_t *num_blocks_per_req; /* PAGED: or NULL */
+    int32_t block_table_stride;
+    int32_t range_stride;              /* RANGES: as kvw_slot_mapping_ranges */
+    const int32_t *range_start;
+    const int32_t *range_len;
+    const int32_t *range_cum;
+    const int32_t *num_ranges;
+    const void *k_cache;
+    const void *v_cache;
+    int64_t num_blocks;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    float scale;                       /* e.g. 1 / sqrt(head_dim) */
+    float *out;
+    void *workspace;
+    int64_t workspace_bytes;
+    int32_t *err_flag;
+} kvw_decode_args;
+
+/* Bytes of workspace kvw_decode_attention needs for these sizes. */
+int64_t kvw_decode_workspace_size(int32_t num_reqs, int32_t max_context, int32_t num_q_heads,
+                                  int32_t head_dim);
+
+/* Size of kvw_decode_args as compiled into the library (binding check). */
+size_t kvw_decode_args_size(void);
+
+kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream);
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,8 @@ from .kvw import (  # noqa: F401
     KVW_SLOTS_PRECOMPUTED,
     KVW_SLOTS_RANGES,
     KvwError,
+    kvw_decode_attention,
+    kvw_decode_workspace_size,
     kvw_kv_write,
     kvw_map_ranges_to_kernel_blocks,
     kvw_map_to_kernel_blocks,

@@ -13,8 +13,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCE = os.path.join(PKG, "csrc", "kvw.hip")
-SOURCES = (SOURCE, os.path.join(PKG, "csrc", "range_alloc.cpp"),
-           os.path.join(PKG, "csrc", "kvw_error.cpp"))
+SOURCES = (SOURCE, os.path.join(PKG, "csrc", "decode_attention.hip"),
+           os.path.join(PKG, "csrc", "range_alloc.cpp"), os.path.join(PKG, "csrc", "kvw_error.cpp"))
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libkvw.so")
 BENCH_SOURCE = os.path.join(PKG, "csrc", "bench_alloc.cpp")

@@ -1,0 +1,130 @@
+// Device helpers shared by the kernels of libkvw.so (kvw.hip, decode_attention.hip):
+// wave constants, sticky flags, count clamping, 16-byte memory access and the
+// wavefront-level search.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kvw.h"
+
+namespace {
+
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void raise_flags(int32_t *err, uint32_t flags)
+{
+    if (err && flags) atomicOr(err, static_cast<int>(flags));
+}
+
+__device__ __forceinline__ int64_t clamp_count(int32_t c, int32_t stride, uint32_t &flags)
+{
+    if (c < 0) { flags |= KVW_FLAG_COUNT; return 0; }
+    if (c > stride) { flags |= KVW_FLAG_COUNT; return stride; }
+    return c;
+}
+
+__device__ __forceinline__ bool expandable(int64_t id, int64_t k)
+{
+    return id >= 0 && id * k + (k - 1) <= INT32_MAX;
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const uint8_t *p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    else return *reinterpret_cast<const u32x4 *>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(uint8_t *p, u32x4 v)
+{
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+    else *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// ---- wavefront-level search -------------------------------------------------
+// The 64 lanes of a wave hold 64 evenly spaced entries of a sorted array (one
+// vector load) and each lane ranks its own key among them with a 6-step
+// ds_bpermute search, which touches no memory.  A second load of the window
+// that holds every lane's answer finishes the search, so two dependent loads
+// replace the ~log2(n) of a per-lane binary search: the request of a token is
+// found in query_start_loc this way, and the run of a position in range_cum
+// (the range descriptors are loaded once for the consecutive positions of a
+// wave, not once per position).
+
+// Number of lanes whose sample is <= x; samples are non-decreasing over the
+// lanes and lanes without a sample hold INT64_MAX.  Every lane runs every
+// shuffle (a permute that reads an inactive lane gets no defined value).
+__device__ __forceinline__ int wave_rank(int64_t sample, int64_t x)
+{
+    const bool all = __shfl(sample, kWave - 1) <= x;
+    int cnt = 0;
+#pragma unroll
+    for (int b = kWave / 2; b >= 1; b >>= 1) {
+        const int64_t probe = __shfl(sample, cnt + b - 1);
+        cnt += probe <= x ? b : 0;
+    }
+    return all ? kWave : cnt;
+}
+
+__device__ __forceinline__ int32_t wave_min(int32_t v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ int32_t wave_max(int32_t v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+    return v;
+}
+
+// Largest i in [0, n) with v[i] <= x (this lane's key), or -1; v sorted.
+// Every lane of the wave calls it with the same v and n; lanes with
+// part == false get -1 and do not shape the search.  When the lanes' answers
+// lie too far apart for one 128-entry window, each lane finishes with a
+// binary search inside its own 1/64 bucket.
+__device__ int32_t wave_upper_index(const int32_t *v, int32_t n, int64_t x, bool part)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    if (n <= 0) return -1;
+    int32_t lo = 0, len = n;
+    if (len > 2 * kWave) {
+        const int32_t step = (len + kWave - 1) / kWave;
+        const int32_t idx = lane * step;
+        const int cnt = wave_rank(idx < len ? static_cast<int64_t>(v[idx]) : INT64_MAX, x);
+        int32_t b_lo = INT32_MAX, b_hi = INT32_MIN;  // this lane's bucket [b_lo, b_hi)
+        if (part && cnt > 0) {
+            b_lo = (cnt - 1) * step;
+            b_hi = min(cnt * step, len);
+        }
+        const int32_t u_lo = wave_min(b_lo), u_hi = wave_max(b_hi);
+        if (u_lo == INT32_MAX) return -1;  // no taking-part lane has an answer
+        if (u_hi - u_lo > 2 * kWave) {
+            if (!part || cnt == 0) return -1;
+            int32_t a = b_lo, h = b_hi;  // v[a] <= x
+            while (h - a > 1) {
+                const int32_t mid = (a + h) >> 1;
+                if (v[mid] <= x) a = mid; else h = mid;
+            }
+            return a;
+        }
+        lo = u_lo;
+        len = u_hi - u_lo;
+    }
+    // window of at most 128 entries: two samples per lane, loaded together
+    const int64_t s0 = lane < len ? static_cast<int64_t>(v[lo + lane]) : INT64_MAX;
+    const int64_t s1 = lane + kWave < len ? static_cast<int64_t>(v[lo + kWave + lane]) : INT64_MAX;
+    int cnt = wave_rank(s0, x);
+    const int cnt1 = wave_rank(s1, x);
+    if (cnt == kWave) cnt += cnt1;
+    return (part && cnt > 0) ? lo + cnt - 1 : -1;
+}
+
+}  // namespace

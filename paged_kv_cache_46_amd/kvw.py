@@ -15,7 +15,7 @@ import torch
 
 from .build import LIBRARY
 
-KVW_ABI_VERSION = 3
+KVW_ABI_VERSION = 4
 KVW_PAD_ID = -1
 KVW_MAX_RANGE_STRIDE = 65536
 KVW_OK, KVW_ERR_INVALID_ARG, KVW_ERR_UNSUPPORTED, KVW_ERR_RANGE_CAP, KVW_ERR_HIP = range(5)
@@ -52,6 +52,18 @@ class kvw_kv_write_args(ctypes.Structure):
     ]
 
 
+class kvw_decode_args(ctypes.Structure):
+    _fields_ = [
+        ("mode", _I32), ("num_reqs", _I32), ("q", _P), ("context_lens", _P),
+        ("max_context", _I32), ("block_size", _I32), ("block_table", _P),
+        ("num_blocks_per_req", _P), ("block_table_stride", _I32), ("range_stride", _I32),
+        ("range_start", _P), ("range_len", _P), ("range_cum", _P), ("num_ranges", _P),
+        ("k_cache", _P), ("v_cache", _P), ("num_blocks", _I64), ("num_q_heads", _I32),
+        ("num_kv_heads", _I32), ("head_dim", _I32), ("scale", ctypes.c_float), ("out", _P),
+        ("workspace", _P), ("workspace_bytes", _I64), ("err_flag", _P),
+    ]
+
+
 _lib = None
 
 
@@ -75,6 +87,7 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
         "kvw_ranges_to_block_table": [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _I32, _P, _P,
                                       _P],
         "kvw_kv_write": [ctypes.POINTER(kvw_kv_write_args), _P],
+        "kvw_decode_attention": [ctypes.POINTER(kvw_decode_args), _P],
     }
     for name, argtypes in sigs.items():
         fn = getattr(lib, name)
@@ -83,10 +96,15 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kvw_abi_version.restype = _I32
     lib.kvw_last_error.restype = ctypes.c_char_p
     lib.kvw_kv_write_args_size.restype = ctypes.c_size_t
+    lib.kvw_decode_args_size.restype = ctypes.c_size_t
+    lib.kvw_decode_workspace_size.argtypes = [_I32, _I32, _I32, _I32]
+    lib.kvw_decode_workspace_size.restype = _I64
     if lib.kvw_abi_version() != KVW_ABI_VERSION:
         raise RuntimeError(f"libkvw ABI {lib.kvw_abi_version()} != binding ABI {KVW_ABI_VERSION}")
     if lib.kvw_kv_write_args_size() != ctypes.sizeof(kvw_kv_write_args):
         raise RuntimeError("kvw_kv_write_args layout differs between library and binding")
+    if lib.kvw_decode_args_size() != ctypes.sizeof(kvw_decode_args):
+        raise RuntimeError("kvw_decode_args layout differs between library and binding")
     _lib = lib
     return lib
 
@@ -264,3 +282,57 @@ def kvw_kv_write(*, mode, key, value, k_cache, v_cache, num_blocks, block_size,
             a.num_ranges = _dev(num_ranges, torch.int32, "num_ranges")
             a.range_stride = _stride(range_start)
     _check(library().kvw_kv_write(ctypes.byref(a), _stream(stream)))
+
+
+def kvw_decode_workspace_size(num_reqs, max_context, num_q_heads, head_dim=128) -> int:
+    return int(library().kvw_decode_workspace_size(num_reqs, max_context, num_q_heads, head_dim))
+
+
+def kvw_decode_attention(*, mode, q, k_cache, v_cache, context_lens, max_context, num_blocks,
+                         block_size, out, block_table=None, num_blocks_per_req=None,
+                         range_start=None, range_len=None, range_cum=None, num_ranges=None,
+                         scale=None, workspace=None, err_flag=None, stream=None):
+    """Decode attention over the paged cache (see include/kvw.h).
+
+    q: [num_reqs, num_q_heads, head_dim] 2-byte (bf16) tensor; k_cache, v_cache:
+    [num_blocks * block_size, num_kv_heads, head_dim]; out: float32 like q.  workspace:
+    a byte tensor of kvw_decode_workspace_size(...) bytes, allocated here when None.
+    """
+    if q.dim() != 3 or k_cache.dim() != 3 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [R, Hq, D] and the caches [rows, Hkv, D]")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous() \
+                or t.element_size() != 2:
+            raise ValueError(f"{name} must be a contiguous GPU tensor of a 2-byte dtype")
+    if out.shape != q.shape or out.dtype != torch.float32:
+        raise ValueError("out must be float32 with q's shape")
+    num_reqs, hq, d = (int(x) for x in q.shape)
+    hkv = int(k_cache.shape[1])
+    need = kvw_decode_workspace_size(num_reqs, int(max_context), hq, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    a = kvw_decode_args()
+    a.mode, a.num_reqs = int(mode), num_reqs
+    a.q = q.data_ptr()
+    a.context_lens = _dev(context_lens, torch.int32, "context_lens")
+    a.max_context, a.block_size = int(max_context), int(block_size)
+    if mode == KVW_SLOTS_PAGED:
+        a.block_table = _dev(block_table, torch.int32, "block_table", optional=True)
+        a.block_table_stride = _stride(block_table)
+        a.num_blocks_per_req = _dev(num_blocks_per_req, torch.int32, "num_blocks_per_req",
+                                    optional=True)
+    else:
+        a.range_start = _dev(range_start, torch.int32, "range_start")
+        a.range_len = _dev(range_len, torch.int32, "range_len")
+        a.range_cum = _dev(range_cum, torch.int32, "range_cum")
+        a.num_ranges = _dev(num_ranges, torch.int32, "num_ranges")
+        a.range_stride = _stride(range_start)
+    a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+    a.num_blocks = int(num_blocks)
+    a.num_q_heads, a.num_kv_heads, a.head_dim = hq, hkv, d
+    a.scale = float(scale if scale is not None else d ** -0.5)
+    a.out = out.data_ptr()
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.err_flag = _dev(err_flag, torch.int32, "err_flag", optional=True)
+    _check(library().kvw_decode_attention(ctypes.byref(a), _stream(stream)))

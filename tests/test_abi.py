@@ -62,6 +62,10 @@ def test_abi_version_and_struct_layout(lib):
     fields = re.search(r"typedef struct kvw_kv_write_args \{(.*?)\} kvw_kv_write_args;", text, re.S)
     c_names = re.findall(r"\*?\s*(\w+);", re.sub(r"/\*.*?\*/", "", fields.group(1), flags=re.S))
     assert c_names == [f[0] for f in kvw.kvw.kvw_kv_write_args._fields_]
+    assert lib.kvw_decode_args_size() == ctypes.sizeof(kvw.kvw.kvw_decode_args)
+    fields = re.search(r"typedef struct kvw_decode_args \{(.*?)\} kvw_decode_args;", text, re.S)
+    c_names = re.findall(r"\*?\s*(\w+);", re.sub(r"/\*.*?\*/", "", fields.group(1), flags=re.S))
+    assert c_names == [f[0] for f in kvw.kvw.kvw_decode_args._fields_]
 
 
 def _err(lib):
@@ -189,3 +193,56 @@ def test_binding_rejects_missing_library(tmp_path):
             binding.library(str(tmp_path / "absent.so"))
     finally:
         binding._lib = saved
+
+
+def _decode(**kw):
+    a = kvw.kvw.kvw_decode_args()
+    base = dict(mode=kvw.KVW_SLOTS_PAGED, num_reqs=4, q=P, context_lens=P, max_context=1000,
+                block_size=16, block_table=P, num_blocks_per_req=P, block_table_stride=64,
+                range_stride=8, range_start=P, range_len=P, range_cum=P, num_ranges=P,
+                k_cache=P, v_cache=P, num_blocks=256, num_q_heads=32, num_kv_heads=8,
+                head_dim=128, scale=0.088, out=P, workspace=P, workspace_bytes=1 << 30)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_workspace_size(lib):
+    ws = lib.kvw_decode_workspace_size
+    ws.restype = ctypes.c_int64
+    # per request, per 256-position chunk and query head: 128 sums, the chunk max and sum
+    assert ws(4, 1000, 32, 128) == 4 * 4 * 32 * 130 * 4
+    assert ws(4, 1024, 32, 128) == 4 * 4 * 32 * 130 * 4
+    assert ws(4, 1025, 32, 128) == 4 * 5 * 32 * 130 * 4
+    assert ws(4, 0, 32, 128) == 0
+    assert ws(-1, 10, 32, 128) == -1
+
+
+def test_decode_validation(lib):
+    f = lib.kvw_decode_attention
+    assert f(None, None) == INVALID
+    assert f(ctypes.byref(_decode(mode=kvw.KVW_SLOTS_PRECOMPUTED)), None) == INVALID
+    assert f(ctypes.byref(_decode(head_dim=64)), None) == UNSUPPORTED
+    assert f(ctypes.byref(_decode(num_q_heads=64, num_kv_heads=8)), None) == UNSUPPORTED
+    assert f(ctypes.byref(_decode(num_q_heads=12, num_kv_heads=4)), None) == UNSUPPORTED  # 3 per head
+    assert f(ctypes.byref(_decode(num_q_heads=32, num_kv_heads=32)), None) == UNSUPPORTED
+    assert f(ctypes.byref(_decode(num_q_heads=16, num_kv_heads=1)), None) == UNSUPPORTED  # 16 per head
+    assert f(ctypes.byref(_decode(num_q_heads=30, num_kv_heads=8)), None) == UNSUPPORTED
+    assert f(ctypes.byref(_decode(block_size=0)), None) == INVALID
+    assert f(ctypes.byref(_decode(max_context=-1)), None) == INVALID
+    assert f(ctypes.byref(_decode(num_reqs=70000)), None) == INVALID
+    assert f(ctypes.byref(_decode(num_blocks=1 << 60)), None) == INVALID   # cache size overflow
+    assert f(ctypes.byref(_decode(q=P + 4)), None) == INVALID
+    assert f(ctypes.byref(_decode(out=None)), None) == INVALID
+    assert f(ctypes.byref(_decode(k_cache=P + 8)), None) == INVALID
+    assert f(ctypes.byref(_decode(err_flag=P + 2)), None) == INVALID
+    assert f(ctypes.byref(_decode(block_table=None)), None) == INVALID
+    assert f(ctypes.byref(_decode(block_table_stride=-1)), None) == INVALID
+    assert f(ctypes.byref(_decode(mode=kvw.KVW_SLOTS_RANGES, range_cum=None)), None) == INVALID
+    assert f(ctypes.byref(_decode(mode=kvw.KVW_SLOTS_RANGES, range_stride=1 << 20)),
+             None) == RANGE_CAP
+    assert f(ctypes.byref(_decode(workspace_bytes=4 * 4 * 32 * 130 * 4 - 1)), None) == INVALID
+    assert "workspace" in _err(lib)
+    assert f(ctypes.byref(_decode(workspace=None)), None) == INVALID
+    assert f(ctypes.byref(_decode(num_reqs=0)), None) == OK   # nothing to do: no launch

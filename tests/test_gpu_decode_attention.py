@@ -1,0 +1,392 @@
+"""Decode attention over the paged cache: HIP path vs CPU oracle (needs an MI355X).
+
+The read side of the method: each request's query attends its context positions
+0 .. n-1, whose slots the kernel resolves again from the block table (paged) or
+from the range descriptors (range arithmetic).  The expected slots come from the
+oracle's own slot mapping over those positions; the expected output from the
+oracle's fp64 attention over the same slots.  Expected flag words are the oracle
+slot mapping's, plus KVW_FLAG_COUNT where a context length is clamped and
+KVW_FLAG_SLOT_OOB where a slot lies past the cache (such positions are skipped).
+
+Tolerance: the kernel works in fp32 (unit roundoff u = 2^-24) from exact bf16
+inputs.  To first order in u, with C the number of 256-position chunks, the
+output error is at most
+    u * max|V| * (2C + 100 + 40 * scale * |q| * max_j |k_j|)
+per (request, query head): 66u from the per-lane sums of p*v plus the shuffles,
+(C + 1)u and (C + 11)u from the chunk merge of numerator and denominator, a few
+u from expf, and twice the score error (each score is a 128-term fp32 dot product
+of scaled q and k, error <= 13u scale |q||k|, plus the rounding of s - max).
+The bound is written out in `tolerance` below.  Requests with no readable
+position must give exactly 0.
+
+The bound grows with the context, so at 128K a single dropped position would hide
+under it.  The "integers" inputs close that gap bit-exactly: with K = 0 every
+weight is exactly 1, and with V on the small integers every fp32 sum the kernel
+forms is an exact integer, so out * n (n the readable positions) must round to the
+oracle's integer sum in every dimension; a position dropped, read twice or read
+from the wrong slot changes that sum.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_46_amd as kvw
+from parity import DEV, dev, host, new_flag, say
+from workloads import Request, config, custom, decode_inputs, long_context
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+FLAG_COUNT, FLAG_BAD_BLOCK, FLAG_SLOT_OOB = 2, 4, 8
+CHUNK = 256
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kvw.library()
+    yield
+    torch.cuda.synchronize()
+
+
+def f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+class Layout:
+    """What the slots are resolved from: a block table or range descriptors, at block_size."""
+
+    def __init__(self, w, block_size=None, table=None, nbpr=None, rs=None, rl=None, rc=None,
+                 nr=None, num_blocks=None):
+        self.bs = block_size or w.block_size
+        self.num_blocks = num_blocks if num_blocks is not None else w.num_blocks
+        self.table = w.block_table if table is None else table
+        self.nbpr = w.num_blocks_per_req if nbpr is None else nbpr
+        self.rs = w.range_start if rs is None else rs
+        self.rl = w.range_len if rl is None else rl
+        self.rc = w.range_cum if rc is None else rc
+        self.nr = w.num_ranges if nr is None else nr
+
+    @property
+    def rows(self) -> int:
+        return self.num_blocks * self.bs
+
+
+def expected_slots(lay: Layout, mode: str, ctx: np.ndarray):
+    """Per request, the slots of positions 0 .. ctx[r]-1 by the oracle's slot mapping (slots past
+    the cache become -1 and raise KVW_FLAG_SLOT_OOB), and the flag word."""
+    orc = oracle.get()
+    num_reqs = len(ctx)
+    qsl = np.zeros(num_reqs + 1, np.int32)
+    qsl[1:] = np.cumsum(ctx)
+    m = int(qsl[-1])
+    if m == 0:
+        return [np.zeros(0, np.int64) for _ in range(num_reqs)], 0
+    pos = np.concatenate([np.arange(c, dtype=np.int64) for c in ctx])
+    if mode == "paged":
+        slots, flags = orc.slot_mapping_paged(qsl, num_reqs, pos, m, lay.table, lay.nbpr, lay.bs)
+    else:
+        slots, flags = orc.slot_mapping_ranges(qsl, num_reqs, pos, m, lay.rs, lay.rl, lay.rc,
+                                               lay.nr, lay.bs)
+    slots = slots.copy()
+    past = slots >= lay.rows
+    if past.any():
+        slots[past] = -1
+        flags |= FLAG_SLOT_OOB
+    return [slots[qsl[r]:qsl[r + 1]] for r in range(num_reqs)], flags
+
+
+def run_gpu(mode, lay: Layout, q, ctx_given, max_context, kc, vc, scale=None, num_reqs=None):
+    num_reqs = q.shape[0] if num_reqs is None else num_reqs
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
+    flag = new_flag()
+    common = dict(q=dev(q), k_cache=kc, v_cache=vc, context_lens=dev(np.asarray(ctx_given,
+                                                                              np.int32)),
+                  max_context=max_context, num_blocks=lay.num_blocks, block_size=lay.bs, out=out,
+                  scale=scale, err_flag=flag)
+    if mode == "paged":
+        kvw.kvw_decode_attention(mode=kvw.KVW_SLOTS_PAGED, block_table=dev(lay.table),
+                                 num_blocks_per_req=dev(lay.nbpr), **common)
+    else:
+        kvw.kvw_decode_attention(mode=kvw.KVW_SLOTS_RANGES, range_start=dev(lay.rs),
+                                 range_len=dev(lay.rl), range_cum=dev(lay.rc),
+                                 num_ranges=dev(lay.nr), **common)
+    torch.cuda.synchronize()
+    return host(out), int(flag.item())
+
+
+def place_caches(rows_total, rows, k, v):
+    """Device K/V caches [rows_total][Hkv][D], zero except the given rows."""
+    hkv, d = k.shape[1], k.shape[2]
+    kc = torch.zeros((rows_total, hkv, d), dtype=torch.int16, device=DEV)
+    vc = torch.zeros_like(kc)
+    idx = torch.from_numpy(np.asarray(rows, np.int64)).to(DEV)
+    kc[idx] = dev(k)
+    vc[idx] = dev(v)
+    return kc, vc
+
+
+def tolerance(qh, kr, vr, n_chunks, scale):
+    """First-order fp32 error bound of one request's output (see the module docstring).
+    qh: [Hq][D] float; kr, vr: [n][Hkv][D] float (the request's readable rows)."""
+    hq, hkv = qh.shape[0], kr.shape[1]
+    g = hq // hkv
+    kmax = np.sqrt((kr.astype(np.float64) ** 2).sum(axis=2)).max(axis=0)  # [Hkv]
+    vmax = np.abs(vr).max(axis=(0, 2)).astype(np.float64)                # [Hkv]
+    qn = np.sqrt((qh.astype(np.float64) ** 2).sum(axis=1))               # [Hq]
+    heads = np.arange(hq) // g
+    return U * vmax[heads] * (2 * n_chunks + 100 + 40 * abs(scale) * qn * kmax[heads])
+
+
+def check(gpu, q, slots, rows, k, v, ctx_eff, sel, hq, hkv, scale, tag, exact=False):
+    """Compare gpu[sel] with the oracle; rows/k/v hold the cache rows the requests read.
+    exact: K is 0 and V integer-valued, so out * n must round to the oracle's sum exactly."""
+    orc = oracle.get()
+    order = np.argsort(rows)
+    rows_s = np.asarray(rows, np.int64)[order]
+    local = []
+    for r in sel:
+        s = slots[r]
+        idx = np.full(len(s), -1, np.int64)
+        ok = s >= 0
+        if ok.any():
+            j = np.searchsorted(rows_s, s[ok])
+            assert (j < len(rows_s)).all() and (rows_s[j] == s[ok]).all(), "a read row is not drawn"
+            idx[ok] = order[j]
+        local.append(idx)
+    want = orc.decode_attention(q, k, v, local, np.asarray(sel, np.int32), hq, hkv, scale)
+    ratio = 0.0
+    for i, r in enumerate(sel):
+        got = gpu[r]
+        assert np.isfinite(got).all(), f"{tag}: request {r} has non-finite output"
+        idx = local[i][local[i] >= 0]
+        if len(idx) == 0:
+            assert (got == 0).all(), f"{tag}: request {r} reads nothing but is not 0"
+            continue
+        if exact:
+            n = len(idx)
+            g_sum = np.rint(got.astype(np.float64) * n)
+            o_sum = np.rint(want[i] * n)
+            assert np.abs(want[i] * n - o_sum).max() < 1e-6       # the oracle's sums are integers
+            bad = np.argwhere(g_sum != o_sum)
+            assert len(bad) == 0, f"{tag}: request {r}: {len(bad)} sums differ, first {bad[:3]}"
+            continue
+        tol = tolerance(f32(q[r]), f32(k[idx]), f32(v[idx]), -(-int(ctx_eff[r]) // CHUNK), scale)
+        err = np.abs(got.astype(np.float64) - want[i]).max(axis=1)
+        worst = int(np.argmax(err / tol))
+        assert (err <= tol).all(), (f"{tag}: request {r} head {worst}: error {err[worst]:.3e} "
+                                    f"over the bound {tol[worst]:.3e}")
+        ratio = max(ratio, float(err[worst] / tol[worst]))
+    say(f"[decode] {tag}: largest error is {ratio:.3f} of the bound")
+
+
+def parity(w, mode, hq, seed, lay=None, ctx_given=None, max_context=None, scale=None, sel=None,
+           draw_rows=None, kind="normal"):
+    """Decode over layout `lay` (default: w's) with fresh q/K/V; check outputs and flags."""
+    lay = lay or Layout(w)
+    hkv = w.num_kv_heads
+    ctx_w = np.array([rq.end for rq in w.requests] + [0] * (w.num_reqs - len(w.requests)),
+                     np.int64)
+    ctx_given = ctx_w if ctx_given is None else np.asarray(ctx_given, np.int64)
+    if max_context is None:
+        max_context = int(max(ctx_given.max(initial=0), 0))
+    ctx_eff = np.clip(ctx_given, 0, max_context)
+    count_flag = FLAG_COUNT if (ctx_eff != ctx_given).any() else 0
+    slots, flags = expected_slots(lay, mode, ctx_eff)
+    sel = list(range(w.num_reqs)) if sel is None else list(sel)
+    if draw_rows is None:  # every row of the pool
+        rows = None
+    else:
+        rows = np.unique(np.concatenate([slots[r][slots[r] >= 0] for r in sel] +
+                                        [np.zeros(0, np.int64)]))
+    q, _, rows, k, v = decode_inputs(w, hq, seed, rows=rows if rows is not None else
+                                     np.arange(lay.rows, dtype=np.int64), kind=kind)
+    scale = float(scale if scale is not None else w.head_dim ** -0.5)
+    say(f"[decode] {w.name} {mode} Hq {hq} Hkv {hkv} bs {lay.bs} reqs {w.num_reqs} "
+        f"max_context {max_context} checked {len(sel)} rows {len(rows)} scale {scale:.4f} "
+        f"inputs {kind}")
+    kc, vc = place_caches(lay.rows, rows, k, v)
+    gpu, gflag = run_gpu(mode, lay, q, ctx_given, max_context, kc, vc, scale=scale)
+    assert gflag == flags | count_flag, f"flags {gflag} != {flags | count_flag}"
+    check(gpu, q, slots, rows, k, v, ctx_eff, sel, hq, hkv, scale, f"{w.name}/{mode}",
+          exact=kind == "integers")
+    return gpu, slots
+
+
+# ---------------------------------------------------------------------------
+# small workloads: ragged contexts around the 256-position chunk, every head grouping
+# ---------------------------------------------------------------------------
+def _dec(name, seed, contexts, bs, runs, hkv, pool, dummies=0, **kw):
+    reqs = [Request(int(c), 1 if c else 0) for c in contexts]
+    return custom(name, seed, reqs, block_size=bs, num_blocks=pool, runs=runs, num_kv_heads=hkv,
+                  dummy_reqs=dummies, **kw)
+
+
+def small_decodes():
+    rng = np.random.Generator(np.random.PCG64([4711, 0]))
+    return [
+        # (workload, query heads)
+        (_dec("ragged_g4", 1, [1, 255, 256, 257, 700, 1500, 3000, 4097, 0], 16,
+              ("count", 1, 6), 8, 1200, dummies=2), 32),
+        (_dec("bs32_g8", 2, rng.integers(1, 2000, 12), 32, ("count", 1, 4), 4, 1024), 32),
+        (_dec("bs64_g1_16heads", 3, [63, 64, 65, 1000, 2049], 64, ("len", 1, 3), 16, 128), 16),
+        (_dec("bs16_g2", 4, rng.integers(1, 1200, 9), 16, ("len", 1, 8), 2, 900), 4),
+        (_dec("one_head", 5, [1, 2, 300, 513], 16, ("count", 1, 3), 1, 128), 1),
+        (_dec("g8_one_kv_head", 6, [17, 600, 1025], 16, ("count", 2, 5), 1, 160), 8),
+        # one block per run: the search over range_cum spans many entries
+        (_dec("many_runs", 7, [3000, 4000, 257], 16, ("len", 1, 1), 8, 600,
+              range_stride=300), 32),
+        # block size 1: a chunk's 256 positions fall in 256 different runs
+        (_dec("bs1_many_runs", 8, [600, 1100, 5], 1, ("len", 1, 1), 4, 2000,
+              range_stride=1200), 16),
+    ]
+
+
+SMALL = small_decodes()
+
+
+@pytest.mark.parametrize("mode", ["paged", "ranges"])
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c[0].name)
+def test_decode_small(case, mode):
+    w, hq = case
+    parity(w, mode, hq, seed=100 + len(w.name))
+    parity(w, mode, hq, seed=200 + len(w.name), kind="integers")
+
+
+def test_decode_scale_and_longer_max_context():
+    w, hq = SMALL[0]
+    for mode in ("paged", "ranges"):
+        parity(w, mode, hq, seed=3, scale=0.3, max_context=5000)   # chunks past every context
+        parity(w, mode, hq, seed=4, scale=1.0)
+
+
+@pytest.mark.parametrize("mode", ["paged", "ranges"])
+def test_decode_context_clamped(mode):
+    """Lengths above max_context or negative are clamped (KVW_FLAG_COUNT)."""
+    w, hq = SMALL[0]
+    ctx = np.array([rq.end for rq in w.requests] + [0, 0], np.int64)
+    ctx[3] = 99999          # past max_context: clamped to it
+    ctx[8] = -7             # negative: no position, output 0
+    ctx[9] = 300            # a dummy request with no blocks: every position is unmapped
+    parity(w, mode, hq, seed=5, ctx_given=ctx, max_context=2000)
+
+
+@pytest.mark.parametrize("mode", ["paged", "ranges"])
+def test_decode_unmapped_tail(mode):
+    """Positions past a request's blocks or ranges are skipped (whole chunks may be empty);
+    counts above the stride are clamped with KVW_FLAG_COUNT."""
+    w, hq = SMALL[0]
+    nbpr = w.num_blocks_per_req.copy()
+    nr = w.num_ranges.copy()
+    nbpr[4], nbpr[6], nbpr[7] = 5, 0, w.table_stride + 3
+    nr[4], nr[6], nr[7] = 1, 0, w.range_stride + 3
+    lay = Layout(w, nbpr=nbpr, nr=nr)
+    parity(w, mode, hq, seed=6, lay=lay)
+
+
+def test_decode_bad_blocks():
+    """A negative block id is skipped with KVW_FLAG_BAD_BLOCK; a block past the pool with
+    KVW_FLAG_SLOT_OOB."""
+    w, hq = SMALL[0]
+    table = w.block_table.copy()
+    table[5, 3] = -4
+    table[6, 1] = w.num_blocks + 2
+    parity(w, "paged", hq, seed=7, lay=Layout(w, table=table))
+    rs = w.range_start.copy()
+    rs[6, 0] = w.num_blocks + 10
+    parity(w, "ranges", hq, seed=8, lay=Layout(w, rs=rs))
+
+
+def test_decode_empty():
+    w, hq = SMALL[0]
+    lay = Layout(w)
+    q, _, rows, k, v = decode_inputs(w, hq, 9, rows=np.arange(lay.rows, dtype=np.int64))
+    kc, vc = place_caches(lay.rows, rows, k, v)
+    ctx = np.array([rq.end for rq in w.requests] + [0, 0], np.int64)
+    for mode in ("paged", "ranges"):
+        gpu, flag = run_gpu(mode, lay, q, np.zeros_like(ctx), 0, kc, vc)
+        assert flag == 0 and (gpu == 0).all()
+        gpu, flag = run_gpu(mode, lay, q, ctx, 0, kc, vc)   # every length clamped to 0
+        assert flag == FLAG_COUNT and (gpu == 0).all()
+    out = torch.full((0, hq, 128), 1.0, dtype=torch.float32, device=DEV)
+    kvw.kvw_decode_attention(mode=kvw.KVW_SLOTS_PAGED, q=dev(q[:0]), k_cache=kc, v_cache=vc,
+                             context_lens=dev(ctx[:0].astype(np.int32)), max_context=100,
+                             num_blocks=lay.num_blocks, block_size=lay.bs, out=out,
+                             block_table=dev(lay.table), num_blocks_per_req=dev(lay.nbpr))
+    torch.cuda.synchronize()
+
+
+def test_decode_reads_what_the_write_wrote():
+    """One step end to end: kv_write stores each decode token's K/V, then decode attention reads
+    the cache; the oracle does the same with its own write."""
+    orc = oracle.get()
+    w, hq = SMALL[0]
+    lay = Layout(w)
+    q, ctx, rows, k, v = decode_inputs(w, hq, 10, rows=np.arange(lay.rows, dtype=np.int64))
+    kc, vc = place_caches(lay.rows, rows, k, v)
+    key_h, value_h = w.kv_layer(0, 0), w.kv_layer(1, 0)
+    slots_w, _ = orc.slot_mapping_ranges(w.query_start_loc, w.num_reqs, w.positions,
+                                         w.max_num_tokens, w.range_start, w.range_len,
+                                         w.range_cum, w.num_ranges, w.block_size)
+    hkv = w.num_kv_heads
+    kh = k.reshape(lay.rows, hkv * 128).copy()
+    vh = v.reshape(lay.rows, hkv * 128).copy()
+    orc.kv_write(slots_w, key_h[None], value_h[None], w.num_blocks, w.block_size, kh, vh)
+    slot_out = torch.empty(w.max_num_tokens, dtype=torch.int64, device=DEV)
+    kvw.kvw_kv_write(mode=kvw.KVW_SLOTS_RANGES, query_start_loc=dev(w.query_start_loc),
+                     num_reqs=w.num_reqs, positions=dev(w.positions),
+                     max_num_tokens=w.max_num_tokens, range_start=dev(w.range_start),
+                     range_len=dev(w.range_len), range_cum=dev(w.range_cum),
+                     num_ranges=dev(w.num_ranges), block_size=w.block_size,
+                     num_blocks=w.num_blocks,
+                     key=dev(key_h).view(1, w.max_num_tokens, hkv, 128),
+                     value=dev(value_h).view(1, w.max_num_tokens, hkv, 128),
+                     k_cache=kc, v_cache=vc, slot_mapping_out=slot_out)
+    gpu, flag = run_gpu("ranges", lay, q, ctx, int(ctx.max()), kc, vc)
+    assert flag == 0
+    slots, _ = expected_slots(lay, "ranges", ctx)
+    check(gpu, q, slots, rows, kh.reshape(lay.rows, hkv, 128), vh.reshape(lay.rows, hkv, 128),
+          ctx, list(range(w.num_reqs)), hq, hkv, w.head_dim ** -0.5, "after write")
+
+
+# ---------------------------------------------------------------------------
+# full sizes: sampled requests against the oracle, the rest by a property
+# ---------------------------------------------------------------------------
+def full_size(w, lay, hq, sel, seed, kind="normal"):
+    """Both modes on the full workload; only the rows that `sel` reads hold drawn K/V.  Every
+    other request that reads none of them sees zeros and must give exactly 0 (an oversubscribed
+    pool shares history blocks between requests; those are only checked to be finite)."""
+    outs = []
+    for mode in ("paged", "ranges"):
+        gpu, slots = parity(w, mode, hq, seed, lay=lay, sel=sel, draw_rows=True, kind=kind)
+        drawn = np.unique(np.concatenate([slots[r][slots[r] >= 0] for r in sel]))
+        zero = 0
+        for r in range(w.num_reqs):
+            if r in sel:
+                continue
+            assert np.isfinite(gpu[r]).all()
+            if not np.isin(slots[r], drawn).any():
+                assert (gpu[r] == 0).all(), f"request {r} reads only zeros but is not 0"
+                zero += 1
+        say(f"[decode] {zero} of {w.num_reqs - len(sel)} unsampled requests read only zeros")
+        assert zero > 0
+        outs.append(gpu)
+    # the two resolutions give the same slots, so the same arithmetic and the same bits
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_decode_step_full():
+    """256 decodes with context U[1, 8192], Llama-3-8B heads (32 query / 8 key-value)."""
+    w = config("decode_step")
+    full_size(w, Layout(w), 32, sel=[0, 17, 100, 201, 255], seed=11)
+    full_size(w, Layout(w), 32, sel=[5, 64, 130, 250], seed=13, kind="integers")
+
+
+@pytest.mark.parametrize("r", [1, 4096])
+def test_decode_long_context_full(r):
+    """16 requests at 128K context, 32 query / 8 key-value heads, manager block size 32."""
+    w = long_context(r)
+    full_size(w, Layout(w), 32, sel=[3 + r % 11], seed=12)
+    full_size(w, Layout(w), 32, sel=[9 + r % 5], seed=14, kind="integers")

@@ -10,9 +10,11 @@ from .gen import (  # noqa: F401
     BF16_MARKER_ONE,
     BF16_SENTINEL,
     CONFIG_NAMES,
+    Request,
     Workload,
     config,
     custom,
+    decode_inputs,
     long_context,
     range_tables,
     small_cases,

@@ -501,3 +501,36 @@ def range_tables(seed: int, runs_per_row: Sequence[int], *, max_len: int = 3,
         cum[r, :n] = np.concatenate([[0], np.cumsum(ln)[:-1]]) if n else []
         num[r] = n
     return start, length, cum, num
+
+
+def decode_inputs(w: Workload, num_q_heads: int, seed: int, rows=None, num_kv_heads=None,
+                  head_dim=None, kind: str = "normal"):
+    """Queries, context lengths and cache contents for decode attention over w's layout.
+
+    q: bf16 bits [num_reqs][num_q_heads][head_dim]; context_lens: the context of every real
+    request (its `end`), 0 for dummy requests.  K and V rows [rows][num_kv_heads][head_dim]
+    are drawn for the given cache rows (all rows of the pool when None) and returned with the
+    row ids; every other row is left to the caller (zeros).  kind "normal": K, V ~ N(0, 1);
+    kind "integers": K = 0 and V uniform on the integers -8 .. 8 (all exact in bf16).
+    """
+    hkv = num_kv_heads or w.num_kv_heads
+    d = head_dim or w.head_dim
+    rng = np.random.Generator(np.random.PCG64([seed, 5]))
+    q = _bf16_normal(rng, w.num_reqs * num_q_heads * d).reshape(w.num_reqs, num_q_heads, d)
+    ctx = np.zeros(w.num_reqs, np.int32)
+    for r, rq in enumerate(w.requests):
+        ctx[r] = rq.end
+    if rows is None:
+        rows = np.arange(w.num_blocks * w.block_size, dtype=np.int64)
+    rows = np.asarray(rows, np.int64)
+    shape = (len(rows), hkv, d)
+    if kind == "normal":
+        k = _bf16_normal(rng, len(rows) * hkv * d).reshape(shape)
+        v = _bf16_normal(rng, len(rows) * hkv * d).reshape(shape)
+    elif kind == "integers":
+        k = np.zeros(shape, np.uint16)
+        ints = rng.integers(-8, 9, size=shape, dtype=np.int32).astype(np.float32)
+        v = (ints.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    else:
+        raise ValueError(f"unknown kind {kind!r}")
+    return q, ctx, rows, k, v
