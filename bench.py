@@ -76,6 +76,8 @@ def parse():
                    help="long_context (default) is the 128K study above; the others time the\n"
                         "fused write (paged and ranges) on that config, flushing L2 and MALL\n"
                         "before every step; ms_per_step is then the fused call's event time")
+    p.add_argument("--no-decode", action="store_true",
+                   help="skip the decode-attention (read path) measurements")
     p.add_argument("--copy-calibration-mib", type=int, default=512,
                    help="size of the plain device copy timed as the practical ceiling "
                         "(read + write of this many MiB); 0 to skip")
@@ -384,6 +386,11 @@ def main():
                 f"{avg * 1e3:6.1f} us = {tp[f'TP{tpn}']['gbps']:.0f} GB/s")
             del tp_call, k_r, v_r
 
+    dec = None
+    if not args.no_decode:
+        del cache
+        dec = decode_attention(args, d, dev, stream, timed)
+
     copy_ceiling = None
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -454,11 +461,92 @@ def main():
         "copy_ceiling": copy_ceiling,
         "context_parallel": cp,
         "tensor_parallel": tp,
+        "decode_attention": dec,
         "host_allocator": host_alloc,
         "variants": {k_: {kk: (round(vv, 6) if isinstance(vv, float) else vv)
                           for kk, vv in v.items()} for k_, v in results.items()},
     }
     print(json.dumps(line), flush=True)
+
+
+DECODE_Q_HEADS = 32  # Llama-3-8B attention: 32 query heads over the 8 key/value heads
+
+
+def decode_bytes(w, ctx, num_q_heads, mode):
+    """Algorithmic bytes of one decode-attention call: every readable position's K and V rows
+    for all key/value heads, the queries read and the fp32 outputs written, and the mapping
+    entries the positions resolve through (4 B per block-table entry in use; 12 B per range
+    descriptor in use plus the count).  The chunk workspace is not counted."""
+    import numpy as np
+    kv = int(ctx.sum()) * w.num_kv_heads * w.head_dim * 2 * 2
+    qo = w.num_reqs * num_q_heads * w.head_dim * (2 + 4)
+    if mode == "paged":
+        mapping = 4 * int(np.minimum(-(-ctx // w.block_size), w.num_blocks_per_req).sum())
+    else:
+        mapping = 12 * int(w.num_ranges.sum()) + 4 * w.num_reqs
+    return kv + qo + mapping
+
+
+def decode_attention(args, d, dev, stream, timed):
+    """Decode attention (one query per request) over the same cache layouts, paged gather vs
+    range arithmetic: the 128K-context batch (16 requests) at 1 and 4096 ranges per request,
+    and the 256-request decode step.  Time per call (both launches) from HIP events."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_46_amd as kvw
+    from workloads import config, decode_inputs, long_context
+
+    out = {}
+    for wname, wl in (("long_context_r1", lambda: long_context(1)),
+                      ("long_context_r4096", lambda: long_context(4096)),
+                      ("decode_step", lambda: config("decode_step"))):
+        w = wl()
+        hq = DECODE_Q_HEADS
+        q, ctx, _, _, _ = decode_inputs(w, hq, 77, rows=np.zeros(0, np.int64))
+        ctx = ctx.astype(np.int64)
+        max_ctx = int(ctx.max())
+        rows = w.num_blocks * w.block_size
+        kc = torch.empty((rows, w.num_kv_heads, w.head_dim), dtype=torch.int16, device=dev)
+        vc = torch.empty_like(kc)
+        # random bf16 payload drawn on the device (timing only; values do not change the work)
+        for t in (kc, vc):
+            t.view(torch.bfloat16).normal_()
+        qd = d(q)
+        cl = d(ctx.astype(np.int32))
+        o = torch.empty((w.num_reqs, hq, w.head_dim), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(16, kvw.kvw_decode_workspace_size(w.num_reqs, max_ctx, hq)),
+                         dtype=torch.uint8, device=dev)
+        maps = {"paged": dict(mode=kvw.KVW_SLOTS_PAGED, block_table=d(w.block_table),
+                              num_blocks_per_req=d(w.num_blocks_per_req)),
+                "ranges": dict(mode=kvw.KVW_SLOTS_RANGES, range_start=d(w.range_start),
+                               range_len=d(w.range_len), range_cum=d(w.range_cum),
+                               num_ranges=d(w.num_ranges))}
+        for mode, mp in maps.items():
+            def call(ev, mp=mp):
+                if ev is not None:
+                    ev[0].record(stream)
+                kvw.kvw_decode_attention(q=qd, k_cache=kc, v_cache=vc, context_lens=cl,
+                                         max_context=max_ctx, num_blocks=w.num_blocks,
+                                         block_size=w.block_size, out=o, workspace=ws, **mp)
+                if ev is not None:
+                    ev[1].record(stream)
+            wall, ev_ms = timed(call, args.warmup, args.steps)
+            avg = statistics.fmean(ev_ms)
+            nbytes = decode_bytes(w, ctx, hq, mode)
+            key = f"{wname}_{mode}"
+            out[key] = {"requests": w.num_reqs, "positions": int(ctx.sum()),
+                        "max_context": max_ctx, "q_heads": hq, "kv_heads": w.num_kv_heads,
+                        "block_size": w.block_size, "call_ms_avg": round(avg, 5),
+                        "call_ms_wall": round(wall, 5), "algorithmic_bytes": nbytes,
+                        "gbps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                        "frac_of_peak": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            log(f"[bench] decode attention {key:26s} {avg * 1e3:8.1f} us = "
+                f"{out[key]['gbps']:5.0f} GB/s ({100 * out[key]['frac_of_peak']:.1f}%)")
+            del call
+        del kc, vc, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_config(args):
