@@ -6,25 +6,28 @@
 // position's block again) and "The Direction" (M7: range arithmetic in the
 // attention kernels).  The attention is the standard scaled dot product.
 //
-// The work is HBM-bound.  Per position a wave reads 256 B of K and 256 B of V
-// for its key/value head and does 2 * G * 128 multiply-adds (G query heads per
-// key/value head): about G/2 flop per byte, under 20 TFLOP/s of fp32 vector
-// work at 8 TB/s, so matrix cores would buy nothing.
+// The work is HBM-bound on paper: per position a wave reads 256 B of K and
+// 256 B of V for its key/value head and does 2 * G * 128 multiply-adds (G
+// query heads per key/value head), G flop per byte: 32 TFLOP/s at 8 TB/s for
+// G = 4.  That is 40% of the fp32 vector rate without packed math, so the
+// vector instructions per position are kept few: the q.k products run on
+// v_dot2c_f32_bf16 straight from the bf16 pairs, the 16-lane sums on DPP
+// adds, the exponentials on v_exp_f32 in base 2, and the running maximum is
+// only moved when it grows by more than 2^8.
 //
-// decode_partial_kernel<MODE, G>: one workgroup per (256-position chunk,
+// decode_partial_kernel<MODE, G>: one workgroup per (1024-position chunk,
 // request), one wave per key/value head.
-//   0. The workgroup resolves the slots of its positions once, into LDS:
-//      the block-table gather (PAGED) or range arithmetic with the wavefront
-//      search over range_cum (RANGES).  Every head then reads them from LDS.
-//   1. Scores: 16 lanes per position, 8 head dims (16 B of K) per lane; the
-//      lane's G query rows sit in registers, pre-scaled; a 4-step xor shuffle
-//      sums the 16 partial dot products.  Scores go to LDS.
-//   2. The chunk's maximum and exponentials per query head, in LDS.
-//   3. Values: the same lane layout accumulates p * V in registers; two xor
-//      shuffles fold the four position groups of a wave.  The chunk's
-//      (max, sum, weighted values) go to the workspace.
+//   0. The workgroup resolves the slots of its positions once, into LDS: the
+//      block-table gather (PAGED) or range arithmetic with the wavefront
+//      search over range_cum (RANGES).  Every head reads them from LDS.
+//   1. One pass over the chunk: 16 lanes per position, 8 head dims (16 B of
+//      K and of V) per lane, four positions per wave and U positions per lane
+//      group in flight.  Each lane group keeps, per query head, a running
+//      maximum m (log2 units), sum l and weighted values acc (online softmax).
+//   2. The four lane groups are merged with cross-row shuffles and the
+//      chunk's (m, l, acc) go to the workspace.
 // decode_combine_kernel: per (query head, request), one thread per head dim
-// merges the chunks with the usual rescaling by exp(m_c - max m).
+// merges the chunks with the rescaling by 2^(m_c - max m).
 
 #include <hip/hip_runtime.h>
 
@@ -39,13 +42,17 @@ using kvw_detail::fail;
 
 namespace {
 
-constexpr int kChunk = 256;                          // positions per workgroup
+constexpr int kChunk = 1024;                         // positions per workgroup
+constexpr int kSplitUnit = 256;                      // workspace is sized per 256 positions
 constexpr int kHeadDim = 128;                        // supported head_dim
 constexpr int kLanesPerRow = kHeadDim / 8;           // 16 lanes x 8 bf16
-constexpr int kRowsPerPass = kWave / kLanesPerRow;   // 4 positions per wave pass
-constexpr int kUnroll = 4;                           // passes whose loads are issued together
+constexpr int kRowsPerPass = kWave / kLanesPerRow;   // 4 positions per wave load
 constexpr int kMaxKvHeads = 16;
-constexpr int kMaxQHeads = 32;                       // score tile: 32 KiB of LDS
+constexpr int kMaxQHeads = 32;
+constexpr float kRescaleLog2 = 8.f;                  // move the running max past this growth
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 struct DecodeArgs {
     const uint16_t *q;
@@ -60,7 +67,7 @@ struct DecodeArgs {
     const uint8_t *v_cache;
     float *out;
     float *ws_acc;  // [num_reqs][splits][num_q_heads][head_dim]
-    float *ws_ml;   // [num_reqs][splits][num_q_heads][2]: chunk max, chunk sum
+    float *ws_ml;   // [num_reqs][splits][num_q_heads][2]: chunk max (log2 units), chunk sum
     int32_t *err_flag;
     int64_t cache_rows;
     int32_t num_reqs;
@@ -71,7 +78,7 @@ struct DecodeArgs {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t splits;
-    float scale;
+    float scale_log2;  // scale * log2(e): scores in base-2 exponent units
 };
 
 __device__ __forceinline__ int32_t context_of(const DecodeArgs &a, int32_t r, uint32_t &flags)
@@ -85,15 +92,52 @@ __device__ __forceinline__ int32_t context_of(const DecodeArgs &a, int32_t r, ui
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// x + the same register of another lane of its 16-lane row, picked by a DPP control.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x)
+{
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a row, left in every lane: pair swap, quad swap,
+// then the mirrors inside each half row and inside the row.
+__device__ __forceinline__ float row_sum16(float x)
+{
+    x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
+    x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
+    x = dpp_add<0x141>(x);  // row_half_mirror
+    x = dpp_add<0x140>(x);  // row_mirror
+    return x;
+}
+
+// q . k over one lane's 8 head dims, from the bf16 pairs.  Each vector element is
+// copied to a scalar before the bit cast: a bit cast applied to the element
+// expression itself reads the vector's first element.
+__device__ __forceinline__ float dot8(const u32x4 &q, const u32x4 &k)
+{
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t qi = q[i], ki = k[i];
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qi),
+                                            __builtin_bit_cast(bf16x2, ki), s, false);
+    }
+    return s;
+}
+
+// Positions in flight per lane group, per query-head grouping (register budget).
+template <int G>
+constexpr int unroll_of() { return G <= 2 ? 8 : (G == 4 ? 4 : 2); }
+
 // Threads per workgroup: one wave per key/value head, at most 16 and at most
-// 32 / G (so the G-row register tiles fit the per-thread budget).
+// 32 / G (the query heads the score tiles cover).
 template <int G>
 constexpr int partial_threads() { return kWave * (G <= 2 ? kMaxKvHeads : kMaxQHeads / G); }
 
 template <int MODE, int G>
 __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(DecodeArgs a)
 {
-    extern __shared__ float s_p[];           // [num_kv_heads * G][kChunk] scores, then weights
+    constexpr int U = unroll_of<G>();
     __shared__ int64_t s_slot[kChunk];
     const int32_t r = blockIdx.y;
     const int32_t c = blockIdx.x;
@@ -106,7 +150,7 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
     const int32_t bs = a.block_size;
 
     // 0. slots of this chunk's positions, resolved once for every head
-    for (int base = 0; base < kChunk; base += blockDim.x) {  // uniform trip count
+    for (int base = 0; base < cnt; base += blockDim.x) {  // uniform trip count
         const int t = base + static_cast<int>(threadIdx.x);
         const bool in = t < cnt;
         const int64_t p = c0 + t;
@@ -138,117 +182,102 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
         }
         int64_t slot = b < 0 ? -1 : b * bs + (p - lb * bs);
         if (slot >= a.cache_rows) { flags |= KVW_FLAG_SLOT_OOB; slot = -1; }
-        if (t < kChunk) s_slot[t] = slot;
+        if (in) s_slot[t] = slot;
     }
     __syncthreads();
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;       // key/value head of this wave
     const int sub = lane % kLanesPerRow;     // which 8 head dims
-    const int grp = lane / kLanesPerRow;     // which of the pass's 4 positions
+    const int grp = lane / kLanesPerRow;     // which of the four positions of a wave load
     const int hq0 = w * G;                   // first query head of the group
     const int64_t row_bytes = static_cast<int64_t>(a.num_kv_heads) * kHeadDim * 2;
     const int64_t head_off = static_cast<int64_t>(w) * kHeadDim * 2 + sub * 16;
-    float *sp = s_p + static_cast<int64_t>(hq0) * kChunk;
+    const uint8_t *kb = a.k_cache + head_off;
+    const uint8_t *vb = a.v_cache + head_off;
 
-    // 1. scores
-    float qv[G][8];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const u32x4 qw = load16<false>(reinterpret_cast<const uint8_t *>(
-            a.q + (static_cast<int64_t>(r) * a.num_q_heads + hq0 + g) * kHeadDim + sub * 8));
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            qv[g][2 * k] = bf16_lo(qw[k]) * a.scale;
-            qv[g][2 * k + 1] = bf16_hi(qw[k]) * a.scale;
-        }
-    }
-    for (int base = 0; base < cnt; base += kRowsPerPass * kUnroll) {
-        u32x4 kw[kUnroll];
-        int64_t sl[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int tok = base + u * kRowsPerPass + grp;
-            sl[u] = tok < cnt ? s_slot[tok] : -1;
-            kw[u] = sl[u] >= 0 ? load16<true>(a.k_cache + sl[u] * row_bytes + head_off) : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int tok = base + u * kRowsPerPass + grp;
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                float s = 0.f;
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    s += qv[g][2 * k] * bf16_lo(kw[u][k]) + qv[g][2 * k + 1] * bf16_hi(kw[u][k]);
-                s += __shfl_xor(s, 8);
-                s += __shfl_xor(s, 4);
-                s += __shfl_xor(s, 2);
-                s += __shfl_xor(s, 1);
-                if (sub == 0 && tok < cnt) sp[g * kChunk + tok] = sl[u] >= 0 ? s : -INFINITY;
-            }
-        }
-    }
-    __syncthreads();
-
-    // 2. maximum and exponentials per query head of the group
-    float m[G], l[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        float mx = -INFINITY;
-        for (int t = lane; t < cnt; t += kWave) mx = fmaxf(mx, sp[g * kChunk + t]);
-#pragma unroll
-        for (int o = kWave / 2; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        float sum = 0.f;
-        for (int t = lane; t < cnt; t += kWave) {
-            const float e = mx == -INFINITY ? 0.f : expf(sp[g * kChunk + t] - mx);
-            sp[g * kChunk + t] = e;
-            sum += e;
-        }
-#pragma unroll
-        for (int o = kWave / 2; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-        m[g] = mx;
-        l[g] = sum;
-    }
-    __syncthreads();
-
-    // 3. weighted values
-    float acc[G][8];
+    u32x4 qw[G];
 #pragma unroll
     for (int g = 0; g < G; ++g)
+        qw[g] = load16<false>(reinterpret_cast<const uint8_t *>(
+            a.q + (static_cast<int64_t>(r) * a.num_q_heads + hq0 + g) * kHeadDim + sub * 8));
+
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[g][k] = 0.f;
-    for (int base = 0; base < cnt; base += kRowsPerPass * kUnroll) {
-        u32x4 vw[kUnroll];
-        int toks[kUnroll];
+    }
+
+    // 1. one pass: scores, running maximum, weights and weighted values
+    for (int base = 0; base < cnt; base += kRowsPerPass * U) {  // uniform trip count
+        u32x4 kw[U], vw[U];
+        bool ok[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int tok = base + u * kRowsPerPass + grp;
-            const int64_t slot = tok < cnt ? s_slot[tok] : -1;
-            toks[u] = slot >= 0 ? tok : -1;
-            vw[u] = slot >= 0 ? load16<true>(a.v_cache + slot * row_bytes + head_off) : u32x4{0, 0, 0, 0};
+            const int64_t sl = tok < cnt ? s_slot[tok] : -1;
+            ok[u] = sl >= 0;
+            kw[u] = ok[u] ? load16<true>(kb + sl * row_bytes) : u32x4{0, 0, 0, 0};
+            vw[u] = ok[u] ? load16<true>(vb + sl * row_bytes) : u32x4{0, 0, 0, 0};
         }
+        float sc[U][G];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            if (toks[u] < 0) continue;
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float p = sp[g * kChunk + toks[u]];
+                const float t = row_sum16(dot8(qw[g], kw[u])) * a.scale_log2;  // every lane
+                sc[u][g] = ok[u] ? t : -INFINITY;
+            }
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    acc[g][2 * k] += p * bf16_lo(vw[u][k]);
-                    acc[g][2 * k + 1] += p * bf16_hi(vw[u][k]);
-                }
+        for (int g = 0; g < G; ++g) {
+            float mx = sc[0][g];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
+            if (mx > m[g] + kRescaleLog2) {  // also when m is still -inf and a score is finite
+                const float alpha = __builtin_amdgcn_exp2f(m[g] - mx);
+                l[g] *= alpha;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[g][k] *= alpha;
+                m[g] = mx;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                vf[2 * k] = bf16_lo(vw[u][k]);
+                vf[2 * k + 1] = bf16_hi(vw[u][k]);
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float p = ok[u] ? __builtin_amdgcn_exp2f(sc[u][g] - m[g]) : 0.f;
+                l[g] += p;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[g][k] += p * vf[k];
             }
         }
     }
+
+    // 2. merge the four lane groups (cross-row shuffles), then store the chunk's partials
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int o = kLanesPerRow; o < kWave; o <<= 1) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            acc[g][k] += __shfl_xor(acc[g][k], 16);
-            acc[g][k] += __shfl_xor(acc[g][k], 32);
+        for (int g = 0; g < G; ++g) {
+            const float mo = __shfl_xor(m[g], o);
+            const float lo = __shfl_xor(l[g], o);
+            const float mm = fmaxf(m[g], mo);
+            const float ea = m[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[g] - mm);
+            const float eb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mm);
+            l[g] = l[g] * ea + lo * eb;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[g][k] = acc[g][k] * ea + __shfl_xor(acc[g][k], o) * eb;
+            m[g] = mm;
         }
+    }
     const int64_t part = (static_cast<int64_t>(r) * a.splits + c) * a.num_q_heads + hq0;
     if (grp == 0) {
 #pragma unroll
@@ -268,34 +297,61 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
     raise_flags(a.err_flag, flags);
 }
 
-// out[r][h][d] from the chunks of request r: sum_c e^(m_c - M) acc_c[d] / sum_c e^(m_c - M) l_c.
+// Sum or maximum over the workgroup's two waves, in every thread.
+__device__ __forceinline__ float block2_reduce(float v, bool is_max, float *s_red)
+{
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+        const float t = __shfl_xor(v, o);
+        v = is_max ? fmaxf(v, t) : v + t;
+    }
+    if ((threadIdx.x & (kWave - 1)) == 0) s_red[threadIdx.x / kWave] = v;
+    __syncthreads();
+    v = is_max ? fmaxf(s_red[0], s_red[1]) : s_red[0] + s_red[1];
+    __syncthreads();
+    return v;
+}
+
+// out[r][h][d] from the chunks of request r:
+//   sum_c 2^(m_c - M) acc_c[d] / sum_c 2^(m_c - M) l_c,  M = max of m_c over chunks with l_c > 0.
 // This launch covers every request whatever max_context is, so it reports a clamped length.
 __global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(DecodeArgs a)
 {
+    __shared__ float s_red[kHeadDim / kWave];
     const int32_t h = blockIdx.x, r = blockIdx.y, d = threadIdx.x;
     uint32_t flags = 0;
     const int32_t n = context_of(a, r, flags);
     if (h == 0 && d == 0) raise_flags(a.err_flag, flags);
     const int32_t chunks = (n + kChunk - 1) / kChunk;
     const int64_t base = static_cast<int64_t>(r) * a.splits * a.num_q_heads + h;
+    const float *ml = a.ws_ml + base * 2;
+    const int64_t step = static_cast<int64_t>(a.num_q_heads) * 2;
     float mx = -INFINITY;
-    for (int32_t c = 0; c < chunks; ++c) {
-        const int64_t i = base + static_cast<int64_t>(c) * a.num_q_heads;
-        if (a.ws_ml[i * 2 + 1] > 0.f) mx = fmaxf(mx, a.ws_ml[i * 2]);
+    for (int32_t c = d; c < chunks; c += kHeadDim)
+        if (ml[c * step + 1] > 0.f) mx = fmaxf(mx, ml[c * step]);
+    mx = block2_reduce(mx, true, s_red);
+    float den = 0.f;
+    for (int32_t c = d; c < chunks; c += kHeadDim) {
+        const float lc = ml[c * step + 1];
+        if (lc > 0.f) den += __builtin_amdgcn_exp2f(ml[c * step] - mx) * lc;
     }
-    float num = 0.f, den = 0.f;
+    den = block2_reduce(den, false, s_red);
+    float num = 0.f;
+    const float *acc = a.ws_acc + base * kHeadDim + d;
+    const int64_t acc_step = static_cast<int64_t>(a.num_q_heads) * kHeadDim;
+#pragma unroll 8
     for (int32_t c = 0; c < chunks; ++c) {
-        const int64_t i = base + static_cast<int64_t>(c) * a.num_q_heads;
-        const float lc = a.ws_ml[i * 2 + 1];
-        if (!(lc > 0.f)) continue;
-        const float e = expf(a.ws_ml[i * 2] - mx);
-        den += e * lc;
-        num += e * a.ws_acc[i * kHeadDim + d];
+        const float lc = ml[c * step + 1];
+        const float e = lc > 0.f ? __builtin_amdgcn_exp2f(ml[c * step] - mx) : 0.f;
+        num += e * acc[c * acc_step];
     }
     a.out[(static_cast<int64_t>(r) * a.num_q_heads + h) * kHeadDim + d] = den > 0.f ? num / den : 0.f;
 }
 
 int64_t splits_for(int32_t max_context) { return (static_cast<int64_t>(max_context) + kChunk - 1) / kChunk; }
+
+// Workspace granule: per 256 positions, so that the size does not depend on the chunk length.
+int64_t split_units(int32_t max_context) { return (static_cast<int64_t>(max_context) + kSplitUnit - 1) / kSplitUnit; }
 
 bool aligned_to(const void *p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
 
@@ -318,7 +374,7 @@ int64_t kvw_decode_workspace_size(int32_t num_reqs, int32_t max_context, int32_t
                                   int32_t head_dim)
 {
     if (num_reqs < 0 || max_context < 0 || num_q_heads < 0 || head_dim < 0) return -1;
-    return static_cast<int64_t>(num_reqs) * splits_for(max_context) * num_q_heads *
+    return static_cast<int64_t>(num_reqs) * split_units(max_context) * num_q_heads *
            (head_dim + 2) * static_cast<int64_t>(sizeof(float));
 }
 
@@ -396,13 +452,13 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
     a.range_stride = g.range_stride;
     a.num_q_heads = g.num_q_heads;
     a.num_kv_heads = g.num_kv_heads;
-    a.scale = g.scale;
+    a.scale_log2 = g.scale * kLog2e;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (a.splits > 0) {
         const dim3 grid(static_cast<unsigned>(a.splits), static_cast<unsigned>(g.num_reqs));
         const dim3 block(static_cast<unsigned>(g.num_kv_heads * kWave));
-        const size_t lds = static_cast<size_t>(g.num_q_heads) * kChunk * sizeof(float);
+        const size_t lds = 0;
         if (g.mode == KVW_SLOTS_PAGED) launch_partial<KVW_SLOTS_PAGED>(group, grid, block, lds, s, a);
         else launch_partial<KVW_SLOTS_RANGES>(group, grid, block, lds, s, a);
         const hipError_t e = hipGetLastError();

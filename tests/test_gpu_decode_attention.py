@@ -9,15 +9,21 @@ slot mapping's, plus KVW_FLAG_COUNT where a context length is clamped and
 KVW_FLAG_SLOT_OOB where a slot lies past the cache (such positions are skipped).
 
 Tolerance: the kernel works in fp32 (unit roundoff u = 2^-24) from exact bf16
-inputs.  To first order in u, with C the number of 256-position chunks, the
-output error is at most
-    u * max|V| * (2C + 100 + 40 * scale * |q| * max_j |k_j|)
-per (request, query head): 66u from the per-lane sums of p*v plus the shuffles,
-(C + 1)u and (C + 11)u from the chunk merge of numerator and denominator, a few
-u from expf, and twice the score error (each score is a 128-term fp32 dot product
-of scaled q and k, error <= 13u scale |q||k|, plus the rounding of s - max).
-The bound is written out in `tolerance` below.  Requests with no readable
-position must give exactly 0.
+inputs, in base-2 exponent units (scores s = log2(e) * scale * q.k).  Its
+summation structure: chunks of P = 1024 positions; in a chunk four lane groups
+each fold P/4 positions into a running (max m, sum l, weighted values acc),
+moving m only when it grows by more than 8, so a group rescales at most
+R = 1 + ceil(2S/8) times, S = log2(e) * scale * |q| * max_j |k_j| bounding |s|;
+the groups are merged in two steps and the C = ceil(n/P) chunks in a second
+launch.  To first order in u the output error is then at most
+    u * max|V| * (P/2 + 6R + 2C + 60 + 20S)
+per (request, query head): P/4 + R + C + 5 roundings along the numerator's
+longest chain and P/4 + R + C + 12 along the denominator's, 2u per base-2
+exponential (each p, and the R + 3 rescale factors a term can meet), and the
+score error (4 two-term dot steps, 4 row adds, the scale product and the
+subtraction of m: at most u(12S + 8) in log2 units, each weight moving by ln 2
+times that, twice).  The bound is written out in `tolerance` below.  Requests
+with no readable position must give exactly 0.
 
 The bound grows with the context, so at 128K a single dropped position would hide
 under it.  The "integers" inputs close that gap bit-exactly: with K = 0 every
@@ -39,7 +45,6 @@ pytestmark = pytest.mark.gpu
 
 U = 2.0 ** -24
 FLAG_COUNT, FLAG_BAD_BLOCK, FLAG_SLOT_OOB = 2, 4, 8
-CHUNK = 256
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -128,16 +133,24 @@ def place_caches(rows_total, rows, k, v):
     return kc, vc
 
 
-def tolerance(qh, kr, vr, n_chunks, scale):
+CHUNK_P = 1024        # positions per workgroup of the kernel
+RESCALE_LOG2 = 8.0    # growth of the running maximum that triggers a rescale
+
+
+def tolerance(qh, kr, vr, n, scale):
     """First-order fp32 error bound of one request's output (see the module docstring).
-    qh: [Hq][D] float; kr, vr: [n][Hkv][D] float (the request's readable rows)."""
+    qh: [Hq][D] float; kr, vr: [m][Hkv][D] float (the request's readable rows); n: its
+    context length."""
     hq, hkv = qh.shape[0], kr.shape[1]
     g = hq // hkv
     kmax = np.sqrt((kr.astype(np.float64) ** 2).sum(axis=2)).max(axis=0)  # [Hkv]
     vmax = np.abs(vr).max(axis=(0, 2)).astype(np.float64)                # [Hkv]
     qn = np.sqrt((qh.astype(np.float64) ** 2).sum(axis=1))               # [Hq]
     heads = np.arange(hq) // g
-    return U * vmax[heads] * (2 * n_chunks + 100 + 40 * abs(scale) * qn * kmax[heads])
+    big_s = np.log2(np.e) * abs(scale) * qn * kmax[heads]
+    rescales = 1 + np.ceil(2 * big_s / RESCALE_LOG2)
+    chunks = -(-int(n) // CHUNK_P)
+    return U * vmax[heads] * (CHUNK_P / 2 + 6 * rescales + 2 * chunks + 60 + 20 * big_s)
 
 
 def check(gpu, q, slots, rows, k, v, ctx_eff, sel, hq, hkv, scale, tag, exact=False):
@@ -173,7 +186,7 @@ def check(gpu, q, slots, rows, k, v, ctx_eff, sel, hq, hkv, scale, tag, exact=Fa
             bad = np.argwhere(g_sum != o_sum)
             assert len(bad) == 0, f"{tag}: request {r}: {len(bad)} sums differ, first {bad[:3]}"
             continue
-        tol = tolerance(f32(q[r]), f32(k[idx]), f32(v[idx]), -(-int(ctx_eff[r]) // CHUNK), scale)
+        tol = tolerance(f32(q[r]), f32(k[idx]), f32(v[idx]), ctx_eff[r], scale)
         err = np.abs(got.astype(np.float64) - want[i]).max(axis=1)
         worst = int(np.argmax(err / tol))
         assert (err <= tol).all(), (f"{tag}: request {r} head {worst}: error {err[worst]:.3e} "
