@@ -78,6 +78,9 @@ def parse():
                         "before every step; ms_per_step is then the fused call's event time")
     p.add_argument("--no-decode", action="store_true",
                    help="skip the decode-attention (read path) measurements")
+    p.add_argument("--decode-only", action="store_true",
+                   help="run only the decode-attention measurements (for profiling); prints\n"
+                        "their JSON object instead of the benchmark line")
     p.add_argument("--copy-calibration-mib", type=int, default=512,
                    help="size of the plain device copy timed as the practical ceiling "
                         "(read + write of this many MiB); 0 to skip")
@@ -102,6 +105,28 @@ def counter_traffic():
     return c.get("traffic_bytes_per_launch")
 
 
+def timed(fn, n_warm, n_steps):
+    """Wall ms per call over n_steps bare calls (between two synchronizations), then the
+    per-call HIP-event times of a second, instrumented pass of n_steps calls (the event
+    records cost the stream a few microseconds, so they stay out of the wall time)."""
+    import torch
+    for _ in range(n_warm):
+        fn(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_steps):
+        fn(None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_steps)]
+    torch.cuda.synchronize()
+    for i in range(n_steps):
+        fn(evs[i])
+    torch.cuda.synchronize()
+    return wall * 1e3 / n_steps, [a.elapsed_time(b) for a, b in evs]
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -123,6 +148,13 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload != "long_context":
         bench_config(args)
+        return
+    if args.decode_only:
+        def d_(a):
+            a = np.ascontiguousarray(a)
+            return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+        print(json.dumps(decode_attention(args, d_, dev, torch.cuda.current_stream(), timed)),
+              flush=True)
         return
 
     def d(a):
@@ -152,26 +184,6 @@ def main():
     fused_bytes = real_tokens * base.num_layers * 4 * bpt + real_tokens * 16
     # the scatter kernel alone: K and V rows read and written + slot read (8 B)
     scatter_bytes = real_tokens * base.num_layers * 4 * bpt + real_tokens * 8
-
-    def timed(fn, n_warm, n_steps):
-        """Wall ms per call over n_steps bare calls (between two synchronizations), then the
-        per-call HIP-event times of a second, instrumented pass of n_steps calls (the event
-        records cost the stream a few microseconds, so they stay out of the wall time)."""
-        for _ in range(n_warm):
-            fn(None)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(n_steps):
-            fn(None)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n_steps)]
-        torch.cuda.synchronize()
-        for i in range(n_steps):
-            fn(evs[i])
-        torch.cuda.synchronize()
-        return wall * 1e3 / n_steps, [a.elapsed_time(b) for a, b in evs]
 
     results = {}
     scatter = None
@@ -523,27 +535,35 @@ def decode_attention(args, d, dev, stream, timed):
                                range_len=d(w.range_len), range_cum=d(w.range_cum),
                                num_ranges=d(w.num_ranges))}
         for mode, mp in maps.items():
-            def call(ev, mp=mp):
-                if ev is not None:
-                    ev[0].record(stream)
-                kvw.kvw_decode_attention(q=qd, k_cache=kc, v_cache=vc, context_lens=cl,
-                                         max_context=max_ctx, num_blocks=w.num_blocks,
-                                         block_size=w.block_size, out=o, workspace=ws, **mp)
-                if ev is not None:
-                    ev[1].record(stream)
-            wall, ev_ms = timed(call, args.warmup, args.steps)
-            avg = statistics.fmean(ev_ms)
             nbytes = decode_bytes(w, ctx, hq, mode)
             key = f"{wname}_{mode}"
+            by_chunk = {}
+            for chunk in (0, 256, 512, 1024):  # 0: the library's own choice, reported first
+                def call(ev, mp=mp, chunk=chunk):
+                    if ev is not None:
+                        ev[0].record(stream)
+                    kvw.kvw_decode_attention(q=qd, k_cache=kc, v_cache=vc, context_lens=cl,
+                                             max_context=max_ctx, num_blocks=w.num_blocks,
+                                             block_size=w.block_size, out=o, workspace=ws,
+                                             chunk_positions=chunk, **mp)
+                    if ev is not None:
+                        ev[1].record(stream)
+                wall, ev_ms = timed(call, args.warmup, args.steps)
+                avg = statistics.fmean(ev_ms)
+                by_chunk[chunk] = (avg, wall)
+                log(f"[bench] decode attention {key:26s} chunk {chunk or 'auto':>4} "
+                    f"{avg * 1e3:8.1f} us = {nbytes / (avg * 1e-3) / 1e9:5.0f} GB/s "
+                    f"({100 * nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS:.1f}%)")
+                del call
+            avg, wall = by_chunk[0]
             out[key] = {"requests": w.num_reqs, "positions": int(ctx.sum()),
                         "max_context": max_ctx, "q_heads": hq, "kv_heads": w.num_kv_heads,
                         "block_size": w.block_size, "call_ms_avg": round(avg, 5),
                         "call_ms_wall": round(wall, 5), "algorithmic_bytes": nbytes,
                         "gbps": round(nbytes / (avg * 1e-3) / 1e9, 1),
-                        "frac_of_peak": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
-            log(f"[bench] decode attention {key:26s} {avg * 1e3:8.1f} us = "
-                f"{out[key]['gbps']:5.0f} GB/s ({100 * out[key]['frac_of_peak']:.1f}%)")
-            del call
+                        "frac_of_peak": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                        "call_ms_by_chunk": {str(c): round(v[0], 5) for c, v in by_chunk.items()
+                                             if c}}
         del kc, vc, ws
         torch.cuda.empty_cache()
     return out

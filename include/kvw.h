@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define KVW_ABI_VERSION 4
+#define KVW_ABI_VERSION 5
 #define KVW_PAD_ID (-1)
 /* Largest accepted range_stride (range descriptors per request). */
 #define KVW_MAX_RANGE_STRIDE 65536
@@ -333,9 +333,10 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream);
  * range descriptors); a position without a block (pad id) is skipped.  For
  * query head h and key/value head g = h / (num_q_heads / num_kv_heads):
  *   out[r][h] = sum_j softmax_j(scale * q[r][h] . K[slot_j][g]) * V[slot_j][g]
- * computed in fp32 from bf16 inputs; no position gives 0.  Each position's
- * slot is resolved once per 256-position chunk and staged in LDS for all
- * heads; chunks are combined in a second launch through `workspace`.
+ * computed in fp32 from bf16 inputs; no position gives 0.  Each workgroup
+ * takes a chunk of chunk_positions positions of one request, resolves their
+ * slots once into LDS for all heads and folds them into a running softmax;
+ * the chunks are combined in a second launch through `workspace`.
  *   q                  bf16 [num_reqs][num_q_heads][head_dim], 16-byte aligned
  *   context_lens       int32 [num_reqs] (device); clamped to [0, max_context]
  *                      with KVW_FLAG_COUNT
@@ -345,6 +346,8 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream);
  *                      (one layer, the K/V write's layout), 16-byte aligned
  *   out                fp32 [num_reqs][num_q_heads][head_dim]
  *   workspace          device memory of kvw_decode_workspace_size(...) bytes
+ *   chunk_positions    positions per workgroup: 256, 512 or 1024; 0 picks one from
+ *                      num_reqs and max_context (results differ only in rounding)
  * Supported: head_dim 128; num_kv_heads 1..16; num_q_heads <= 32;
  * num_q_heads / num_kv_heads in {1, 2, 4, 8}; else KVW_ERR_UNSUPPORTED.  Flags: KVW_FLAG_COUNT,
  * KVW_FLAG_BAD_BLOCK, KVW_FLAG_SLOT_OOB (slot past the cache: skipped).
@@ -375,6 +378,7 @@ typedef struct kvw_decode_args {
     void *workspace;
     int64_t workspace_bytes;
     int32_t *err_flag;
+    int32_t chunk_positions;           /* 256, 512, 1024, or 0 (chosen by the library) */
 } kvw_decode_args;
 
 /* Bytes of workspace kvw_decode_attention needs for these sizes. */

@@ -15,8 +15,8 @@
 // adds, the exponentials on v_exp_f32 in base 2, and the running maximum is
 // only moved when it grows by more than 2^8.
 //
-// decode_partial_kernel<MODE, G>: one workgroup per (1024-position chunk,
-// request), one wave per key/value head.
+// decode_partial_kernel<MODE, G>: one workgroup per (chunk of 256, 512 or 1024
+// positions, request), one wave per key/value head.
 //   0. The workgroup resolves the slots of its positions once, into LDS: the
 //      block-table gather (PAGED) or range arithmetic with the wavefront
 //      search over range_cum (RANGES).  Every head reads them from LDS.
@@ -26,8 +26,9 @@
 //      maximum m (log2 units), sum l and weighted values acc (online softmax).
 //   2. The four lane groups are merged with cross-row shuffles and the
 //      chunk's (m, l, acc) go to the workspace.
-// decode_combine_kernel: per (query head, request), one thread per head dim
-// merges the chunks with the rescaling by 2^(m_c - max m).
+// decode_combine_kernel<SLICES>: per (query head, request), one thread per
+// head dim and slice of the chunks (one slice, or four when a request can have
+// 64 chunks or more) merges the chunks with the rescaling by 2^(m_c - max m).
 
 #include <hip/hip_runtime.h>
 
@@ -42,8 +43,8 @@ using kvw_detail::fail;
 
 namespace {
 
-constexpr int kChunk = 1024;                         // positions per workgroup
-constexpr int kSplitUnit = 256;                      // workspace is sized per 256 positions
+constexpr int kMaxChunk = 1024;                      // positions per workgroup, at most
+constexpr int kMinChunk = 256;                       // ... and at least; the workspace is sized per 256
 constexpr int kHeadDim = 128;                        // supported head_dim
 constexpr int kLanesPerRow = kHeadDim / 8;           // 16 lanes x 8 bf16
 constexpr int kRowsPerPass = kWave / kLanesPerRow;   // 4 positions per wave load
@@ -78,6 +79,7 @@ struct DecodeArgs {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t splits;
+    int32_t chunk;      // positions per workgroup
     float scale_log2;  // scale * log2(e): scores in base-2 exponent units
 };
 
@@ -138,15 +140,15 @@ template <int MODE, int G>
 __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(DecodeArgs a)
 {
     constexpr int U = unroll_of<G>();
-    __shared__ int64_t s_slot[kChunk];
+    __shared__ int64_t s_slot[kMaxChunk];
     const int32_t r = blockIdx.y;
     const int32_t c = blockIdx.x;
     uint32_t flags = 0;
     const int32_t n = context_of(a, r, flags);  // a clamp is reported by the combine launch
     flags = 0;
-    const int64_t c0 = static_cast<int64_t>(c) * kChunk;
+    const int64_t c0 = static_cast<int64_t>(c) * a.chunk;
     if (c0 >= n) return;  // uniform over the workgroup: no barrier is skipped by part of it
-    const int32_t cnt = static_cast<int32_t>(n - c0 < kChunk ? n - c0 : kChunk);
+    const int32_t cnt = static_cast<int32_t>(n - c0 < a.chunk ? n - c0 : a.chunk);
     const int32_t bs = a.block_size;
 
     // 0. slots of this chunk's positions, resolved once for every head
@@ -297,8 +299,9 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
     raise_flags(a.err_flag, flags);
 }
 
-// Sum or maximum over the workgroup's two waves, in every thread.
-__device__ __forceinline__ float block2_reduce(float v, bool is_max, float *s_red)
+// Sum or maximum over the workgroup's waves, in every thread.
+template <int WAVES>
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float *s_red)
 {
 #pragma unroll
     for (int o = kWave / 2; o >= 1; o >>= 1) {
@@ -307,51 +310,76 @@ __device__ __forceinline__ float block2_reduce(float v, bool is_max, float *s_re
     }
     if ((threadIdx.x & (kWave - 1)) == 0) s_red[threadIdx.x / kWave] = v;
     __syncthreads();
-    v = is_max ? fmaxf(s_red[0], s_red[1]) : s_red[0] + s_red[1];
+    v = s_red[0];
+#pragma unroll
+    for (int i = 1; i < WAVES; ++i) v = is_max ? fmaxf(v, s_red[i]) : v + s_red[i];
     __syncthreads();
     return v;
 }
 
 // out[r][h][d] from the chunks of request r:
 //   sum_c 2^(m_c - M) acc_c[d] / sum_c 2^(m_c - M) l_c,  M = max of m_c over chunks with l_c > 0.
-// This launch covers every request whatever max_context is, so it reports a clamped length.
-__global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(DecodeArgs a)
+// Thread (slice, d) sums the numerator over chunks slice, slice + SLICES, ...; the
+// slices are added in LDS.  This launch covers every request whatever max_context
+// is, so it reports a clamped length.
+template <int SLICES>
+__global__ __launch_bounds__(kHeadDim * SLICES) void decode_combine_kernel(DecodeArgs a)
 {
-    __shared__ float s_red[kHeadDim / kWave];
-    const int32_t h = blockIdx.x, r = blockIdx.y, d = threadIdx.x;
+    constexpr int kThreads = kHeadDim * SLICES;
+    __shared__ float s_red[kThreads / kWave];
+    __shared__ float s_num[SLICES][kHeadDim];
+    const int32_t h = blockIdx.x, r = blockIdx.y;
+    const int tid = threadIdx.x, d = tid % kHeadDim, slice = tid / kHeadDim;
     uint32_t flags = 0;
     const int32_t n = context_of(a, r, flags);
-    if (h == 0 && d == 0) raise_flags(a.err_flag, flags);
-    const int32_t chunks = (n + kChunk - 1) / kChunk;
+    if (h == 0 && tid == 0) raise_flags(a.err_flag, flags);
+    const int32_t chunks = static_cast<int32_t>((static_cast<int64_t>(n) + a.chunk - 1) / a.chunk);
     const int64_t base = static_cast<int64_t>(r) * a.splits * a.num_q_heads + h;
     const float *ml = a.ws_ml + base * 2;
     const int64_t step = static_cast<int64_t>(a.num_q_heads) * 2;
     float mx = -INFINITY;
-    for (int32_t c = d; c < chunks; c += kHeadDim)
+    for (int32_t c = tid; c < chunks; c += kThreads)
         if (ml[c * step + 1] > 0.f) mx = fmaxf(mx, ml[c * step]);
-    mx = block2_reduce(mx, true, s_red);
+    mx = block_reduce<kThreads / kWave>(mx, true, s_red);
     float den = 0.f;
-    for (int32_t c = d; c < chunks; c += kHeadDim) {
+    for (int32_t c = tid; c < chunks; c += kThreads) {
         const float lc = ml[c * step + 1];
         if (lc > 0.f) den += __builtin_amdgcn_exp2f(ml[c * step] - mx) * lc;
     }
-    den = block2_reduce(den, false, s_red);
+    den = block_reduce<kThreads / kWave>(den, false, s_red);
     float num = 0.f;
     const float *acc = a.ws_acc + base * kHeadDim + d;
     const int64_t acc_step = static_cast<int64_t>(a.num_q_heads) * kHeadDim;
 #pragma unroll 8
-    for (int32_t c = 0; c < chunks; ++c) {
+    for (int32_t c = slice; c < chunks; c += SLICES) {
         const float lc = ml[c * step + 1];
         const float e = lc > 0.f ? __builtin_amdgcn_exp2f(ml[c * step] - mx) : 0.f;
         num += e * acc[c * acc_step];
     }
-    a.out[(static_cast<int64_t>(r) * a.num_q_heads + h) * kHeadDim + d] = den > 0.f ? num / den : 0.f;
+    if (SLICES > 1) {
+        s_num[slice][d] = num;
+        __syncthreads();
+    }
+    if (slice == 0) {
+#pragma unroll
+        for (int i = 1; i < SLICES; ++i) num += s_num[i][d];
+        a.out[(static_cast<int64_t>(r) * a.num_q_heads + h) * kHeadDim + d] = den > 0.f ? num / den : 0.f;
+    }
 }
 
-int64_t splits_for(int32_t max_context) { return (static_cast<int64_t>(max_context) + kChunk - 1) / kChunk; }
+int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
-// Workspace granule: per 256 positions, so that the size does not depend on the chunk length.
-int64_t split_units(int32_t max_context) { return (static_cast<int64_t>(max_context) + kSplitUnit - 1) / kSplitUnit; }
+// Positions per workgroup when the caller leaves it open: the longest chunk that
+// still gives at least 8 workgroups per compute unit (2048 on 256 CUs, four
+// rounds of the two that fit) when every request runs to max_context.  Longer
+// chunks mean fewer partials to merge; the bound keeps the last round of
+// workgroups a small part of the launch.
+int32_t auto_chunk(int32_t num_reqs, int32_t max_context)
+{
+    int32_t c = kMaxChunk;
+    while (c > kMinChunk && static_cast<int64_t>(num_reqs) * ceil_div(max_context, c) < 2048) c /= 2;
+    return c;
+}
 
 bool aligned_to(const void *p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
 
@@ -374,7 +402,7 @@ int64_t kvw_decode_workspace_size(int32_t num_reqs, int32_t max_context, int32_t
                                   int32_t head_dim)
 {
     if (num_reqs < 0 || max_context < 0 || num_q_heads < 0 || head_dim < 0) return -1;
-    return static_cast<int64_t>(num_reqs) * split_units(max_context) * num_q_heads *
+    return static_cast<int64_t>(num_reqs) * ceil_div(max_context, kMinChunk) * num_q_heads *
            (head_dim + 2) * static_cast<int64_t>(sizeof(float));
 }
 
@@ -400,6 +428,10 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
                     group);
     if (g.num_blocks > INT64_MAX / g.block_size / g.num_kv_heads / (kHeadDim * 2))
         return fail(KVW_ERR_INVALID_ARG, "%s: cache size overflows", fn);
+    if (g.chunk_positions != 0 && g.chunk_positions != 256 && g.chunk_positions != 512 &&
+        g.chunk_positions != 1024)
+        return fail(KVW_ERR_INVALID_ARG, "%s: chunk_positions %d is not 0, 256, 512 or 1024", fn,
+                    g.chunk_positions);
     if (g.err_flag && !aligned_to(g.err_flag, 4))
         return fail(KVW_ERR_INVALID_ARG, "%s: err_flag misaligned", fn);
     if (g.num_reqs == 0) return KVW_OK;
@@ -440,7 +472,8 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
     a.k_cache = static_cast<const uint8_t *>(g.k_cache);
     a.v_cache = static_cast<const uint8_t *>(g.v_cache);
     a.out = g.out;
-    a.splits = static_cast<int32_t>(splits_for(g.max_context));
+    a.chunk = g.chunk_positions ? g.chunk_positions : auto_chunk(g.num_reqs, g.max_context);
+    a.splits = static_cast<int32_t>(ceil_div(g.max_context, a.chunk));
     a.ws_acc = static_cast<float *>(g.workspace);
     a.ws_ml = a.ws_acc + static_cast<int64_t>(g.num_reqs) * a.splits * g.num_q_heads * kHeadDim;
     a.err_flag = g.err_flag;
@@ -464,9 +497,9 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(KVW_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     }
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(static_cast<unsigned>(g.num_q_heads),
-                                                   static_cast<unsigned>(g.num_reqs)),
-                       dim3(kHeadDim), 0, s, a);
+    const dim3 cgrid(static_cast<unsigned>(g.num_q_heads), static_cast<unsigned>(g.num_reqs));
+    if (a.splits >= 64) hipLaunchKernelGGL(decode_combine_kernel<4>, cgrid, dim3(kHeadDim * 4), 0, s, a);
+    else hipLaunchKernelGGL(decode_combine_kernel<1>, cgrid, dim3(kHeadDim), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(KVW_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KVW_OK;

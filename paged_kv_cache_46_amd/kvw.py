@@ -15,7 +15,7 @@ import torch
 
 from .build import LIBRARY
 
-KVW_ABI_VERSION = 4
+KVW_ABI_VERSION = 5
 KVW_PAD_ID = -1
 KVW_MAX_RANGE_STRIDE = 65536
 KVW_OK, KVW_ERR_INVALID_ARG, KVW_ERR_UNSUPPORTED, KVW_ERR_RANGE_CAP, KVW_ERR_HIP = range(5)
@@ -61,6 +61,7 @@ class kvw_decode_args(ctypes.Structure):
         ("k_cache", _P), ("v_cache", _P), ("num_blocks", _I64), ("num_q_heads", _I32),
         ("num_kv_heads", _I32), ("head_dim", _I32), ("scale", ctypes.c_float), ("out", _P),
         ("workspace", _P), ("workspace_bytes", _I64), ("err_flag", _P),
+        ("chunk_positions", _I32),
     ]
 
 
@@ -291,7 +292,8 @@ def kvw_decode_workspace_size(num_reqs, max_context, num_q_heads, head_dim=128) 
 def kvw_decode_attention(*, mode, q, k_cache, v_cache, context_lens, max_context, num_blocks,
                          block_size, out, block_table=None, num_blocks_per_req=None,
                          range_start=None, range_len=None, range_cum=None, num_ranges=None,
-                         scale=None, workspace=None, err_flag=None, stream=None):
+                         scale=None, workspace=None, err_flag=None, stream=None,
+                         chunk_positions=0):
     """Decode attention over the paged cache (see include/kvw.h).
 
     q: [num_reqs, num_q_heads, head_dim] 2-byte (bf16) tensor; k_cache, v_cache:
@@ -335,4 +337,5 @@ def kvw_decode_attention(*, mode, q, k_cache, v_cache, context_lens, max_context
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.err_flag = _dev(err_flag, torch.int32, "err_flag", optional=True)
+    a.chunk_positions = int(chunk_positions)
     _check(library().kvw_decode_attention(ctypes.byref(a), _stream(stream)))

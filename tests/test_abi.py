@@ -245,4 +245,6 @@ def test_decode_validation(lib):
     assert f(ctypes.byref(_decode(workspace_bytes=4 * 4 * 32 * 130 * 4 - 1)), None) == INVALID
     assert "workspace" in _err(lib)
     assert f(ctypes.byref(_decode(workspace=None)), None) == INVALID
+    assert f(ctypes.byref(_decode(chunk_positions=128)), None) == INVALID
+    assert f(ctypes.byref(_decode(chunk_positions=768)), None) == INVALID
     assert f(ctypes.byref(_decode(num_reqs=0)), None) == OK   # nothing to do: no launch

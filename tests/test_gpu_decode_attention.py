@@ -10,13 +10,15 @@ KVW_FLAG_SLOT_OOB where a slot lies past the cache (such positions are skipped).
 
 Tolerance: the kernel works in fp32 (unit roundoff u = 2^-24) from exact bf16
 inputs, in base-2 exponent units (scores s = log2(e) * scale * q.k).  Its
-summation structure: chunks of P = 1024 positions; in a chunk four lane groups
-each fold P/4 positions into a running (max m, sum l, weighted values acc),
+summation structure: chunks of P = 256, 512 or 1024 positions; in a chunk four lane
+groups each fold P/4 positions into a running (max m, sum l, weighted values acc),
 moving m only when it grows by more than 8, so a group rescales at most
 R = 1 + ceil(2S/8) times, S = log2(e) * scale * |q| * max_j |k_j| bounding |s|;
 the groups are merged in two steps and the C = ceil(n/P) chunks in a second
 launch.  To first order in u the output error is then at most
-    u * max|V| * (P/2 + 6R + 2C + 60 + 20S)
+    u * max|V| * (P/2 + 6R + 2C + 60 + 20S),
+taken at P = 1024 for the first term and P = 256 for C, so that it holds for
+every chunk length:
 per (request, query head): P/4 + R + C + 5 roundings along the numerator's
 longest chain and P/4 + R + C + 12 along the denominator's, 2u per base-2
 exponential (each p, and the R + 3 rescale factors a term can meet), and the
@@ -103,14 +105,15 @@ def expected_slots(lay: Layout, mode: str, ctx: np.ndarray):
     return [slots[qsl[r]:qsl[r + 1]] for r in range(num_reqs)], flags
 
 
-def run_gpu(mode, lay: Layout, q, ctx_given, max_context, kc, vc, scale=None, num_reqs=None):
+def run_gpu(mode, lay: Layout, q, ctx_given, max_context, kc, vc, scale=None, num_reqs=None,
+            chunk=0):
     num_reqs = q.shape[0] if num_reqs is None else num_reqs
     out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV)
     flag = new_flag()
     common = dict(q=dev(q), k_cache=kc, v_cache=vc, context_lens=dev(np.asarray(ctx_given,
                                                                               np.int32)),
                   max_context=max_context, num_blocks=lay.num_blocks, block_size=lay.bs, out=out,
-                  scale=scale, err_flag=flag)
+                  scale=scale, err_flag=flag, chunk_positions=chunk)
     if mode == "paged":
         kvw.kvw_decode_attention(mode=kvw.KVW_SLOTS_PAGED, block_table=dev(lay.table),
                                  num_blocks_per_req=dev(lay.nbpr), **common)
@@ -133,7 +136,7 @@ def place_caches(rows_total, rows, k, v):
     return kc, vc
 
 
-CHUNK_P = 1024        # positions per workgroup of the kernel
+CHUNK_MAX, CHUNK_MIN = 1024, 256   # positions per workgroup of the kernel
 RESCALE_LOG2 = 8.0    # growth of the running maximum that triggers a rescale
 
 
@@ -149,8 +152,8 @@ def tolerance(qh, kr, vr, n, scale):
     heads = np.arange(hq) // g
     big_s = np.log2(np.e) * abs(scale) * qn * kmax[heads]
     rescales = 1 + np.ceil(2 * big_s / RESCALE_LOG2)
-    chunks = -(-int(n) // CHUNK_P)
-    return U * vmax[heads] * (CHUNK_P / 2 + 6 * rescales + 2 * chunks + 60 + 20 * big_s)
+    chunks = -(-int(n) // CHUNK_MIN)
+    return U * vmax[heads] * (CHUNK_MAX / 2 + 6 * rescales + 2 * chunks + 60 + 20 * big_s)
 
 
 def check(gpu, q, slots, rows, k, v, ctx_eff, sel, hq, hkv, scale, tag, exact=False):
@@ -196,7 +199,7 @@ def check(gpu, q, slots, rows, k, v, ctx_eff, sel, hq, hkv, scale, tag, exact=Fa
 
 
 def parity(w, mode, hq, seed, lay=None, ctx_given=None, max_context=None, scale=None, sel=None,
-           draw_rows=None, kind="normal"):
+           draw_rows=None, kind="normal", chunk=0):
     """Decode over layout `lay` (default: w's) with fresh q/K/V; check outputs and flags."""
     lay = lay or Layout(w)
     hkv = w.num_kv_heads
@@ -219,9 +222,9 @@ def parity(w, mode, hq, seed, lay=None, ctx_given=None, max_context=None, scale=
     scale = float(scale if scale is not None else w.head_dim ** -0.5)
     say(f"[decode] {w.name} {mode} Hq {hq} Hkv {hkv} bs {lay.bs} reqs {w.num_reqs} "
         f"max_context {max_context} checked {len(sel)} rows {len(rows)} scale {scale:.4f} "
-        f"inputs {kind}")
+        f"inputs {kind} chunk {chunk or 'auto'}")
     kc, vc = place_caches(lay.rows, rows, k, v)
-    gpu, gflag = run_gpu(mode, lay, q, ctx_given, max_context, kc, vc, scale=scale)
+    gpu, gflag = run_gpu(mode, lay, q, ctx_given, max_context, kc, vc, scale=scale, chunk=chunk)
     assert gflag == flags | count_flag, f"flags {gflag} != {flags | count_flag}"
     check(gpu, q, slots, rows, k, v, ctx_eff, sel, hq, hkv, scale, f"{w.name}/{mode}",
           exact=kind == "integers")
@@ -266,6 +269,17 @@ def test_decode_small(case, mode):
     w, hq = case
     parity(w, mode, hq, seed=100 + len(w.name))
     parity(w, mode, hq, seed=200 + len(w.name), kind="integers")
+
+
+@pytest.mark.parametrize("chunk", [256, 512, 1024])
+@pytest.mark.parametrize("mode", ["paged", "ranges"])
+def test_decode_chunk_lengths(mode, chunk):
+    """Every chunk length the kernel takes, on contexts around its multiples."""
+    w, hq = SMALL[0]
+    parity(w, mode, hq, seed=20 + chunk, chunk=chunk)
+    parity(w, mode, hq, seed=21 + chunk, chunk=chunk, kind="integers")
+    w, hq = SMALL[2]
+    parity(w, mode, hq, seed=22 + chunk, chunk=chunk)
 
 
 def test_decode_scale_and_longer_max_context():
