@@ -417,3 +417,85 @@ def test_decode_long_context_full(r):
     w = long_context(r)
     full_size(w, Layout(w), 32, sel=[3 + r % 11], seed=12)
     full_size(w, Layout(w), 32, sel=[9 + r % 5], seed=14, kind="integers")
+
+
+# ---------------------------------------------------------------------------
+# graph capture: launch shapes depend only on num_reqs, max_context and strides
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["paged", "ranges"])
+def test_decode_graph_replay(mode):
+    """Captured once at a padded request count and max_context, replayed with three batches of
+    other lengths, layouts and queries (inputs refilled eagerly between replays).  Every replay
+    equals an eager call bit for bit, and the oracle within the bound."""
+    reqs, max_ctx, pool, bs, hkv, hq, stride, rstride = 10, 3000, 2400, 16, 8, 32, 188, 8
+
+    def batch(seed):
+        rng = np.random.Generator(np.random.PCG64([seed, 3]))
+        n = int(rng.integers(5, reqs + 1))
+        return _dec(f"graph_{seed}", seed, rng.integers(1, max_ctx + 1, n), bs, ("count", 1, 5),
+                    hkv, pool, dummies=reqs - n, table_stride=stride, range_stride=rstride)
+
+    batches = [batch(4900 + i) for i in range(3)]
+    rows = pool * bs
+    q_s = torch.empty((reqs, hq, 128), dtype=torch.int16, device=DEV)
+    ctx_s = torch.empty(reqs, dtype=torch.int32, device=DEV)
+    maps = {"block_table": torch.empty((reqs, stride), dtype=torch.int32, device=DEV),
+            "num_blocks_per_req": torch.empty(reqs, dtype=torch.int32, device=DEV),
+            "range_start": torch.empty((reqs, rstride), dtype=torch.int32, device=DEV),
+            "range_len": torch.empty((reqs, rstride), dtype=torch.int32, device=DEV),
+            "range_cum": torch.empty((reqs, rstride), dtype=torch.int32, device=DEV),
+            "num_ranges": torch.empty(reqs, dtype=torch.int32, device=DEV)}
+    kc = torch.empty((rows, hkv, 128), dtype=torch.int16, device=DEV)
+    vc = torch.empty_like(kc)
+    out = torch.empty((reqs, hq, 128), dtype=torch.float32, device=DEV)
+    out_eager = torch.empty_like(out)
+    ws = torch.empty(kvw.kvw_decode_workspace_size(reqs, max_ctx, hq), dtype=torch.uint8,
+                     device=DEV)
+    flag = new_flag()
+    used = (("block_table", "num_blocks_per_req") if mode == "paged" else
+            ("range_start", "range_len", "range_cum", "num_ranges"))
+    kind = kvw.KVW_SLOTS_PAGED if mode == "paged" else kvw.KVW_SLOTS_RANGES
+
+    def call(o):
+        kvw.kvw_decode_attention(mode=kind, q=q_s, k_cache=kc, v_cache=vc, context_lens=ctx_s,
+                                 max_context=max_ctx, num_blocks=pool, block_size=bs, out=o,
+                                 workspace=ws, err_flag=flag, **{k: maps[k] for k in used})
+
+    def load(w, seed):
+        q, ctx, _, k, v = decode_inputs(w, hq, seed, rows=np.arange(rows, dtype=np.int64))
+        q_s.copy_(dev(q))
+        ctx_s.copy_(dev(ctx))
+        kc.copy_(dev(k))
+        vc.copy_(dev(v))
+        for name in used:
+            maps[name].copy_(dev(getattr(w, name)))
+        flag.zero_()
+        return q, ctx, k, v
+
+    load(batches[0], 1)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(out)
+    torch.cuda.synchronize()
+
+    for rep, w in enumerate(batches + batches[:1]):
+        say(f"[decode graph] {mode} replay {rep}: {w.describe()}")
+        q, ctx, k, v = load(w, 10 + rep)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host(out)
+        assert int(flag.item()) == 0
+        call(out_eager)
+        torch.cuda.synchronize()
+        assert np.array_equal(got, host(out_eager)), "replay differs from the eager call"
+        slots, _ = expected_slots(Layout(w), mode, ctx.astype(np.int64))
+        check(got, q, slots, np.arange(rows, dtype=np.int64), k, v, ctx, list(range(reqs)), hq,
+              hkv, 128 ** -0.5, f"graph {mode} replay {rep}")
