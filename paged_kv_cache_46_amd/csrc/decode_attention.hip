@@ -26,6 +26,12 @@
 //      maximum m (log2 units), sum l and weighted values acc (online softmax).
 //   2. The four lane groups are merged with cross-row shuffles and the
 //      chunk's (m, l, acc) go to the workspace.
+// decode_plan_kernel: for batches of 32 requests or more, one workgroup lists
+// the (request, chunk) pairs that hold positions: every full chunk first, then
+// the requests' last, partial chunks from the longest down (16 length
+// classes), so that the short ones fill the last round of workgroups.  The
+// partial kernel then takes its pair from the list.  The order decides only
+// the schedule: each pair has its own place in the workspace.
 // decode_combine_kernel<SLICES>: per (query head, request), one thread per
 // head dim and slice of the chunks (one slice, or four when a request can have
 // 64 chunks or more) merges the chunks with the rescaling by 2^(m_c - max m).
@@ -45,6 +51,9 @@ namespace {
 
 constexpr int kMaxChunk = 1024;                      // positions per workgroup, at most
 constexpr int kMinChunk = 256;                       // ... and at least; the workspace is sized per 256
+constexpr int kPlanThreads = 1024;                   // the plan kernel's one workgroup
+constexpr int kTailClasses = 16;                     // length classes of the partial chunks
+constexpr int32_t kPlanMinReqs = 32;                 // batches this large get a work list
 constexpr int kHeadDim = 128;                        // supported head_dim
 constexpr int kLanesPerRow = kHeadDim / 8;           // 16 lanes x 8 bf16
 constexpr int kRowsPerPass = kWave / kLanesPerRow;   // 4 positions per wave load
@@ -69,6 +78,8 @@ struct DecodeArgs {
     float *out;
     float *ws_acc;  // [num_reqs][splits][num_q_heads][head_dim]
     float *ws_ml;   // [num_reqs][splits][num_q_heads][2]: chunk max (log2 units), chunk sum
+    int2 *units;         // work list (request, chunk), or NULL: the grid is (chunk, request)
+    int32_t *unit_count; // entries of the work list
     int32_t *err_flag;
     int64_t cache_rows;
     int32_t num_reqs;
@@ -141,8 +152,16 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
 {
     constexpr int U = unroll_of<G>();
     __shared__ int64_t s_slot[kMaxChunk];
-    const int32_t r = blockIdx.y;
-    const int32_t c = blockIdx.x;
+    int32_t r, c;
+    if (a.units) {
+        if (static_cast<int32_t>(blockIdx.x) >= *a.unit_count) return;  // uniform
+        const int2 rc = a.units[blockIdx.x];
+        r = rc.x;
+        c = rc.y;
+    } else {
+        r = blockIdx.y;
+        c = blockIdx.x;
+    }
     uint32_t flags = 0;
     const int32_t n = context_of(a, r, flags);  // a clamp is reported by the combine launch
     flags = 0;
@@ -299,6 +318,47 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
     raise_flags(a.err_flag, flags);
 }
 
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
+{
+    __shared__ int32_t s_full, s_full_cur, s_total;
+    __shared__ int32_t s_cls[kTailClasses], s_base[kTailClasses], s_cur[kTailClasses];
+    const int tid = threadIdx.x;
+    if (tid == 0) { s_full = 0; s_full_cur = 0; }
+    if (tid < kTailClasses) { s_cls[tid] = 0; s_cur[tid] = 0; }
+    __syncthreads();
+    for (int32_t r = tid; r < a.num_reqs; r += kPlanThreads) {
+        uint32_t unused = 0;
+        const int32_t n = context_of(a, r, unused);  // clamps are reported by the combine launch
+        const int32_t nf = n / a.chunk, rem = n % a.chunk;
+        if (nf) atomicAdd(&s_full, nf);
+        if (rem) atomicAdd(&s_cls[(rem - 1) * kTailClasses / a.chunk], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int32_t base = s_full;
+        for (int k = kTailClasses - 1; k >= 0; --k) {
+            s_base[k] = base;
+            base += s_cls[k];
+        }
+        s_total = base;
+    }
+    __syncthreads();
+    for (int32_t r = tid; r < a.num_reqs; r += kPlanThreads) {
+        uint32_t unused = 0;
+        const int32_t n = context_of(a, r, unused);
+        const int32_t nf = n / a.chunk, rem = n % a.chunk;
+        if (nf) {
+            const int32_t at = atomicAdd(&s_full_cur, nf);
+            for (int32_t i = 0; i < nf; ++i) a.units[at + i] = make_int2(r, i);
+        }
+        if (rem) {
+            const int k = (rem - 1) * kTailClasses / a.chunk;
+            a.units[s_base[k] + atomicAdd(&s_cur[k], 1)] = make_int2(r, nf);
+        }
+    }
+    if (tid == 0) *a.unit_count = s_total;
+}
+
 // Sum or maximum over the workgroup's waves, in every thread.
 template <int WAVES>
 __device__ __forceinline__ float block_reduce(float v, bool is_max, float *s_red)
@@ -402,8 +462,11 @@ int64_t kvw_decode_workspace_size(int32_t num_reqs, int32_t max_context, int32_t
                                   int32_t head_dim)
 {
     if (num_reqs < 0 || max_context < 0 || num_q_heads < 0 || head_dim < 0) return -1;
-    return static_cast<int64_t>(num_reqs) * ceil_div(max_context, kMinChunk) * num_q_heads *
-           (head_dim + 2) * static_cast<int64_t>(sizeof(float));
+    // chunk partials (head_dim sums, max, sum per query head) and one work-list entry per chunk,
+    // counted per 256 positions so that every chunk length fits; then the list's length
+    return static_cast<int64_t>(num_reqs) * ceil_div(max_context, kMinChunk) *
+               (static_cast<int64_t>(num_q_heads) * (head_dim + 2) * sizeof(float) + sizeof(int2)) +
+           16;
 }
 
 size_t kvw_decode_args_size(void) { return sizeof(kvw_decode_args); }
@@ -476,6 +539,11 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
     a.splits = static_cast<int32_t>(ceil_div(g.max_context, a.chunk));
     a.ws_acc = static_cast<float *>(g.workspace);
     a.ws_ml = a.ws_acc + static_cast<int64_t>(g.num_reqs) * a.splits * g.num_q_heads * kHeadDim;
+    const int64_t units = static_cast<int64_t>(g.num_reqs) * a.splits;
+    const bool plan = g.num_reqs >= kPlanMinReqs && units <= INT32_MAX;
+    // the list follows the partials: an 8-byte aligned offset (two floats per entry above)
+    a.units = plan ? reinterpret_cast<int2 *>(a.ws_ml + units * g.num_q_heads * 2) : nullptr;
+    a.unit_count = plan ? reinterpret_cast<int32_t *>(a.units + units) : nullptr;
     a.err_flag = g.err_flag;
     a.cache_rows = g.num_blocks * g.block_size;
     a.num_reqs = g.num_reqs;
@@ -489,7 +557,9 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (a.splits > 0) {
-        const dim3 grid(static_cast<unsigned>(a.splits), static_cast<unsigned>(g.num_reqs));
+        if (plan) hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+        const dim3 grid = plan ? dim3(static_cast<unsigned>(units))
+                               : dim3(static_cast<unsigned>(a.splits), static_cast<unsigned>(g.num_reqs));
         const dim3 block(static_cast<unsigned>(g.num_kv_heads * kWave));
         const size_t lds = 0;
         if (g.mode == KVW_SLOTS_PAGED) launch_partial<KVW_SLOTS_PAGED>(group, grid, block, lds, s, a);

@@ -211,11 +211,12 @@ def _decode(**kw):
 def test_decode_workspace_size(lib):
     ws = lib.kvw_decode_workspace_size
     ws.restype = ctypes.c_int64
-    # per request, per 256-position chunk and query head: 128 sums, the chunk max and sum
-    assert ws(4, 1000, 32, 128) == 4 * 4 * 32 * 130 * 4
-    assert ws(4, 1024, 32, 128) == 4 * 4 * 32 * 130 * 4
-    assert ws(4, 1025, 32, 128) == 4 * 5 * 32 * 130 * 4
-    assert ws(4, 0, 32, 128) == 0
+    # per request and 256 positions: per query head 128 sums, the chunk max and sum (fp32), and
+    # one 8-byte work-list entry; then 16 bytes for the list's length
+    assert ws(4, 1000, 32, 128) == 4 * 4 * (32 * 130 * 4 + 8) + 16
+    assert ws(4, 1024, 32, 128) == 4 * 4 * (32 * 130 * 4 + 8) + 16
+    assert ws(4, 1025, 32, 128) == 4 * 5 * (32 * 130 * 4 + 8) + 16
+    assert ws(4, 0, 32, 128) == 16
     assert ws(-1, 10, 32, 128) == -1
 
 
@@ -242,7 +243,7 @@ def test_decode_validation(lib):
     assert f(ctypes.byref(_decode(mode=kvw.KVW_SLOTS_RANGES, range_cum=None)), None) == INVALID
     assert f(ctypes.byref(_decode(mode=kvw.KVW_SLOTS_RANGES, range_stride=1 << 20)),
              None) == RANGE_CAP
-    assert f(ctypes.byref(_decode(workspace_bytes=4 * 4 * 32 * 130 * 4 - 1)), None) == INVALID
+    assert f(ctypes.byref(_decode(workspace_bytes=4 * 4 * (32 * 130 * 4 + 8) + 15)), None) == INVALID
     assert "workspace" in _err(lib)
     assert f(ctypes.byref(_decode(workspace=None)), None) == INVALID
     assert f(ctypes.byref(_decode(chunk_positions=128)), None) == INVALID

@@ -257,10 +257,14 @@ def small_decodes():
         # block size 1: a chunk's 256 positions fall in 256 different runs
         (_dec("bs1_many_runs", 8, [600, 1100, 5], 1, ("len", 1, 1), 4, 2000,
               range_stride=1200), 16),
+        # 40 requests (a work list orders the chunks): empty ones, exact chunk multiples, tails
+        (_dec("plan_40_reqs", 9, list(rng.integers(0, 2200, 34)) + [0, 256, 512, 1024, 2048, 1],
+              16, ("count", 1, 4), 8, 6000, dummies=3), 32),
     ]
 
 
 SMALL = small_decodes()
+PLAN_CASE = SMALL[-1]
 
 
 @pytest.mark.parametrize("mode", ["paged", "ranges"])
@@ -280,6 +284,9 @@ def test_decode_chunk_lengths(mode, chunk):
     parity(w, mode, hq, seed=21 + chunk, chunk=chunk, kind="integers")
     w, hq = SMALL[2]
     parity(w, mode, hq, seed=22 + chunk, chunk=chunk)
+    w, hq = PLAN_CASE
+    parity(w, mode, hq, seed=23 + chunk, chunk=chunk)
+    parity(w, mode, hq, seed=24 + chunk, chunk=chunk, kind="integers")
 
 
 def test_decode_scale_and_longer_max_context():
@@ -289,14 +296,15 @@ def test_decode_scale_and_longer_max_context():
         parity(w, mode, hq, seed=4, scale=1.0)
 
 
+@pytest.mark.parametrize("case", [0, -1], ids=["direct", "work_list"])
 @pytest.mark.parametrize("mode", ["paged", "ranges"])
-def test_decode_context_clamped(mode):
+def test_decode_context_clamped(mode, case):
     """Lengths above max_context or negative are clamped (KVW_FLAG_COUNT)."""
-    w, hq = SMALL[0]
-    ctx = np.array([rq.end for rq in w.requests] + [0, 0], np.int64)
+    w, hq = SMALL[case]
+    ctx = np.array([rq.end for rq in w.requests] + [0] * (w.num_reqs - len(w.requests)), np.int64)
     ctx[3] = 99999          # past max_context: clamped to it
-    ctx[8] = -7             # negative: no position, output 0
-    ctx[9] = 300            # a dummy request with no blocks: every position is unmapped
+    ctx[len(w.requests) - 1] = -7   # negative: no position, output 0
+    ctx[len(w.requests)] = 300      # a dummy request with no blocks: every position is unmapped
     parity(w, mode, hq, seed=5, ctx_given=ctx, max_context=2000)
 
 
