@@ -55,11 +55,13 @@ constexpr int kPlanThreads = 1024;                   // the plan kernel's one wo
 constexpr int kTailClasses = 16;                     // length classes of the partial chunks
 constexpr int32_t kPlanMinReqs = 32;                 // batches this large get a work list
 constexpr int kHeadDim = 128;                        // supported head_dim
-constexpr int kLanesPerRow = kHeadDim / 8;           // 16 lanes x 8 bf16
-constexpr int kRowsPerPass = kWave / kLanesPerRow;   // 4 positions per wave load
+constexpr int kRowLanes = 16;                        // lanes per position row of one head (8 was
+                                                     // slower: fewer instructions, fewer waves)
 constexpr int kMaxKvHeads = 16;
 constexpr int kMaxQHeads = 32;
 constexpr float kRescaleLog2 = 8.f;                  // move the running max past this growth
+constexpr float kNoMax = -1e30f;                     // running max before any position: finite, so
+                                                     // a masked score's weight 2^(-inf - m) is 0
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -105,30 +107,30 @@ __device__ __forceinline__ int32_t context_of(const DecodeArgs &a, int32_t r, ui
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// x + the same register of another lane of its 16-lane row, picked by a DPP control.
+// x + the same register of another lane of its row, picked by a DPP control.
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float x)
 {
     return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 16 lanes of a row, left in every lane: pair swap, quad swap,
-// then the mirrors inside each half row and inside the row.
-__device__ __forceinline__ float row_sum16(float x)
+// Sum over the L lanes of a row (L = 8 or 16), left in every lane: pair swap,
+// quad swap, the mirror inside each half row, then (L = 16) inside the row.
+template <int L>
+__device__ __forceinline__ float row_sum(float x)
 {
-    x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
-    x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
-    x = dpp_add<0x141>(x);  // row_half_mirror
-    x = dpp_add<0x140>(x);  // row_mirror
+    x = dpp_add<0xB1>(x);                   // quad_perm [1,0,3,2]
+    x = dpp_add<0x4E>(x);                   // quad_perm [2,3,0,1]
+    x = dpp_add<0x141>(x);                  // row_half_mirror
+    if (L == 16) x = dpp_add<0x140>(x);     // row_mirror
     return x;
 }
 
-// q . k over one lane's 8 head dims, from the bf16 pairs.  Each vector element is
+// s + q . k over 8 head dims, from the bf16 pairs.  Each vector element is
 // copied to a scalar before the bit cast: a bit cast applied to the element
 // expression itself reads the vector's first element.
-__device__ __forceinline__ float dot8(const u32x4 &q, const u32x4 &k)
+__device__ __forceinline__ float dot8(const u32x4 &q, const u32x4 &k, float s)
 {
-    float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t qi = q[i], ki = k[i];
@@ -138,19 +140,26 @@ __device__ __forceinline__ float dot8(const u32x4 &q, const u32x4 &k)
     return s;
 }
 
-// Positions in flight per lane group, per query-head grouping (register budget).
-template <int G>
-constexpr int unroll_of() { return G <= 2 ? 8 : (G == 4 ? 4 : 2); }
+// Positions in flight per lane group, per query-head grouping and row width
+// (register budget): with 8 lanes per row a lane holds twice the dims.
+template <int G, int L>
+constexpr int unroll_of()
+{
+    return L == 16 ? (G <= 2 ? 8 : (G == 4 ? 4 : 2)) : (G <= 2 ? 4 : (G == 4 ? 2 : 1));
+}
 
 // Threads per workgroup: one wave per key/value head, at most 16 and at most
 // 32 / G (the query heads the score tiles cover).
 template <int G>
 constexpr int partial_threads() { return kWave * (G <= 2 ? kMaxKvHeads : kMaxQHeads / G); }
 
-template <int MODE, int G>
+template <int MODE, int G, int L>
 __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(DecodeArgs a)
 {
-    constexpr int U = unroll_of<G>();
+    constexpr int U = unroll_of<G, L>();
+    constexpr int NV = kHeadDim / (L * 8);   // 16-byte pieces of a row per lane (1 or 2)
+    constexpr int DPL = NV * 8;              // head dims per lane
+    constexpr int RPP = kWave / L;           // positions per wave load
     __shared__ int64_t s_slot[kMaxChunk];
     int32_t r, c;
     if (a.units) {
@@ -209,47 +218,55 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;       // key/value head of this wave
-    const int sub = lane % kLanesPerRow;     // which 8 head dims
-    const int grp = lane / kLanesPerRow;     // which of the four positions of a wave load
+    const int sub = lane % L;                // which DPL head dims
+    const int grp = lane / L;                // which of the RPP positions of a wave load
     const int hq0 = w * G;                   // first query head of the group
     const int64_t row_bytes = static_cast<int64_t>(a.num_kv_heads) * kHeadDim * 2;
-    const int64_t head_off = static_cast<int64_t>(w) * kHeadDim * 2 + sub * 16;
+    const int64_t head_off = static_cast<int64_t>(w) * kHeadDim * 2 + sub * DPL * 2;
     const uint8_t *kb = a.k_cache + head_off;
     const uint8_t *vb = a.v_cache + head_off;
 
-    u32x4 qw[G];
+    u32x4 qw[G][NV];
 #pragma unroll
     for (int g = 0; g < G; ++g)
-        qw[g] = load16<false>(reinterpret_cast<const uint8_t *>(
-            a.q + (static_cast<int64_t>(r) * a.num_q_heads + hq0 + g) * kHeadDim + sub * 8));
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+            qw[g][j] = load16<false>(reinterpret_cast<const uint8_t *>(
+                a.q + (static_cast<int64_t>(r) * a.num_q_heads + hq0 + g) * kHeadDim + sub * DPL + 8 * j));
 
-    float m[G], l[G], acc[G][8];
+    float m[G], l[G], acc[G][DPL];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        m[g] = -INFINITY;
+        m[g] = kNoMax;
         l[g] = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) acc[g][k] = 0.f;
+        for (int k = 0; k < DPL; ++k) acc[g][k] = 0.f;
     }
 
     // 1. one pass: scores, running maximum, weights and weighted values
-    for (int base = 0; base < cnt; base += kRowsPerPass * U) {  // uniform trip count
-        u32x4 kw[U], vw[U];
+    for (int base = 0; base < cnt; base += RPP * U) {  // uniform trip count
+        u32x4 kw[U][NV], vw[U][NV];
         bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int tok = base + u * kRowsPerPass + grp;
+            const int tok = base + u * RPP + grp;
             const int64_t sl = tok < cnt ? s_slot[tok] : -1;
             ok[u] = sl >= 0;
-            kw[u] = ok[u] ? load16<true>(kb + sl * row_bytes) : u32x4{0, 0, 0, 0};
-            vw[u] = ok[u] ? load16<true>(vb + sl * row_bytes) : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                kw[u][j] = ok[u] ? load16<true>(kb + sl * row_bytes + 16 * j) : u32x4{0, 0, 0, 0};
+                vw[u][j] = ok[u] ? load16<true>(vb + sl * row_bytes + 16 * j) : u32x4{0, 0, 0, 0};
+            }
         }
         float sc[U][G];
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float t = row_sum16(dot8(qw[g], kw[u])) * a.scale_log2;  // every lane
+                float t = 0.f;
+#pragma unroll
+                for (int j = 0; j < NV; ++j) t = dot8(qw[g][j], kw[u][j], t);
+                t = row_sum<L>(t) * a.scale_log2;  // every lane
                 sc[u][g] = ok[u] ? t : -INFINITY;
             }
 #pragma unroll
@@ -257,45 +274,48 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
             float mx = sc[0][g];
 #pragma unroll
             for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][g]);
-            if (mx > m[g] + kRescaleLog2) {  // also when m is still -inf and a score is finite
+            if (mx > m[g] + kRescaleLog2) {  // also at the first position (m = kNoMax)
                 const float alpha = __builtin_amdgcn_exp2f(m[g] - mx);
                 l[g] *= alpha;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) acc[g][k] *= alpha;
+                for (int k = 0; k < DPL; ++k) acc[g][k] *= alpha;
                 m[g] = mx;
             }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float vf[8];
+            float vf[DPL];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                vf[2 * k] = bf16_lo(vw[u][k]);
-                vf[2 * k + 1] = bf16_hi(vw[u][k]);
-            }
+            for (int j = 0; j < NV; ++j)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    vf[8 * j + 2 * k] = bf16_lo(vw[u][j][k]);
+                    vf[8 * j + 2 * k + 1] = bf16_hi(vw[u][j][k]);
+                }
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                const float p = ok[u] ? __builtin_amdgcn_exp2f(sc[u][g] - m[g]) : 0.f;
+                const float p = __builtin_amdgcn_exp2f(sc[u][g] - m[g]);  // 0 for a masked score
                 l[g] += p;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) acc[g][k] += p * vf[k];
+                for (int k = 0; k < DPL; ++k) acc[g][k] += p * vf[k];
             }
         }
     }
 
-    // 2. merge the four lane groups (cross-row shuffles), then store the chunk's partials
+    // 2. merge the lane groups (cross-row shuffles), then store the chunk's partials.  A group
+    // that saw no position keeps m = kNoMax and l = 0, so its factor is 0 or multiplies zeros.
 #pragma unroll
-    for (int o = kLanesPerRow; o < kWave; o <<= 1) {
+    for (int o = L; o < kWave; o <<= 1) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const float mo = __shfl_xor(m[g], o);
             const float lo = __shfl_xor(l[g], o);
             const float mm = fmaxf(m[g], mo);
-            const float ea = m[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[g] - mm);
-            const float eb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mm);
+            const float ea = __builtin_amdgcn_exp2f(m[g] - mm);
+            const float eb = __builtin_amdgcn_exp2f(mo - mm);
             l[g] = l[g] * ea + lo * eb;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) acc[g][k] = acc[g][k] * ea + __shfl_xor(acc[g][k], o) * eb;
+            for (int k = 0; k < DPL; ++k) acc[g][k] = acc[g][k] * ea + __shfl_xor(acc[g][k], o) * eb;
             m[g] = mm;
         }
     }
@@ -303,9 +323,9 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
     if (grp == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            float *dst = a.ws_acc + (part + g) * kHeadDim + sub * 8;
+            float *dst = a.ws_acc + (part + g) * kHeadDim + sub * DPL;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) dst[k] = acc[g][k];
+            for (int k = 0; k < DPL; ++k) dst[k] = acc[g][k];
         }
     }
     if (lane == 0) {
@@ -447,10 +467,10 @@ template <int MODE>
 void launch_partial(int group, dim3 grid, dim3 block, size_t lds, hipStream_t s, const DecodeArgs &a)
 {
     switch (group) {
-    case 1: hipLaunchKernelGGL((decode_partial_kernel<MODE, 1>), grid, block, lds, s, a); break;
-    case 2: hipLaunchKernelGGL((decode_partial_kernel<MODE, 2>), grid, block, lds, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_partial_kernel<MODE, 4>), grid, block, lds, s, a); break;
-    default: hipLaunchKernelGGL((decode_partial_kernel<MODE, 8>), grid, block, lds, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_partial_kernel<MODE, 1, kRowLanes>), grid, block, lds, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_partial_kernel<MODE, 2, kRowLanes>), grid, block, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_partial_kernel<MODE, 4, kRowLanes>), grid, block, lds, s, a); break;
+    default: hipLaunchKernelGGL((decode_partial_kernel<MODE, 8, kRowLanes>), grid, block, lds, s, a); break;
     }
 }
 
