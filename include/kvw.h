@@ -336,7 +336,10 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream);
  * computed in fp32 from bf16 inputs; no position gives 0.  Each workgroup
  * takes a chunk of chunk_positions positions of one request, resolves their
  * slots once into LDS for all heads and folds them into a running softmax;
- * the chunks are combined in a second launch through `workspace`.
+ * the chunks are combined in a second launch through `workspace`.  For 32
+ * requests or more, a first launch lists the chunks that hold positions in
+ * `workspace` (full chunks first, then the partial ones longest first); the
+ * order affects only the schedule, not the result.
  *   q                  bf16 [num_reqs][num_q_heads][head_dim], 16-byte aligned
  *   context_lens       int32 [num_reqs] (device); clamped to [0, max_context]
  *                      with KVW_FLAG_COUNT
@@ -345,7 +348,9 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream);
  *   k_cache, v_cache   bf16 [num_blocks * block_size][num_kv_heads][head_dim]
  *                      (one layer, the K/V write's layout), 16-byte aligned
  *   out                fp32 [num_reqs][num_q_heads][head_dim]
- *   workspace          device memory of kvw_decode_workspace_size(...) bytes
+ *   workspace          device memory of kvw_decode_workspace_size(...) bytes, owned by
+ *                      the caller; its contents need no initialisation and are
+ *                      overwritten; calls that overlap on one workspace race
  *   chunk_positions    positions per workgroup: 256, 512 or 1024; 0 picks one from
  *                      num_reqs and max_context (results differ only in rounding)
  * Supported: head_dim 128; num_kv_heads 1..16; num_q_heads <= 32;
