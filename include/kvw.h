@@ -353,8 +353,9 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream);
  *                      overwritten; calls that overlap on one workspace race
  *   chunk_positions    positions per workgroup: 256, 512 or 1024; 0 picks one from
  *                      num_reqs and max_context (results differ only in rounding)
- * Supported: head_dim 128; num_kv_heads 1..16; num_q_heads <= 32;
- * num_q_heads / num_kv_heads in {1, 2, 4, 8}; else KVW_ERR_UNSUPPORTED.  Flags: KVW_FLAG_COUNT,
+ * Supported: head_dim 128; num_q_heads / num_kv_heads G in {1, 2, 4, 8};
+ * num_kv_heads 1..16, or 1..8 when G = 8 (so up to 64 query heads); else
+ * KVW_ERR_UNSUPPORTED.  Flags: KVW_FLAG_COUNT,
  * KVW_FLAG_BAD_BLOCK, KVW_FLAG_SLOT_OOB (slot past the cache: skipped).
  */
 typedef struct kvw_decode_args {

@@ -57,8 +57,7 @@ constexpr int32_t kPlanMinReqs = 32;                 // batches this large get a
 constexpr int kHeadDim = 128;                        // supported head_dim
 constexpr int kRowLanes = 16;                        // lanes per position row of one head (8 was
                                                      // slower: fewer instructions, fewer waves)
-constexpr int kMaxKvHeads = 16;
-constexpr int kMaxQHeads = 32;
+constexpr int kMaxKvHeads = 16;                      // 8 when G = 8 (register budget, below)
 constexpr float kRescaleLog2 = 8.f;                  // move the running max past this growth
 constexpr float kNoMax = -1e30f;                     // running max before any position: finite, so
                                                      // a masked score's weight 2^(-inf - m) is 0
@@ -148,10 +147,11 @@ constexpr int unroll_of()
     return L == 16 ? (G <= 2 ? 8 : (G == 4 ? 4 : 2)) : (G <= 2 ? 4 : (G == 4 ? 2 : 1));
 }
 
-// Threads per workgroup: one wave per key/value head, at most 16 and at most
-// 32 / G (the query heads the score tiles cover).
+// Threads per workgroup: one wave per key/value head, at most 16, or 8 for G = 8
+// whose 8-row register tiles need more than the 128 VGPRs a 16-wave workgroup
+// leaves each wave.
 template <int G>
-constexpr int partial_threads() { return kWave * (G <= 2 ? kMaxKvHeads : kMaxQHeads / G); }
+constexpr int partial_threads() { return kWave * (G <= 4 ? kMaxKvHeads : kMaxKvHeads / 2); }
 
 template <int MODE, int G, int L>
 __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(DecodeArgs a)
@@ -501,14 +501,14 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
     if (g.num_reqs < 0 || g.max_context < 0 || g.block_size <= 0 || g.num_blocks < 0 ||
         g.num_q_heads <= 0 || g.num_kv_heads <= 0 || g.num_reqs > 65535)
         return fail(KVW_ERR_INVALID_ARG, "%s: a size is out of range", fn);
-    if (g.head_dim != kHeadDim || g.num_kv_heads > kMaxKvHeads || g.num_q_heads > kMaxQHeads ||
-        g.num_q_heads % g.num_kv_heads != 0)
+    if (g.head_dim != kHeadDim || g.num_kv_heads > kMaxKvHeads || g.num_q_heads % g.num_kv_heads != 0)
         return fail(KVW_ERR_UNSUPPORTED, "%s: head_dim %d, %d query / %d key-value heads not supported",
                     fn, g.head_dim, g.num_q_heads, g.num_kv_heads);
     const int group = g.num_q_heads / g.num_kv_heads;
-    if (group != 1 && group != 2 && group != 4 && group != 8)
-        return fail(KVW_ERR_UNSUPPORTED, "%s: %d query heads per key/value head not supported", fn,
-                    group);
+    if ((group != 1 && group != 2 && group != 4 && group != 8) ||
+        g.num_kv_heads > (group <= 4 ? kMaxKvHeads : kMaxKvHeads / 2))
+        return fail(KVW_ERR_UNSUPPORTED, "%s: %d query heads over %d key/value heads not supported",
+                    fn, g.num_q_heads, g.num_kv_heads);
     if (g.num_blocks > INT64_MAX / g.block_size / g.num_kv_heads / (kHeadDim * 2))
         return fail(KVW_ERR_INVALID_ARG, "%s: cache size overflows", fn);
     if (g.chunk_positions != 0 && g.chunk_positions != 256 && g.chunk_positions != 512 &&

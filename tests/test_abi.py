@@ -225,9 +225,9 @@ def test_decode_validation(lib):
     assert f(None, None) == INVALID
     assert f(ctypes.byref(_decode(mode=kvw.KVW_SLOTS_PRECOMPUTED)), None) == INVALID
     assert f(ctypes.byref(_decode(head_dim=64)), None) == UNSUPPORTED
-    assert f(ctypes.byref(_decode(num_q_heads=64, num_kv_heads=8)), None) == UNSUPPORTED
+    assert f(ctypes.byref(_decode(num_q_heads=128, num_kv_heads=16)), None) == UNSUPPORTED  # G=8, 16 kv
     assert f(ctypes.byref(_decode(num_q_heads=12, num_kv_heads=4)), None) == UNSUPPORTED  # 3 per head
-    assert f(ctypes.byref(_decode(num_q_heads=32, num_kv_heads=32)), None) == UNSUPPORTED
+    assert f(ctypes.byref(_decode(num_q_heads=32, num_kv_heads=32)), None) == UNSUPPORTED  # 32 kv heads
     assert f(ctypes.byref(_decode(num_q_heads=16, num_kv_heads=1)), None) == UNSUPPORTED  # 16 per head
     assert f(ctypes.byref(_decode(num_q_heads=30, num_kv_heads=8)), None) == UNSUPPORTED
     assert f(ctypes.byref(_decode(block_size=0)), None) == INVALID

@@ -257,6 +257,10 @@ def small_decodes():
         # block size 1: a chunk's 256 positions fall in 256 different runs
         (_dec("bs1_many_runs", 8, [600, 1100, 5], 1, ("len", 1, 1), 4, 2000,
               range_stride=1200), 16),
+        # 64 query heads: over 8 key/value heads (8 per head, 8 waves) and over 16 (4 per head,
+        # 16 waves)
+        (_dec("hq64_g8", 10, [1, 700, 1300, 2100], 16, ("count", 1, 3), 8, 400), 64),
+        (_dec("hq64_g4_16heads", 11, [513, 1025, 90], 32, ("count", 1, 3), 16, 120), 64),
         # 40 requests (a work list orders the chunks): empty ones, exact chunk multiples, tails
         (_dec("plan_40_reqs", 9, list(rng.integers(0, 2200, 34)) + [0, 256, 512, 1024, 2048, 1],
               16, ("count", 1, 4), 8, 6000, dummies=3), 32),
