@@ -15,8 +15,9 @@
 // adds, the exponentials on v_exp_f32 in base 2, and the running maximum is
 // only moved when it grows by more than 2^8.
 //
-// decode_partial_kernel<MODE, G>: one workgroup per (chunk of 256, 512 or 1024
-// positions, request), one wave per key/value head.
+// decode_partial_kernel<MODE, G, L>: one workgroup per (chunk of 256, 512 or
+// 1024 positions, request), one wave per key/value head, L = 16 lanes per
+// position row.
 //   0. The workgroup resolves the slots of its positions once, into LDS: the
 //      block-table gather (PAGED) or range arithmetic with the wavefront
 //      search over range_cum (RANGES).  Every head reads them from LDS.
