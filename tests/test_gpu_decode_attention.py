@@ -511,3 +511,57 @@ def test_decode_graph_replay(mode):
         slots, _ = expected_slots(Layout(w), mode, ctx.astype(np.int64))
         check(got, q, slots, np.arange(rows, dtype=np.int64), k, v, ctx, list(range(reqs)), hq,
               hkv, 128 ** -0.5, f"graph {mode} replay {rep}")
+
+
+def test_decode_through_the_written_table():
+    """The whole step, then the read: kv_write (ranges, manager block size 32) stores the step's
+    K/V and, in its slot-mapping launch, the attention side's table at kernel block size 16;
+    decode attention then reads the cache through that table (paged, bs 16) and through the
+    manager's range descriptors (ranges, bs 32).  Same slots, so the two outputs are equal bit
+    for bit, and both match the oracle."""
+    orc = oracle.get()
+    reqs = [Request(e, n) for e, n in ((700, 40), (1500, 1), (2048, 300), (33, 33), (1025, 7))]
+    w = custom("step_then_read", 4990, reqs, block_size=32, num_blocks=300, runs=("count", 1, 4),
+               kernel_block_size=16, dummy_reqs=2)
+    hq, hkv, k = 32, w.num_kv_heads, w.blocks_per_kv_block
+    rows = w.num_blocks * w.block_size
+    q, ctx, _, kh, vh = decode_inputs(w, hq, 77, rows=np.arange(rows, dtype=np.int64))
+    kc, vc = place_caches(rows, np.arange(rows, dtype=np.int64), kh, vh)
+    key_h, value_h = w.kv_layer(0, 0), w.kv_layer(1, 0)
+    width = w.table_stride * k
+    table = torch.full((w.num_reqs, width), -5, dtype=torch.int32, device=DEV)
+    counts = torch.full((w.num_reqs,), -5, dtype=torch.int32, device=DEV)
+    flag = new_flag()
+    kvw.kvw_kv_write(mode=kvw.KVW_SLOTS_RANGES, query_start_loc=dev(w.query_start_loc),
+                     num_reqs=w.num_reqs, positions=dev(w.positions),
+                     max_num_tokens=w.max_num_tokens, range_start=dev(w.range_start),
+                     range_len=dev(w.range_len), range_cum=dev(w.range_cum),
+                     num_ranges=dev(w.num_ranges), block_size=w.block_size,
+                     num_blocks=w.num_blocks,
+                     key=dev(key_h).view(1, w.max_num_tokens, hkv, 128),
+                     value=dev(value_h).view(1, w.max_num_tokens, hkv, 128),
+                     k_cache=kc, v_cache=vc,
+                     slot_mapping_out=torch.empty(w.max_num_tokens, dtype=torch.int64, device=DEV),
+                     table_out=table, table_counts_out=counts, table_block_size=16, err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    # the oracle's cache after its own write of the same step
+    slots_w, _ = orc.slot_mapping_ranges(w.query_start_loc, w.num_reqs, w.positions,
+                                         w.max_num_tokens, w.range_start, w.range_len,
+                                         w.range_cum, w.num_ranges, w.block_size)
+    ek = kh.reshape(rows, hkv * 128).copy()
+    ev = vh.reshape(rows, hkv * 128).copy()
+    orc.kv_write(slots_w, key_h[None], value_h[None], w.num_blocks, w.block_size, ek, ev)
+    # read through the written kernel-unit table (paged, bs 16) and the manager's ranges (bs 32)
+    lay16 = Layout(w, block_size=16, num_blocks=w.num_blocks * k, table=host(table),
+                   nbpr=host(counts))
+    got16, f16 = run_gpu("paged", lay16, q, ctx, int(ctx.max()), kc, vc)
+    got32, f32_ = run_gpu("ranges", Layout(w), q, ctx, int(ctx.max()), kc, vc)
+    assert f16 == 0 and f32_ == 0
+    assert np.array_equal(got16, got32), "the two resolutions differ"
+    slots, _ = expected_slots(Layout(w), "ranges", ctx.astype(np.int64))
+    slots16, _ = expected_slots(lay16, "paged", ctx.astype(np.int64))
+    assert all(np.array_equal(a, b) for a, b in zip(slots, slots16))
+    check(got16, q, slots, np.arange(rows, dtype=np.int64), ek.reshape(rows, hkv, 128),
+          ev.reshape(rows, hkv, 128), ctx, list(range(w.num_reqs)), hq, hkv, 128 ** -0.5,
+          "through the written table")
