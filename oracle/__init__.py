@@ -65,7 +65,7 @@ class Oracle:
         lib.orc_ranges_to_block_table.argtypes = [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _P,
                                                   _I32, _P, _P]
         lib.orc_decode_attention.argtypes = [_P, _P, _P, _I64, _P, _P, _P, _I32, _I32, _I32,
-                                             _I32, ctypes.c_double, _P]
+                                             _I32, ctypes.c_double, _P, _P]
         lib.orc_decode_attention.restype = ctypes.c_int
         lib.orc_coord_n.argtypes = [_I64] * 5
         lib.orc_coord_n.restype = _I64
@@ -210,10 +210,11 @@ class Oracle:
 
     # -- decode attention over the paged cache -------------------------------
     def decode_attention(self, q, k_cache, v_cache, slots_per_req, reqs, num_q_heads: int,
-                         num_kv_heads: int, scale: float) -> np.ndarray:
+                         num_kv_heads: int, scale: float, with_lse: bool = False):
         """out[i][h][d] (float64) for requests reqs[i]; slots_per_req[i] lists the slots of
         positions 0, 1, ... of that request.  q: uint16 [R][Hq][D]; caches: uint16
-        [rows][Hkv][D] (bf16 bit patterns)."""
+        [rows][Hkv][D] (bf16 bit patterns).  with_lse: also return lse[i][h], the natural log
+        of the softmax normalizer (-inf with no token)."""
         qq = _c(q, np.uint16)
         kc = _c(k_cache, np.uint16)
         vc = _c(v_cache, np.uint16)
@@ -225,11 +226,13 @@ class Oracle:
         begin[1:] = np.cumsum([len(s) for s in slots_per_req])
         rq = _c(reqs, np.int32)
         out = np.zeros((len(rq), num_q_heads, head_dim), np.float64)
+        lse = np.zeros((len(rq), num_q_heads), np.float64) if with_lse else None
         rc = self.lib.orc_decode_attention(_ptr(qq), _ptr(kc), _ptr(vc), rows, _ptr(slots),
                                            _ptr(begin), _ptr(rq), len(rq), num_q_heads,
-                                           num_kv_heads, head_dim, float(scale), _ptr(out))
+                                           num_kv_heads, head_dim, float(scale), _ptr(out),
+                                           _ptr(lse))
         self._check(rc, "decode_attention")
-        return out
+        return (out, lse) if with_lse else out
 
     # -- coordinate form ---------------------------------------------------
     def coord_n(self, layer, block, token, num_blocks, block_size) -> int:

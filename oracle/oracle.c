@@ -508,12 +508,19 @@ static double attention_score(const uint16_t *qh, const uint16_t *kr, int32_t he
  *   w_j = exp(s_j - max s) / sum_j' exp(s_j' - max s)
  *   out[i][h][d] = sum_j w_j * V[slot_j][g][d]
  * in double precision (bf16 inputs widened exactly); no token gives 0.
+ * lse_out (may be NULL) receives, per selected request and query head, the
+ * natural log of the softmax normalizer, log sum_j exp(s_j) = max s +
+ * log sum_j exp(s_j - max s), or -inf with no token.  That is what merges
+ * attention computed over disjoint sets of positions (for instance the
+ * positions each context-parallel rank holds, [P2] "Entwurfsmotivation"):
+ * with L = log sum_r exp(lse_r), out = sum_r exp(lse_r - L) out_r.
  * Cache rows: [cache_rows][num_kv_heads][head_dim] bf16.
  */
 int orc_decode_attention(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
                          int64_t cache_rows, const int64_t *slots, const int64_t *begin,
                          const int32_t *reqs, int32_t num_sel, int32_t num_q_heads,
-                         int32_t num_kv_heads, int32_t head_dim, double scale, double *out)
+                         int32_t num_kv_heads, int32_t head_dim, double scale, double *out,
+                         double *lse_out)
 {
     if (num_sel < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         num_q_heads % num_kv_heads != 0 || cache_rows < 0)
@@ -527,6 +534,7 @@ int orc_decode_attention(const uint16_t *q, const uint16_t *k_cache, const uint1
             const uint16_t *qh = q + ((int64_t)reqs[i] * num_q_heads + h) * head_dim;
             double *o = out + ((int64_t)i * num_q_heads + h) * head_dim;
             for (int32_t d = 0; d < head_dim; ++d) o[d] = 0.0;
+            if (lse_out) lse_out[(int64_t)i * num_q_heads + h] = -1.0 / 0.0;
             /* scores and their maximum */
             double smax = -1.0 / 0.0;
             int64_t n = 0;
@@ -545,6 +553,7 @@ int orc_decode_attention(const uint16_t *q, const uint16_t *k_cache, const uint1
                 const uint16_t *kr = k_cache + (slots[j] * num_kv_heads + g) * head_dim;
                 denom += exp(attention_score(qh, kr, head_dim, scale) - smax);
             }
+            if (lse_out) lse_out[(int64_t)i * num_q_heads + h] = smax + log(denom);
             for (int64_t j = begin[i]; j < begin[i + 1]; ++j) {
                 if (slots[j] < 0) continue;
                 const uint16_t *kr = k_cache + (slots[j] * num_kv_heads + g) * head_dim;

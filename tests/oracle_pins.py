@@ -558,6 +558,45 @@ def pin_attention(orc):
     c = orc.decode_attention(q, k, v, [[3, -1, 9, 11, -1, 20, 21, 33]], [0], hq, hkv, scale)
     e = orc.decode_attention(q, k, v, [sl], [0], hq, hkv, scale)
     assert np.array_equal(c, e)
+    pin_attention_lse(orc, q, k, v, q2, k2, q3, sl, hq, hkv, scale)
+
+
+def pin_attention_lse(orc, q, k, v, q2, k2, q3, sl, hq, hkv, scale):
+    """The log of the softmax normalizer: closed forms, and the identity that merges attention
+    over disjoint position sets (what context-parallel ranks combine)."""
+    group = hq // hkv
+    qv, kv_ = _bf16_value(q), _bf16_value(k)
+    # one token: its score
+    _, lse = orc.decode_attention(q, k, v, [[7]], [1], hq, hkv, scale, with_lse=True)
+    for h in range(hq):
+        assert np.isclose(lse[0, h], scale * float(np.dot(qv[1, h], kv_[7, h // group])),
+                          rtol=0, atol=1e-13)
+    # no token: -inf
+    _, lse = orc.decode_attention(q, k, v, [[]], [1], hq, hkv, scale, with_lse=True)
+    assert np.all(lse == -np.inf)
+    # zero query: every score 0, so log n
+    _, lse = orc.decode_attention(np.zeros_like(q), k, v, [sl], [0], hq, hkv, scale, with_lse=True)
+    assert np.allclose(lse, np.log(len(sl)), rtol=0, atol=1e-14)
+    # two one-hot keys: log(1 + e^(2 scale))
+    _, lse = orc.decode_attention(q2, k2, v, [[4, 5]], [2], hq, hkv, scale, with_lse=True)
+    assert np.allclose(lse, np.log1p(np.exp(2.0 * scale)), rtol=0, atol=1e-14)
+    # a dominant score of 1000 among zeros: 1000 (exp(1000) overflows unless the max is taken out)
+    _, lse = orc.decode_attention(q3, k2, v, [[1, 2, 5, 8]], [0], hq, hkv, 1.0, with_lse=True)
+    assert np.allclose(lse, 1000.0, rtol=0, atol=1e-12)
+    # merging attention over a split of the positions gives the whole: with L = logaddexp of the
+    # parts' lse, out = sum exp(lse_part - L) out_part; an empty part (lse -inf) adds nothing
+    full, lf = orc.decode_attention(q, k, v, [sl], [0], hq, hkv, scale, with_lse=True)
+    for part_a in ([3, 11, 21], [3, 9, 11, 20, 21, 33], [33]):
+        part_b = [s_ for s_ in sl if s_ not in part_a]
+        oa, la = orc.decode_attention(q, k, v, [part_a], [0], hq, hkv, scale, with_lse=True)
+        ob, lb = orc.decode_attention(q, k, v, [part_b], [0], hq, hkv, scale, with_lse=True)
+        big = np.logaddexp(la, lb)
+        with np.errstate(invalid="ignore"):
+            wa = np.where(la == -np.inf, 0.0, np.exp(la - big))
+            wb = np.where(lb == -np.inf, 0.0, np.exp(lb - big))
+        merged = wa[..., None] * oa + wb[..., None] * ob
+        assert np.allclose(merged, full, rtol=0, atol=1e-12)
+        assert np.allclose(big, lf, rtol=0, atol=1e-12)
 
 
 def pin_coordinates(orc):

@@ -29,7 +29,7 @@ int orc_ranges_to_block_table(const int32_t *, const int32_t *, const int32_t *,
 int64_t orc_coord_offset(int64_t, int64_t, int64_t, int64_t, int64_t, int64_t);
 int orc_decode_attention(const uint16_t *, const uint16_t *, const uint16_t *, int64_t,
                          const int64_t *, const int64_t *, const int32_t *, int32_t, int32_t,
-                         int32_t, int32_t, double, double *);
+                         int32_t, int32_t, double, double *, double *);
 int orc_kv_write(const int64_t *, int64_t, int32_t, const uint8_t *, const uint8_t *, int64_t,
                  int64_t, int64_t, int32_t, int64_t, uint8_t *, uint8_t *, int64_t, int64_t,
                  uint32_t *);
@@ -90,7 +90,7 @@ int main(void)
         /* decode attention: 4 q heads over 2 kv heads of 8 dims; cache rows reinterpret kc */
         {
             static uint16_t qa[R * 4 * 8];
-            static double oa[R * 4 * 8];
+            static double oa[R * 4 * 8], lse[R * 4];
             int64_t aslots[M], begin[R + 1];
             int32_t sel[R];
             for (int i = 0; i < R * 4 * 8; ++i) qa[i] = (uint16_t)(0x3C00 + below(0x800));
@@ -101,7 +101,7 @@ int main(void)
                 for (int64_t j = begin[r]; j < begin[r + 1]; ++j) aslots[j] = below(100) - 2;
             }
             CALL(orc_decode_attention(qa, (const uint16_t *)kc, (const uint16_t *)vc, 100, aslots,
-                                      begin, sel, R, 4, 2, 8, 0.35, oa));
+                                      begin, sel, R, 4, 2, 8, 0.35, oa, (trial & 1) ? lse : NULL));
         }
     }
     if (ok * 10 < calls * 9) {  /* nearly every call must get past its argument checks */

@@ -57,6 +57,8 @@ MUTANTS = {
                                 "int64_t offset = o;\n            for (int64_t i = 0; i < n; ++i) {"),
     "expansion_counts_unscaled": ("if (counts_out) counts_out[r] = (int32_t)(count * k);",
                                   "if (counts_out) counts_out[r] = (int32_t)count;"),
+    "attention_lse_without_max": ("lse_out[(int64_t)i * num_q_heads + h] = smax + log(denom);",
+                                  "lse_out[(int64_t)i * num_q_heads + h] = log(denom);"),
     "attention_drops_scale": ("    return sc * scale;\n}", "    return sc;\n}"),
     "attention_heads_interleaved": ("            int64_t g = h / group;", "            int64_t g = h % num_kv_heads;"),
     "attention_no_max_shift": ("denom += exp(attention_score(qh, kr, head_dim, scale) - smax);",
