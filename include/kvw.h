@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define KVW_ABI_VERSION 5
+#define KVW_ABI_VERSION 6
 #define KVW_PAD_ID (-1)
 /* Largest accepted range_stride (range descriptors per request). */
 #define KVW_MAX_RANGE_STRIDE 65536
@@ -353,6 +353,15 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream);
  *                      overwritten; calls that overlap on one workspace race
  *   chunk_positions    positions per workgroup: 256, 512 or 1024; 0 picks one from
  *                      num_reqs and max_context (results differ only in rounding)
+ *   cp_world_size, cp_rank, cp_interleave_size
+ *                      decode context parallelism ([P2] "Entwurfsmotivation"; the
+ *                      placement of kvw_slot_mapping_paged): this rank attends only
+ *                      the positions it holds, from its own cache of block_size slots
+ *                      per block; the others are skipped without a flag.  0 or 1 = none.
+ *                      KVW_ERR_INVALID_ARG as kvw_slot_mapping_paged
+ *   lse_out            NULL, or fp32 [num_reqs][num_q_heads]: log sum_j exp(s_j) over
+ *                      the positions attended (natural log; -inf with none), what
+ *                      kvw_decode_merge needs to combine the ranks' results
  * Supported: head_dim 128; num_q_heads / num_kv_heads G in {1, 2, 4, 8};
  * num_kv_heads 1..16, or 1..8 when G = 8 (so up to 64 query heads); else
  * KVW_ERR_UNSUPPORTED.  Flags: KVW_FLAG_COUNT,
@@ -385,6 +394,10 @@ typedef struct kvw_decode_args {
     int64_t workspace_bytes;
     int32_t *err_flag;
     int32_t chunk_positions;           /* 256, 512, 1024, or 0 (chosen by the library) */
+    int32_t cp_world_size;             /* context parallelism: 0 or 1 = none */
+    int32_t cp_rank;
+    int32_t cp_interleave_size;
+    float *lse_out;                    /* NULL or fp32 [num_reqs][num_q_heads] */
 } kvw_decode_args;
 
 /* Bytes of workspace kvw_decode_attention needs for these sizes. */
@@ -395,6 +408,25 @@ int64_t kvw_decode_workspace_size(int32_t num_reqs, int32_t max_context, int32_t
 size_t kvw_decode_args_size(void);
 
 kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream);
+
+/*
+ * Merges decode attention computed over disjoint sets of each request's
+ * positions, for instance by the ranks of decode context parallelism: with
+ * L = log sum_p exp(lse_p),
+ *   out[r][h][d] = sum_p exp(lse_p[r][h] - L) * outs_p[r][h][d],  lse_out = L.
+ * A part with lse -inf (no position) adds nothing; none with a position gives
+ * out 0 and lse -inf.
+ *   outs      fp32 [num_parts][num_reqs][num_q_heads][head_dim] (device), the
+ *             parts' kvw_decode_attention outputs stacked
+ *   lses      fp32 [num_parts][num_reqs][num_q_heads] (device), their lse_out
+ *   out       fp32 [num_reqs][num_q_heads][head_dim]; lse_out NULL or fp32
+ *             [num_reqs][num_q_heads]
+ * Errors: KVW_ERR_INVALID_ARG for num_parts < 1, head_dim outside 1..1024,
+ * num_reqs or num_q_heads outside their ranges, NULL or misaligned pointers.
+ */
+kvw_status kvw_decode_merge(int32_t num_parts, int32_t num_reqs, int32_t num_q_heads,
+                            int32_t head_dim, const float *outs, const float *lses, float *out,
+                            float *lse_out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -63,6 +63,7 @@ constexpr float kRescaleLog2 = 8.f;                  // move the running max pas
 constexpr float kNoMax = -1e30f;                     // running max before any position: finite, so
                                                      // a masked score's weight 2^(-inf - m) is 0
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -93,6 +94,10 @@ struct DecodeArgs {
     int32_t num_kv_heads;
     int32_t splits;
     int32_t chunk;      // positions per workgroup
+    int32_t cp_world;   // context parallelism: world size (<= 1: none), this rank, interleave
+    int32_t cp_rank;
+    int32_t cp_interleave;
+    float *lse_out;     // [num_reqs][num_q_heads] natural-log normalizer, or NULL
     float scale_log2;  // scale * log2(e): scores in base-2 exponent units
 };
 
@@ -185,10 +190,13 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
         const int t = base + static_cast<int>(threadIdx.x);
         const bool in = t < cnt;
         const int64_t p = c0 + t;
-        const int64_t lb = in ? p / bs : 0;
+        int64_t lb = 0;
+        int32_t off = 0;
+        // a position of another context-parallel rank holds nothing here: skipped, no flag
+        const bool mine = in && cp_locate(p, bs, a.cp_world, a.cp_rank, a.cp_interleave, lb, off);
         int64_t b = -1;
         if (MODE == KVW_SLOTS_PAGED) {
-            if (in) {
+            if (mine) {
                 int64_t bound = a.table_stride;
                 if (a.num_blocks_per_req)
                     bound = clamp_count(a.num_blocks_per_req[r], a.table_stride, flags);
@@ -200,10 +208,10 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
         } else {
             uint32_t nflags = 0;
             const int32_t nr = static_cast<int32_t>(clamp_count(a.num_ranges[r], a.range_stride, nflags));
-            if (in) flags |= nflags;
+            if (mine) flags |= nflags;
             const int64_t row = static_cast<int64_t>(r) * a.range_stride;
-            const int32_t i = wave_upper_index(a.range_cum + row, nr, lb, in);  // every lane calls
-            if (in && i >= 0) {
+            const int32_t i = wave_upper_index(a.range_cum + row, nr, lb, mine);  // every lane calls
+            if (mine && i >= 0) {
                 const int64_t cm = a.range_cum[row + i];
                 if (lb >= cm && lb < cm + a.range_len[row + i]) {
                     b = static_cast<int64_t>(a.range_start[row + i]) + (lb - cm);
@@ -211,7 +219,7 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
                 }
             }
         }
-        int64_t slot = b < 0 ? -1 : b * bs + (p - lb * bs);
+        int64_t slot = b < 0 ? -1 : b * bs + off;
         if (slot >= a.cache_rows) { flags |= KVW_FLAG_SLOT_OOB; slot = -1; }
         if (in) s_slot[t] = slot;
     }
@@ -445,7 +453,36 @@ __global__ __launch_bounds__(kHeadDim * SLICES) void decode_combine_kernel(Decod
 #pragma unroll
         for (int i = 1; i < SLICES; ++i) num += s_num[i][d];
         a.out[(static_cast<int64_t>(r) * a.num_q_heads + h) * kHeadDim + d] = den > 0.f ? num / den : 0.f;
+        // log sum_j e^(s_j) = ln 2 * (M + log2(den)), scores in base-2 units; -inf with no position
+        if (a.lse_out && d == 0)
+            a.lse_out[static_cast<int64_t>(r) * a.num_q_heads + h] =
+                den > 0.f ? (mx + log2f(den)) * kLn2 : -INFINITY;
     }
+}
+
+// out[r][h][d] = sum_p e^(lse_p - L) out_p[r][h][d], L = log sum_p e^(lse_p), over the parts'
+// stacked results; a part with lse -inf (no position) adds nothing; no part with a position
+// gives 0 and -inf.
+__global__ __launch_bounds__(1024) void decode_merge_kernel(int32_t parts, int32_t num_reqs,
+                                                            int32_t num_q_heads, int32_t head_dim,
+                                                            const float *outs, const float *lses,
+                                                            float *out, float *lse_out)
+{
+    const int32_t h = blockIdx.x, r = blockIdx.y, d = threadIdx.x;
+    const int64_t row = static_cast<int64_t>(r) * num_q_heads + h;
+    const int64_t part_rows = static_cast<int64_t>(num_reqs) * num_q_heads;
+    float mx = -INFINITY;
+    for (int32_t p = 0; p < parts; ++p) mx = fmaxf(mx, lses[p * part_rows + row]);
+    float num = 0.f, den = 0.f;
+    if (mx != -INFINITY) {
+        for (int32_t p = 0; p < parts; ++p) {
+            const float e = __builtin_amdgcn_exp2f((lses[p * part_rows + row] - mx) * kLog2e);
+            den += e;
+            num += e * outs[(p * part_rows + row) * head_dim + d];
+        }
+    }
+    out[row * head_dim + d] = den > 0.f ? num / den : 0.f;
+    if (lse_out && d == 0) lse_out[row] = den > 0.f ? mx + log2f(den) * kLn2 : -INFINITY;
 }
 
 int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
@@ -492,6 +529,27 @@ int64_t kvw_decode_workspace_size(int32_t num_reqs, int32_t max_context, int32_t
 
 size_t kvw_decode_args_size(void) { return sizeof(kvw_decode_args); }
 
+kvw_status kvw_decode_merge(int32_t num_parts, int32_t num_reqs, int32_t num_q_heads,
+                            int32_t head_dim, const float *outs, const float *lses, float *out,
+                            float *lse_out, void *stream)
+{
+    const char *fn = "kvw_decode_merge";
+    if (num_parts < 1 || num_reqs < 0 || num_reqs > 65535 || num_q_heads <= 0 ||
+        num_q_heads > 65535 || head_dim <= 0 || head_dim > 1024)
+        return fail(KVW_ERR_INVALID_ARG, "%s: a size is out of range", fn);
+    if (num_reqs == 0) return KVW_OK;
+    if (!outs || !lses || !out || !aligned_to(outs, 4) || !aligned_to(lses, 4) ||
+        !aligned_to(out, 4) || (lse_out && !aligned_to(lse_out, 4)))
+        return fail(KVW_ERR_INVALID_ARG, "%s: a pointer is NULL or misaligned", fn);
+    hipLaunchKernelGGL(decode_merge_kernel,
+                       dim3(static_cast<unsigned>(num_q_heads), static_cast<unsigned>(num_reqs)),
+                       dim3(static_cast<unsigned>(head_dim)), 0, reinterpret_cast<hipStream_t>(stream),
+                       num_parts, num_reqs, num_q_heads, head_dim, outs, lses, out, lse_out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(KVW_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return KVW_OK;
+}
+
 kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
 {
     const char *fn = "kvw_decode_attention";
@@ -518,6 +576,13 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
                     g.chunk_positions);
     if (g.err_flag && !aligned_to(g.err_flag, 4))
         return fail(KVW_ERR_INVALID_ARG, "%s: err_flag misaligned", fn);
+    if (g.lse_out && !aligned_to(g.lse_out, 4))
+        return fail(KVW_ERR_INVALID_ARG, "%s: lse_out misaligned", fn);
+    {
+        const kvw_status st = kvw_detail::check_cp(fn, g.block_size, g.cp_world_size, g.cp_rank,
+                                                    g.cp_interleave_size);
+        if (st != KVW_OK) return st;
+    }
     if (g.num_reqs == 0) return KVW_OK;
     if (!g.q || !aligned_to(g.q, 16) || !g.context_lens || !aligned_to(g.context_lens, 4) ||
         !g.out || !aligned_to(g.out, 4))
@@ -557,6 +622,10 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
     a.v_cache = static_cast<const uint8_t *>(g.v_cache);
     a.out = g.out;
     a.chunk = g.chunk_positions ? g.chunk_positions : auto_chunk(g.num_reqs, g.max_context);
+    a.cp_world = g.cp_world_size;
+    a.cp_rank = g.cp_rank;
+    a.cp_interleave = g.cp_interleave_size > 0 ? g.cp_interleave_size : 1;
+    a.lse_out = g.lse_out;
     a.splits = static_cast<int32_t>(ceil_div(g.max_context, a.chunk));
     a.ws_acc = static_cast<float *>(g.workspace);
     a.ws_ml = a.ws_acc + static_cast<int64_t>(g.num_reqs) * a.splits * g.num_q_heads * kHeadDim;

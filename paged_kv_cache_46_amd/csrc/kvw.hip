@@ -154,46 +154,10 @@ __device__ __forceinline__ int32_t find_request(const int32_t *qsl, int32_t num_
 }
 
 
-// Logical block lb and in-block offset off of position p >= 0 on this rank.
-// Without context parallelism lb = p / bs and off = p % bs.  With W ranks
-// and interleave I the ranks deal positions in chunks of I, round robin; a
-// table entry covers a virtual block of bs*W positions, of which each rank
-// keeps its own, in order, in its block of bs slots:
-//   owner = (p / I) % W,  lb = p / (bs*W),  o = p % (bs*W),
-//   off = (o / (I*W)) * I + o % I.
-// Returns false when another rank holds p.  bs*W fits an int32 (host check).
+// Logical block and in-block offset of position p on this rank (cp_locate).
 __device__ __forceinline__ bool locate(const MapArgs &a, int64_t p, int64_t &lb, int32_t &off)
 {
-    const uint32_t bs = static_cast<uint32_t>(a.block_size);
-    if (a.cp_world <= 1) {
-        if (p <= INT32_MAX) {
-            const uint32_t q = static_cast<uint32_t>(p) / bs;
-            lb = q;
-            off = static_cast<int32_t>(static_cast<uint32_t>(p) - q * bs);
-        } else {
-            lb = p / a.block_size;
-            off = static_cast<int32_t>(p - lb * a.block_size);
-        }
-        return true;
-    }
-    const int64_t w = a.cp_world, il = a.cp_interleave, span = static_cast<int64_t>(bs) * w;
-    int64_t o;
-    if (p <= INT32_MAX) {
-        const uint32_t up = static_cast<uint32_t>(p);
-        if ((up / static_cast<uint32_t>(il)) % static_cast<uint32_t>(w) !=
-            static_cast<uint32_t>(a.cp_rank))
-            return false;
-        const uint32_t q = up / static_cast<uint32_t>(span);
-        lb = q;
-        o = up - q * static_cast<uint32_t>(span);
-    } else {
-        if ((p / il) % w != a.cp_rank) return false;
-        lb = p / span;
-        o = p - lb * span;
-    }
-    const uint32_t uo = static_cast<uint32_t>(o), ui = static_cast<uint32_t>(il);
-    off = static_cast<int32_t>((uo / (ui * static_cast<uint32_t>(w))) * ui + uo % ui);
-    return true;
+    return cp_locate(p, a.block_size, a.cp_world, a.cp_rank, a.cp_interleave, lb, off);
 }
 
 // Paged gather: one table load per position.
@@ -612,6 +576,7 @@ __global__ __launch_bounds__(kBlockThreads) void fill_table_kernel(
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+using kvw_detail::check_cp;
 using kvw_detail::fail;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -677,19 +642,6 @@ kvw_status check_ranges(const char *fn, int32_t num_reqs, const int32_t *start, 
 
 // Context-parallel parameters: world 0 means none; from 1 up the rank must lie
 // in [0, world) and the interleave size divide block_size.
-kvw_status check_cp(const char *fn, int32_t block_size, int32_t world, int32_t rank,
-                    int32_t interleave)
-{
-    KVW_REQUIRE(world >= 0, "%s: cp_world_size %d is negative", fn, world);
-    if (world == 0) return KVW_OK;
-    KVW_REQUIRE(rank >= 0 && rank < world, "%s: cp_rank %d outside [0, %d)", fn, rank, world);
-    KVW_REQUIRE(interleave >= 1 && block_size % interleave == 0,
-                "%s: cp_interleave_size %d does not divide block_size %d", fn, interleave, block_size);
-    KVW_REQUIRE(static_cast<int64_t>(block_size) * world <= INT32_MAX,
-                "%s: block_size * cp_world_size overflows int32", fn);
-    return KVW_OK;
-}
-
 MapArgs make_map_args(const int32_t *qsl, int32_t num_reqs, const int64_t *positions,
                       int64_t max_num_tokens, int32_t block_size, int32_t cp_world,
                       int32_t cp_rank, int32_t cp_interleave, int32_t *err_flag)

@@ -127,4 +127,47 @@ __device__ int32_t wave_upper_index(const int32_t *v, int32_t n, int64_t x, bool
     return (part && cnt > 0) ? lo + cnt - 1 : -1;
 }
 
+// Logical block lb and in-block offset off of position p >= 0 on this rank.
+// Without context parallelism (world <= 1) lb = p / bs and off = p % bs.  With
+// W ranks and interleave I the ranks deal positions in chunks of I, round
+// robin; a table entry covers a virtual block of bs*W positions, of which each
+// rank keeps its own, in order, in its block of bs slots:
+//   owner = (p / I) % W,  lb = p / (bs*W),  o = p % (bs*W),
+//   off = (o / (I*W)) * I + o % I.
+// Returns false when another rank holds p.  bs*W fits an int32 (host check).
+__device__ __forceinline__ bool cp_locate(int64_t p, int32_t block_size, int32_t world,
+                                          int32_t rank, int32_t interleave, int64_t &lb,
+                                          int32_t &off)
+{
+    const uint32_t bs = static_cast<uint32_t>(block_size);
+    if (world <= 1) {
+        if (p <= INT32_MAX) {
+            const uint32_t q = static_cast<uint32_t>(p) / bs;
+            lb = q;
+            off = static_cast<int32_t>(static_cast<uint32_t>(p) - q * bs);
+        } else {
+            lb = p / block_size;
+            off = static_cast<int32_t>(p - lb * block_size);
+        }
+        return true;
+    }
+    const int64_t w = world, il = interleave, span = static_cast<int64_t>(bs) * w;
+    int64_t o;
+    if (p <= INT32_MAX) {
+        const uint32_t up = static_cast<uint32_t>(p);
+        if ((up / static_cast<uint32_t>(il)) % static_cast<uint32_t>(w) != static_cast<uint32_t>(rank))
+            return false;
+        const uint32_t q = up / static_cast<uint32_t>(span);
+        lb = q;
+        o = up - q * static_cast<uint32_t>(span);
+    } else {
+        if ((p / il) % w != rank) return false;
+        lb = p / span;
+        o = p - lb * span;
+    }
+    const uint32_t uo = static_cast<uint32_t>(o), ui = static_cast<uint32_t>(il);
+    off = static_cast<int32_t>((uo / (ui * static_cast<uint32_t>(w))) * ui + uo % ui);
+    return true;
+}
+
 }  // namespace

@@ -15,7 +15,7 @@ import torch
 
 from .build import LIBRARY
 
-KVW_ABI_VERSION = 5
+KVW_ABI_VERSION = 6
 KVW_PAD_ID = -1
 KVW_MAX_RANGE_STRIDE = 65536
 KVW_OK, KVW_ERR_INVALID_ARG, KVW_ERR_UNSUPPORTED, KVW_ERR_RANGE_CAP, KVW_ERR_HIP = range(5)
@@ -61,7 +61,8 @@ class kvw_decode_args(ctypes.Structure):
         ("k_cache", _P), ("v_cache", _P), ("num_blocks", _I64), ("num_q_heads", _I32),
         ("num_kv_heads", _I32), ("head_dim", _I32), ("scale", ctypes.c_float), ("out", _P),
         ("workspace", _P), ("workspace_bytes", _I64), ("err_flag", _P),
-        ("chunk_positions", _I32),
+        ("chunk_positions", _I32), ("cp_world_size", _I32), ("cp_rank", _I32),
+        ("cp_interleave_size", _I32), ("lse_out", _P),
     ]
 
 
@@ -89,6 +90,7 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
                                       _P],
         "kvw_kv_write": [ctypes.POINTER(kvw_kv_write_args), _P],
         "kvw_decode_attention": [ctypes.POINTER(kvw_decode_args), _P],
+        "kvw_decode_merge": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P],
     }
     for name, argtypes in sigs.items():
         fn = getattr(lib, name)
@@ -293,7 +295,8 @@ def kvw_decode_attention(*, mode, q, k_cache, v_cache, context_lens, max_context
                          block_size, out, block_table=None, num_blocks_per_req=None,
                          range_start=None, range_len=None, range_cum=None, num_ranges=None,
                          scale=None, workspace=None, err_flag=None, stream=None,
-                         chunk_positions=0):
+                         chunk_positions=0, cp_world_size=1, cp_rank=0, cp_interleave_size=1,
+                         lse_out=None):
     """Decode attention over the paged cache (see include/kvw.h).
 
     q: [num_reqs, num_q_heads, head_dim] 2-byte (bf16) tensor; k_cache, v_cache:
@@ -338,4 +341,28 @@ def kvw_decode_attention(*, mode, q, k_cache, v_cache, context_lens, max_context
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.err_flag = _dev(err_flag, torch.int32, "err_flag", optional=True)
     a.chunk_positions = int(chunk_positions)
+    a.cp_world_size, a.cp_rank = int(cp_world_size), int(cp_rank)
+    a.cp_interleave_size = int(cp_interleave_size)
+    if lse_out is not None and (lse_out.dtype != torch.float32 or tuple(lse_out.shape) != (num_reqs, hq)):
+        raise ValueError("lse_out must be float32 [num_reqs, num_q_heads]")
+    a.lse_out = _dev(lse_out, torch.float32, "lse_out", optional=True)
     _check(library().kvw_decode_attention(ctypes.byref(a), _stream(stream)))
+
+
+def kvw_decode_merge(outs, lses, out, lse_out=None, stream=None):
+    """Merge decode attention over disjoint position sets (see include/kvw.h).
+
+    outs: float32 [parts, num_reqs, num_q_heads, head_dim]; lses: float32 [parts, num_reqs,
+    num_q_heads]; out: float32 [num_reqs, num_q_heads, head_dim]; lse_out: optional float32
+    [num_reqs, num_q_heads].
+    """
+    if outs.dim() != 4 or tuple(lses.shape) != tuple(outs.shape[:3]) or \
+            tuple(out.shape) != tuple(outs.shape[1:]):
+        raise ValueError("outs [P, R, Hq, D], lses [P, R, Hq] and out [R, Hq, D] must agree")
+    parts, num_reqs, hq, d = (int(x) for x in outs.shape)
+    _check(library().kvw_decode_merge(parts, num_reqs, hq, d,
+                                      _dev(outs, torch.float32, "outs"),
+                                      _dev(lses, torch.float32, "lses"),
+                                      _dev(out, torch.float32, "out"),
+                                      _dev(lse_out, torch.float32, "lse_out", optional=True),
+                                      _stream(stream)))

@@ -248,4 +248,20 @@ def test_decode_validation(lib):
     assert f(ctypes.byref(_decode(workspace=None)), None) == INVALID
     assert f(ctypes.byref(_decode(chunk_positions=128)), None) == INVALID
     assert f(ctypes.byref(_decode(chunk_positions=768)), None) == INVALID
+    assert f(ctypes.byref(_decode(cp_world_size=2, cp_rank=2, cp_interleave_size=1)), None) == INVALID
+    assert f(ctypes.byref(_decode(cp_world_size=2, cp_rank=1, cp_interleave_size=3)), None) == INVALID
+    assert f(ctypes.byref(_decode(cp_world_size=-1)), None) == INVALID
+    assert f(ctypes.byref(_decode(lse_out=P + 2)), None) == INVALID
     assert f(ctypes.byref(_decode(num_reqs=0)), None) == OK   # nothing to do: no launch
+
+
+def test_decode_merge_validation(lib):
+    f = lib.kvw_decode_merge
+    assert f(0, 4, 32, 128, P, P, P, None, None) == INVALID        # no part
+    assert f(2, 4, 32, 0, P, P, P, None, None) == INVALID          # head_dim
+    assert f(2, 4, 32, 2048, P, P, P, None, None) == INVALID
+    assert f(2, -1, 32, 128, P, P, P, None, None) == INVALID
+    assert f(2, 4, 32, 128, None, P, P, None, None) == INVALID
+    assert f(2, 4, 32, 128, P, P + 2, P, None, None) == INVALID
+    assert f(2, 4, 32, 128, P, P, P, P + 1, None) == INVALID
+    assert f(2, 0, 32, 128, P, P, P, None, None) == OK             # nothing to do: no launch

@@ -565,3 +565,115 @@ def test_decode_through_the_written_table():
     check(got16, q, slots, np.arange(rows, dtype=np.int64), ek.reshape(rows, hkv, 128),
           ev.reshape(rows, hkv, 128), ctx, list(range(w.num_reqs)), hq, hkv, 128 ** -0.5,
           "through the written table")
+
+
+# ---------------------------------------------------------------------------
+# decode context parallelism: each rank attends its own positions; log-sum-exp merge
+# ---------------------------------------------------------------------------
+def lse_tolerance(qh, kr, n, scale, lse):
+    """Bound on |lse error| per query head, from the same summation structure as `tolerance`:
+    the normalizer's relative error plus the score error, plus the final rounding."""
+    hq, hkv = qh.shape[0], kr.shape[1]
+    g = hq // hkv
+    kmax = np.sqrt((kr.astype(np.float64) ** 2).sum(axis=2)).max(axis=0)
+    qn = np.sqrt((qh.astype(np.float64) ** 2).sum(axis=1))
+    big_s = np.log2(np.e) * abs(scale) * qn * kmax[np.arange(hq) // g]
+    rescales = 1 + np.ceil(2 * big_s / RESCALE_LOG2)
+    chunks = -(-int(n) // CHUNK_MIN)
+    return U * (CHUNK_MAX / 2 + 6 * rescales + 2 * chunks + 60 + 20 * big_s + np.abs(lse))
+
+
+@pytest.mark.parametrize("world,inter", [(1, 1), (2, 1), (2, 16), (3, 4), (4, 8)])
+@pytest.mark.parametrize("mode", ["paged", "ranges"])
+def test_decode_context_parallel(mode, world, inter):
+    """Each rank attends the positions it holds, from its own cache (block_size slots per block,
+    the write's context-parallel placement), and reports its log-sum-exp; kvw_decode_merge of the
+    ranks' results equals attention over every position.  Every rank is also checked alone."""
+    orc = oracle.get()
+    reqs = [Request(e, 1 if e else 0) for e in (1, 300, 1000, 2500, 40, 0, 777)]
+    w = custom("cp_read", 4995, reqs, block_size=16, num_blocks=700, runs=("count", 1, 4),
+               dummy_reqs=1)
+    hq, hkv, bs, scale = 32, w.num_kv_heads, w.block_size, 128 ** -0.5
+    ctx = np.array([rq.end for rq in w.requests] + [0], np.int64)
+    total = int(ctx.sum())
+    first = np.concatenate([[0], np.cumsum(ctx)[:-1]])       # flat index of each request's position 0
+    q, _, _, k_flat, v_flat = decode_inputs(w, hq, 31, rows=np.arange(total, dtype=np.int64))
+    # the oracle's attention over every position: flat rows, slot = flat index
+    flat_slots = [np.arange(first[r], first[r] + ctx[r], dtype=np.int64) for r in range(w.num_reqs)]
+    want, want_lse = orc.decode_attention(q, k_flat, v_flat, flat_slots, np.arange(w.num_reqs),
+                                          hq, hkv, scale, with_lse=True)
+    qsl = np.zeros(w.num_reqs + 1, np.int32)
+    qsl[1:] = np.cumsum(ctx)
+    pos = np.concatenate([np.arange(c, dtype=np.int64) for c in ctx])
+    rows = w.num_blocks * bs
+    outs = torch.empty((world, w.num_reqs, hq, 128), dtype=torch.float32, device=DEV)
+    lses = torch.empty((world, w.num_reqs, hq), dtype=torch.float32, device=DEV)
+    qd, cl = dev(q), dev(ctx.astype(np.int32))
+    for rank in range(world):
+        # this rank's slots (-1 for the other ranks' positions), from the oracle
+        if mode == "paged":
+            sl, fl = orc.slot_mapping_paged_cp(qsl, w.num_reqs, pos, total, w.block_table,
+                                               w.num_blocks_per_req, bs, world, rank, inter)
+        else:
+            sl, fl = orc.slot_mapping_ranges_cp(qsl, w.num_reqs, pos, total, w.range_start,
+                                                w.range_len, w.range_cum, w.num_ranges, bs, world,
+                                                rank, inter)
+        assert fl == 0
+        held = sl >= 0
+        kr = np.zeros((rows, hkv, 128), np.uint16)
+        vr = np.zeros_like(kr)
+        kr[sl[held]] = k_flat[held]          # position t of the flat order sits at its slot
+        vr[sl[held]] = v_flat[held]
+        kc, vc = dev(kr), dev(vr)
+        flag = new_flag()
+        common = dict(q=qd, k_cache=kc, v_cache=vc, context_lens=cl, max_context=int(ctx.max()),
+                      num_blocks=w.num_blocks, block_size=bs, out=outs[rank], err_flag=flag,
+                      cp_world_size=world, cp_rank=rank, cp_interleave_size=inter,
+                      lse_out=lses[rank])
+        if mode == "paged":
+            kvw.kvw_decode_attention(mode=kvw.KVW_SLOTS_PAGED, block_table=dev(w.block_table),
+                                     num_blocks_per_req=dev(w.num_blocks_per_req), **common)
+        else:
+            kvw.kvw_decode_attention(mode=kvw.KVW_SLOTS_RANGES, range_start=dev(w.range_start),
+                                     range_len=dev(w.range_len), range_cum=dev(w.range_cum),
+                                     num_ranges=dev(w.num_ranges), **common)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == 0
+        # the rank alone: attention over the positions it holds
+        rank_slots = [sl[qsl[r]:qsl[r + 1]] for r in range(w.num_reqs)]
+        say(f"[decode cp] {mode} W={world} I={inter} rank {rank}: {int(held.sum())} of {total}")
+        got = host(outs[rank])
+        check(got, q, rank_slots, np.arange(rows, dtype=np.int64), kr, vr, ctx,
+              list(range(w.num_reqs)), hq, hkv, scale, f"cp {mode} W={world} rank {rank}")
+        o_r, l_r = orc.decode_attention(q, kr, vr, rank_slots, np.arange(w.num_reqs), hq, hkv,
+                                        scale, with_lse=True)
+        g_l = host(lses[rank]).astype(np.float64)
+        for r in range(w.num_reqs):
+            mine = rank_slots[r][rank_slots[r] >= 0]
+            if len(mine) == 0:
+                assert np.all(g_l[r] == -np.inf)
+                continue
+            tol = lse_tolerance(f32(q[r]), f32(kr[mine]), ctx[r], scale, l_r[r])
+            assert np.all(np.abs(g_l[r] - l_r[r]) <= tol), f"rank {rank} request {r}: lse"
+    # the merge of the ranks' results against attention over every position
+    merged = torch.full((w.num_reqs, hq, 128), float("nan"), dtype=torch.float32, device=DEV)
+    merged_lse = torch.full((w.num_reqs, hq), float("nan"), dtype=torch.float32, device=DEV)
+    kvw.kvw_decode_merge(outs, lses, merged, merged_lse)
+    torch.cuda.synchronize()
+    got = host(merged).astype(np.float64)
+    got_lse = host(merged_lse).astype(np.float64)
+    ratio = 0.0
+    for r in range(w.num_reqs):
+        if ctx[r] == 0:
+            assert (got[r] == 0).all() and np.all(got_lse[r] == -np.inf)
+            continue
+        rows_r = flat_slots[r]
+        tol = tolerance(f32(q[r]), f32(k_flat[rows_r]), f32(v_flat[rows_r]), ctx[r], scale)
+        err = np.abs(got[r] - want[r]).max(axis=1)
+        assert (err <= tol).all(), f"merged request {r}: error {err.max():.3e}"
+        ltol = lse_tolerance(f32(q[r]), f32(k_flat[rows_r]), ctx[r], scale, want_lse[r])
+        assert np.all(np.abs(got_lse[r] - want_lse[r]) <= ltol), f"merged request {r}: lse"
+        ratio = max(ratio, float((err / tol).max()))
+    say(f"[decode cp] {mode} W={world} I={inter}: merged, largest error {ratio:.3f} of the bound")
+    if world == 1:  # one part: the merge returns it
+        assert np.array_equal(host(merged), host(outs[0]))
