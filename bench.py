@@ -564,9 +564,55 @@ def decode_attention(args, d, dev, stream, timed):
                         "frac_of_peak": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                         "call_ms_by_chunk": {str(c): round(v[0], 5) for c, v in by_chunk.items()
                                              if c}}
+        if wname == "long_context_r4096":
+            out["context_parallel_W2"] = decode_context_parallel(
+                args, w, ctx, qd, cl, kc, vc, ws, maps["paged"], hq, timed, stream, kvw, torch)
         del kc, vc, ws
         torch.cuda.empty_cache()
     return out
+
+
+def decode_context_parallel(args, w, ctx, qd, cl, kc, vc, ws, paged, hq, timed, stream, kvw, torch):
+    """Decode context parallelism at W = 2, interleave 1, paged: each rank attends the half of
+    the positions it holds (timed one rank after the other on this GPU, each from a cache of
+    block_size slots per block), then the ranks' results are merged by their log-sum-exp."""
+    world = 2
+    max_ctx = int(ctx.max())
+    outs = torch.empty((world, w.num_reqs, hq, w.head_dim), dtype=torch.float32, device=kc.device)
+    lses = torch.empty((world, w.num_reqs, hq), dtype=torch.float32, device=kc.device)
+    res = {}
+    for rank in range(world):
+        def call(ev, rank=rank):
+            if ev is not None:
+                ev[0].record(stream)
+            kvw.kvw_decode_attention(q=qd, k_cache=kc, v_cache=vc, context_lens=cl,
+                                     max_context=max_ctx, num_blocks=w.num_blocks,
+                                     block_size=w.block_size, out=outs[rank], workspace=ws,
+                                     cp_world_size=world, cp_rank=rank, cp_interleave_size=1,
+                                     lse_out=lses[rank], **paged)
+            if ev is not None:
+                ev[1].record(stream)
+        _, ev_ms = timed(call, args.warmup, args.steps)
+        avg = statistics.fmean(ev_ms)
+        held = int(ctx.sum()) // world
+        nbytes = held * w.num_kv_heads * w.head_dim * 2 * 2 + w.num_reqs * hq * w.head_dim * 6
+        res[f"rank{rank}"] = {"positions": held, "call_ms_avg": round(avg, 5),
+                              "gbps": round(nbytes / (avg * 1e-3) / 1e9, 1),
+                              "frac_of_peak": round(nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        log(f"[bench] decode attention context parallel W=2 rank {rank}: {avg * 1e3:8.1f} us = "
+            f"{res[f'rank{rank}']['gbps']:5.0f} GB/s")
+    merged = torch.empty((w.num_reqs, hq, w.head_dim), dtype=torch.float32, device=kc.device)
+
+    def merge(ev):
+        if ev is not None:
+            ev[0].record(stream)
+        kvw.kvw_decode_merge(outs, lses, merged)
+        if ev is not None:
+            ev[1].record(stream)
+    _, ev_ms = timed(merge, args.warmup, args.steps)
+    res["merge_ms_avg"] = round(statistics.fmean(ev_ms), 5)
+    log(f"[bench] decode attention context parallel W=2 merge: {res['merge_ms_avg'] * 1e3:.1f} us")
+    return res
 
 
 def bench_config(args):

@@ -182,13 +182,21 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
     flags = 0;
     const int64_t c0 = static_cast<int64_t>(c) * a.chunk;
     if (c0 >= n) return;  // uniform over the workgroup: no barrier is skipped by part of it
-    const int32_t cnt = static_cast<int32_t>(n - c0 < a.chunk ? n - c0 : a.chunk);
+    const int32_t span = static_cast<int32_t>(n - c0 < a.chunk ? n - c0 : a.chunk);
     const int32_t bs = a.block_size;
 
-    // 0. slots of this chunk's positions, resolved once for every head
-    for (int base = 0; base < cnt; base += blockDim.x) {  // uniform trip count
+    // 0. slots of this chunk's positions, resolved once for every head and packed in position
+    // order: a position that holds nothing here (another context-parallel rank's, or a pad
+    // slot) takes no place, so the pass below runs over cnt held positions only.  Each wave
+    // counts its held positions (ballot); the counts of the waves before it give its offset.
+    __shared__ int32_t s_wave_count[kMaxKvHeads];
+    const int nwaves = static_cast<int>(blockDim.x) / kWave;
+    const int wave_id = static_cast<int>(threadIdx.x) / kWave;
+    const int lane_id = static_cast<int>(threadIdx.x) & (kWave - 1);
+    int32_t cnt = 0;  // held positions packed so far: the same value in every thread
+    for (int base = 0; base < span; base += blockDim.x) {  // uniform trip count
         const int t = base + static_cast<int>(threadIdx.x);
-        const bool in = t < cnt;
+        const bool in = t < span;
         const int64_t p = c0 + t;
         int64_t lb = 0;
         int32_t off = 0;
@@ -221,9 +229,16 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
         }
         int64_t slot = b < 0 ? -1 : b * bs + off;
         if (slot >= a.cache_rows) { flags |= KVW_FLAG_SLOT_OOB; slot = -1; }
-        if (in) s_slot[t] = slot;
+        const bool held = in && slot >= 0;
+        const uint64_t mask = __ballot(held);
+        if (lane_id == 0) s_wave_count[wave_id] = __popcll(mask);
+        __syncthreads();
+        int32_t at = cnt;
+        for (int i = 0; i < wave_id; ++i) at += s_wave_count[i];
+        if (held) s_slot[at + __popcll(mask & ((uint64_t{1} << lane_id) - 1))] = slot;
+        for (int i = 0; i < nwaves; ++i) cnt += s_wave_count[i];
+        __syncthreads();  // the counts are rewritten by the next round
     }
-    __syncthreads();
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;       // key/value head of this wave
