@@ -20,7 +20,9 @@
 // position row.
 //   0. The workgroup resolves the slots of its positions once, into LDS: the
 //      block-table gather (PAGED) or range arithmetic with the wavefront
-//      search over range_cum (RANGES).  Every head reads them from LDS.
+//      search over range_cum (RANGES).  Positions that hold nothing here
+//      (another context-parallel rank's, pad slots) are dropped and the rest
+//      packed in order.  Every head reads them from LDS.
 //   1. One pass over the chunk: 16 lanes per position, 8 head dims (16 B of
 //      K and of V) per lane, four positions per wave and U positions per lane
 //      group in flight.  Each lane group keeps, per query head, a running
