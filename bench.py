@@ -25,6 +25,13 @@ rank writes its share of the batch into its own cache.  And per
 tensor-parallel rank (TP = 2, 4, 8 over the 8 KV heads): rows of 2048/TP
 bytes, every token.
 
+The read side is measured too ("decode_attention"): decode attention, one
+query per request with 32 query heads over the 8 KV heads, over the 128K
+layouts (R = 1 and 4096) and the 256-request decode step, paged gather vs
+range arithmetic, at every chunk length; and decode context parallelism at
+W = 2 (each rank's share, then the log-sum-exp merge).  --decode-only runs
+just that part (for profiling).
+
 `value` is tokens/s of paged_r4096; every variant is reported under
 "variants", with the fused call's time (HIP events on the launch stream)
 and the time of the one-kernel schedule.
