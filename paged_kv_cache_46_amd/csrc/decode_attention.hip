@@ -10,14 +10,15 @@
 // 256 B of V for its key/value head and does 2 * G * 128 multiply-adds (G
 // query heads per key/value head), G flop per byte: 32 TFLOP/s at 8 TB/s for
 // G = 4.  That is 40% of the fp32 vector rate without packed math, so the
-// vector instructions per position are kept few: the q.k products run on
-// v_dot2c_f32_bf16 straight from the bf16 pairs, the 16-lane sums on DPP
-// adds, the exponentials on v_exp_f32 in base 2, and the running maximum is
-// only moved when it grows by more than 2^8.
+// vector instructions per position are kept few.  For G = 4 and 8 the q.k
+// products run on matrix cores (decode_partial_mfma_kernel); for G = 1 and 2
+// on v_dot2c_f32_bf16 straight from the bf16 pairs with 16-lane sums on DPP
+// adds (decode_partial_kernel).  The exponentials run on v_exp_f32 in base 2,
+// and the running maximum is only moved when it grows by more than 2^8.
 //
-// decode_partial_kernel<MODE, G, L>: one workgroup per (chunk of 256, 512 or
-// 1024 positions, request), one wave per key/value head, L = 16 lanes per
-// position row.
+// decode_partial_kernel<MODE, G, L> (G = 1, 2) and decode_partial_mfma_kernel<MODE, G>
+// (G = 4, 8): one workgroup per (chunk of 256, 512 or 1024 positions, request),
+// one wave per key/value head, L = 16 lanes per position row for P.V.
 //   0. The workgroup resolves the slots of its positions once, into LDS: the
 //      block-table gather (PAGED) or range arithmetic with the wavefront
 //      search over range_cum (RANGES).  Positions that hold nothing here
@@ -68,6 +69,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct DecodeArgs {
     const uint16_t *q;
@@ -113,6 +116,25 @@ __device__ __forceinline__ int32_t context_of(const DecodeArgs &a, int32_t r, ui
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// max(x, the same register of another lane of its row), picked by a DPP control.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float x)
+{
+    return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY),
+                                                               __float_as_int(x), CTRL, 0xF, 0xF,
+                                                               false)));
+}
+
+// Maximum over the 16 lanes of a row, left in every lane (the pattern of row_sum).
+__device__ __forceinline__ float row_max16(float x)
+{
+    x = dpp_max<0xB1>(x);
+    x = dpp_max<0x4E>(x);
+    x = dpp_max<0x141>(x);
+    x = dpp_max<0x140>(x);
+    return x;
+}
 
 // x + the same register of another lane of its row, picked by a DPP control.
 template <int CTRL>
@@ -161,37 +183,16 @@ constexpr int unroll_of()
 template <int G>
 constexpr int partial_threads() { return kWave * (G <= 4 ? kMaxKvHeads : kMaxKvHeads / 2); }
 
-template <int MODE, int G, int L>
-__global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(DecodeArgs a)
+// The slots of positions c0 .. c0+span-1 of request r, resolved once for every
+// head and packed into s_slot in position order; returns how many there are.  A
+// position that holds nothing here (another context-parallel rank's, or a pad
+// slot) takes no place.  Each wave counts its held positions (ballot); the counts
+// of the waves before it give its offset.  Every thread of the workgroup calls it.
+template <int MODE>
+__device__ int32_t stage_slots(const DecodeArgs &a, int32_t r, int64_t c0, int32_t span,
+                               int64_t *s_slot, int32_t *s_wave_count, uint32_t &flags)
 {
-    constexpr int U = unroll_of<G, L>();
-    constexpr int NV = kHeadDim / (L * 8);   // 16-byte pieces of a row per lane (1 or 2)
-    constexpr int DPL = NV * 8;              // head dims per lane
-    constexpr int RPP = kWave / L;           // positions per wave load
-    __shared__ int64_t s_slot[kMaxChunk];
-    int32_t r, c;
-    if (a.units) {
-        if (static_cast<int32_t>(blockIdx.x) >= *a.unit_count) return;  // uniform
-        const int2 rc = a.units[blockIdx.x];
-        r = rc.x;
-        c = rc.y;
-    } else {
-        r = blockIdx.y;
-        c = blockIdx.x;
-    }
-    uint32_t flags = 0;
-    const int32_t n = context_of(a, r, flags);  // a clamp is reported by the combine launch
-    flags = 0;
-    const int64_t c0 = static_cast<int64_t>(c) * a.chunk;
-    if (c0 >= n) return;  // uniform over the workgroup: no barrier is skipped by part of it
-    const int32_t span = static_cast<int32_t>(n - c0 < a.chunk ? n - c0 : a.chunk);
     const int32_t bs = a.block_size;
-
-    // 0. slots of this chunk's positions, resolved once for every head and packed in position
-    // order: a position that holds nothing here (another context-parallel rank's, or a pad
-    // slot) takes no place, so the pass below runs over cnt held positions only.  Each wave
-    // counts its held positions (ballot); the counts of the waves before it give its offset.
-    __shared__ int32_t s_wave_count[kMaxKvHeads];
     const int nwaves = static_cast<int>(blockDim.x) / kWave;
     const int wave_id = static_cast<int>(threadIdx.x) / kWave;
     const int lane_id = static_cast<int>(threadIdx.x) & (kWave - 1);
@@ -241,6 +242,37 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
         for (int i = 0; i < nwaves; ++i) cnt += s_wave_count[i];
         __syncthreads();  // the counts are rewritten by the next round
     }
+    return cnt;
+}
+
+template <int MODE, int G, int L>
+__global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(DecodeArgs a)
+{
+    constexpr int U = unroll_of<G, L>();
+    constexpr int NV = kHeadDim / (L * 8);   // 16-byte pieces of a row per lane (1 or 2)
+    constexpr int DPL = NV * 8;              // head dims per lane
+    constexpr int RPP = kWave / L;           // positions per wave load
+    __shared__ int64_t s_slot[kMaxChunk];
+    int32_t r, c;
+    if (a.units) {
+        if (static_cast<int32_t>(blockIdx.x) >= *a.unit_count) return;  // uniform
+        const int2 rc = a.units[blockIdx.x];
+        r = rc.x;
+        c = rc.y;
+    } else {
+        r = blockIdx.y;
+        c = blockIdx.x;
+    }
+    uint32_t flags = 0;
+    const int32_t n = context_of(a, r, flags);  // a clamp is reported by the combine launch
+    flags = 0;
+    const int64_t c0 = static_cast<int64_t>(c) * a.chunk;
+    if (c0 >= n) return;  // uniform over the workgroup: no barrier is skipped by part of it
+    const int32_t span = static_cast<int32_t>(n - c0 < a.chunk ? n - c0 : a.chunk);
+
+    // 0. slots of this chunk's positions, resolved once for every head, packed in LDS
+    __shared__ int32_t s_wave_count[kMaxKvHeads];
+    const int32_t cnt = stage_slots<MODE>(a, r, c0, span, s_slot, s_wave_count, flags);
 
     const int lane = threadIdx.x & (kWave - 1);
     const int w = threadIdx.x / kWave;       // key/value head of this wave
@@ -405,6 +437,185 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
     if (tid == 0) *a.unit_count = s_total;
 }
 
+// q.k on matrix cores for G = 4 or 8 query heads per key/value head (one wave
+// per key/value head, tiles of 16 positions).  The scores of a tile are one
+// 16 x 16 product over 4 steps of 32 head dims (v_mfma_f32_16x16x32_bf16: lane
+// l holds the query rows' dims 8*(l/16) .. +8 of step k as the A operand, the K
+// row of position l%16 as the B operand, and gets scores of rows 4*(l/16) .. +3,
+// column l%16).  The G query heads fill rows 0..G-1; the other rows are zero and
+// masked.  The
+// softmax runs in that layout (a row's maximum over the tile's 16 positions by
+// DPP, one exponential per lane and row), and the weights and the rescale factors
+// go through a per-wave LDS tile to the P.V lanes, which accumulate in fp32 on
+// the vector units as in decode_partial_kernel (16 lanes per position row).
+template <int MODE, int G>
+__global__ __launch_bounds__(partial_threads<G>()) void decode_partial_mfma_kernel(DecodeArgs a)
+{
+    constexpr int kTile = 16;
+    constexpr int kWaves = partial_threads<G>() / kWave;
+    __shared__ int64_t s_slot[kMaxChunk];
+    __shared__ int32_t s_wave_count[kMaxKvHeads];
+    __shared__ __attribute__((aligned(16))) float s_p[kWaves][kTile][16];  // [position][row]
+    __shared__ __attribute__((aligned(16))) float s_alpha[kWaves][16];
+    int32_t r, c;
+    if (a.units) {
+        if (static_cast<int32_t>(blockIdx.x) >= *a.unit_count) return;  // uniform
+        const int2 rc = a.units[blockIdx.x];
+        r = rc.x;
+        c = rc.y;
+    } else {
+        r = blockIdx.y;
+        c = blockIdx.x;
+    }
+    uint32_t flags = 0;
+    const int32_t n = context_of(a, r, flags);  // a clamp is reported by the combine launch
+    flags = 0;
+    const int64_t c0 = static_cast<int64_t>(c) * a.chunk;
+    if (c0 >= n) return;  // uniform over the workgroup
+    const int32_t span = static_cast<int32_t>(n - c0 < a.chunk ? n - c0 : a.chunk);
+    const int32_t cnt = stage_slots<MODE>(a, r, c0, span, s_slot, s_wave_count, flags);
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;       // key/value head of this wave
+    const int col = lane % kTile;            // MFMA side: position of the tile; P.V side: dims
+    const int rg = lane / kTile;             // MFMA side: rows 4*rg .. +3; P.V side: position group
+    const int hq0 = w * G;
+    const int64_t row_bytes = static_cast<int64_t>(a.num_kv_heads) * kHeadDim * 2;
+    const uint8_t *kbase = a.k_cache + static_cast<int64_t>(w) * kHeadDim * 2 + rg * 16;
+    const uint8_t *vbase = a.v_cache + static_cast<int64_t>(w) * kHeadDim * 2 + col * 16;
+
+    bf16x8 qa[4];  // A operand: query row col, dims 32*k + 8*rg .. +8
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        u32x4 v = u32x4{0, 0, 0, 0};
+        if (col < G)
+            v = load16<false>(reinterpret_cast<const uint8_t *>(
+                a.q + (static_cast<int64_t>(r) * a.num_q_heads + hq0 + col) * kHeadDim + 32 * k + 8 * rg));
+        qa[k] = __builtin_bit_cast(bf16x8, v);
+    }
+    float m[4];                   // MFMA side: running maximum of rows 4*rg + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m[i] = kNoMax;
+    float l[G], acc[G][8];        // P.V side
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        l[g] = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[g][k] = 0.f;
+    }
+    float *tile = &s_p[w][0][0];
+    float *alpha_row = &s_alpha[w][0];
+
+    for (int tb = 0; tb < cnt; tb += kTile) {  // uniform trip count
+        // loads: K of position tb + col as the B operand, V of positions tb + 4u + rg
+        const int tk = tb + col;
+        const int64_t slk = tk < cnt ? s_slot[tk] : -1;
+        u32x4 kw[4], vw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            kw[k] = slk >= 0 ? load16<true>(kbase + slk * row_bytes + 64 * k) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int tv = tb + 4 * u + rg;
+            const int64_t slv = tv < cnt ? s_slot[tv] : -1;
+            vw[u] = slv >= 0 ? load16<true>(vbase + slv * row_bytes) : u32x4{0, 0, 0, 0};
+        }
+        // scores of the tile: rows 4*rg + i, column col
+        f32x4 sc4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            sc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[k], __builtin_bit_cast(bf16x8, kw[k]),
+                                                          sc4, 0, 0, 0);
+        float p[4], alpha[4];
+        bool moved = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float sc = (slk >= 0 && 4 * rg + i < G) ? sc4[i] * a.scale_log2 : -INFINITY;
+            const float mx = row_max16(sc);
+            alpha[i] = 1.f;
+            if (mx > m[i] + kRescaleLog2) {  // also at the first position (m = kNoMax)
+                alpha[i] = __builtin_amdgcn_exp2f(m[i] - mx);
+                m[i] = mx;
+                moved = true;
+            }
+            p[i] = __builtin_amdgcn_exp2f(sc - m[i]);  // 0 for a masked score
+        }
+        // to the P.V side: weights [position][row] and the rows' rescale factors
+        *reinterpret_cast<f32x4 *>(tile + col * 16 + 4 * rg) = f32x4{p[0], p[1], p[2], p[3]};
+        if (col == 0) *reinterpret_cast<f32x4 *>(alpha_row + 4 * rg) = f32x4{alpha[0], alpha[1], alpha[2], alpha[3]};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (__ballot(moved)) {  // uniform: some row of the wave moved its maximum
+            float al[G];
+#pragma unroll
+            for (int j = 0; j < G / 4; ++j) {
+                const f32x4 aj = *reinterpret_cast<const f32x4 *>(alpha_row + 4 * j);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) al[4 * j + i] = aj[i];
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                l[g] *= al[g];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[g][k] *= al[g];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float pv[G];
+#pragma unroll
+            for (int j = 0; j < G / 4; ++j) {
+                const f32x4 pj = *reinterpret_cast<const f32x4 *>(tile + (4 * u + rg) * 16 + 4 * j);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pv[4 * j + i] = pj[i];
+            }
+            float vf[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                vf[2 * k] = bf16_lo(vw[u][k]);
+                vf[2 * k + 1] = bf16_hi(vw[u][k]);
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                l[g] += pv[g];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[g][k] += pv[g] * vf[k];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();  // the tile is rewritten by the next iteration
+    }
+
+    // the four P.V position groups share each row's maximum: plain sums across them
+#pragma unroll
+    for (int o = kTile; o < kWave; o <<= 1) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            l[g] += __shfl_xor(l[g], o);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[g][k] += __shfl_xor(acc[g][k], o);
+        }
+    }
+    const int64_t part = (static_cast<int64_t>(r) * a.splits + c) * a.num_q_heads + hq0;
+    if (rg == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float *dst = a.ws_acc + (part + g) * kHeadDim + col * 8;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) dst[k] = acc[g][k];
+        }
+    }
+    if (col == 0 && 4 * rg < G) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a.ws_ml[(part + 4 * rg + i) * 2] = m[i];
+            a.ws_ml[(part + 4 * rg + i) * 2 + 1] = l[4 * rg + i];
+        }
+    }
+    raise_flags(a.err_flag, flags);
+}
+
 // Sum or maximum over the workgroup's waves, in every thread.
 template <int WAVES>
 __device__ __forceinline__ float block_reduce(float v, bool is_max, float *s_red)
@@ -524,8 +735,8 @@ void launch_partial(int group, dim3 grid, dim3 block, size_t lds, hipStream_t s,
     switch (group) {
     case 1: hipLaunchKernelGGL((decode_partial_kernel<MODE, 1, kRowLanes>), grid, block, lds, s, a); break;
     case 2: hipLaunchKernelGGL((decode_partial_kernel<MODE, 2, kRowLanes>), grid, block, lds, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_partial_kernel<MODE, 4, kRowLanes>), grid, block, lds, s, a); break;
-    default: hipLaunchKernelGGL((decode_partial_kernel<MODE, 8, kRowLanes>), grid, block, lds, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_partial_mfma_kernel<MODE, 4>), grid, block, lds, s, a); break;
+    default: hipLaunchKernelGGL((decode_partial_mfma_kernel<MODE, 8>), grid, block, lds, s, a); break;
     }
 }
 

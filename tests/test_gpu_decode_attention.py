@@ -24,8 +24,11 @@ longest chain and P/4 + R + C + 12 along the denominator's, 2u per base-2
 exponential (each p, and the R + 3 rescale factors a term can meet), and the
 score error (4 two-term dot steps, 4 row adds, the scale product and the
 subtraction of m: at most u(12S + 8) in log2 units, each weight moving by ln 2
-times that, twice).  The bound is written out in `tolerance` below.  Requests
-with no readable position must give exactly 0.
+times that, twice).  With 4 or 8 query heads per key/value head the kernel takes
+q.k on matrix cores, a 128-term fp32 accumulation whose order the hardware fixes,
+so the score error is taken as u(129S + 8) and the last term becomes 190S.  The
+bound is written out in `tolerance` below.  Requests with no readable position
+must give exactly 0.
 
 The bound grows with the context, so at 128K a single dropped position would hide
 under it.  The "integers" inputs close that gap bit-exactly: with K = 0 every
@@ -153,7 +156,14 @@ def tolerance(qh, kr, vr, n, scale):
     big_s = np.log2(np.e) * abs(scale) * qn * kmax[heads]
     rescales = 1 + np.ceil(2 * big_s / RESCALE_LOG2)
     chunks = -(-int(n) // CHUNK_MIN)
-    return U * vmax[heads] * (CHUNK_MAX / 2 + 6 * rescales + 2 * chunks + 60 + 20 * big_s)
+    return U * vmax[heads] * (CHUNK_MAX / 2 + 6 * rescales + 2 * chunks + 60 +
+                              score_coefficient(g) * big_s)
+
+
+def score_coefficient(group):
+    """Weight of S in the bounds: 20 for the vector path's q.k (1 or 2 query heads per
+    key/value head), 190 for the matrix-core path (4 or 8; see the module docstring)."""
+    return 190 if group >= 4 else 20
 
 
 def check(gpu, q, slots, rows, k, v, ctx_eff, sel, hq, hkv, scale, tag, exact=False):
@@ -580,7 +590,8 @@ def lse_tolerance(qh, kr, n, scale, lse):
     big_s = np.log2(np.e) * abs(scale) * qn * kmax[np.arange(hq) // g]
     rescales = 1 + np.ceil(2 * big_s / RESCALE_LOG2)
     chunks = -(-int(n) // CHUNK_MIN)
-    return U * (CHUNK_MAX / 2 + 6 * rescales + 2 * chunks + 60 + 20 * big_s + np.abs(lse))
+    return U * (CHUNK_MAX / 2 + 6 * rescales + 2 * chunks + 60 + score_coefficient(g) * big_s +
+                np.abs(lse))
 
 
 @pytest.mark.parametrize("world,inter", [(1, 1), (2, 1), (2, 16), (3, 4), (4, 8)])
