@@ -36,9 +36,9 @@
 // classes), so that the short ones fill the last round of workgroups.  The
 // partial kernel then takes its pair from the list.  The order decides only
 // the schedule: each pair has its own place in the workspace.
-// decode_combine_kernel<SLICES>: per (query head, request), one thread per
-// head dim and slice of the chunks (one slice, or four when a request can have
-// 64 chunks or more) merges the chunks with the rescaling by 2^(m_c - max m).
+// decode_combine_kernel: per (query head, request), 256 threads merge the
+// chunks with the rescaling by 2^(m_c - max m): eight slices of the chunks,
+// four head dims per thread.
 
 #include <hip/hip_runtime.h>
 
@@ -57,6 +57,7 @@ constexpr int kMaxChunk = 1024;                      // positions per workgroup,
 constexpr int kMinChunk = 256;                       // ... and at least; the workspace is sized per 256
 constexpr int kPlanThreads = 1024;                   // the plan kernel's one workgroup
 constexpr int kTailClasses = 16;                     // length classes of the partial chunks
+constexpr int kCombineThreads = 256;                 // combine workgroup: 8 chunk slices x 32 threads
 constexpr int32_t kPlanMinReqs = 32;                 // batches this large get a work list
 constexpr int kHeadDim = 128;                        // supported head_dim
 constexpr int kRowLanes = 16;                        // lanes per position row of one head (8 was
@@ -620,75 +621,75 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_mfma_kern
     raise_flags(a.err_flag, flags);
 }
 
-// Sum or maximum over the workgroup's waves, in every thread.
-template <int WAVES>
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float *s_red)
-{
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) {
-        const float t = __shfl_xor(v, o);
-        v = is_max ? fmaxf(v, t) : v + t;
-    }
-    if ((threadIdx.x & (kWave - 1)) == 0) s_red[threadIdx.x / kWave] = v;
-    __syncthreads();
-    v = s_red[0];
-#pragma unroll
-    for (int i = 1; i < WAVES; ++i) v = is_max ? fmaxf(v, s_red[i]) : v + s_red[i];
-    __syncthreads();
-    return v;
-}
-
 // out[r][h][d] from the chunks of request r:
 //   sum_c 2^(m_c - M) acc_c[d] / sum_c 2^(m_c - M) l_c,  M = max of m_c over chunks with l_c > 0.
-// Thread (slice, d) sums the numerator over chunks slice, slice + SLICES, ...; the
-// slices are added in LDS.  This launch covers every request whatever max_context
-// is, so it reports a clamped length.
-template <int SLICES>
-__global__ __launch_bounds__(kHeadDim * SLICES) void decode_combine_kernel(DecodeArgs a)
+// Two load phases, so that few memory round trips stand between launch and result:
+//   1. every thread reads the (m, l) of chunks tid, tid + 256, ... and the
+//      workgroup's maximum M follows from wave shuffles and one barrier;
+//   2. thread (slice, quad) sums, over chunks slice, slice + 8, ..., the weighted
+//      acc of head dims 4*quad .. +3 (one 16-byte load per chunk, 16 chunks in
+//      flight) and the weighted l; the eight slices are added in LDS.
+// This launch covers every request whatever max_context is, so it reports a
+// clamped length.
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeArgs a)
 {
-    constexpr int kThreads = kHeadDim * SLICES;
-    __shared__ float s_red[kThreads / kWave];
-    __shared__ float s_num[SLICES][kHeadDim];
+    constexpr int kQuads = kHeadDim / 4;
+    constexpr int kSlices = kCombineThreads / kQuads;
+    __shared__ float s_max[kCombineThreads / kWave];
+    __shared__ __attribute__((aligned(16))) float s_num[kSlices][kHeadDim];
+    __shared__ float s_den[kSlices];
     const int32_t h = blockIdx.x, r = blockIdx.y;
-    const int tid = threadIdx.x, d = tid % kHeadDim, slice = tid / kHeadDim;
+    const int tid = threadIdx.x, quad = tid % kQuads, slice = tid / kQuads;
     uint32_t flags = 0;
     const int32_t n = context_of(a, r, flags);
     if (h == 0 && tid == 0) raise_flags(a.err_flag, flags);
     const int32_t chunks = static_cast<int32_t>((static_cast<int64_t>(n) + a.chunk - 1) / a.chunk);
     const int64_t base = static_cast<int64_t>(r) * a.splits * a.num_q_heads + h;
-    const float *ml = a.ws_ml + base * 2;
-    const int64_t step = static_cast<int64_t>(a.num_q_heads) * 2;
+    const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + base;  // (m, l) of chunk c at c*Hq
+    const int64_t step = a.num_q_heads;
+
     float mx = -INFINITY;
-    for (int32_t c = tid; c < chunks; c += kThreads)
-        if (ml[c * step + 1] > 0.f) mx = fmaxf(mx, ml[c * step]);
-    mx = block_reduce<kThreads / kWave>(mx, true, s_red);
-    float den = 0.f;
-    for (int32_t c = tid; c < chunks; c += kThreads) {
-        const float lc = ml[c * step + 1];
-        if (lc > 0.f) den += __builtin_amdgcn_exp2f(ml[c * step] - mx) * lc;
+    for (int32_t c = tid; c < chunks; c += kCombineThreads) {
+        const float2 v = ml[c * step];
+        if (v.y > 0.f) mx = fmaxf(mx, v.x);
     }
-    den = block_reduce<kThreads / kWave>(den, false, s_red);
-    float num = 0.f;
-    const float *acc = a.ws_acc + base * kHeadDim + d;
-    const int64_t acc_step = static_cast<int64_t>(a.num_q_heads) * kHeadDim;
-#pragma unroll 8
-    for (int32_t c = slice; c < chunks; c += SLICES) {
-        const float lc = ml[c * step + 1];
-        const float e = lc > 0.f ? __builtin_amdgcn_exp2f(ml[c * step] - mx) : 0.f;
-        num += e * acc[c * acc_step];
-    }
-    if (SLICES > 1) {
-        s_num[slice][d] = num;
-        __syncthreads();
-    }
-    if (slice == 0) {
 #pragma unroll
-        for (int i = 1; i < SLICES; ++i) num += s_num[i][d];
-        a.out[(static_cast<int64_t>(r) * a.num_q_heads + h) * kHeadDim + d] = den > 0.f ? num / den : 0.f;
+    for (int o = kWave / 2; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((tid & (kWave - 1)) == 0) s_max[tid / kWave] = mx;
+    __syncthreads();
+    mx = s_max[0];
+#pragma unroll
+    for (int i = 1; i < kCombineThreads / kWave; ++i) mx = fmaxf(mx, s_max[i]);
+
+    float num0 = 0.f, num1 = 0.f, num2 = 0.f, num3 = 0.f, den = 0.f;
+    const f32x4 *acc = reinterpret_cast<const f32x4 *>(a.ws_acc + base * kHeadDim) + quad;
+    const int64_t acc_step = static_cast<int64_t>(a.num_q_heads) * (kHeadDim / 4);
+#pragma unroll 16
+    for (int32_t c = slice; c < chunks; c += kSlices) {
+        const float2 v = ml[c * step];
+        const f32x4 x = acc[c * acc_step];
+        const float e = v.y > 0.f ? __builtin_amdgcn_exp2f(v.x - mx) : 0.f;
+        num0 += e * x[0];
+        num1 += e * x[1];
+        num2 += e * x[2];
+        num3 += e * x[3];
+        den += e * v.y;
+    }
+    *reinterpret_cast<f32x4 *>(&s_num[slice][4 * quad]) = f32x4{num0, num1, num2, num3};
+    if (quad == 0) s_den[slice] = den;
+    __syncthreads();
+    if (tid < kHeadDim) {
+        float sum = s_num[0][tid], dsum = s_den[0];
+#pragma unroll
+        for (int i = 1; i < kSlices; ++i) {
+            sum += s_num[i][tid];
+            dsum += s_den[i];
+        }
+        a.out[(static_cast<int64_t>(r) * a.num_q_heads + h) * kHeadDim + tid] = dsum > 0.f ? sum / dsum : 0.f;
         // log sum_j e^(s_j) = ln 2 * (M + log2(den)), scores in base-2 units; -inf with no position
-        if (a.lse_out && d == 0)
+        if (a.lse_out && tid == 0)
             a.lse_out[static_cast<int64_t>(r) * a.num_q_heads + h] =
-                den > 0.f ? (mx + log2f(den)) * kLn2 : -INFINITY;
+                dsum > 0.f ? (mx + log2f(dsum)) * kLn2 : -INFINITY;
     }
 }
 
@@ -890,8 +891,7 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
         if (e != hipSuccess) return fail(KVW_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     }
     const dim3 cgrid(static_cast<unsigned>(g.num_q_heads), static_cast<unsigned>(g.num_reqs));
-    if (a.splits >= 64) hipLaunchKernelGGL(decode_combine_kernel<4>, cgrid, dim3(kHeadDim * 4), 0, s, a);
-    else hipLaunchKernelGGL(decode_combine_kernel<1>, cgrid, dim3(kHeadDim), 0, s, a);
+    hipLaunchKernelGGL(decode_combine_kernel, cgrid, dim3(kCombineThreads), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(KVW_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KVW_OK;
