@@ -565,7 +565,7 @@ def decode_attention(args, d, dev, stream, timed):
             nbytes = decode_bytes(w, ctx, hq, mode)
             key = f"{wname}_{mode}"
             by_chunk = {}
-            for chunk in (0, 256, 512, 1024):  # 0: the library's own choice, reported first
+            for chunk in (0, 256, 512, 1024, 2048):  # 0: the library's own choice, reported first
                 def call(ev, mp=mp, chunk=chunk):
                     if ev is not None:
                         ev[0].record(stream)

@@ -351,7 +351,7 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream);
  *   workspace          device memory of kvw_decode_workspace_size(...) bytes, owned by
  *                      the caller; its contents need no initialisation and are
  *                      overwritten; calls that overlap on one workspace race
- *   chunk_positions    positions per workgroup: 256, 512 or 1024; 0 picks one from
+ *   chunk_positions    positions per workgroup: 256, 512, 1024 or 2048; 0 picks one from
  *                      num_reqs and max_context (results differ only in rounding)
  *   cp_world_size, cp_rank, cp_interleave_size
  *                      decode context parallelism ([P2] "Entwurfsmotivation"; the
@@ -393,7 +393,7 @@ typedef struct kvw_decode_args {
     void *workspace;
     int64_t workspace_bytes;
     int32_t *err_flag;
-    int32_t chunk_positions;           /* 256, 512, 1024, or 0 (chosen by the library) */
+    int32_t chunk_positions;           /* 256, 512, 1024, 2048, or 0 (chosen by the library) */
     int32_t cp_world_size;             /* context parallelism: 0 or 1 = none */
     int32_t cp_rank;
     int32_t cp_interleave_size;

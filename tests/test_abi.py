@@ -248,6 +248,7 @@ def test_decode_validation(lib):
     assert f(ctypes.byref(_decode(workspace=None)), None) == INVALID
     assert f(ctypes.byref(_decode(chunk_positions=128)), None) == INVALID
     assert f(ctypes.byref(_decode(chunk_positions=768)), None) == INVALID
+    assert f(ctypes.byref(_decode(chunk_positions=4096)), None) == INVALID
     assert f(ctypes.byref(_decode(cp_world_size=2, cp_rank=2, cp_interleave_size=1)), None) == INVALID
     assert f(ctypes.byref(_decode(cp_world_size=2, cp_rank=1, cp_interleave_size=3)), None) == INVALID
     assert f(ctypes.byref(_decode(cp_world_size=-1)), None) == INVALID

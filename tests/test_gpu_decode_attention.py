@@ -10,14 +10,14 @@ KVW_FLAG_SLOT_OOB where a slot lies past the cache (such positions are skipped).
 
 Tolerance: the kernel works in fp32 (unit roundoff u = 2^-24) from exact bf16
 inputs, in base-2 exponent units (scores s = log2(e) * scale * q.k).  Its
-summation structure: chunks of P = 256, 512 or 1024 positions; in a chunk four lane
+summation structure: chunks of P = 256, 512, 1024 or 2048 positions; in a chunk four lane
 groups each fold P/4 positions into a running (max m, sum l, weighted values acc),
 moving m only when it grows by more than 8, so a group rescales at most
 R = 1 + ceil(2S/8) times, S = log2(e) * scale * |q| * max_j |k_j| bounding |s|;
 the groups are merged in two steps and the C = ceil(n/P) chunks in a second
 launch.  To first order in u the output error is then at most
     u * max|V| * (P/2 + 6R + 2C + 60 + 20S),
-taken at P = 1024 for the first term and P = 256 for C, so that it holds for
+taken at P = 2048 for the first term and P = 256 for C, so that it holds for
 every chunk length:
 per (request, query head): P/4 + R + C + 5 roundings along the numerator's
 longest chain and P/4 + R + C + 12 along the denominator's, 2u per base-2
@@ -139,7 +139,7 @@ def place_caches(rows_total, rows, k, v):
     return kc, vc
 
 
-CHUNK_MAX, CHUNK_MIN = 1024, 256   # positions per workgroup of the kernel
+CHUNK_MAX, CHUNK_MIN = 2048, 256   # positions per workgroup of the kernel
 RESCALE_LOG2 = 8.0    # growth of the running maximum that triggers a rescale
 
 
@@ -289,7 +289,7 @@ def test_decode_small(case, mode):
     parity(w, mode, hq, seed=200 + len(w.name), kind="integers")
 
 
-@pytest.mark.parametrize("chunk", [256, 512, 1024])
+@pytest.mark.parametrize("chunk", [256, 512, 1024, 2048])
 @pytest.mark.parametrize("mode", ["paged", "ranges"])
 def test_decode_chunk_lengths(mode, chunk):
     """Every chunk length the kernel takes, on contexts around its multiples."""
