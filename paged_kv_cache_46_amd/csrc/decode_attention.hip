@@ -38,7 +38,8 @@
 // the schedule: each pair has its own place in the workspace.
 // decode_combine_kernel: per (query head, request), 256 threads merge the
 // chunks with the rescaling by 2^(m_c - max m): eight slices of the chunks,
-// four head dims per thread.
+// four head dims per thread.  decode_combine_small_kernel: the same with one
+// wave per (query head, request) when no request has more than 16 chunks.
 
 #include <hip/hip_runtime.h>
 
@@ -58,6 +59,7 @@ constexpr int kMinChunk = 256;                       // ... and at least; the wo
 constexpr int kPlanThreads = 1024;                   // the plan kernel's one workgroup
 constexpr int kTailClasses = 16;                     // length classes of the partial chunks
 constexpr int kCombineThreads = 256;                 // combine workgroup: 8 chunk slices x 32 threads
+constexpr int kSmallChunks = 16;                     // chunks per request, at most, for the one-wave combine
 constexpr int32_t kPlanMinReqs = 32;                 // batches this large get a work list
 constexpr int kHeadDim = 128;                        // supported head_dim
 constexpr int kRowLanes = 16;                        // lanes per position row of one head (8 was
@@ -693,6 +695,62 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(DecodeA
     }
 }
 
+// The same merge when no request has more than kSmallChunks chunks: one wave per
+// (query head, request), two head dims per lane, four query heads per workgroup.
+// Every lane reads the (m, l) of all the request's chunks (one address per load,
+// shared by the wave), so the maximum needs no exchange between lanes, and the
+// acc loads do not wait for it: one memory round trip and no barrier, where the
+// general kernel's 256-thread workgroup per head is mostly idle at a few chunks.
+// The sums run over the chunks in order.  Reports a clamped length like the
+// general kernel.
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_small_kernel(DecodeArgs a)
+{
+    const int32_t h = static_cast<int32_t>(blockIdx.x) * (kCombineThreads / kWave) +
+                      static_cast<int32_t>(threadIdx.x) / kWave;
+    const int32_t r = blockIdx.y;
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t flags = 0;
+    const int32_t n = context_of(a, r, flags);
+    if (blockIdx.x == 0 && threadIdx.x == 0) raise_flags(a.err_flag, flags);
+    if (h >= a.num_q_heads) return;  // uniform over the wave; nothing below waits on others
+    const int32_t chunks = static_cast<int32_t>((static_cast<int64_t>(n) + a.chunk - 1) / a.chunk);
+    const int64_t base = static_cast<int64_t>(r) * a.splits * a.num_q_heads + h;
+    const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + base;
+    const float2 *acc = reinterpret_cast<const float2 *>(a.ws_acc + base * kHeadDim) + lane;
+    const int64_t step = a.num_q_heads;
+    const int64_t acc_step = static_cast<int64_t>(a.num_q_heads) * (kHeadDim / 2);
+    float2 v[kSmallChunks], x[kSmallChunks];
+#pragma unroll
+    for (int c = 0; c < kSmallChunks; ++c) {
+        v[c] = make_float2(0.f, 0.f);
+        x[c] = make_float2(0.f, 0.f);
+        if (c < chunks) {
+            v[c] = ml[c * step];
+            x[c] = acc[c * acc_step];
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kSmallChunks; ++c)
+        if (v[c].y > 0.f) mx = fmaxf(mx, v[c].x);
+    float num0 = 0.f, num1 = 0.f, den = 0.f;
+#pragma unroll
+    for (int c = 0; c < kSmallChunks; ++c) {
+        const float e = v[c].y > 0.f ? __builtin_amdgcn_exp2f(v[c].x - mx) : 0.f;
+        num0 += e * x[c].x;
+        num1 += e * x[c].y;
+        den += e * v[c].y;
+    }
+    // out is only 4-byte aligned: two scalar stores
+    float *dst = a.out + (static_cast<int64_t>(r) * a.num_q_heads + h) * kHeadDim + 2 * lane;
+    dst[0] = den > 0.f ? num0 / den : 0.f;
+    dst[1] = den > 0.f ? num1 / den : 0.f;
+    // log sum_j e^(s_j) = ln 2 * (M + log2(den)), scores in base-2 units; -inf with no position
+    if (a.lse_out && lane == 0)
+        a.lse_out[static_cast<int64_t>(r) * a.num_q_heads + h] =
+            den > 0.f ? (mx + log2f(den)) * kLn2 : -INFINITY;
+}
+
 // out[r][h][d] = sum_p e^(lse_p - L) out_p[r][h][d], L = log sum_p e^(lse_p), over the parts'
 // stacked results; a part with lse -inf (no position) adds nothing; no part with a position
 // gives 0 and -inf.
@@ -898,8 +956,15 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(KVW_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     }
-    const dim3 cgrid(static_cast<unsigned>(g.num_q_heads), static_cast<unsigned>(g.num_reqs));
-    hipLaunchKernelGGL(decode_combine_kernel, cgrid, dim3(kCombineThreads), 0, s, a);
+    if (a.splits <= kSmallChunks) {
+        constexpr int kHeadsPerGroup = kCombineThreads / kWave;
+        const dim3 cgrid(static_cast<unsigned>((g.num_q_heads + kHeadsPerGroup - 1) / kHeadsPerGroup),
+                         static_cast<unsigned>(g.num_reqs));
+        hipLaunchKernelGGL(decode_combine_small_kernel, cgrid, dim3(kCombineThreads), 0, s, a);
+    } else {
+        const dim3 cgrid(static_cast<unsigned>(g.num_q_heads), static_cast<unsigned>(g.num_reqs));
+        hipLaunchKernelGGL(decode_combine_kernel, cgrid, dim3(kCombineThreads), 0, s, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(KVW_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KVW_OK;
