@@ -28,9 +28,11 @@ bytes, every token.
 The read side is measured too ("decode_attention"): decode attention, one
 query per request with 32 query heads over the 8 KV heads, over the 128K
 layouts (R = 1 and 4096) and the 256-request decode step, paged gather vs
-range arithmetic, at every chunk length; and decode context parallelism at
-W = 2 (each rank's share, then the log-sum-exp merge).  --decode-only runs
-just that part (for profiling).
+range arithmetic, at every chunk length; the R = 1 layout also with 8, 16
+and 64 query heads (1, 2 and 8 per KV head); and decode context parallelism
+at W = 2 (each rank's share, then the log-sum-exp merge).  Each decode
+workload opens with half a second of untimed calls.  --decode-only runs just
+that part (for profiling).
 
 `value` is tokens/s of paged_r4096; every variant is reported under
 "variants", with the fused call's time (HIP events on the launch stream)
@@ -592,8 +594,9 @@ def decode_attention(args, d, dev, stream, timed):
                         "call_ms_by_chunk": {str(c): round(v[0], 5) for c, v in by_chunk.items()
                                              if c}}
         if wname == "long_context_r1":
-            out["long_context_r1_paged_g8"] = decode_g8(args, w, ctx, kc, vc, maps["paged"], d,
-                                                        timed, stream, kvw, torch)
+            for hq_g in (8, 16, 64):  # G = 1, 2 (the vector kernel) and 8 query heads per KV head
+                out[f"long_context_r1_paged_g{hq_g // w.num_kv_heads}"] = decode_heads(
+                    args, w, ctx, kc, vc, maps["paged"], d, timed, stream, kvw, torch, hq_g)
         if wname == "long_context_r4096":
             out["context_parallel_W2"] = decode_context_parallel(
                 args, w, ctx, qd, cl, kc, vc, ws, maps["paged"], hq, timed, stream, kvw, torch)
@@ -602,14 +605,14 @@ def decode_attention(args, d, dev, stream, timed):
     return out
 
 
-def decode_g8(args, w, ctx, kc, vc, paged, d, timed, stream, kvw, torch):
-    """The 128K batch with 64 query heads over the same 8 key/value heads (G = 8, a 70B-class
-    attention shape), paged, at the library's own chunk length."""
+def decode_heads(args, w, ctx, kc, vc, paged, d, timed, stream, kvw, torch, hq):
+    """The 128K batch with hq query heads over the same 8 key/value heads (8 or 16: one or two
+    per key/value head, the vector kernel; 64: eight, a 70B-class attention shape), paged, at
+    the library's own chunk length."""
     import numpy as np
 
     from workloads import decode_inputs
 
-    hq = 64
     q = decode_inputs(w, hq, 78, rows=np.zeros(0, np.int64))[0]
     qd = d(q)
     cl = d(ctx.astype(np.int32))
@@ -629,7 +632,7 @@ def decode_g8(args, w, ctx, kc, vc, paged, d, timed, stream, kvw, torch):
     wall, ev_ms = timed(call, args.warmup, args.steps)
     avg = statistics.fmean(ev_ms)
     nbytes = decode_bytes(w, ctx, hq, "paged")
-    log(f"[bench] decode attention long_context_r1_paged G=8     {avg * 1e3:8.1f} us = "
+    log(f"[bench] decode attention long_context_r1_paged G={hq // w.num_kv_heads}     {avg * 1e3:8.1f} us = "
         f"{nbytes / (avg * 1e-3) / 1e9:5.0f} GB/s "
         f"({100 * nbytes / (avg * 1e-3) / 1e9 / HBM_PEAK_GBPS:.1f}%)")
     return {"q_heads": hq, "kv_heads": w.num_kv_heads, "call_ms_avg": round(avg, 5),

@@ -172,13 +172,10 @@ __device__ __forceinline__ float dot8(const u32x4 &q, const u32x4 &k, float s)
     return s;
 }
 
-// Positions in flight per lane group, per query-head grouping and row width
-// (register budget): with 8 lanes per row a lane holds twice the dims.
-template <int G, int L>
-constexpr int unroll_of()
-{
-    return L == 16 ? (G <= 2 ? 8 : (G == 4 ? 4 : 2)) : (G <= 2 ? 4 : (G == 4 ? 2 : 1));
-}
+// Positions in flight per lane group (register budget): 8 at 16 lanes per row,
+// 4 at 8 lanes per row, where a lane holds twice the head dims.
+template <int L>
+constexpr int unroll_of() { return L == 16 ? 8 : 4; }
 
 // Threads per workgroup: one wave per key/value head, at most 16, or 8 for G = 8
 // whose 8-row register tiles need more than the 128 VGPRs a 16-wave workgroup
@@ -251,7 +248,8 @@ __device__ int32_t stage_slots(const DecodeArgs &a, int32_t r, int64_t c0, int32
 template <int MODE, int G, int L>
 __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(DecodeArgs a)
 {
-    constexpr int U = unroll_of<G, L>();
+    static_assert(G == 1 || G == 2, "4 and 8 query heads per key/value head take the matrix-core kernel");
+    constexpr int U = unroll_of<L>();
     constexpr int NV = kHeadDim / (L * 8);   // 16-byte pieces of a row per lane (1 or 2)
     constexpr int DPL = NV * 8;              // head dims per lane
     constexpr int RPP = kWave / L;           // positions per wave load
