@@ -61,6 +61,7 @@ constexpr int kTailClasses = 16;                     // length classes of the pa
 constexpr int kCombineThreads = 256;                 // combine workgroup: 8 chunk slices x 32 threads
 constexpr int kSmallChunks = 16;                     // chunks per request, at most, for the one-wave combine
 constexpr int32_t kPlanMinReqs = 32;                 // batches this large get a work list
+constexpr int64_t kAutoMinGroups = 256;              // the automatic chunk keeps a workgroup per CU
 constexpr int kHeadDim = 128;                        // supported head_dim
 constexpr int kRowLanes = 16;                        // lanes per position row of one head (8 was
                                                      // slower: fewer instructions, fewer waves)
@@ -781,18 +782,18 @@ int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
 // rounds of the two that fit) when every request runs to max_context.  Longer
 // chunks mean fewer partials to merge; the bound keeps the last round of
 // workgroups a small part of the launch.
-// The automatic chunk length.  A batch too small for the work list takes 2048
-// positions per workgroup when that still gives 1024 workgroups (16 requests of
-// 128K positions: 1% faster than 1024, 3% at 64 query heads over 8); a larger
-// batch's requests are uneven, and there longer chunks leave the last round of
-// workgroups partly empty.  Otherwise the longest of 1024, 512 and 256 that gives
-// 2048 workgroups or more, else 256.
+// The automatic chunk length: the longest of 2048, 1024, 512 and 256 positions
+// that still gives every compute unit a workgroup, num_reqs * ceil(max_context /
+// chunk) >= 256.  Longer chunks spread each workgroup's fixed cost (slot staging,
+// the partial's write) over more positions; fewer workgroups than compute units
+// leave some idle.  A batch of 32 requests or more, which gets the work list,
+// stops at 1024: its requests are often uneven, and longer chunks leave its last
+// round of workgroups partly empty (the 256-request decode step with contexts
+// U[1, 8192] is 4% slower at 2048).  Only num_reqs and max_context are known here.
 int32_t auto_chunk(int32_t num_reqs, int32_t max_context)
 {
-    if (num_reqs < kPlanMinReqs && static_cast<int64_t>(num_reqs) * ceil_div(max_context, kMaxChunk) >= 1024)
-        return kMaxChunk;
-    int32_t c = kMaxChunk / 2;
-    while (c > kMinChunk && static_cast<int64_t>(num_reqs) * ceil_div(max_context, c) < 2048) c /= 2;
+    int32_t c = num_reqs < kPlanMinReqs ? kMaxChunk : kMaxChunk / 2;
+    while (c > kMinChunk && static_cast<int64_t>(num_reqs) * ceil_div(max_context, c) < kAutoMinGroups) c /= 2;
     return c;
 }
 
