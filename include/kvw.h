@@ -351,8 +351,10 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream);
  *   workspace          device memory of kvw_decode_workspace_size(...) bytes, owned by
  *                      the caller; its contents need no initialisation and are
  *                      overwritten; calls that overlap on one workspace race
- *   chunk_positions    positions per workgroup: 256, 512, 1024 or 2048; 0 picks one from
- *                      num_reqs and max_context (results differ only in rounding)
+ *   chunk_positions    positions per workgroup: 256, 512, 1024 or 2048; 0 picks the
+ *                      longest that gives num_reqs * ceil(max_context / chunk) >= 256
+ *                      workgroups (at most 1024 for 32 requests or more); results
+ *                      differ only in rounding
  *   cp_world_size, cp_rank, cp_interleave_size
  *                      decode context parallelism ([P2] "Entwurfsmotivation"; the
  *                      placement of kvw_slot_mapping_paged): this rank attends only
