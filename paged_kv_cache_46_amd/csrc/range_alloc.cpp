@@ -17,12 +17,15 @@
 // is the larger is written first, so the second leaf-to-root walk stops where
 // the two paths meet.  After creation nothing is heap-allocated except when a
 // row's extent list, the extent pool or the cache map outgrows its capacity.
+// The prefix cache's key -> extent map is open addressing with linear probing
+// over a power-of-two table at most half full (no per-entry heap node, no
+// division to find a bucket), with deletion by backward shift, so no
+// tombstones accumulate.
 
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <new>
-#include <unordered_map>
 #include <vector>
 
 #include "kvw_alloc.h"
@@ -42,6 +45,89 @@ struct Extent {
     uint64_t key = 0;
 };
 
+// Cache key -> extent id.  Empty slots hold id -1.  Keys and ids sit in two
+// arrays, so a probe run reads densely packed keys (one array of slots holding
+// both was measured slower).  The hash is the 64-bit finalizer of MurmurHash3
+// (a fixed bijection with good avalanche), so keys that differ only in high
+// bits still spread over the table.
+class KeyMap {
+public:
+    KeyMap() { rehash(1024); }
+
+    size_t size() const { return count_; }
+
+    // the id stored under key, or -1
+    int32_t find(uint64_t key) const
+    {
+        for (size_t i = home(key);; i = (i + 1) & mask_) {
+            if (ids_[i] < 0) return -1;
+            if (keys_[i] == key) return ids_[i];
+        }
+    }
+
+    // key must not be present; may throw std::bad_alloc when the table grows
+    void insert(uint64_t key, int32_t id)
+    {
+        if (2 * (count_ + 1) > ids_.size()) rehash(2 * ids_.size());
+        place(key, id);
+        ++count_;
+    }
+
+    // key must be present
+    void erase(uint64_t key)
+    {
+        size_t i = home(key);
+        while (keys_[i] != key || ids_[i] < 0) i = (i + 1) & mask_;
+        // backward shift: pull later entries of the probe run into the hole
+        // when their home does not lie cyclically in (hole, slot]
+        for (size_t j = (i + 1) & mask_; ids_[j] >= 0; j = (j + 1) & mask_) {
+            const size_t h = home(keys_[j]);
+            const bool stays = i <= j ? (i < h && h <= j) : (i < h || h <= j);
+            if (stays) continue;
+            keys_[i] = keys_[j];
+            ids_[i] = ids_[j];
+            i = j;
+        }
+        ids_[i] = -1;
+        --count_;
+    }
+
+private:
+    static uint64_t mix(uint64_t k)
+    {
+        k ^= k >> 33;
+        k *= 0xff51afd7ed558ccdULL;
+        k ^= k >> 33;
+        k *= 0xc4ceb9fe1a85ec53ULL;
+        k ^= k >> 33;
+        return k;
+    }
+    size_t home(uint64_t key) const { return static_cast<size_t>(mix(key)) & mask_; }
+
+    void place(uint64_t key, int32_t id)
+    {
+        size_t i = home(key);
+        while (ids_[i] >= 0) i = (i + 1) & mask_;
+        keys_[i] = key;
+        ids_[i] = id;
+    }
+
+    void rehash(size_t cap)
+    {
+        std::vector<uint64_t> keys(cap);
+        std::vector<int32_t> ids(cap, -1);
+        keys.swap(keys_);
+        ids.swap(ids_);
+        mask_ = cap - 1;
+        for (size_t i = 0; i < ids.size(); ++i)
+            if (ids[i] >= 0) place(keys[i], ids[i]);
+    }
+
+    std::vector<uint64_t> keys_;
+    std::vector<int32_t> ids_;
+    size_t mask_ = 0, count_ = 0;
+};
+
 }  // namespace
 
 struct kvw_alloc {
@@ -58,7 +144,7 @@ struct kvw_alloc {
     std::vector<int32_t> spare;  // unused extent ids
     int64_t live = 0;
     std::vector<std::vector<int32_t>> rows;
-    std::unordered_map<uint64_t, int32_t> cache;
+    KeyMap cache;
     int32_t lru_head = -1, lru_tail = -1;
     int64_t cache_only_chunks = 0;
 
@@ -347,7 +433,7 @@ kvw_status kvw_alloc_cache_insert(kvw_alloc *a, uint64_t key, int32_t row, int64
     if (first < 0 || count <= 0 || first % a->align || count % a->align)
         return fail(KVW_ERR_INVALID_ARG, "%s: blocks [%lld, +%lld) are not aligned to %d", fn,
                     (long long)first, (long long)count, a->align);
-    if (a->cache.count(key)) return fail(KVW_ERR_INVALID_ARG, "%s: key already cached", fn);
+    if (a->cache.find(key) >= 0) return fail(KVW_ERR_INVALID_ARG, "%s: key already cached", fn);
     const int64_t fc = first / a->align, cc = count / a->align;
     std::vector<int32_t> &r = a->rows[row];
     int64_t off = 0;
@@ -376,7 +462,7 @@ kvw_status kvw_alloc_cache_insert(kvw_alloc *a, uint64_t key, int32_t row, int64
             a->ext[id].start = start + head;
             a->ext[id].len = mid;
         }
-        a->cache.emplace(key, id);
+        a->cache.insert(key, id);
         a->ext[id].cached = true;
         a->ext[id].key = key;
         return KVW_OK;
@@ -389,15 +475,15 @@ kvw_status kvw_alloc_cache_acquire(kvw_alloc *a, uint64_t key, int32_t row)
 {
     const char *fn = "kvw_alloc_cache_acquire";
     if (!row_ok(a, row)) return fail(KVW_ERR_INVALID_ARG, "%s: no allocator or row %d", fn, row);
-    const auto it = a->cache.find(key);
-    if (it == a->cache.end()) return fail(KVW_ERR_NOT_FOUND, "%s: key not cached", fn);
+    const int32_t id = a->cache.find(key);
+    if (id < 0) return fail(KVW_ERR_NOT_FOUND, "%s: key not cached", fn);
     try {
-        a->rows[row].push_back(it->second);
+        a->rows[row].push_back(id);
     } catch (const std::bad_alloc &) {
         return fail(KVW_ERR_UNSUPPORTED, "%s: out of host memory", fn);
     }
-    Extent &e = a->ext[it->second];
-    if (e.refs == 0) a->lru_unlink(it->second);
+    Extent &e = a->ext[id];
+    if (e.refs == 0) a->lru_unlink(id);
     ++e.refs;
     return KVW_OK;
 }
@@ -543,17 +629,22 @@ kvw_status kvw_coord_offset(int64_t layer, int64_t block, int64_t token, int64_t
                             int64_t num_blocks, int64_t block_size, int64_t bytes_per_token,
                             int64_t *offset)
 {
-    // unsigned compares reject negative coordinates too; each size is below
-    // 2^63, so the 128-bit product below cannot wrap
+    // unsigned compares reject negative coordinates too
     if (!offset || bytes_per_token < 0 || static_cast<uint64_t>(layer) >= static_cast<uint64_t>(num_layers) ||
         static_cast<uint64_t>(block) >= static_cast<uint64_t>(num_blocks) ||
         static_cast<uint64_t>(token) >= static_cast<uint64_t>(block_size))
         return fail(KVW_ERR_INVALID_ARG, "kvw_coord_offset: coordinate out of range");
-    using u128 = unsigned __int128;
-    const u128 n = ((static_cast<u128>(layer) * static_cast<uint64_t>(num_blocks) +
-                     static_cast<uint64_t>(block)) * static_cast<uint64_t>(block_size) +
-                    static_cast<uint64_t>(token)) * static_cast<uint64_t>(bytes_per_token);
-    if (n > static_cast<u128>(INT64_MAX))
+    // Checked 64-bit steps.  The sizes are at least 1 here (each exceeds its
+    // coordinate), so with bytes_per_token >= 1 every partial value is at most
+    // the result, and a step wraps only when the result exceeds 2^64 - 1.
+    uint64_t n = 0;
+    if (bytes_per_token > 0 &&
+        (__builtin_mul_overflow(static_cast<uint64_t>(layer), static_cast<uint64_t>(num_blocks), &n) ||
+         __builtin_add_overflow(n, static_cast<uint64_t>(block), &n) ||
+         __builtin_mul_overflow(n, static_cast<uint64_t>(block_size), &n) ||
+         __builtin_add_overflow(n, static_cast<uint64_t>(token), &n) ||
+         __builtin_mul_overflow(n, static_cast<uint64_t>(bytes_per_token), &n) ||
+         n > static_cast<uint64_t>(INT64_MAX)))
         return fail(KVW_ERR_UNSUPPORTED, "kvw_coord_offset: offset overflows int64");
     *offset = static_cast<int64_t>(n);
     return KVW_OK;

@@ -18,7 +18,8 @@ from .build import LIBRARY
 KVW_ABI_VERSION = 6
 KVW_PAD_ID = -1
 KVW_MAX_RANGE_STRIDE = 65536
-KVW_OK, KVW_ERR_INVALID_ARG, KVW_ERR_UNSUPPORTED, KVW_ERR_RANGE_CAP, KVW_ERR_HIP = range(5)
+(KVW_OK, KVW_ERR_INVALID_ARG, KVW_ERR_UNSUPPORTED, KVW_ERR_RANGE_CAP, KVW_ERR_HIP,
+ KVW_ERR_NO_SPACE, KVW_ERR_NOT_FOUND) = range(7)
 KVW_FLAG_NUM_TOKENS, KVW_FLAG_COUNT, KVW_FLAG_BAD_BLOCK, KVW_FLAG_SLOT_OOB = 1, 2, 4, 8
 KVW_SLOTS_PRECOMPUTED, KVW_SLOTS_PAGED, KVW_SLOTS_RANGES = 0, 1, 2
 KVW_SCHEDULE_AUTO, KVW_SCHEDULE_TWO_KERNELS, KVW_SCHEDULE_ONE_KERNEL = 0, 1, 2

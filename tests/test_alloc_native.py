@@ -11,7 +11,7 @@ import pytest
 import alloc_pins as AP
 from oracle.range_alloc import RangeAllocOracle
 from paged_kv_cache_46_amd.range_alloc import RangeAllocator, kvw_coord_offset
-from paged_kv_cache_46_amd.kvw import KvwError
+from paged_kv_cache_46_amd.kvw import KVW_ERR_NOT_FOUND as NOT_FOUND, KVW_OK as OK, KvwError
 
 
 def native(num_blocks, alignment, first_block, rows):
@@ -95,6 +95,54 @@ def test_coord_offset():
             kvw_coord_offset(*bad, L, B, T, bpt)
     with pytest.raises(KvwError):
         kvw_coord_offset(1, 0, 0, 2, 1 << 40, 1 << 20, 1 << 10)   # overflows int64
+    # no row bytes: offset 0 whatever the coordinate sizes, products that would wrap included
+    assert kvw_coord_offset(1, 5, 7, 2, 1 << 40, 1 << 40, 0) == 0
+    # the largest offsets: exactly representable, and one step past int64
+    top = (1 << 62) - 1
+    assert kvw_coord_offset(0, 0, top, 1, 1, 1 << 62, 2) == 2 * top
+    assert kvw_coord_offset(1, 0, 0, 2, 1 << 31, 1 << 31, 1) == 1 << 62
+    with pytest.raises(KvwError):
+        kvw_coord_offset(0, 0, top, 1, 1, 1 << 62, 3)   # 3 * (2^62 - 1) > 2^63 - 1
+    with pytest.raises(KvwError):
+        kvw_coord_offset((1 << 40) - 1, 1, 0, 1 << 40, 1 << 40, 1, 1 << 30)  # wraps 2^64 early
+
+
+@pytest.mark.parametrize("key_kind", ["high_bits", "random"])
+def test_prefix_cache_many_keys(key_kind):
+    """Thousands of cached ranges through insert, LRU eviction, acquire and re-insert: every key
+    is found exactly while it is cached (the key table grows and deletes under long probe
+    runs; keys that differ only in their high bits must still spread)."""
+    n = 6000
+    rng = np.random.default_rng(77)
+    if key_kind == "high_bits":
+        keys = [(i + 1) << 40 for i in range(n)]
+    else:
+        keys = [int(k) for k in rng.choice(np.iinfo(np.int64).max, size=n, replace=False)]
+    a = native(4 * n, 1, 0, 8)
+    for k in keys:                        # cache-only 1-block ranges, oldest first
+        assert a.extend(0, 1) == OK
+        assert a.cache_insert(k, 0, 0, 1) == OK
+        assert a.release(0) == OK
+    assert a.cache_insert(keys[0], 1, 0, 1) != OK  # row 1 holds nothing: refused
+    st, ev = a.cache_evict(n // 3)
+    assert st == OK and ev == n // 3
+    gone, live = set(keys[:n // 3]), keys[n // 3:]
+    for k in rng.permutation(keys).tolist():
+        st = a.cache_acquire(int(k), 2)
+        assert (st == NOT_FOUND) if k in gone else (st == OK), (k, st)
+    assert a.release(2) == OK              # the acquired ranges become cache-only again
+    for k in list(gone)[:500]:             # evicted keys can be cached again
+        assert a.extend(3, 1) == OK
+        assert a.cache_insert(k, 3, 0, 1) == OK
+        assert a.release(3) == OK
+    assert a.extend(3, 1) == OK
+    assert a.cache_insert(live[0], 3, 0, 1) != OK  # a key cached twice: refused
+    assert a.release(3) == OK
+    assert a.stats()["cache_entries"] == len(live) + 500
+    st, ev = a.cache_evict(1 << 30)
+    assert st == OK and ev == len(live) + 500 and a.stats()["cache_entries"] == 0
+    for k in keys[:50] + live[-50:]:
+        assert a.cache_acquire(k, 4) == NOT_FOUND
 
 
 def test_create_rejects_bad_pools():
