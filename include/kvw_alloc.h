@@ -145,6 +145,35 @@ kvw_status kvw_coord_offset(int64_t layer, int64_t block, int64_t token, int64_t
                             int64_t num_blocks, int64_t block_size, int64_t bytes_per_token,
                             int64_t *offset);
 
+/* The same computation inline, for per-token host loops that should not pay a
+ * call into the shared library: the same result and status as
+ * kvw_coord_offset for every input, but no error message is recorded
+ * (kvw_last_error is left as it was).  kvw_coord_offset is this function plus
+ * the message.  Needs GCC or Clang (checked-arithmetic builtins). */
+static inline kvw_status kvw_coord_offset_inline(int64_t layer, int64_t block, int64_t token,
+                                                 int64_t num_layers, int64_t num_blocks,
+                                                 int64_t block_size, int64_t bytes_per_token,
+                                                 int64_t *offset)
+{
+    uint64_t n = 0;
+    /* unsigned compares reject negative coordinates too */
+    if (!offset || bytes_per_token < 0 || (uint64_t)layer >= (uint64_t)num_layers ||
+        (uint64_t)block >= (uint64_t)num_blocks || (uint64_t)token >= (uint64_t)block_size)
+        return KVW_ERR_INVALID_ARG;
+    /* Checked 64-bit steps.  The sizes are at least 1 here (each exceeds its
+     * coordinate), so with bytes_per_token >= 1 every partial value is at most
+     * the result, and a step wraps only when the result exceeds 2^64 - 1. */
+    if (bytes_per_token > 0 &&
+        (__builtin_mul_overflow((uint64_t)layer, (uint64_t)num_blocks, &n) ||
+         __builtin_add_overflow(n, (uint64_t)block, &n) ||
+         __builtin_mul_overflow(n, (uint64_t)block_size, &n) ||
+         __builtin_add_overflow(n, (uint64_t)token, &n) ||
+         __builtin_mul_overflow(n, (uint64_t)bytes_per_token, &n) || n > (uint64_t)INT64_MAX))
+        return KVW_ERR_UNSUPPORTED;
+    *offset = (int64_t)n;
+    return KVW_OK;
+}
+
 #ifdef __cplusplus
 }
 #endif

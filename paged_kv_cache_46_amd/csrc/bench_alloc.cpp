@@ -1,5 +1,7 @@
 // Host benchmark of the range allocator and the checked coordinate offset,
-// calling libkvw.so through its C ABI (include/kvw_alloc.h).
+// calling libkvw.so through its C ABI (include/kvw_alloc.h).  The offset
+// scenarios use the header's inline form, as a per-token host loop would; one
+// more scenario times the same offset through the library call.
 //
 // Harness as in "Range-addressed KV cache blocks for the vLLM serving
 // engine", "Benchmark Methodology" (host benchmark): each scenario runs
@@ -18,6 +20,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "kvw_alloc.h"
@@ -31,6 +34,16 @@ struct Result {
 };
 
 volatile int64_t g_sink;  // keeps results observable
+
+// The checked offset as a per-token host loop calls it: inline from the
+// header, or (kLibrary) through the shared library's kvw_coord_offset.
+template <bool kLibrary>
+inline kvw_status coord_offset(int64_t layer, int64_t block, int64_t token, int64_t *off)
+{
+    return kLibrary ? kvw_coord_offset(layer, block, token, kLayers, kBlocks, kTokens, kBytes, off)
+                    : kvw_coord_offset_inline(layer, block, token, kLayers, kBlocks, kTokens,
+                                              kBytes, off);
+}
 
 void check(kvw_status st, const char *what)
 {
@@ -78,30 +91,31 @@ int main(int argc, char **argv)
     const int64_t iters = argc > 1 ? std::atoll(argv[1]) : 200000;
     const int rounds = argc > 2 ? std::atoi(argv[2]) : 20;
 
-    // map/offset single: one checked closed-form offset
-    {
+    // map/offset single: one checked closed-form offset, at a varying coordinate
+    auto offset_single = [&](auto library, const char *name, const char *what) {
         int64_t seed = 12345;
         auto call = [&](int64_t i) {
             seed = seed * 6364136223846793005LL + 1442695040888963407LL;  // vary the coordinate
             const uint64_t u = static_cast<uint64_t>(seed) >> 11;
-            int64_t off;
-            kvw_coord_offset(static_cast<int64_t>(u % kLayers), static_cast<int64_t>((u >> 5) % kBlocks),
-                             static_cast<int64_t>((u >> 21) % kTokens), kLayers, kBlocks, kTokens,
-                             kBytes, &off);
+            int64_t off = 0;
+            coord_offset<decltype(library)::value>(static_cast<int64_t>(u % kLayers),
+                                                   static_cast<int64_t>((u >> 5) % kBlocks),
+                                                   static_cast<int64_t>((u >> 21) % kTokens), &off);
             g_sink = off + i;
         };
-        emit("map/offset single", "ns/op", "one checked closed-form offset", iters, rounds,
-             run(iters, rounds, [](int) {}, call, 1.0));
-    }
+        emit(name, "ns/op", what, iters, rounds, run(iters, rounds, [](int) {}, call, 1.0));
+    };
+    offset_single(std::false_type{}, "map/offset single", "one checked closed-form offset");
+    offset_single(std::true_type{}, "map/offset single, library call",
+                  "the same through the shared library (kvw_coord_offset)");
     // map/offset decode walk: one new token per step of a request holding a contiguous range
     {
         int64_t pos = 0;
         const int64_t start = 1000;
         auto call = [&](int64_t) {
             const int64_t p = pos++ % (kTokens * 4096);
-            int64_t off;
-            kvw_coord_offset(7, start + p / kTokens, p % kTokens, kLayers, kBlocks, kTokens, kBytes,
-                             &off);
+            int64_t off = 0;
+            coord_offset<false>(7, start + p / kTokens, p % kTokens, &off);
             g_sink = off;
         };
         emit("map/offset decode walk", "ns/op", "one new token per step", iters, rounds,
@@ -111,10 +125,9 @@ int main(int argc, char **argv)
     {
         const int64_t walk = 4096, start = 2000, calls = std::max<int64_t>(1, iters / walk);
         auto call = [&](int64_t) {
-            int64_t acc = 0, off;
+            int64_t acc = 0, off = 0;
             for (int64_t p = 0; p < walk; ++p) {
-                kvw_coord_offset(3, start + p / kTokens, p % kTokens, kLayers, kBlocks, kTokens,
-                                 kBytes, &off);
+                coord_offset<false>(3, start + p / kTokens, p % kTokens, &off);
                 acc += off;
             }
             g_sink = acc;

@@ -629,24 +629,10 @@ kvw_status kvw_coord_offset(int64_t layer, int64_t block, int64_t token, int64_t
                             int64_t num_blocks, int64_t block_size, int64_t bytes_per_token,
                             int64_t *offset)
 {
-    // unsigned compares reject negative coordinates too
-    if (!offset || bytes_per_token < 0 || static_cast<uint64_t>(layer) >= static_cast<uint64_t>(num_layers) ||
-        static_cast<uint64_t>(block) >= static_cast<uint64_t>(num_blocks) ||
-        static_cast<uint64_t>(token) >= static_cast<uint64_t>(block_size))
-        return fail(KVW_ERR_INVALID_ARG, "kvw_coord_offset: coordinate out of range");
-    // Checked 64-bit steps.  The sizes are at least 1 here (each exceeds its
-    // coordinate), so with bytes_per_token >= 1 every partial value is at most
-    // the result, and a step wraps only when the result exceeds 2^64 - 1.
-    uint64_t n = 0;
-    if (bytes_per_token > 0 &&
-        (__builtin_mul_overflow(static_cast<uint64_t>(layer), static_cast<uint64_t>(num_blocks), &n) ||
-         __builtin_add_overflow(n, static_cast<uint64_t>(block), &n) ||
-         __builtin_mul_overflow(n, static_cast<uint64_t>(block_size), &n) ||
-         __builtin_add_overflow(n, static_cast<uint64_t>(token), &n) ||
-         __builtin_mul_overflow(n, static_cast<uint64_t>(bytes_per_token), &n) ||
-         n > static_cast<uint64_t>(INT64_MAX)))
-        return fail(KVW_ERR_UNSUPPORTED, "kvw_coord_offset: offset overflows int64");
-    *offset = static_cast<int64_t>(n);
+    const kvw_status st = kvw_coord_offset_inline(layer, block, token, num_layers, num_blocks,
+                                                  block_size, bytes_per_token, offset);
+    if (st == KVW_ERR_INVALID_ARG) return fail(st, "kvw_coord_offset: coordinate out of range");
+    if (st != KVW_OK) return fail(st, "kvw_coord_offset: offset overflows int64");
     return KVW_OK;
 }
 
