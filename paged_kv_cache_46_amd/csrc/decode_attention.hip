@@ -478,13 +478,16 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_mfma_kern
     const int32_t cnt = stage_slots<MODE>(a, r, c0, span, s_slot, s_wave_count, flags);
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;       // key/value head of this wave
+    const int w = threadIdx.x / kWave;       // wave of the workgroup: its LDS tile
+    // key/value head of this wave: the workgroups of a chunk split the heads (blockIdx.z)
+    const int kvh = static_cast<int>(blockIdx.z * (blockDim.x / kWave)) + w;
+    if (kvh >= a.num_kv_heads) return;       // no block-wide barrier follows the staging
     const int col = lane % kTile;            // MFMA side: position of the tile; P.V side: dims
     const int rg = lane / kTile;             // MFMA side: rows 4*rg .. +3; P.V side: position group
-    const int hq0 = w * G;
+    const int hq0 = kvh * G;
     const int64_t row_bytes = static_cast<int64_t>(a.num_kv_heads) * kHeadDim * 2;
-    const uint8_t *kbase = a.k_cache + static_cast<int64_t>(w) * kHeadDim * 2 + rg * 16;
-    const uint8_t *vbase = a.v_cache + static_cast<int64_t>(w) * kHeadDim * 2 + col * 16;
+    const uint8_t *kbase = a.k_cache + static_cast<int64_t>(kvh) * kHeadDim * 2 + rg * 16;
+    const uint8_t *vbase = a.v_cache + static_cast<int64_t>(kvh) * kHeadDim * 2 + col * 16;
 
     bf16x8 qa[4];  // A operand: query row col, dims 32*k + 8*rg .. +8
 #pragma unroll
@@ -946,9 +949,15 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (a.splits > 0) {
         if (plan) hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
-        const dim3 grid = plan ? dim3(static_cast<unsigned>(units))
-                               : dim3(static_cast<unsigned>(a.splits), static_cast<unsigned>(g.num_reqs));
-        const dim3 block(static_cast<unsigned>(g.num_kv_heads * kWave));
+        // G = 8: 156 VGPRs leave room for 3 waves per SIMD, so a compute unit holds one
+        // 8-wave workgroup with 4 wave slots idle; the heads of a chunk are split over two
+        // workgroups instead (each stages the chunk's slots), and three fit per unit
+        const unsigned zsplit = (group == 8 && g.num_kv_heads > 4) ? 2u : 1u;
+        const unsigned waves = (static_cast<unsigned>(g.num_kv_heads) + zsplit - 1) / zsplit;
+        const dim3 grid = plan ? dim3(static_cast<unsigned>(units), 1u, zsplit)
+                               : dim3(static_cast<unsigned>(a.splits), static_cast<unsigned>(g.num_reqs),
+                                      zsplit);
+        const dim3 block(waves * kWave);
         const size_t lds = 0;
         if (g.mode == KVW_SLOTS_PAGED) launch_partial<KVW_SLOTS_PAGED>(group, grid, block, lds, s, a);
         else launch_partial<KVW_SLOTS_RANGES>(group, grid, block, lds, s, a);

@@ -271,6 +271,9 @@ def small_decodes():
         # 16 waves)
         (_dec("hq64_g8", 10, [1, 700, 1300, 2100], 16, ("count", 1, 3), 8, 400), 64),
         (_dec("hq64_g4_16heads", 11, [513, 1025, 90], 32, ("count", 1, 3), 16, 120), 64),
+        # 40 query heads over 5 key/value heads (G = 8): a chunk's heads split over two
+        # workgroups of three waves, the second with one wave idle
+        (_dec("hq40_g8_5heads", 13, [300, 1100, 2100, 17], 16, ("count", 1, 3), 5, 400), 40),
         # 6 query heads over 3 key/value heads: the combine's last group of four heads is partial
         (_dec("hq6_g2_3heads", 12, [40, 900, 1800, 2500], 16, ("count", 1, 3), 3, 500), 6),
         # 40 requests (a work list orders the chunks): empty ones, exact chunk multiples, tails
