@@ -18,7 +18,9 @@
 //
 // decode_partial_kernel<MODE, G, L> (G = 1, 2) and decode_partial_mfma_kernel<MODE, G>
 // (G = 4, 8): one workgroup per (chunk of 256, 512, 1024 or 2048 positions, request),
-// one wave per key/value head, L = 16 lanes per position row for P.V.
+// one wave per key/value head, L = 16 lanes per position row for P.V.  At G = 8
+// with more than 4 key/value heads, two workgroups share a chunk, half the heads
+// each (grid z).
 //   0. The workgroup resolves the slots of its positions once, into LDS: the
 //      block-table gather (PAGED) or range arithmetic with the wavefront
 //      search over range_cum (RANGES).  Positions that hold nothing here
