@@ -446,6 +446,14 @@ def test_decode_long_context_full(r):
     full_size(w, Layout(w), 32, sel=[9 + r % 5], seed=14, kind="integers")
 
 
+def test_decode_long_context_full_64_heads():
+    """16 requests at 128K context with 64 query heads over the 8 key-value heads (G = 8, a
+    70B-class shape): each chunk's heads go to two workgroups, at full size."""
+    w = long_context(4096)
+    full_size(w, Layout(w), 64, sel=[6], seed=15)
+    full_size(w, Layout(w), 64, sel=[12], seed=16, kind="integers")
+
+
 # ---------------------------------------------------------------------------
 # graph capture: launch shapes depend only on num_reqs, max_context and strides
 # ---------------------------------------------------------------------------
