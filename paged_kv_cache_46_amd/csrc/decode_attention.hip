@@ -513,23 +513,41 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_mfma_kern
     float *tile = &s_p[w][0][0];
     float *alpha_row = &s_alpha[w][0];
 
+    // K of the first tile (position col) as the B operand.  Every load below is
+    // unconditional: a lane without a position reads row 0 (in the cache whenever
+    // the chunk holds a position) and drops the value.  Loads under a branch would
+    // make the compiler wait for all of them before the first product; in straight
+    // code it waits only for the loads the product needs.
+    int64_t slk = col < cnt ? s_slot[col] : -1;
+    u32x4 kw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const u32x4 t = load16<false>(kbase + (slk >= 0 ? slk : 0) * row_bytes + 64 * k);
+        kw[k] = slk >= 0 ? t : u32x4{0, 0, 0, 0};
+    }
     for (int tb = 0; tb < cnt; tb += kTile) {  // uniform trip count
         // loads: K of position tb + col as the B operand, V of positions tb + 4u + rg.
         // One K load covers 64 B of each of 16 rows, so every 128 B line is split
         // over two loads: K goes through the cache with the default policy (with
         // the streaming hint 2% of the lines were fetched twice).  V loads cover
         // whole rows and keep the hint (without it the kernel is 11% slower).
-        const int tk = tb + col;
-        const int64_t slk = tk < cnt ? s_slot[tk] : -1;
-        u32x4 kw[4], vw[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            kw[k] = slk >= 0 ? load16<false>(kbase + slk * row_bytes + 64 * k) : u32x4{0, 0, 0, 0};
+        // This tile's K (kw, slot slk) was loaded during the previous tile; the next
+        // tile's K goes out here, after this tile's V, and arrives while this tile's
+        // scores, softmax and P.V run.
+        u32x4 vw[4], kn[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int tv = tb + 4 * u + rg;
             const int64_t slv = tv < cnt ? s_slot[tv] : -1;
-            vw[u] = slv >= 0 ? load16<true>(vbase + slv * row_bytes) : u32x4{0, 0, 0, 0};
+            const u32x4 t = load16<true>(vbase + (slv >= 0 ? slv : 0) * row_bytes);
+            vw[u] = slv >= 0 ? t : u32x4{0, 0, 0, 0};
+        }
+        const int tn = tb + kTile + col;
+        const int64_t sln = tn < cnt ? s_slot[tn] : -1;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const u32x4 t = load16<false>(kbase + (sln >= 0 ? sln : 0) * row_bytes + 64 * k);
+            kn[k] = sln >= 0 ? t : u32x4{0, 0, 0, 0};
         }
         // scores of the tile: rows 4*rg + i, column col
         f32x4 sc4 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -596,6 +614,9 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_mfma_kern
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();  // the tile is rewritten by the next iteration
+#pragma unroll
+        for (int k = 0; k < 4; ++k) kw[k] = kn[k];
+        slk = sln;
     }
 
     // the four P.V position groups share each row's maximum: plain sums across them
