@@ -252,7 +252,8 @@ template <int MODE, int G, int L>
 __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(DecodeArgs a)
 {
     static_assert(G == 1 || G == 2, "4 and 8 query heads per key/value head take the matrix-core kernel");
-    constexpr int U = unroll_of<L>();
+    // G = 2 keeps 6 positions per lane group in flight: 8 would not fit 128 VGPRs
+    constexpr int U = G == 2 ? 6 : unroll_of<L>();
     constexpr int NV = kHeadDim / (L * 8);   // 16-byte pieces of a row per lane (1 or 2)
     constexpr int DPL = NV * 8;              // head dims per lane
     constexpr int RPP = kWave / L;           // positions per wave load
@@ -309,44 +310,29 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_kernel(De
     for (int base = 0; base < cnt; base += RPP * U) {  // uniform trip count
         u32x4 kw[U][NV], vw[U][NV];
         bool ok[U];
-        if constexpr (G == 1) {
-            // All K loads, then all V loads, none under a branch (a lane without a
-            // position reads row 0, in the cache whenever the chunk holds a position,
-            // and drops the value): the scores then wait only for K while V is in
-            // flight.  (At G = 2 the extra registers would spill.)
-            int64_t sl[U];
+        // All K loads, then all V loads, none under a branch (a lane without a
+        // position reads row 0, in the cache whenever the chunk holds a position, and
+        // drops the value): the scores then wait only for K while V is in flight.
+        int64_t sl[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int tok = base + u * RPP + grp;
-                const int64_t s_ = tok < cnt ? s_slot[tok] : -1;
-                ok[u] = s_ >= 0;
-                sl[u] = ok[u] ? s_ : 0;
+        for (int u = 0; u < U; ++u) {
+            const int tok = base + u * RPP + grp;
+            const int64_t s_ = tok < cnt ? s_slot[tok] : -1;
+            ok[u] = s_ >= 0;
+            sl[u] = ok[u] ? s_ : 0;
 #pragma unroll
-                for (int j = 0; j < NV; ++j) {
-                    const u32x4 t = load16<true>(kb + sl[u] * row_bytes + 16 * j);
-                    kw[u][j] = ok[u] ? t : u32x4{0, 0, 0, 0};
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int j = 0; j < NV; ++j) {
-                    const u32x4 t = load16<true>(vb + sl[u] * row_bytes + 16 * j);
-                    vw[u][j] = ok[u] ? t : u32x4{0, 0, 0, 0};
-                }
-        } else {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int tok = base + u * RPP + grp;
-                const int64_t sl = tok < cnt ? s_slot[tok] : -1;
-                ok[u] = sl >= 0;
-#pragma unroll
-                for (int j = 0; j < NV; ++j) {
-                    kw[u][j] = ok[u] ? load16<true>(kb + sl * row_bytes + 16 * j) : u32x4{0, 0, 0, 0};
-                    vw[u][j] = ok[u] ? load16<true>(vb + sl * row_bytes + 16 * j) : u32x4{0, 0, 0, 0};
-                }
+            for (int j = 0; j < NV; ++j) {
+                const u32x4 t = load16<true>(kb + sl[u] * row_bytes + 16 * j);
+                kw[u][j] = ok[u] ? t : u32x4{0, 0, 0, 0};
             }
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const u32x4 t = load16<true>(vb + sl[u] * row_bytes + 16 * j);
+                vw[u][j] = ok[u] ? t : u32x4{0, 0, 0, 0};
+            }
         float sc[U][G];
 #pragma unroll
         for (int u = 0; u < U; ++u)
