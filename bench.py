@@ -139,7 +139,7 @@ def timed(fn, n_warm, n_steps):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
+        print("bench.py: measures one GPU only; multi-GPU runs are not part of it "
               "(the write path shards with no exchange step: each GPU writes its own cache shard)",
               file=sys.stderr, flush=True)
         sys.exit(2)

@@ -78,7 +78,7 @@ extern "C" {
 typedef enum kvw_status {
     KVW_OK = 0,
     KVW_ERR_INVALID_ARG = 1, /* a host-side argument is out of its domain */
-    KVW_ERR_UNSUPPORTED = 2, /* a well-formed request this build does not handle */
+    KVW_ERR_UNSUPPORTED = 2, /* a well-formed request the library does not support */
     KVW_ERR_RANGE_CAP = 3,   /* range_stride above KVW_MAX_RANGE_STRIDE */
     KVW_ERR_HIP = 4,         /* the HIP runtime reported an error */
     KVW_ERR_NO_SPACE = 5,    /* allocator: not enough blocks even after eviction */
