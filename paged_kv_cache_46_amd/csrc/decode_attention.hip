@@ -816,11 +816,6 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(int32_t parts, int32
 
 int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
-// Positions per workgroup when the caller leaves it open: the longest chunk that
-// still gives at least 8 workgroups per compute unit (2048 on 256 CUs, four
-// rounds of the two that fit) when every request runs to max_context.  Longer
-// chunks mean fewer partials to merge; the bound keeps the last round of
-// workgroups a small part of the launch.
 // The automatic chunk length: the longest of 2048, 1024, 512 and 256 positions
 // that still gives every compute unit a workgroup, num_reqs * ceil(max_context /
 // chunk) >= 256.  Longer chunks spread each workgroup's fixed cost (slot staging,
