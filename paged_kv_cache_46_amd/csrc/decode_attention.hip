@@ -853,10 +853,17 @@ int64_t kvw_decode_workspace_size(int32_t num_reqs, int32_t max_context, int32_t
 {
     if (num_reqs < 0 || max_context < 0 || num_q_heads < 0 || head_dim < 0) return -1;
     // chunk partials (head_dim sums, max, sum per query head) and one work-list entry per chunk,
-    // counted per 256 positions so that every chunk length fits; then the list's length
-    return static_cast<int64_t>(num_reqs) * ceil_div(max_context, kMinChunk) *
-               (static_cast<int64_t>(num_q_heads) * (head_dim + 2) * sizeof(float) + sizeof(int2)) +
-           16;
+    // counted per 256 positions so that every chunk length fits; then the list's length.
+    // -1 when the size does not fit int64.
+    int64_t per_chunk = 0, chunks = 0, bytes = 0;
+    if (__builtin_mul_overflow(static_cast<int64_t>(num_q_heads),
+                               (static_cast<int64_t>(head_dim) + 2) * static_cast<int64_t>(sizeof(float)),
+                               &per_chunk) ||
+        __builtin_add_overflow(per_chunk, static_cast<int64_t>(sizeof(int2)), &per_chunk) ||
+        __builtin_mul_overflow(static_cast<int64_t>(num_reqs), ceil_div(max_context, kMinChunk), &chunks) ||
+        __builtin_mul_overflow(chunks, per_chunk, &bytes) || __builtin_add_overflow(bytes, int64_t{16}, &bytes))
+        return -1;
+    return bytes;
 }
 
 size_t kvw_decode_args_size(void) { return sizeof(kvw_decode_args); }
@@ -938,6 +945,7 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
             return fail(KVW_ERR_INVALID_ARG, "%s: a range descriptor array is NULL or misaligned", fn);
     }
     const int64_t need = kvw_decode_workspace_size(g.num_reqs, g.max_context, g.num_q_heads, g.head_dim);
+    if (need < 0) return fail(KVW_ERR_INVALID_ARG, "%s: the workspace size overflows", fn);
     if (need > 0 && (!g.workspace || !aligned_to(g.workspace, 16) || g.workspace_bytes < need))
         return fail(KVW_ERR_INVALID_ARG, "%s: workspace of %lld bytes needed", fn, (long long)need);
 

@@ -274,6 +274,9 @@ def test_decode_workspace_size(lib):
     assert ws(4, 1025, 32, 128) == 4 * 5 * (32 * 130 * 4 + 8) + 16
     assert ws(4, 0, 32, 128) == 16
     assert ws(-1, 10, 32, 128) == -1
+    # sizes whose product does not fit int64 (head_dim + 2 itself past int32 here)
+    assert ws(65535, 2**31 - 1, 2**31 - 1, 2**31 - 1) == -1
+    assert ws(1, 256, 1, 2**31 - 1) == (2**31 + 1) * 4 + 8 + 16
 
 
 def test_decode_validation(lib):
