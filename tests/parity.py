@@ -94,27 +94,54 @@ def kv_device(w: Workload):
     return key, value
 
 
+_WINDOWS: Dict[int, tuple] = {}
+
+
+def _windows(rows: int, row_elems: int):
+    """Host buffers of at least `rows` rows for one comparison window, kept across calls (per
+    row width, largest so far): first touches of fresh pages took most of the time of a
+    whole-cache comparison (a 128K cache plane is 4 GiB)."""
+    have = _WINDOWS.get(row_elems)
+    if have is None or have[0].shape[0] < rows:
+        _WINDOWS.pop(row_elems, None)
+        ek = np.empty((rows, row_elems), np.uint16)
+        ev = np.empty_like(ek)
+        staged = torch.empty((rows, row_elems), dtype=torch.int16, pin_memory=True)
+        _WINDOWS[row_elems] = (ek, ev, staged)
+    return _WINDOWS[row_elems]
+
+
+def _words(a: np.ndarray) -> np.ndarray:
+    """A flat view in the widest unsigned words the row width allows (faster equality)."""
+    flat = a.reshape(-1)
+    return flat.view(np.uint64) if flat.nbytes % 8 == 0 else flat
+
+
 def compare_caches(w: Workload, caches: Caches, slots_oracle: np.ndarray, key_h: np.ndarray,
                    value_h: np.ndarray, num_blocks: int, block_size: int,
                    window_rows: int = 1 << 19) -> int:
-    """Bytewise comparison of both cache planes against oracle windows; returns oracle flags."""
+    """Bytewise comparison of both cache planes against oracle windows; returns oracle flags.
+
+    Each window of rows is written by the oracle into sentinel-filled host buffers and
+    compared with the same rows copied from the device."""
     orc = oracle.get()
     flags = 0
     rows = caches.rows
-    for a in range(0, rows, window_rows):
-        b = min(rows, a + window_rows)
-        ek = np.full((b - a, caches.row_elems), BF16_SENTINEL, np.uint16)
-        ev = np.full_like(ek, BF16_SENTINEL)
+    win = max(1, min(window_rows, rows))
+    ek_all, ev_all, staged = _windows(win, caches.row_elems)
+    for a in range(0, rows, win):
+        b = min(rows, a + win)
+        ek, ev = ek_all[:b - a], ev_all[:b - a]
+        ek.fill(BF16_SENTINEL)
+        ev.fill(BF16_SENTINEL)
         flags |= orc.kv_write(slots_oracle, key_h, value_h, num_blocks, block_size, ek, ev,
                               row_begin=a)
-        gk = host(caches.k[a:b])
-        if not np.array_equal(gk, ek):
-            bad = np.nonzero((gk != ek).any(axis=1))[0]
-            raise AssertionError(f"{w.name}: K cache differs at {len(bad)} rows, first row "
-                                 f"{a + int(bad[0])}")
-        gv = host(caches.v[a:b])
-        if not np.array_equal(gv, ev):
-            bad = np.nonzero((gv != ev).any(axis=1))[0]
-            raise AssertionError(f"{w.name}: V cache differs at {len(bad)} rows, first row "
-                                 f"{a + int(bad[0])}")
+        for plane, name, exp in ((caches.k, "K", ek), (caches.v, "V", ev)):
+            st = staged[:b - a]
+            st.copy_(plane[a:b])
+            got = st.numpy().view(np.uint16)
+            if not np.array_equal(_words(got), _words(exp)):
+                bad = np.nonzero((got != exp).any(axis=1))[0]
+                raise AssertionError(f"{w.name}: {name} cache differs at {len(bad)} rows, first "
+                                     f"row {a + int(bad[0])}")
     return flags

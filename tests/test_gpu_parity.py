@@ -158,8 +158,9 @@ def test_long_context_slots_and_expansion(r):
 # ---------------------------------------------------------------------------
 # K/V write with the attention-side table made in the same launch
 # ---------------------------------------------------------------------------
-def check_kv_write_with_table(w, mode, k, pad=3):
-    """Fused write that also returns the kernel-unit block table: slots, caches, table, counts."""
+def check_kv_write_with_table(w, mode, k, pad=3, payload=None):
+    """Fused write that also returns the kernel-unit block table: slots, caches, table, counts.
+    payload: ((key_h, value_h), (key, value)) to use instead of the workload's own."""
     say(f"[kv_write+table] {w.describe()} mode={mode} k={k}")
     variant, _, sched = mode.partition("-")
     orc = oracle.get()
@@ -173,9 +174,12 @@ def check_kv_write_with_table(w, mode, k, pad=3):
     else:
         o_table, o_counts, t_flags = orc.ranges_to_block_table(
             w.range_start, w.range_len, w.range_cum, w.num_ranges, w.block_size, kbs, width)
-    key_h, value_h = w.kv_plane(0), w.kv_plane(1)
-    key = dev(key_h).view(w.num_layers, w.max_num_tokens, w.num_kv_heads, w.head_dim)
-    value = dev(value_h).view_as(key)
+    if payload is None:
+        key_h, value_h = w.kv_plane(0), w.kv_plane(1)
+        key = dev(key_h).view(w.num_layers, w.max_num_tokens, w.num_kv_heads, w.head_dim)
+        value = dev(value_h).view_as(key)
+    else:
+        (key_h, value_h), (key, value) = payload
     caches = Caches(w.num_layers, w.num_blocks, w.block_size, w.row_elems)
     table = torch.full((w.num_reqs, width), -5, dtype=torch.int32, device=DEV)
     counts = torch.full((w.num_reqs,), -5, dtype=torch.int32, device=DEV)
@@ -214,11 +218,12 @@ def test_kv_write_with_table(w, mode):
     check_kv_write_with_table(w, mode, k=2 if w.block_size % 2 == 0 else 1)
 
 
-@pytest.mark.parametrize("mode", ["paged", "ranges", "paged-noslots"])
-@pytest.mark.parametrize("r", [1, 4096])
+@pytest.mark.parametrize("mode", ["paged", "ranges", "paged-noslots", "ranges-noslots"])
+@pytest.mark.parametrize("r", [1, 16, 512, 4096])
 def test_kv_write_with_table_long_context(r, mode):
-    """128K: the step's kernel-unit table (32 -> 16) written by the slot-mapping launch."""
-    check_kv_write_with_table(long_context(r), mode, k=2, pad=0)
+    """128K: the step's kernel-unit table (32 -> 16) written by the slot-mapping launch (or, in
+    the one-kernel schedule, by a launch before it); slots, table, counts and the whole cache."""
+    check_kv_write_with_table(long_context(r), mode, k=2, pad=0, payload=long_context_payload())
 
 
 @pytest.mark.parametrize("mode", ["paged-two", "ranges-two", "paged-one", "ranges-one"])
@@ -294,27 +299,85 @@ def test_kv_write_study(name, mode):
     check_kv_write(config(name), mode)
 
 
-@pytest.mark.parametrize("keep_slots", [True, False], ids=["slots", "noslots"])
+def _short_prefills():
+    """Many short prefill chunks over rows of one- and two-block runs: a wave of 64 tokens holds
+    several requests, most positions lie below their request's last run, and the lanes outside
+    the wave's first request search their own rows."""
+    r = np.random.default_rng(4741)
+    reqs = [Request(int(r.integers(40, 3000)), int(r.integers(1, 48))) for _ in range(70)]
+    return custom("short_prefills", 4741, reqs, block_size=16, num_blocks=20000,
+                  runs=("len", 1, 2), num_kv_heads=2, head_dim=64,
+                  max_num_tokens=sum(q.n_new for q in reqs) + 37)
+
+
+def _many_runs():
+    """Rows of up to 41,000 one-block runs at block size 1 (range_stride 41,000): finding a run
+    takes three levels of the one-kernel search (more than 16,384 entries), a 40,000-token
+    prefill crosses every run of its row, and the others end inside their last runs."""
+    reqs = [Request(40000, 40000), Request(30000, 900), Request(25000, 1), Request(41000, 5000)]
+    n = sum(q.n_new for q in reqs)
+    return custom("many_runs", 4742, reqs, block_size=1, num_blocks=140000, runs=("len", 1, 1),
+                  num_kv_heads=1, head_dim=64, max_num_tokens=n + 99)
+
+
+SEARCH_CASES = [_short_prefills, _many_runs]
+
+
+@pytest.mark.parametrize("variant", ["paged", "ranges"])
+@pytest.mark.parametrize("make", SEARCH_CASES, ids=lambda f: f.__name__.strip("_"))
+def test_slot_mapping_search_paths(make, variant):
+    w = make()
+    say(f"[slots] {w.describe()} {variant}")
+    g, gf = gpu_slots(w, DeviceInputs(w), variant)
+    o, of = oracle_slots(w, variant)
+    assert np.array_equal(g, o) and gf == of == 0
+
+
+@pytest.mark.parametrize("mode", WRITE_MODES)
+@pytest.mark.parametrize("make", SEARCH_CASES, ids=lambda f: f.__name__.strip("_"))
+def test_kv_write_search_paths(make, mode):
+    check_kv_write(make(), mode)
+
+
+_LC_PAYLOAD = {}
+
+
+def long_context_payload():
+    """The K/V payload of the 128K batch, on the host and on the device, drawn once from the
+    R = 1 workload's seed and shared by the four layouts: they schedule the same requests and
+    positions and differ only in block placement, so one payload serves them all (drawing
+    2 x 256 MiB of bf16 takes about 25 s on the host)."""
+    if not _LC_PAYLOAD:
+        w = long_context(1)
+        key_h, value_h = w.kv_plane(0), w.kv_plane(1)
+        shape = (1, w.max_num_tokens, w.num_kv_heads, w.head_dim)
+        _LC_PAYLOAD["host"] = (key_h, value_h)
+        _LC_PAYLOAD["dev"] = (dev(key_h).view(shape), dev(value_h).view(shape))
+    return _LC_PAYLOAD["host"], _LC_PAYLOAD["dev"]
+
+
+@pytest.mark.parametrize("schedule", ["two", "one", "noslots"])
 @pytest.mark.parametrize("variant", ["paged", "ranges_bs32", "ranges_expanded"])
-@pytest.mark.parametrize("r", [1, 4096])
-def test_kv_write_long_context(r, variant, keep_slots):
-    """128K context, fused write of 131,072 tokens into an 8 GiB cache, whole cache compared."""
-    if variant == "paged" and r != 1:
-        pytest.skip("the paged table does not depend on the range count")
+@pytest.mark.parametrize("r", [1, 16, 512, 4096])
+def test_kv_write_long_context(r, variant, schedule):
+    """128K context, fused write of 131,072 tokens into an 8 GiB cache, whole cache compared
+    byte for byte, at every range count: the block table expanded 32 -> 16 (paged), the
+    manager-unit ranges at block size 32, and the ranges expanded to block size 16; with two
+    kernels, with one kernel keeping the slot mapping, and with no slot-mapping output (one
+    kernel under the automatic schedule)."""
     w = long_context(r)
-    say(f"[kv_write long] {w.describe()} {variant}")
+    say(f"[kv_write long] {w.describe()} {variant} schedule={schedule}")
     orc = oracle.get()
     d = DeviceInputs(w)
     k = w.blocks_per_kv_block
-    key_h, value_h = w.kv_plane(0), w.kv_plane(1)
-    key = dev(key_h).view(1, w.max_num_tokens, w.num_kv_heads, w.head_dim)
-    value = dev(value_h).view_as(key)
+    (key_h, value_h), (key, value) = long_context_payload()
     bs_k, nb_k = w.kernel_block_size, w.kernel_num_blocks
-    suffix = "" if keep_slots else "-noslots"
+    suffix = "-" + schedule
     caches = Caches(1, nb_k, bs_k, w.row_elems)
-    o_slots, _ = orc.slot_mapping_ranges(w.query_start_loc, w.num_reqs, w.positions,
-                                         w.max_num_tokens, w.range_start, w.range_len,
-                                         w.range_cum, w.num_ranges, w.block_size)
+    o_slots, o_flags = orc.slot_mapping_ranges(w.query_start_loc, w.num_reqs, w.positions,
+                                               w.max_num_tokens, w.range_start, w.range_len,
+                                               w.range_cum, w.num_ranges, w.block_size)
+    assert o_flags == 0
     if variant == "paged":
         kt = torch.empty((w.max_num_reqs, w.table_stride * k), dtype=torch.int32, device=DEV)
         kvw.kvw_map_to_kernel_blocks(d.block_table, d.nbpr, w.block_size, bs_k, kt)
