@@ -90,6 +90,13 @@ def parse():
     p.add_argument("--decode-only", action="store_true",
                    help="run only the decode-attention measurements (for profiling); prints\n"
                         "their JSON object instead of the benchmark line")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the other four study configs (reported under \"configs\")")
+    p.add_argument("--slot-mapping-only", action="store_true",
+                   help="run only the slot mapping, paged then ranges, 10 calls each with L2 and\n"
+                        "MALL evicted before every call, on the 128K layouts (R = 1, 16, 512,\n"
+                        "4096; manager units), the decode step and the mixed batch, in that order\n"
+                        "(for hardware-counter profiles); prints the order of the calls as JSON")
     p.add_argument("--copy-calibration-mib", type=int, default=512,
                    help="size of the plain device copy timed as the practical ceiling "
                         "(read + write of this many MiB); 0 to skip")
@@ -155,6 +162,9 @@ def main():
     kvw.library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.slot_mapping_only:
+        print(json.dumps(slot_mapping_only()), flush=True)
+        return
     if args.workload != "long_context":
         bench_config(args)
         return
@@ -195,7 +205,7 @@ def main():
     scatter_bytes = real_tokens * base.num_layers * 4 * bpt + real_tokens * 8
 
     results = {}
-    scatter = None
+    scatter = contiguous_ms = None
     for name in variants:
         kind, _, r = name.partition("_r")
         if kind not in ("paged", "ranges") or not r.isdigit():
@@ -331,6 +341,22 @@ def main():
             scatter = statistics.fmean(sc_ms)
             log(f"[bench] kv_scatter_kernel alone ({name} slots): {scatter * 1e3:.1f} us = "
                 f"{scatter_bytes / (scatter * 1e-3) / 1e9:.0f} GB/s")
+            # The same copy kernel with the destination made contiguous (slot t for token t):
+            # the rate this 16-byte non-temporal copy reaches without the scattered blocks.
+            ident = torch.arange(M, dtype=torch.int64, device=dev)
+
+            def contiguous(ev, ident=ident, w=w):
+                if ev is not None:
+                    ev[0].record(stream)
+                kvw.kvw_kv_write(mode=kvw.KVW_SLOTS_PRECOMPUTED, key=key, value=value,
+                                 k_cache=cache[0], v_cache=cache[1], num_blocks=w.num_blocks,
+                                 block_size=w.block_size, slot_mapping_in=ident)
+                if ev is not None:
+                    ev[1].record(stream)
+            _, ct_ms = timed(contiguous, args.warmup, args.steps)
+            contiguous_ms = statistics.fmean(ct_ms)
+            log(f"[bench] the same copy to a contiguous destination: {contiguous_ms * 1e3:.1f} us = "
+                f"{scatter_bytes / (contiguous_ms * 1e-3) / 1e9:.0f} GB/s")
         del step, fused_call, single, write, expand, table_only, table_copy, table_dst
 
     # Context parallelism on the headline layout: the manager's 32-token blocks are the virtual
@@ -407,6 +433,11 @@ def main():
                 f"{avg * 1e3:6.1f} us = {tp[f'TP{tpn}']['gbps']:.0f} GB/s")
             del tp_call, k_r, v_r
 
+    configs = None
+    if not args.no_configs:
+        configs = {name: config_results(name, args.steps, args.warmup,
+                                        graph=name in GRAPH_CONFIGS) for name in STUDY_CONFIGS}
+
     dec = None
     if not args.no_decode:
         del cache
@@ -428,11 +459,22 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / reps
-        copy_ceiling = {"what": "torch device-to-device copy_", "bytes_moved": 2 * n, "ms": ms,
-                        "gbps": 2 * n / (ms * 1e-3) / 1e9}
-        log(f"[bench] device copy of {args.copy_calibration_mib} MiB: {copy_ceiling['gbps']:.0f} GB/s "
+        copy_ceiling = {"torch_copy": {"what": "torch device-to-device copy_", "bytes_moved": 2 * n,
+                                       "ms": ms, "gbps": 2 * n / (ms * 1e-3) / 1e9}}
+        log(f"[bench] device copy of {args.copy_calibration_mib} MiB: {copy_ceiling['torch_copy']['gbps']:.0f} GB/s "
             "(read + write)")
         del src, dst
+
+    if contiguous_ms is not None:
+        copy_ceiling = copy_ceiling or {}
+        copy_ceiling.update({
+            "what": ("kv_scatter_kernel (16-byte non-temporal loads and stores, one 1 KiB slice per "
+                     "wave) on the headline batch with slot t for token t: the step's copy with a "
+                     "contiguous destination"),
+            "bytes_per_launch": scatter_bytes, "ms": round(contiguous_ms, 6),
+            "gbps": round(scatter_bytes / (contiguous_ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(scatter_bytes / (contiguous_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "same_kernel_step_slots_gbps": round(scatter_bytes / (scatter * 1e-3) / 1e9, 1)})
 
     host_alloc = host_allocator()
 
@@ -483,6 +525,7 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_threads": cpu_par,
         "copy_ceiling": copy_ceiling,
+        "configs": configs,
         "context_parallel": cp,
         "tensor_parallel": tp,
         "decode_attention": dec,
@@ -684,8 +727,19 @@ def decode_context_parallel(args, w, ctx, qd, cl, kc, vc, ws, paged, hq, timed, 
     return res
 
 
-def bench_config(args):
-    """Fused write (paged, ranges) on one of the other study configs."""
+STUDY_CONFIGS = ("tiny_prefill", "decode_step", "mixed_chunked", "full_32_layer")
+GRAPH_CONFIGS = ("tiny_prefill", "decode_step")  # launch-bound: also timed as graph replays
+
+
+def config_results(name, steps, warmup, graph=False):
+    """The fused write (paged, ranges) on one of the study configs other than the 128K one.
+
+    Per variant: the fused call under the automatic schedule, the two-kernel and one-kernel
+    schedules forced, and the slot mapping alone, each timed with HIP events after a 512 MiB
+    write that evicts L2 and MALL; with `graph`, also the automatic call captured once in a HIP
+    graph and replayed back to back (the pages run this path under graph replay, with a padded
+    tail).  The K/V payload is seeded N(0, 1) bf16 drawn on the device: its values do not change
+    the work, and the configs' host generator would take a minute for the 32-layer one."""
     import numpy as np
     import torch
 
@@ -699,13 +753,13 @@ def bench_config(args):
         a = np.ascontiguousarray(a)
         return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
 
-    w = config(args.workload)
+    w = config(name)
     L, M, H, D = w.num_layers, w.max_num_tokens, w.num_kv_heads, w.head_dim
     log(f"[bench] workload {w.describe()}")
-    t = time.time()
-    key = d(w.kv_plane(0)).view(L, M, H, D)
-    value = d(w.kv_plane(1)).view(L, M, H, D)
-    log(f"[bench] K/V generated and uploaded in {time.time() - t:.1f}s")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    key = torch.randn((L, M, H, D), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    value = torch.randn((L, M, H, D), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
     rows = L * w.num_blocks * w.block_size
     cache = torch.full((2, rows, H * D), BF16_SENTINEL, dtype=torch.int16, device=dev)
     sm_out = torch.empty(M, dtype=torch.int64, device=dev)
@@ -720,10 +774,32 @@ def bench_config(args):
     }
     real = w.num_tokens
     fused_bytes = real * L * 4 * w.bytes_per_token + real * 16
+
+    def flushed(call):
+        for _ in range(warmup):
+            call()
+        times = []
+        for i in range(steps):
+            scratch.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return times
+
+    def entry(times):
+        ms = statistics.fmean(times)
+        return {"ms_avg": ms, "ms_p10": float(np.percentile(times, 10)),
+                "ms_p90": float(np.percentile(times, 90)), "tokens_per_s": real / (ms * 1e-3),
+                "gbps": fused_bytes / (ms * 1e-3) / 1e9,
+                "frac_of_peak": fused_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+
     results = {}
     schedules = (("", kvw.KVW_SCHEDULE_AUTO), ("_two_kernels", kvw.KVW_SCHEDULE_TWO_KERNELS),
                  ("_one_kernel", kvw.KVW_SCHEDULE_ONE_KERNEL))
-    for name, (mode, mapping) in maps.items():
+    for vname, (mode, mapping) in maps.items():
         for suffix, schedule in schedules:
             def call(mode=mode, mapping=mapping, schedule=schedule):
                 kvw.kvw_kv_write(mode=mode, key=key, value=value, k_cache=cache[0],
@@ -731,65 +807,127 @@ def bench_config(args):
                                  block_size=w.block_size, query_start_loc=qsl,
                                  num_reqs=w.num_reqs, positions=pos, slot_mapping_out=sm_out,
                                  schedule=schedule, **mapping)
-            for _ in range(args.warmup):
-                call()
-            times = []
-            for i in range(args.steps):
-                scratch.fill_(i & 0xFF)
+            r = results[vname + suffix] = entry(flushed(call))
+            log(f"[bench] {w.name} {vname + suffix:20s} {r['ms_avg'] * 1e3:8.1f} us  "
+                f"{r['gbps']:6.0f} GB/s ({100 * r['frac_of_peak']:.1f}%)  "
+                f"{r['tokens_per_s'] / 1e6:.2f} M tokens/s")
+            if graph and not suffix:
+                # `steps` calls captured in one HIP graph, as the write runs inside a replayed
+                # model step: per-call GPU time with the calls back to back (a graph of one call
+                # costs more host time per replay than the kernel runs)
+                g = torch.cuda.CUDAGraph()
+                side = torch.cuda.Stream()
+                side.wait_stream(stream)
+                with torch.cuda.stream(side):
+                    call()
+                stream.wait_stream(side)
+                with torch.cuda.graph(g):
+                    for _ in range(steps):
+                        call()
+                g.replay()
+                reps = 5
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
                 e0.record(stream)
-                call()
+                for _ in range(reps):
+                    g.replay()
                 e1.record(stream)
-                e1.synchronize()
-                times.append(e0.elapsed_time(e1))
-            ms = statistics.fmean(times)
-            key_ = name + suffix
-            results[key_] = {"ms_avg": ms, "ms_p10": float(np.percentile(times, 10)),
-                             "ms_p90": float(np.percentile(times, 90)),
-                             "tokens_per_s": real / (ms * 1e-3),
-                             "gbps": fused_bytes / (ms * 1e-3) / 1e9,
-                             "frac_of_peak": fused_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
-            r = results[key_]
-            log(f"[bench] {key_:20s} {ms * 1e3:8.1f} us  {r['gbps']:6.0f} GB/s "
-                f"({100 * r['frac_of_peak']:.1f}%)  {r['tokens_per_s'] / 1e6:.2f} M tokens/s")
-    # the slot mapping alone (latency-bound: reported in tokens/s)
-    for name, (mode, mapping) in maps.items():
-        def smap(name=name, mapping=mapping):
-            if name == "paged":
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / (reps * steps)
+                results[vname + "_graph_replay"] = {
+                    "ms_avg": ms, "tokens_per_s": real / (ms * 1e-3),
+                    "gbps": fused_bytes / (ms * 1e-3) / 1e9,
+                    "frac_of_peak": fused_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                    "timing": (f"{steps} calls captured in one graph, replayed {reps} times; per call, "
+                               "no flush between calls")}
+                log(f"[bench] {w.name} {vname + '_graph_replay':20s} {ms * 1e3:8.1f} us per call")
+                del g
+    for vname, (mode, mapping) in maps.items():  # the slot mapping alone (latency-bound)
+        def smap(vname=vname, mapping=mapping):
+            if vname == "paged":
                 kvw.kvw_slot_mapping_paged(qsl, w.num_reqs, pos, M, mapping["block_table"],
                                            mapping["num_blocks_per_req"], w.block_size, sm_out)
             else:
                 kvw.kvw_slot_mapping_ranges(qsl, w.num_reqs, pos, M, mapping["range_start"],
                                             mapping["range_len"], mapping["range_cum"],
                                             mapping["num_ranges"], w.block_size, sm_out)
-        for _ in range(args.warmup):
-            smap()
-        times = []
-        for i in range(args.steps):
-            scratch.fill_(i & 0xFF)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            smap()
-            e1.record(stream)
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1))
-        ms = statistics.fmean(times)
-        results[f"slot_mapping_{name}"] = {"ms_avg": ms, "tokens_per_s": real / (ms * 1e-3)}
-        log(f"[bench] slot_mapping_{name:8s} {ms * 1e3:8.1f} us  "
+        ms = statistics.fmean(flushed(smap))
+        results[f"slot_mapping_{vname}"] = {"ms_avg": ms, "tokens_per_s": real / (ms * 1e-3)}
+        log(f"[bench] {w.name} slot_mapping_{vname:8s} {ms * 1e3:8.1f} us  "
             f"{real / (ms * 1e-3) / 1e6:.1f} M tokens/s")
-    head = results["paged"]
+    del cache, key, value, scratch
+    torch.cuda.empty_cache()
+    return {"workload": w.name, "requests": w.num_reqs, "tokens_per_step": real,
+            "max_num_tokens": M, "layers": L, "block_size": w.block_size,
+            "num_blocks": w.num_blocks, "algorithmic_bytes_per_call": fused_bytes,
+            "timing": "HIP events per call after a 512 MiB write evicting L2 and MALL",
+            "variants": {k_: {kk: (round(vv, 6) if isinstance(vv, float) else vv)
+                              for kk, vv in v.items()} for k_, v in results.items()}}
+
+
+def slot_mapping_only():
+    """The slot mapping alone, for hardware-counter runs: per layout, 10 paged then 10 range
+    calls, each after a 512 MiB write that evicts L2 and MALL (so every call fetches its
+    metadata from HBM).  Layouts in order: the 128K batch at R = 1, 16, 512, 4096 (manager
+    block size 32: the write's own mapping), the decode step, the mixed batch.  Returns the
+    order of the calls."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_46_amd as kvw
+    from workloads import config, long_context
+
+    dev = torch.device("cuda:0")
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    order = []
+    layouts = [(f"long_context_r{r}", lambda r=r: long_context(r)) for r in (1, 16, 512, 4096)]
+    layouts += [(n, lambda n=n: config(n)) for n in ("decode_step", "mixed_chunked")]
+    for name, make in layouts:
+        w = make()
+        qsl, pos = d(w.query_start_loc), d(w.positions)
+        bt, nb = d(w.block_table), d(w.num_blocks_per_req)
+        rs, rl, rc, nr = (d(a) for a in (w.range_start, w.range_len, w.range_cum, w.num_ranges))
+        sm = torch.empty(w.max_num_tokens, dtype=torch.int64, device=dev)
+        for variant in ("paged", "ranges"):
+            for i in range(10):
+                scratch.fill_(i)
+                if variant == "paged":
+                    kvw.kvw_slot_mapping_paged(qsl, w.num_reqs, pos, w.max_num_tokens, bt, nb,
+                                               w.block_size, sm)
+                else:
+                    kvw.kvw_slot_mapping_ranges(qsl, w.num_reqs, pos, w.max_num_tokens, rs, rl, rc,
+                                                nr, w.block_size, sm)
+            torch.cuda.synchronize()
+            order.append({"layout": name, "variant": variant, "calls": 10,
+                          "tokens": w.num_tokens, "requests": w.num_reqs,
+                          "runs": int(w.num_ranges[:w.num_reqs].sum())})
+            log(f"[bench] slot mapping {name} {variant}: 10 calls")
+    return {"slot_mapping_calls": order}
+
+
+def bench_config(args):
+    """One JSON line for one of the other study configs (--workload)."""
+    res = config_results(args.workload, args.steps, args.warmup,
+                         graph=args.workload in GRAPH_CONFIGS)
+    head = res["variants"]["paged"]
     line = {
         "metric": METRIC, "value": round(head["tokens_per_s"], 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(head["ms_avg"], 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int64", "data": "synthetic",
-        "config": {"workload": w.name, "requests": w.num_reqs, "tokens_per_step": real,
-                   "max_num_tokens": M, "layers": L, "block_size": w.block_size,
-                   "num_blocks": w.num_blocks, "kv_heads": H, "head_dim": D, "payload": "bf16",
-                   "variant": "paged", "timing": "fused call, HIP events, L2/MALL flushed"},
+        "config": {"workload": res["workload"], "requests": res["requests"],
+                   "tokens_per_step": res["tokens_per_step"], "max_num_tokens": res["max_num_tokens"],
+                   "layers": res["layers"], "block_size": res["block_size"],
+                   "num_blocks": res["num_blocks"], "kv_heads": 8, "head_dim": 128,
+                   "payload": "bf16", "variant": "paged",
+                   "timing": "fused call, HIP events, L2/MALL flushed"},
         "hbm_gbps": round(head["gbps"], 1), "hbm_frac_of_peak": round(head["frac_of_peak"], 4),
-        "algorithmic_bytes_per_step": fused_bytes,
-        "variants": {k_: {kk: round(vv, 6) for kk, vv in v.items()} for k_, v in results.items()},
+        "algorithmic_bytes_per_step": res["algorithmic_bytes_per_call"],
+        "variants": res["variants"],
     }
     print(json.dumps(line), flush=True)
 

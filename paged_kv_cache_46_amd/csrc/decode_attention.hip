@@ -526,17 +526,21 @@ __global__ __launch_bounds__(partial_threads<G>()) void decode_partial_mfma_kern
     float *tile = &s_p[w][0][0];
     float *alpha_row = &s_alpha[w][0];
 
-    // K of the first tile (position col) as the B operand.  Every load below is
-    // unconditional: a lane without a position reads row 0 (in the cache whenever
-    // the chunk holds a position) and drops the value.  Loads under a branch would
-    // make the compiler wait for all of them before the first product; in straight
-    // code it waits only for the loads the product needs.
+    // K of the first tile (position col) as the B operand.  Within a chunk that
+    // holds a position (cnt > 0, uniform) every load below is unconditional: a
+    // lane without a position reads row 0, which is then in the cache, and drops
+    // the value.  Loads under a per-lane branch would make the compiler wait for
+    // all of them before the first product; in straight code it waits only for
+    // the loads the product needs.  A chunk with no position reads nothing (the
+    // cache may then have no rows at all).
     int64_t slk = col < cnt ? s_slot[col] : -1;
-    u32x4 kw[4];
+    u32x4 kw[4] = {};
+    if (cnt > 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const u32x4 t = load16<false>(kbase + (slk >= 0 ? slk : 0) * row_bytes + 64 * k);
-        kw[k] = slk >= 0 ? t : u32x4{0, 0, 0, 0};
+        for (int k = 0; k < 4; ++k) {
+            const u32x4 t = load16<false>(kbase + (slk >= 0 ? slk : 0) * row_bytes + 64 * k);
+            kw[k] = slk >= 0 ? t : u32x4{0, 0, 0, 0};
+        }
     }
     for (int tb = 0; tb < cnt; tb += kTile) {  // uniform trip count
         // loads: K of position tb + col as the B operand, V of positions tb + 4u + rg.

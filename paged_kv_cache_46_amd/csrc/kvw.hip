@@ -59,6 +59,9 @@
 #ifndef KVW_NT_STORES
 #define KVW_NT_STORES 1
 #endif
+#ifndef KVW_TOKEN_WAVE_MAX_ROWS
+#define KVW_TOKEN_WAVE_MAX_ROWS 32768
+#endif
 
 namespace {
 
@@ -139,93 +142,272 @@ __device__ __forceinline__ int64_t device_num_tokens(const MapArgs &a, uint32_t 
     return n;
 }
 
-// Largest r in [0, num_reqs) with qsl[r] <= t, or -1.  With a
-// non-decreasing qsl and t < qsl[num_reqs] this is the request owning t
-// (empty requests are skipped because the last equal entry wins).
-__device__ __forceinline__ int32_t find_request(const int32_t *qsl, int32_t num_reqs, int64_t t)
-{
-    if (num_reqs <= 0 || qsl[0] > t) return -1;
-    int32_t lo = 0, hi = num_reqs;
-    while (hi - lo > 1) {
-        const int32_t mid = (lo + hi) >> 1;
-        if (qsl[mid] <= t) lo = mid; else hi = mid;
-    }
-    return lo;
-}
-
-
 // Logical block and in-block offset of position p on this rank (cp_locate).
 __device__ __forceinline__ bool locate(const MapArgs &a, int64_t p, int64_t &lb, int32_t &off)
 {
     return cp_locate(p, a.block_size, a.cp_world, a.cp_rank, a.cp_interleave, lb, off);
 }
 
-// Paged gather: one table load per position.
+// Paged gather: one table load per position.  The entry is loaded together
+// with the row's count (lb < table_stride keeps it inside the row), so the two
+// loads cost one memory latency, not two.
 __device__ __forceinline__ int64_t paged_block(const MapArgs &a, int32_t r, int64_t lb,
                                                uint32_t &flags)
 {
+    const int32_t b = lb < a.table_stride ? a.block_table[static_cast<int64_t>(r) * a.table_stride + lb] : 0;
     int64_t bound = a.table_stride;
     if (a.num_blocks_per_req) bound = clamp_count(a.num_blocks_per_req[r], a.table_stride, flags);
     if (lb >= bound) return -1;
-    const int32_t b = a.block_table[static_cast<int64_t>(r) * a.table_stride + lb];
     if (b < 0) { flags |= KVW_FLAG_BAD_BLOCK; return -1; }
     return b;
 }
 
-// Range arithmetic: the run whose [cum, cum + len) holds lb, found by binary
-// search over the (strictly increasing) cum column of the request.
-__device__ __forceinline__ int64_t range_block(const MapArgs &a, int32_t r, int64_t lb,
-                                               uint32_t &flags)
+// Block of lb in the run (cum c, length l, start st), or -1.
+__device__ __forceinline__ int64_t run_block(int64_t c, int64_t l, int64_t st, int64_t lb,
+                                             uint32_t &flags)
 {
-    const int64_t n = clamp_count(a.num_ranges[r], a.range_stride, flags);
-    if (n == 0) return -1;
-    const int64_t row = static_cast<int64_t>(r) * a.range_stride;
-    const int32_t *cum = a.range_cum + row;
-    if (lb < cum[0]) return -1;
-    int32_t lo = 0, hi = static_cast<int32_t>(n);
-    while (hi - lo > 1) {
-        const int32_t mid = (lo + hi) >> 1;
-        if (cum[mid] <= lb) lo = mid; else hi = mid;
-    }
-    const int64_t c = cum[lo];
-    if (lb >= c + a.range_len[row + lo]) return -1;
-    const int64_t b = static_cast<int64_t>(a.range_start[row + lo]) + (lb - c);
+    if (lb < c || lb >= c + l) return -1;
+    const int64_t b = st + (lb - c);
     if (b < 0) { flags |= KVW_FLAG_BAD_BLOCK; return -1; }
     return b;
 }
 
-// Slot of token t (fused modes), or the pad id.
+// Run of lb among runs [0, m) of a row whose next run starts at c_end > lb
+// (cum[m] = c_end): the largest i < m with cum[i] <= lb, or -1.  Interpolation
+// first: with runs of equal length the run is i = lb * m / c_end, and with
+// unequal ones it lies near there, so one 64-entry window around that guess,
+// one vector load and a ballot, usually settles it; otherwise the full
+// wave-uniform search.  c_i receives cum[i].
+__device__ __forceinline__ int32_t run_below(const int32_t *cum, int32_t m, int64_t lb,
+                                             int64_t c_end, int64_t &c_i)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    if (m <= 0) return -1;
+    const int32_t g = static_cast<int32_t>(lb * m / c_end);  // 0 <= g < m: 0 <= lb < c_end
+    const int32_t a = max(0, min(g - kWave / 2, m - kWave));
+    const int32_t wlen = min(kWave, m - a);
+    const int32_t cv = lane < wlen ? cum[a + lane] : INT32_MAX;
+    const int32_t cnt = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(__popcll(__ballot(cv <= lb))));
+    if (cnt > 0 && (cnt < wlen || a + wlen == m)) {
+        c_i = __builtin_amdgcn_readlane(cv, cnt - 1);
+        return a + cnt - 1;
+    }
+    if (cnt == 0 && a == 0) return -1;
+    const int32_t i = wave_uniform_upper_index(cum, m, lb);
+    if (i >= 0) c_i = cum[i];
+    return i;
+}
+
+// Slot of token t < num_tokens at position p (one-kernel path: t is the same
+// on every lane of the wave), or the pad id.  All loads are wave-uniform.
 template <int MODE>
-__device__ __forceinline__ int64_t resolve_slot(const MapArgs &a, int64_t t, int64_t num_tokens,
+__device__ __forceinline__ int64_t resolve_slot(const MapArgs &a, int64_t t, int64_t p,
                                                 uint32_t &flags)
 {
-    if (t >= num_tokens) return KVW_PAD_ID;
-    const int32_t r = find_request(a.qsl, a.num_reqs, t);
-    if (r < 0) return KVW_PAD_ID;
-    const int64_t p = a.positions[t];
-    if (p < 0) return KVW_PAD_ID;
-    const int32_t bs = a.block_size;
+    const int32_t r = wave_uniform_upper_index(a.qsl, a.num_reqs, t);
+    if (r < 0 || p < 0) return KVW_PAD_ID;
     int64_t lb;
     int32_t off;
     if (!locate(a, p, lb, off)) return KVW_PAD_ID;  // another context-parallel rank's token
-    const int64_t b = (MODE == kPaged) ? paged_block(a, r, lb, flags) : range_block(a, r, lb, flags);
+    int64_t b;
+    if (MODE == kPaged) {
+        b = paged_block(a, r, lb, flags);
+    } else {
+        const int32_t n = static_cast<int32_t>(clamp_count(a.num_ranges[r], a.range_stride, flags));
+        if (n == 0) return KVW_PAD_ID;
+        const int64_t row = static_cast<int64_t>(r) * a.range_stride;
+        // the last run first, its three fields loaded together; then the runs below it
+        const int64_t c_last = a.range_cum[row + n - 1], l_last = a.range_len[row + n - 1],
+                      s_last = a.range_start[row + n - 1];
+        if (lb >= c_last) {
+            b = run_block(c_last, l_last, s_last, lb, flags);
+        } else {
+            int64_t c_i = 0;
+            const int32_t i = run_below(a.range_cum + row, n - 1, lb, c_last, c_i);
+            if (i < 0) return KVW_PAD_ID;
+            b = run_block(c_i, a.range_len[row + i], a.range_start[row + i], lb, flags);
+        }
+    }
     if (b < 0) return KVW_PAD_ID;
-    return b * bs + off;
+    return b * a.block_size + off;
 }
 
-// Block of lb in run i of request r (i from a search of range_cum), or -1.
-__device__ __forceinline__ int64_t range_block_at(const MapArgs &a, int32_t r, int32_t i, int64_t lb,
-                                                  uint32_t &flags)
+// The first level of the search of one request's runs by the lanes of a wave
+// (the rows of range descriptors are loaded once for the wave's positions):
+// for rows of at most 128 descriptors (width = range_stride), every cum, len
+// and start entry, two per lane; above that, 64 evenly spaced cum entries.
+// None of it depends on the positions or on the row's count, so these loads
+// go out together with the position and count loads; entries past the count
+// are masked afterwards.
+struct RunWindow {
+    int32_t c0, c1, l0, l1, s0, s1;  // window: entries lane and lane + 64
+    int32_t step;                    // 0: window of the whole row; else the cum samples are
+                                     // c0 = cum[lane * step]
+};
+
+__device__ __forceinline__ RunWindow run_window(const MapArgs &a, int64_t row, int32_t width)
 {
-    if (i < 0) return -1;
-    const int64_t row = static_cast<int64_t>(r) * a.range_stride;
-    const int64_t c = a.range_cum[row + i];
-    if (lb < c || lb >= c + a.range_len[row + i]) return -1;
-    const int64_t b = static_cast<int64_t>(a.range_start[row + i]) + (lb - c);
-    if (b < 0) { flags |= KVW_FLAG_BAD_BLOCK; return -1; }
-    return b;
+    const int lane = threadIdx.x & (kWave - 1);
+    RunWindow w{0, 0, 0, 0, 0, 0, 0};
+    if (width <= 0) return w;  // uniform; loads below are unconditional at clamped indices
+    if (width <= 2 * kWave) {
+        const int64_t i0 = row + min(lane, width - 1), i1 = row + min(lane + kWave, width - 1);
+        w.c0 = a.range_cum[i0];
+        w.l0 = a.range_len[i0];
+        w.s0 = a.range_start[i0];
+        w.c1 = a.range_cum[i1];
+        w.l1 = a.range_len[i1];
+        w.s1 = a.range_start[i1];
+    } else {
+        w.step = (width + kWave - 1) / kWave;
+        w.c0 = a.range_cum[row + min(lane * w.step, width - 1)];
+    }
+    return w;
 }
 
+// The search of row `row` (n descriptors, n <= width) for the lanes with part
+// (every lane calls), in two phases so that the loads of several searches go
+// out before any of them is waited on.  run_probe: in window mode the window
+// is already in registers; otherwise the samples give each lane a bucket, and
+// the loads of one window (cum, len and start) covering all of the wave's
+// buckets are issued, or, when the buckets lie too far apart, each lane
+// binary-searches its own bucket.  run_pick: the last i with cum[i] <= lb and
+// that run's descriptor.  Ranks are counted with ballots when the lanes' keys
+// span few values (consecutive positions span few logical blocks: 64 tokens
+// at block size 16 at most 5): one compare and one ballot per distinct key,
+// and the descriptor taken with readlane from the uniform index; otherwise
+// with a shuffle search per lane and shuffles from the lane holding the run.
+constexpr int32_t kNarrowKeys = 16;
+
+struct RunProbe {
+    int32_t lo, len;                 // the window [lo, lo + len) of the row
+    int32_t c0, c1, l0, l1, s0, s1;  // its entries lane and lane + 64
+    int32_t hit;                     // len == 0: this lane's own result, or -1
+    int64_t hc, hl, hs;
+    int32_t kmin, kmax;              // the taking-part lanes' keys (clamped to int32)
+};
+
+// Key of a lane for comparisons with int32 entries: lb clamped (entries are int32).
+__device__ __forceinline__ int32_t key32(int64_t lb) { return lb > INT32_MAX ? INT32_MAX : static_cast<int32_t>(lb); }
+
+// Number of the window's entries <= k (k wave-uniform), the window in (w0, w1) for
+// lanes below len.
+__device__ __forceinline__ int32_t ballot_rank(int32_t w0, int32_t w1, int32_t len, int32_t k)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int32_t c0 = __popcll(__ballot(lane < len && w0 <= k));
+    const int32_t c1 = __popcll(__ballot(lane + kWave < len && w1 <= k));
+    return c0 == kWave ? kWave + c1 : c0;
+}
+
+__device__ RunProbe run_probe(const MapArgs &a, int64_t row, const RunWindow &w, int32_t n,
+                              int64_t lb, bool part)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    RunProbe p{0, n, w.c0, w.c1, w.l0, w.l1, w.s0, w.s1, -1, 0, 0, 0, 0, 0};
+    const int32_t key = key32(lb);
+    p.kmin = wave_min(part ? key : INT32_MAX);
+    p.kmax = wave_max(part ? key : INT32_MIN);
+    if (n <= 0 || p.kmin == INT32_MAX) {
+        p.len = 0;
+        return p;
+    }
+    if (w.step == 0) return p;
+    const bool sampled = lane * w.step < n;
+    int32_t cnt = 0, u_lo, u_hi;
+    if (p.kmax - p.kmin < kNarrowKeys) {
+        // buckets of the smallest and largest key bound every lane's
+        const int32_t cmin = __popcll(__ballot(sampled && w.c0 <= p.kmin));
+        const int32_t cmax = __popcll(__ballot(sampled && w.c0 <= p.kmax));
+        u_lo = cmax == 0 ? INT32_MAX : max(cmin - 1, 0) * w.step;
+        u_hi = min(cmax * w.step, n);
+        if (u_lo != INT32_MAX && u_hi - u_lo > 2 * kWave)
+            for (int32_t k = p.kmin; k <= p.kmax; ++k) {  // each lane's own count
+                const int32_t ck = __popcll(__ballot(sampled && w.c0 <= k));
+                if (key == k) cnt = ck;
+            }
+    } else {
+        cnt = wave_rank(sampled ? static_cast<int64_t>(w.c0) : INT64_MAX, lb);
+        int32_t b_lo = INT32_MAX, b_hi = INT32_MIN;  // this lane's bucket [b_lo, b_hi)
+        if (part && cnt > 0) {
+            b_lo = (cnt - 1) * w.step;
+            b_hi = min(cnt * w.step, n);
+        }
+        u_lo = wave_min(b_lo);
+        u_hi = wave_max(b_hi);
+    }
+    if (u_lo == INT32_MAX || u_hi - u_lo > 2 * kWave) {
+        p.len = 0;
+        if (u_lo != INT32_MAX && part && cnt > 0) {
+            int32_t x = (cnt - 1) * w.step, h = min(cnt * w.step, n);  // cum[x] <= lb
+            while (h - x > 1) {
+                const int32_t mid = (x + h) >> 1;
+                if (a.range_cum[row + mid] <= lb) x = mid; else h = mid;
+            }
+            p.hit = x;
+            p.hc = a.range_cum[row + x];
+            p.hl = a.range_len[row + x];
+            p.hs = a.range_start[row + x];
+        }
+        return p;
+    }
+    p.lo = u_lo;
+    p.len = u_hi - u_lo;  // >= 1; the loads are unconditional at clamped indices
+    const int64_t i0 = row + p.lo + min(lane, p.len - 1), i1 = row + p.lo + min(lane + kWave, p.len - 1);
+    p.c0 = a.range_cum[i0];
+    p.l0 = a.range_len[i0];
+    p.s0 = a.range_start[i0];
+    p.c1 = a.range_cum[i1];
+    p.l1 = a.range_len[i1];
+    p.s1 = a.range_start[i1];
+    return p;
+}
+
+__device__ int32_t run_pick(const RunProbe &p, int64_t lb, bool part, int64_t &c, int64_t &l,
+                            int64_t &st)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    if (p.len == 0) {  // uniform
+        if (!part || p.hit < 0) return -1;
+        c = p.hc;
+        l = p.hl;
+        st = p.hs;
+        return p.hit;
+    }
+    if (p.kmax - p.kmin < kNarrowKeys) {  // uniform
+        const int32_t key = key32(lb);
+        int32_t found = -1;
+        for (int32_t k = p.kmin; k <= p.kmax; ++k) {
+            const int32_t cnt = ballot_rank(p.c0, p.c1, p.len, k);
+            if (cnt == 0) continue;  // uniform: every key k's lane is before the first run
+            const int32_t idx = cnt - 1, src = idx & (kWave - 1);
+            const bool hi = idx >= kWave;
+            const int32_t ck = __builtin_amdgcn_readlane(hi ? p.c1 : p.c0, src);
+            const int32_t lk = __builtin_amdgcn_readlane(hi ? p.l1 : p.l0, src);
+            const int32_t sk = __builtin_amdgcn_readlane(hi ? p.s1 : p.s0, src);
+            if (part && key == k) {
+                c = ck;
+                l = lk;
+                st = sk;
+                found = p.lo + idx;
+            }
+        }
+        return found;
+    }
+    int cnt = wave_rank(lane < p.len ? static_cast<int64_t>(p.c0) : INT64_MAX, lb);
+    const int cnt1 = wave_rank(lane + kWave < p.len ? static_cast<int64_t>(p.c1) : INT64_MAX, lb);
+    if (cnt == kWave) cnt += cnt1;
+    const int32_t k = part && cnt > 0 ? cnt - 1 : -1;  // index inside the window
+    const int src = k >= 0 ? (k & (kWave - 1)) : 0;
+    const int32_t cl = __shfl(p.c0, src), ch = __shfl(p.c1, src);
+    const int32_t ll = __shfl(p.l0, src), lh = __shfl(p.l1, src);
+    const int32_t sl = __shfl(p.s0, src), sh = __shfl(p.s1, src);
+    if (k < 0) return -1;
+    c = k < kWave ? cl : ch;
+    l = k < kWave ? ll : lh;
+    st = k < kWave ? sl : sh;
+    return p.lo + k;
+}
 
 // Entry q of row r of a kernel-unit table expanded from a manager table
 // ([P2] "Entwurfsmotivation"; [P3] section 7): ids[r][i]*k + j for q = i*k + j
@@ -327,38 +509,99 @@ __global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
     }
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x;
     const bool in = t < a.max_num_tokens;  // every lane stays for the wave-wide searches
+    // Loads below are unconditional, at indices clamped into their arrays, and the
+    // values masked afterwards: a load under a per-lane branch makes the compiler
+    // wait for it before the branch joins, which would serialize the loads that are
+    // meant to be in flight together.  Branches around loads are uniform.
     uint32_t nt_flag = 0, flags = 0;
     const int64_t num_tokens = device_num_tokens(a, nt_flag);
     const bool real = in && t < num_tokens;
-    const int64_t p = real ? a.positions[t] : -1;
+    int64_t p = -1;
+    if (num_tokens > 0) {  // uniform; positions past num_tokens are not read
+        const int64_t pv = a.positions[t < num_tokens ? t : num_tokens - 1];
+        if (real) p = pv;
+    }
     const int32_t r = wave_upper_index(a.qsl, a.num_reqs, t, real);
     const int32_t bs = a.block_size;
     int64_t lb = 0;
     int32_t off = 0;
     // a token of another context-parallel rank is padding and reads nothing more
     const bool ok = real && r >= 0 && p >= 0 && locate(a, p, lb, off);
+    const bool has_r = real && r >= 0;
+    const uint64_t reals = __ballot(has_r);
+    const int lane_a = reals ? __builtin_ctzll(reals) : 0;
+    const int32_t lead_a = reals ? __shfl(r, lane_a) : 0;
+    const int32_t r_safe = has_r ? r : lead_a;  // a real request of the wave for every lane
     int64_t b = -1;
     if (MODE == kPaged) {
-        if (ok) b = paged_block(a, r, lb, flags);
-    } else {
-        // lanes of the wave's first request search its range_cum row together
-        const uint64_t oks = __ballot(ok);
-        const int32_t leader = oks ? __shfl(r, __builtin_ctzll(oks)) : -1;
-        int32_t n_lead = 0;
-        if (leader >= 0) {
-            uint32_t unused = 0;
-            n_lead = static_cast<int32_t>(clamp_count(a.num_ranges[leader], a.range_stride, unused));
+        if (reals && a.table_stride > 0) {  // uniform
+            const int64_t lb_in = ok && lb < a.table_stride ? lb : 0;
+            const int32_t entry = a.block_table[static_cast<int64_t>(r_safe) * a.table_stride + lb_in];
+            int64_t bound = a.table_stride;
+            uint32_t count_flags = 0;
+            if (a.num_blocks_per_req)
+                bound = clamp_count(a.num_blocks_per_req[r_safe], a.table_stride, count_flags);
+            if (ok) {
+                flags |= count_flags;
+                if (lb < bound) {
+                    if (entry < 0) flags |= KVW_FLAG_BAD_BLOCK;
+                    else b = entry;
+                }
+            }
+        } else if (ok && a.num_blocks_per_req) {  // stride 0: no entry; the count is still checked
+            uint32_t count_flags = 0;
+            clamp_count(a.num_blocks_per_req[r], a.table_stride, count_flags);
+            flags |= count_flags;
         }
-        const bool coop = ok && r == leader;
-        const int32_t i = wave_upper_index(a.range_cum + static_cast<int64_t>(leader < 0 ? 0 : leader) *
-                                                             a.range_stride,
-                                           n_lead, lb, coop);
-        if (ok) {
-            if (coop) {
-                clamp_count(a.num_ranges[r], a.range_stride, flags);  // the count's flag, per token
-                b = range_block_at(a, r, i, lb, flags);
-            } else {
-                b = range_block(a, r, lb, flags);
+    } else if (reals) {  // uniform
+        // The count of each lane's request, then, together: the request's last run
+        // (where decode positions and the end of a prefill chunk lie) and the first
+        // search level of the rows of the wave's first and last requests when they
+        // hold two lanes or more (a wave of consecutive tokens seldom spans more
+        // requests); those lanes search their row together, the descriptors loaded
+        // once for the wave's positions.  A lane of any other request outside its
+        // last run (rare: a chunk that starts inside the wave) is settled by a
+        // further cooperative search of its request's row.
+        const int lane_b = 63 - __builtin_clzll(reals);
+        const int32_t lead_b = __shfl(r, lane_b);
+        uint32_t count_flags = 0;
+        const int32_t n_all =
+            static_cast<int32_t>(clamp_count(a.num_ranges[r_safe], a.range_stride, count_flags));
+        if (ok) flags |= count_flags;  // the count's flag, per token that uses it
+        const int32_t n = ok ? n_all : 0;
+        const int32_t n_a = __shfl(n_all, lane_a), n_b = __shfl(n_all, lane_b);
+        if (a.range_stride > 0) {  // uniform; with no descriptor every slot is padding
+            const bool two_a = __popcll(__ballot(has_r && r == lead_a)) >= 2;  // uniform
+            const bool two_b = lead_b != lead_a && __popcll(__ballot(has_r && r == lead_b)) >= 2;
+            const int64_t row_a = static_cast<int64_t>(lead_a) * a.range_stride;
+            const int64_t row_b = static_cast<int64_t>(lead_b) * a.range_stride;
+            const int64_t row = static_cast<int64_t>(r_safe) * a.range_stride;
+            const int64_t i_last = row + (n_all > 0 ? n_all - 1 : 0);
+            const int64_t c_last = a.range_cum[i_last], l_last = a.range_len[i_last],
+                          s_last = a.range_start[i_last];
+            const RunWindow win_a = run_window(a, row_a, two_a ? n_a : 0);
+            const RunWindow win_b = run_window(a, row_b, two_b ? n_b : 0);
+            const bool in_a = two_a && n > 0 && r == lead_a;
+            const bool in_b = two_b && n > 0 && r == lead_b;
+            RunProbe pa{}, pb{};
+            if (two_a) pa = run_probe(a, row_a, win_a, n_a, lb, in_a);
+            if (two_b) pb = run_probe(a, row_b, win_b, n_b, lb, in_b);
+            int64_t c = 0, l = 0, st = 0;
+            if (two_a && run_pick(pa, lb, in_a, c, l, st) >= 0 && in_a) b = run_block(c, l, st, lb, flags);
+            if (two_b && run_pick(pb, lb, in_b, c, l, st) >= 0 && in_b) b = run_block(c, l, st, lb, flags);
+            bool pending = false;
+            if (n > 0 && !in_a && !in_b) {
+                if (lb >= c_last) b = run_block(c_last, l_last, s_last, lb, flags);
+                else pending = true;
+            }
+            for (uint64_t left = __ballot(pending); left; left = __ballot(pending)) {  // uniform
+                const int lane_c = __builtin_ctzll(left);
+                const int32_t lead_c = __shfl(r, lane_c), n_c = __shfl(n_all, lane_c);
+                const int64_t row_c = static_cast<int64_t>(lead_c) * a.range_stride;
+                const bool in_c = pending && r == lead_c;
+                const RunProbe pc = run_probe(a, row_c, run_window(a, row_c, n_c), n_c, lb, in_c);
+                if (run_pick(pc, lb, in_c, c, l, st) >= 0 && in_c) b = run_block(c, l, st, lb, flags);
+                if (in_c) pending = false;
             }
         }
     }
@@ -447,41 +690,52 @@ __global__ __launch_bounds__(kScatterThreads) void kv_scatter_small_kernel(const
                                load16<KVW_NT_LOADS>(src + l * c.kv_layer_stride));
 }
 
-// One wave per (token, plane) and layer group (blockIdx.y): the wave first
-// issues the loads of the token's K or V row for the group's first layer,
-// then resolves the slot with scalar loads (the token is wave-uniform) while
-// they are in flight, then stores.  The two planes go to two waves because a
-// wave that moves 2 KiB keeps more transfers in flight per byte than one that
-// moves 4 KiB; the plane-0 wave reports the slot and the flags.  Rows longer
-// than CH KiB are copied in further CH KiB segments once the slot is known.
-template <int MODE, int CH>
+// One wave per (token, plane) (PLANES = 1) or per token (PLANES = 2, both
+// planes) and layer group (blockIdx.y): the wave first issues the loads of
+// the token's K and/or V row for the group's first layer, then resolves the
+// slot with wave-uniform searches while they are in flight, then stores.
+// Two waves per token keep more transfers in flight per byte on large writes;
+// one wave per token halves the slot resolutions, which wins where their
+// latency dominates (small writes, whose grid does not fill the GPU twice).
+// Rows longer than CH KiB are copied in further CH KiB segments once the slot
+// is known.  The wave that holds plane 0 reports the slot and the flags.
+template <int MODE, int CH, int PLANES>
 __global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a, CopyArgs c)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t item = static_cast<int64_t>(blockIdx.x) * kFusedWaves +
                          __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t t = item >> 1;
-    const int plane = static_cast<int>(item & 1);
+    const int64_t t = PLANES == 2 ? item : item >> 1;
+    const int plane0 = PLANES == 2 ? 0 : static_cast<int>(item & 1);  // first plane of the wave
     if (t >= a.max_num_tokens) return;  // whole wave: this kernel has no barrier
     const int l0 = blockIdx.y * c.layers_per_wave;
     const int l1 = min(c.num_layers, l0 + c.layers_per_wave);
     const int64_t bpt = c.bytes_per_token;
     const int64_t lane_off = static_cast<int64_t>(lane) * 16;
-    const uint8_t *src = (plane ? c.value : c.key) + t * c.kv_token_stride + lane_off;
+    const uint8_t *src[PLANES];
+#pragma unroll
+    for (int q = 0; q < PLANES; ++q)
+        src[q] = (plane0 + q ? c.value : c.key) + t * c.kv_token_stride + lane_off;
 
     uint32_t flags = 0;
     const int64_t num_tokens = device_num_tokens(a, flags);
     if (t != 0) flags = 0;
-    const bool real = t < num_tokens;  // rows of padded tokens are not read
-    u32x4 row[CH];
-    if (real && l0 < l1) {
+    const bool real = t < num_tokens;  // rows and positions of padded tokens are not read
+    u32x4 row[PLANES][CH];
+    int64_t p = -1;
+    if (real) {
+        if (l0 < l1) {
 #pragma unroll
-        for (int ch = 0; ch < CH; ++ch)
-            if (lane_off + ch * kSliceBytes < bpt)
-                row[ch] = load16<KVW_NT_LOADS>(src + l0 * c.kv_layer_stride + ch * kSliceBytes);
+            for (int ch = 0; ch < CH; ++ch)
+                if (lane_off + ch * kSliceBytes < bpt)
+#pragma unroll
+                    for (int q = 0; q < PLANES; ++q)
+                        row[q][ch] = load16<KVW_NT_LOADS>(src[q] + l0 * c.kv_layer_stride + ch * kSliceBytes);
+        }
+        p = a.positions[t];
     }
-    int64_t slot = resolve_slot<MODE>(a, t, num_tokens, flags);
-    const bool report = blockIdx.y == 0 && plane == 0;
+    int64_t slot = real ? resolve_slot<MODE>(a, t, p, flags) : KVW_PAD_ID;
+    const bool report = blockIdx.y == 0 && plane0 == 0;
     if (report && lane == 0 && a.slots_out) a.slots_out[t] = slot;
     if (slot >= c.rows_per_layer) {
         if (c.num_layers > 0) flags |= KVW_FLAG_SLOT_OOB;
@@ -490,7 +744,9 @@ __global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a
     if (report && lane == 0) raise_flags(a.err_flag, flags);
     if (slot < 0 || !real) return;
 
-    uint8_t *dst = (plane ? c.v_cache : c.k_cache) + slot * bpt + lane_off;
+    uint8_t *dst[PLANES];
+#pragma unroll
+    for (int q = 0; q < PLANES; ++q) dst[q] = (plane0 + q ? c.v_cache : c.k_cache) + slot * bpt + lane_off;
     for (int l = l0; l < l1; ++l) {
         const int64_t src_l = l * c.kv_layer_stride;
         const int64_t dst_l = static_cast<int64_t>(l) * c.rows_per_layer * bpt;  // l*B*T rows
@@ -499,12 +755,16 @@ __global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a
 #pragma unroll
                 for (int ch = 0; ch < CH; ++ch)
                     if (seg + lane_off + ch * kSliceBytes < bpt)
-                        row[ch] = load16<KVW_NT_LOADS>(src + src_l + seg + ch * kSliceBytes);
+#pragma unroll
+                        for (int q = 0; q < PLANES; ++q)
+                            row[q][ch] = load16<KVW_NT_LOADS>(src[q] + src_l + seg + ch * kSliceBytes);
             }
 #pragma unroll
             for (int ch = 0; ch < CH; ++ch)
                 if (seg + lane_off + ch * kSliceBytes < bpt)
-                    store16<KVW_NT_STORES>(dst + dst_l + seg + ch * kSliceBytes, row[ch]);
+#pragma unroll
+                    for (int q = 0; q < PLANES; ++q)
+                        store16<KVW_NT_STORES>(dst[q] + dst_l + seg + ch * kSliceBytes, row[q][ch]);
         }
     }
 }
@@ -698,17 +958,28 @@ void launch_table(int mode, const MapArgs &a, hipStream_t s)
     }
 }
 
+template <int MODE, int PLANES>
+void launch_fused_shape(const MapArgs &a, const CopyArgs &c, unsigned groups, hipStream_t s)
+{
+    const dim3 grid(grid_for(PLANES == 2 ? a.max_num_tokens : 2 * a.max_num_tokens, kFusedWaves), groups);
+    const dim3 block(kFusedThreads);
+    switch (c.slices_per_row) {
+    case 1: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 1, PLANES>), grid, block, 0, s, a, c); break;
+    case 2: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 2, PLANES>), grid, block, 0, s, a, c); break;
+    case 3: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 3, PLANES>), grid, block, 0, s, a, c); break;
+    default: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, kMaxSlicesPerLane, PLANES>), grid, block, 0, s, a, c);
+    }
+}
+
+// One wave per token for writes of up to KVW_TOKEN_WAVE_MAX_ROWS token rows,
+// one per (token, plane) above.
 template <int MODE>
 void launch_fused(const MapArgs &a, const CopyArgs &c, unsigned groups, hipStream_t s)
 {
-    const dim3 grid(grid_for(2 * a.max_num_tokens, kFusedWaves), groups);  // two planes per token
-    const dim3 block(kFusedThreads);
-    switch (c.slices_per_row) {
-    case 1: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 1>), grid, block, 0, s, a, c); break;
-    case 2: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 2>), grid, block, 0, s, a, c); break;
-    case 3: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 3>), grid, block, 0, s, a, c); break;
-    default: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, kMaxSlicesPerLane>), grid, block, 0, s, a, c);
-    }
+    if (a.max_num_tokens * static_cast<int64_t>(c.num_layers) <= KVW_TOKEN_WAVE_MAX_ROWS)
+        launch_fused_shape<MODE, 2>(a, c, groups, s);
+    else
+        launch_fused_shape<MODE, 1>(a, c, groups, s);
 }
 
 }  // namespace

@@ -85,24 +85,54 @@ __device__ __forceinline__ int32_t wave_max(int32_t v)
     return v;
 }
 
-// Largest i in [0, n) with v[i] <= x (this lane's key), or -1; v sorted.
-// Every lane of the wave calls it with the same v and n; lanes with
-// part == false get -1 and do not shape the search.  When the lanes' answers
-// lie too far apart for one 128-entry window, each lane finishes with a
-// binary search inside its own 1/64 bucket.
-__device__ int32_t wave_upper_index(const int32_t *v, int32_t n, int64_t x, bool part)
+// First level of a wavefront search of the sorted v[0, n): up to 128 entries
+// in registers, two per lane.  For n <= 128 these are all of v; otherwise 64
+// evenly spaced samples, v[lane * step] with step = ceil(n / 64).  Split from
+// the rest of the search so that a caller can issue these loads together with
+// other independent ones (the compiler keeps loads in flight across code that
+// does not use them).
+struct WaveSamples {
+    int64_t s0, s1;  // INT64_MAX where a lane holds no entry
+    int32_t n, step; // step 0: the samples are v itself
+};
+
+__device__ __forceinline__ WaveSamples wave_samples(const int32_t *v, int32_t n)
+{
+    // loads are unconditional, at indices clamped into v, and masked afterwards: a load
+    // under a per-lane branch makes the compiler wait for it before the branch joins
+    const int lane = threadIdx.x & (kWave - 1);
+    WaveSamples s{INT64_MAX, INT64_MAX, n, 0};
+    if (n <= 0) return s;  // uniform
+    if (n > 2 * kWave) {
+        s.step = (n + kWave - 1) / kWave;
+        const int32_t idx = lane * s.step;
+        const int64_t x = v[min(idx, n - 1)];
+        if (idx < n) s.s0 = x;
+    } else {
+        const int64_t x0 = v[min(lane, n - 1)], x1 = v[min(lane + kWave, n - 1)];
+        if (lane < n) s.s0 = x0;
+        if (lane + kWave < n) s.s1 = x1;
+    }
+    return s;
+}
+
+// Largest i in [0, n) with v[i] <= x (this lane's key), or -1; v sorted, s
+// from wave_samples(v, n).  Every lane of the wave calls it with the same v
+// and samples; lanes with part == false get -1 and do not shape the search.
+// When the lanes' answers lie too far apart for one 128-entry window, each
+// lane finishes with a binary search inside its own 1/64 bucket.
+__device__ int32_t wave_search(const int32_t *v, const WaveSamples &s, int64_t x, bool part)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    if (n <= 0) return -1;
-    int32_t lo = 0, len = n;
-    if (len > 2 * kWave) {
-        const int32_t step = (len + kWave - 1) / kWave;
-        const int32_t idx = lane * step;
-        const int cnt = wave_rank(idx < len ? static_cast<int64_t>(v[idx]) : INT64_MAX, x);
+    if (s.n <= 0) return -1;
+    int32_t lo = 0, len = s.n;
+    int64_t s0 = s.s0, s1 = s.s1;
+    if (s.step > 0) {
+        const int cnt = wave_rank(s0, x);
         int32_t b_lo = INT32_MAX, b_hi = INT32_MIN;  // this lane's bucket [b_lo, b_hi)
         if (part && cnt > 0) {
-            b_lo = (cnt - 1) * step;
-            b_hi = min(cnt * step, len);
+            b_lo = (cnt - 1) * s.step;
+            b_hi = min(cnt * s.step, s.n);
         }
         const int32_t u_lo = wave_min(b_lo), u_hi = wave_max(b_hi);
         if (u_lo == INT32_MAX) return -1;  // no taking-part lane has an answer
@@ -115,16 +145,59 @@ __device__ int32_t wave_upper_index(const int32_t *v, int32_t n, int64_t x, bool
             }
             return a;
         }
+        // window of at most 128 entries: two per lane, loaded together (len >= 1)
         lo = u_lo;
         len = u_hi - u_lo;
+        const int64_t x0 = v[lo + min(lane, len - 1)], x1 = v[lo + min(lane + kWave, len - 1)];
+        s0 = lane < len ? x0 : INT64_MAX;
+        s1 = lane + kWave < len ? x1 : INT64_MAX;
     }
-    // window of at most 128 entries: two samples per lane, loaded together
-    const int64_t s0 = lane < len ? static_cast<int64_t>(v[lo + lane]) : INT64_MAX;
-    const int64_t s1 = lane + kWave < len ? static_cast<int64_t>(v[lo + kWave + lane]) : INT64_MAX;
     int cnt = wave_rank(s0, x);
     const int cnt1 = wave_rank(s1, x);
     if (cnt == kWave) cnt += cnt1;
     return (part && cnt > 0) ? lo + cnt - 1 : -1;
+}
+
+// Largest i in [0, n) with v[i] <= x (this lane's key), or -1; v sorted.
+// The two levels of wave_samples and wave_search in one call.
+__device__ __forceinline__ int32_t wave_upper_index(const int32_t *v, int32_t n, int64_t x, bool part)
+{
+    return wave_search(v, wave_samples(v, n), x, part);
+}
+
+// The same search for a key x that is equal on every lane (one token per
+// wave): the entries <= x form a prefix of the sorted v, so a level is one
+// vector load of up to 128 entries (two per lane) and the popcount of a
+// ballot, with no shuffles.  One level covers n <= 128 and two n <= 16,384.
+// With LAST, v[n - 1] is loaded alongside the first level and, when <= x,
+// answers at once (a key in the last run skips the second level).  The
+// result is wave-uniform.
+template <bool LAST = false>
+__device__ __forceinline__ int32_t wave_uniform_upper_index(const int32_t *v, int32_t n, int64_t x)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    if (n <= 0) return -1;
+    int32_t lo = 0, len = n;
+    const int64_t last = LAST ? static_cast<int64_t>(v[n - 1]) : INT64_MAX;
+    bool first = true;
+    while (len > 2 * kWave) {
+        const int32_t step = (len + 2 * kWave - 1) / (2 * kWave);
+        const int32_t i0 = lane * step, i1 = (lane + kWave) * step;
+        const bool p0 = i0 < len && v[lo + i0] <= x;
+        const bool p1 = i1 < len && v[lo + i1] <= x;
+        if (LAST && first && last <= x) return n - 1;
+        first = false;
+        const int32_t cnt = __builtin_amdgcn_readfirstlane(
+            static_cast<int32_t>(__popcll(__ballot(p0)) + __popcll(__ballot(p1))));
+        if (cnt == 0) return -1;  // v[lo] > x: only possible at the first level
+        lo += (cnt - 1) * step;
+        len = min(step, len - (cnt - 1) * step);
+    }
+    const bool p0 = lane < len && v[lo + lane] <= x;
+    const bool p1 = lane + kWave < len && v[lo + kWave + lane] <= x;
+    const int32_t cnt = __builtin_amdgcn_readfirstlane(
+        static_cast<int32_t>(__popcll(__ballot(p0)) + __popcll(__ballot(p1))));
+    return cnt == 0 ? -1 : lo + cnt - 1;
 }
 
 // Logical block lb and in-block offset off of position p >= 0 on this rank.

@@ -372,6 +372,24 @@ def test_decode_empty():
     torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("hq", [8, 32], ids=["vector", "matrix_core"])
+def test_decode_cache_without_rows(hq):
+    """num_blocks = 0 with positions to attend: every slot lies past the cache, so every
+    position is skipped with KVW_FLAG_SLOT_OOB and every output is exactly 0; no chunk holds a
+    position, so none reads the cache (the matrix-core kernel's first-tile load included).  The
+    cache pointers still point at a valid allocation, as the call requires."""
+    w, _ = SMALL[0]
+    lay = Layout(w, num_blocks=0)
+    q = decode_inputs(w, hq, 10, rows=np.zeros(0, np.int64))[0]
+    ctx = np.array([rq.end for rq in w.requests] + [0] * (w.num_reqs - len(w.requests)), np.int64)
+    slots, flags = expected_slots(lay, "paged", ctx)
+    assert flags == FLAG_SLOT_OOB and all((s < 0).all() for s in slots)
+    kc = torch.zeros((16, w.num_kv_heads, w.head_dim), dtype=torch.int16, device=DEV)
+    for mode in ("paged", "ranges"):
+        gpu, flag = run_gpu(mode, lay, q, ctx, int(ctx.max()), kc, kc)
+        assert flag == FLAG_SLOT_OOB and (gpu == 0).all()
+
+
 def test_decode_reads_what_the_write_wrote():
     """One step end to end: kv_write stores each decode token's K/V, then decode attention reads
     the cache; the oracle does the same with its own write."""
