@@ -70,7 +70,7 @@
 extern "C" {
 #endif
 
-#define KVW_ABI_VERSION 6
+#define KVW_ABI_VERSION 7
 #define KVW_PAD_ID (-1)
 /* Largest accepted range_stride (range descriptors per request). */
 #define KVW_MAX_RANGE_STRIDE 65536
@@ -410,6 +410,32 @@ int64_t kvw_decode_workspace_size(int32_t num_reqs, int32_t max_context, int32_t
 size_t kvw_decode_args_size(void);
 
 kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream);
+
+/* Bytes of the static workspace of kvw_decode_attention_noalloc, on each GPU. */
+#define KVW_DECODE_STATIC_WORKSPACE_BYTES (64LL << 20)
+
+/*
+ * kvw_decode_attention for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same operation, kernels and results; the chunk workspace is
+ * a static device array of KVW_DECODE_STATIC_WORKSPACE_BYTES that the library
+ * holds on each GPU it runs on until the process ends, and args->workspace and
+ * args->workspace_bytes are ignored.  The call allocates nothing: its first
+ * call on a GPU looks that GPU's array up (hipGetSymbolAddress, the GPU made
+ * current for the lookup).  The workspace this call needs, with chunk the
+ * chunk length used (chunk_positions, or the library's choice) and
+ * U = num_reqs * ceil(max_context / chunk), is
+ *   U * num_q_heads * (head_dim + 2) * 4 bytes, plus U * 8 + 4 for 32 or more requests;
+ * above KVW_DECODE_STATIC_WORKSPACE_BYTES the call fails with
+ * KVW_ERR_UNSUPPORTED before anything is enqueued (e.g. 256 requests of up to
+ * 8192 positions with 32 query heads need 34 MB at the library's chunk of
+ * 1024; 16 requests of 131,072 positions, 17 MB).  Every call on a GPU uses
+ * that GPU's one array and leaves its contents behind (no call needs them
+ * cleared): calls in stream order are safe, calls that overlap on one GPU
+ * (other streams, other threads) race.
+ * Errors: as kvw_decode_attention; KVW_ERR_HIP if the lookup fails.
+ */
+kvw_status kvw_decode_attention_noalloc(const kvw_decode_args *args, void *stream);
 
 /*
  * Merges decode attention computed over disjoint sets of each request's

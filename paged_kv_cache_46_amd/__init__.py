@@ -17,6 +17,7 @@ from .kvw import (  # noqa: F401
     KVW_SLOTS_RANGES,
     KvwError,
     kvw_decode_attention,
+    kvw_decode_attention_noalloc,
     kvw_decode_merge,
     kvw_decode_workspace_size,
     kvw_kv_write,

@@ -47,6 +47,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "kvw.h"
 #include "kvw_device.h"
@@ -848,6 +849,43 @@ void launch_partial(int group, dim3 grid, dim3 block, size_t lds, hipStream_t s,
     }
 }
 
+// The workspace of kvw_decode_attention_noalloc: one array per GPU, held from the
+// library's load on that GPU until the process ends.  Host code never passes
+// `scratch` itself (on the host the name is a stand-in, not a device address):
+// static_workspace() looks up each GPU's address once, with that GPU current.
+static __device__ __align__(256) uint8_t scratch[KVW_DECODE_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of this GPU's `scratch` (the GPU of `stream`, or the current
+// one for the null stream).
+kvw_status static_workspace(hipStream_t stream, const char *fn, void **out)
+{
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KVW_ERR_HIP, "%s: no device for the stream: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVW_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess)
+            return fail(KVW_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(KVW_ERR_HIP, "%s: hipSetDevice(%d): %s", fn, dev, hipGetErrorString(e));
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !ptr)
+            return fail(KVW_ERR_HIP, "%s: hipGetSymbolAddress of the static workspace on device %d: %s",
+                        fn, dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVW_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -893,9 +931,11 @@ kvw_status kvw_decode_merge(int32_t num_parts, int32_t num_reqs, int32_t num_q_h
     return KVW_OK;
 }
 
-kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
+// kvw_decode_attention with the workspace from args (use_static false) or from
+// this GPU's static array (kvw_decode_attention_noalloc).
+static kvw_status decode_attention_run(const kvw_decode_args *args, void *stream, const char *fn,
+                                       bool use_static)
 {
-    const char *fn = "kvw_decode_attention";
     if (!args) return fail(KVW_ERR_INVALID_ARG, "%s: args is NULL", fn);
     const kvw_decode_args &g = *args;
     if (g.mode != KVW_SLOTS_PAGED && g.mode != KVW_SLOTS_RANGES)
@@ -948,10 +988,26 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
             !aligned_to(g.range_cum, 4) || !aligned_to(g.num_ranges, 4))
             return fail(KVW_ERR_INVALID_ARG, "%s: a range descriptor array is NULL or misaligned", fn);
     }
-    const int64_t need = kvw_decode_workspace_size(g.num_reqs, g.max_context, g.num_q_heads, g.head_dim);
-    if (need < 0) return fail(KVW_ERR_INVALID_ARG, "%s: the workspace size overflows", fn);
-    if (need > 0 && (!g.workspace || !aligned_to(g.workspace, 16) || g.workspace_bytes < need))
-        return fail(KVW_ERR_INVALID_ARG, "%s: workspace of %lld bytes needed", fn, (long long)need);
+    const int32_t chunk = g.chunk_positions ? g.chunk_positions : auto_chunk(g.num_reqs, g.max_context);
+    const int32_t splits = static_cast<int32_t>(ceil_div(g.max_context, chunk));
+    const int64_t units = static_cast<int64_t>(g.num_reqs) * splits;
+    const bool plan = g.num_reqs >= kPlanMinReqs && units <= INT32_MAX;
+    void *workspace = g.workspace;
+    if (!use_static) {
+        const int64_t need = kvw_decode_workspace_size(g.num_reqs, g.max_context, g.num_q_heads, g.head_dim);
+        if (need < 0) return fail(KVW_ERR_INVALID_ARG, "%s: the workspace size overflows", fn);
+        if (need > 0 && (!g.workspace || !aligned_to(g.workspace, 16) || g.workspace_bytes < need))
+            return fail(KVW_ERR_INVALID_ARG, "%s: workspace of %lld bytes needed", fn, (long long)need);
+    } else {
+        // what this call's chunks need: partials, then the work list and its length
+        const int64_t need = units * g.num_q_heads * (kHeadDim + 2) * static_cast<int64_t>(sizeof(float)) +
+                             (plan ? units * static_cast<int64_t>(sizeof(int2)) + 4 : 0);
+        if (need > KVW_DECODE_STATIC_WORKSPACE_BYTES)
+            return fail(KVW_ERR_UNSUPPORTED, "%s: %lld bytes of workspace needed, the static one holds %lld",
+                        fn, (long long)need, (long long)KVW_DECODE_STATIC_WORKSPACE_BYTES);
+        const kvw_status st = static_workspace(reinterpret_cast<hipStream_t>(stream), fn, &workspace);
+        if (st != KVW_OK) return st;
+    }
 
     DecodeArgs a{};
     a.q = static_cast<const uint16_t *>(g.q);
@@ -965,16 +1021,14 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
     a.k_cache = static_cast<const uint8_t *>(g.k_cache);
     a.v_cache = static_cast<const uint8_t *>(g.v_cache);
     a.out = g.out;
-    a.chunk = g.chunk_positions ? g.chunk_positions : auto_chunk(g.num_reqs, g.max_context);
+    a.chunk = chunk;
     a.cp_world = g.cp_world_size;
     a.cp_rank = g.cp_rank;
     a.cp_interleave = g.cp_interleave_size > 0 ? g.cp_interleave_size : 1;
     a.lse_out = g.lse_out;
-    a.splits = static_cast<int32_t>(ceil_div(g.max_context, a.chunk));
-    a.ws_acc = static_cast<float *>(g.workspace);
+    a.splits = splits;
+    a.ws_acc = static_cast<float *>(workspace);
     a.ws_ml = a.ws_acc + static_cast<int64_t>(g.num_reqs) * a.splits * g.num_q_heads * kHeadDim;
-    const int64_t units = static_cast<int64_t>(g.num_reqs) * a.splits;
-    const bool plan = g.num_reqs >= kPlanMinReqs && units <= INT32_MAX;
     // the list follows the partials: an 8-byte aligned offset (two floats per entry above)
     a.units = plan ? reinterpret_cast<int2 *>(a.ws_ml + units * g.num_q_heads * 2) : nullptr;
     a.unit_count = plan ? reinterpret_cast<int32_t *>(a.units + units) : nullptr;
@@ -1019,6 +1073,16 @@ kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(KVW_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return KVW_OK;
+}
+
+kvw_status kvw_decode_attention(const kvw_decode_args *args, void *stream)
+{
+    return decode_attention_run(args, stream, "kvw_decode_attention", false);
+}
+
+kvw_status kvw_decode_attention_noalloc(const kvw_decode_args *args, void *stream)
+{
+    return decode_attention_run(args, stream, "kvw_decode_attention_noalloc", true);
 }
 
 }  // extern "C"

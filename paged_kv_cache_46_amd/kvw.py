@@ -15,7 +15,7 @@ import torch
 
 from .build import LIBRARY
 
-KVW_ABI_VERSION = 6
+KVW_ABI_VERSION = 7
 KVW_PAD_ID = -1
 KVW_MAX_RANGE_STRIDE = 65536
 (KVW_OK, KVW_ERR_INVALID_ARG, KVW_ERR_UNSUPPORTED, KVW_ERR_RANGE_CAP, KVW_ERR_HIP,
@@ -91,6 +91,7 @@ def library(path: str = LIBRARY) -> ctypes.CDLL:
                                       _P],
         "kvw_kv_write": [ctypes.POINTER(kvw_kv_write_args), _P],
         "kvw_decode_attention": [ctypes.POINTER(kvw_decode_args), _P],
+        "kvw_decode_attention_noalloc": [ctypes.POINTER(kvw_decode_args), _P],
         "kvw_decode_merge": [_I32, _I32, _I32, _I32, _P, _P, _P, _P, _P],
     }
     for name, argtypes in sigs.items():
@@ -292,18 +293,11 @@ def kvw_decode_workspace_size(num_reqs, max_context, num_q_heads, head_dim=128) 
     return int(library().kvw_decode_workspace_size(num_reqs, max_context, num_q_heads, head_dim))
 
 
-def kvw_decode_attention(*, mode, q, k_cache, v_cache, context_lens, max_context, num_blocks,
-                         block_size, out, block_table=None, num_blocks_per_req=None,
-                         range_start=None, range_len=None, range_cum=None, num_ranges=None,
-                         scale=None, workspace=None, err_flag=None, stream=None,
-                         chunk_positions=0, cp_world_size=1, cp_rank=0, cp_interleave_size=1,
-                         lse_out=None):
-    """Decode attention over the paged cache (see include/kvw.h).
-
-    q: [num_reqs, num_q_heads, head_dim] 2-byte (bf16) tensor; k_cache, v_cache:
-    [num_blocks * block_size, num_kv_heads, head_dim]; out: float32 like q.  workspace:
-    a byte tensor of kvw_decode_workspace_size(...) bytes, allocated here when None.
-    """
+def _decode_args(mode, q, k_cache, v_cache, context_lens, max_context, num_blocks, block_size,
+                 out, block_table, num_blocks_per_req, range_start, range_len, range_cum,
+                 num_ranges, scale, workspace, err_flag, chunk_positions, cp_world_size, cp_rank,
+                 cp_interleave_size, lse_out):
+    """kvw_decode_args for the decode-attention calls (workspace: a byte tensor or None)."""
     if q.dim() != 3 or k_cache.dim() != 3 or v_cache.shape != k_cache.shape:
         raise ValueError("q must be [R, Hq, D] and the caches [rows, Hkv, D]")
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
@@ -314,9 +308,6 @@ def kvw_decode_attention(*, mode, q, k_cache, v_cache, context_lens, max_context
         raise ValueError("out must be float32 with q's shape")
     num_reqs, hq, d = (int(x) for x in q.shape)
     hkv = int(k_cache.shape[1])
-    need = kvw_decode_workspace_size(num_reqs, int(max_context), hq, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     a = kvw_decode_args()
     a.mode, a.num_reqs = int(mode), num_reqs
     a.q = q.data_ptr()
@@ -338,8 +329,9 @@ def kvw_decode_attention(*, mode, q, k_cache, v_cache, context_lens, max_context
     a.num_q_heads, a.num_kv_heads, a.head_dim = hq, hkv, d
     a.scale = float(scale if scale is not None else d ** -0.5)
     a.out = out.data_ptr()
-    a.workspace = workspace.data_ptr()
-    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.err_flag = _dev(err_flag, torch.int32, "err_flag", optional=True)
     a.chunk_positions = int(chunk_positions)
     a.cp_world_size, a.cp_rank = int(cp_world_size), int(cp_rank)
@@ -347,7 +339,45 @@ def kvw_decode_attention(*, mode, q, k_cache, v_cache, context_lens, max_context
     if lse_out is not None and (lse_out.dtype != torch.float32 or tuple(lse_out.shape) != (num_reqs, hq)):
         raise ValueError("lse_out must be float32 [num_reqs, num_q_heads]")
     a.lse_out = _dev(lse_out, torch.float32, "lse_out", optional=True)
+    return a
+
+
+def kvw_decode_attention(*, mode, q, k_cache, v_cache, context_lens, max_context, num_blocks,
+                         block_size, out, block_table=None, num_blocks_per_req=None,
+                         range_start=None, range_len=None, range_cum=None, num_ranges=None,
+                         scale=None, workspace=None, err_flag=None, stream=None,
+                         chunk_positions=0, cp_world_size=1, cp_rank=0, cp_interleave_size=1,
+                         lse_out=None):
+    """Decode attention over the paged cache (see include/kvw.h).
+
+    q: [num_reqs, num_q_heads, head_dim] 2-byte (bf16) tensor; k_cache, v_cache:
+    [num_blocks * block_size, num_kv_heads, head_dim]; out: float32 like q.  workspace:
+    a byte tensor of kvw_decode_workspace_size(...) bytes, allocated here when None.
+    """
+    if workspace is None:
+        need = kvw_decode_workspace_size(int(q.shape[0]), int(max_context), int(q.shape[1]),
+                                         int(q.shape[2]))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    a = _decode_args(mode, q, k_cache, v_cache, context_lens, max_context, num_blocks, block_size,
+                     out, block_table, num_blocks_per_req, range_start, range_len, range_cum,
+                     num_ranges, scale, workspace, err_flag, chunk_positions, cp_world_size,
+                     cp_rank, cp_interleave_size, lse_out)
     _check(library().kvw_decode_attention(ctypes.byref(a), _stream(stream)))
+
+
+def kvw_decode_attention_noalloc(*, mode, q, k_cache, v_cache, context_lens, max_context,
+                                 num_blocks, block_size, out, block_table=None,
+                                 num_blocks_per_req=None, range_start=None, range_len=None,
+                                 range_cum=None, num_ranges=None, scale=None, err_flag=None,
+                                 stream=None, chunk_positions=0, cp_world_size=1, cp_rank=0,
+                                 cp_interleave_size=1, lse_out=None):
+    """kvw_decode_attention with the library's static per-GPU workspace (see include/kvw.h):
+    nothing is allocated, here or in the library."""
+    a = _decode_args(mode, q, k_cache, v_cache, context_lens, max_context, num_blocks, block_size,
+                     out, block_table, num_blocks_per_req, range_start, range_len, range_cum,
+                     num_ranges, scale, None, err_flag, chunk_positions, cp_world_size, cp_rank,
+                     cp_interleave_size, lse_out)
+    _check(library().kvw_decode_attention_noalloc(ctypes.byref(a), _stream(stream)))
 
 
 def kvw_decode_merge(outs, lses, out, lse_out=None, stream=None):

@@ -315,6 +315,32 @@ def test_decode_validation(lib):
     assert f(ctypes.byref(_decode(num_reqs=0)), None) == OK   # nothing to do: no launch
 
 
+def test_decode_noalloc_validation(lib):
+    """The static-workspace variant validates like kvw_decode_attention (its workspace
+    arguments are ignored) and rejects, before any HIP call, sizes whose workspace exceeds
+    the static array."""
+    f = lib.kvw_decode_attention_noalloc
+    assert f(None, None) == INVALID
+    assert f(ctypes.byref(_decode(mode=kvw.KVW_SLOTS_PRECOMPUTED)), None) == INVALID
+    assert f(ctypes.byref(_decode(head_dim=64)), None) == UNSUPPORTED
+    assert f(ctypes.byref(_decode(block_size=0)), None) == INVALID
+    assert f(ctypes.byref(_decode(q=P + 4)), None) == INVALID
+    assert f(ctypes.byref(_decode(mode=kvw.KVW_SLOTS_RANGES, range_stride=1 << 20)),
+             None) == RANGE_CAP
+    assert f(ctypes.byref(_decode(chunk_positions=768)), None) == INVALID
+    assert f(ctypes.byref(_decode(num_reqs=0, workspace=None, workspace_bytes=0)), None) == OK
+    # 64 requests of 131,072 positions, 32 query heads: the library's chunk for 32 requests or
+    # more is 1024, so 64 * 128 chunks of 32 * 130 fp32 partials (136 MB) plus the work list
+    big = _decode(num_reqs=64, max_context=131072, workspace=None, workspace_bytes=0)
+    assert f(ctypes.byref(big), None) == UNSUPPORTED
+    need = 64 * 128 * 32 * 130 * 4 + 64 * 128 * 8 + 4
+    assert f"{need} bytes" in _err(lib) and str(64 << 20) in _err(lib)
+    # at 2048-position chunks the same batch still needs 68 MB
+    big2 = _decode(num_reqs=64, max_context=131072, chunk_positions=2048, workspace=None,
+                   workspace_bytes=0)
+    assert f(ctypes.byref(big2), None) == UNSUPPORTED
+
+
 def test_decode_merge_validation(lib):
     f = lib.kvw_decode_merge
     assert f(0, 4, 32, 128, P, P, P, None, None) == INVALID        # no part
