@@ -186,7 +186,8 @@ __device__ __forceinline__ int32_t run_below(const int32_t *cum, int32_t m, int6
     const int32_t g = static_cast<int32_t>(lb * m / c_end);  // 0 <= g < m: 0 <= lb < c_end
     const int32_t a = max(0, min(g - kWave / 2, m - kWave));
     const int32_t wlen = min(kWave, m - a);
-    const int32_t cv = lane < wlen ? cum[a + lane] : INT32_MAX;
+    const int32_t cw = cum[a + min(lane, wlen - 1)];  // unconditional at a clamped index
+    const int32_t cv = lane < wlen ? cw : INT32_MAX;
     const int32_t cnt = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(__popcll(__ballot(cv <= lb))));
     if (cnt > 0 && (cnt < wlen || a + wlen == m)) {
         c_i = __builtin_amdgcn_readlane(cv, cnt - 1);
@@ -198,13 +199,13 @@ __device__ __forceinline__ int32_t run_below(const int32_t *cum, int32_t m, int6
     return i;
 }
 
-// Slot of token t < num_tokens at position p (one-kernel path: t is the same
-// on every lane of the wave), or the pad id.  All loads are wave-uniform.
+// Slot of token t < num_tokens of request r (-1: none) at position p
+// (one-kernel path: t is the same on every lane of the wave), or the pad id.
+// All loads are wave-uniform.
 template <int MODE>
-__device__ __forceinline__ int64_t resolve_slot(const MapArgs &a, int64_t t, int64_t p,
+__device__ __forceinline__ int64_t resolve_slot(const MapArgs &a, int32_t r, int64_t p,
                                                 uint32_t &flags)
 {
-    const int32_t r = wave_uniform_upper_index(a.qsl, a.num_reqs, t);
     if (r < 0 || p < 0) return KVW_PAD_ID;
     int64_t lb;
     int32_t off;
@@ -699,7 +700,7 @@ __global__ __launch_bounds__(kScatterThreads) void kv_scatter_small_kernel(const
 // latency dominates (small writes, whose grid does not fill the GPU twice).
 // Rows longer than CH KiB are copied in further CH KiB segments once the slot
 // is known.  The wave that holds plane 0 reports the slot and the flags.
-template <int MODE, int CH, int PLANES>
+template <int MODE, int CH, int PLANES, bool ROWS>
 __global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a, CopyArgs c)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -720,21 +721,33 @@ __global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a
     uint32_t flags = 0;
     const int64_t num_tokens = device_num_tokens(a, flags);
     if (t != 0) flags = 0;
-    const bool real = t < num_tokens;  // rows and positions of padded tokens are not read
+    const bool real = t < num_tokens;  // positions of padded tokens are not read
+    // Vector loads complete in order, and a load under a branch is waited on
+    // before the branch joins.  So the request search's one vector load goes out
+    // first (up to 128 requests: one level), then the rows' first loads, all
+    // unconditional: waiting for the search then leaves the rows in flight while
+    // the slot is resolved with scalar loads.  A padded token's rows are read too
+    // (they lie inside key/value) and never stored; lanes past a row's end read
+    // inside the row.
+    const bool one_level = a.num_reqs <= 2 * kWave;
+    const UniformWindow qw = uniform_window(a.qsl, real && one_level ? a.num_reqs : 0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the search's load ahead of the rows'
     u32x4 row[PLANES][CH];
-    int64_t p = -1;
-    if (real) {
-        if (l0 < l1) {
+    if (ROWS) {  // launches with layers: l0 < l1
 #pragma unroll
-            for (int ch = 0; ch < CH; ++ch)
-                if (lane_off + ch * kSliceBytes < bpt)
+        for (int ch = 0; ch < CH; ++ch) {
+            const int64_t off = min(lane_off + ch * kSliceBytes, bpt - 16) - lane_off;
 #pragma unroll
-                    for (int q = 0; q < PLANES; ++q)
-                        row[q][ch] = load16<KVW_NT_LOADS>(src[q] + l0 * c.kv_layer_stride + ch * kSliceBytes);
+            for (int q = 0; q < PLANES; ++q)
+                row[q][ch] = load16<KVW_NT_LOADS>(src[q] + l0 * c.kv_layer_stride + off);
         }
-        p = a.positions[t];
     }
-    int64_t slot = real ? resolve_slot<MODE>(a, t, p, flags) : KVW_PAD_ID;
+    const int64_t p = real ? a.positions[t] : -1;
+    int64_t slot = KVW_PAD_ID;
+    if (real) {
+        const int32_t r = one_level ? uniform_rank(qw, t) : wave_uniform_upper_index(a.qsl, a.num_reqs, t);
+        slot = resolve_slot<MODE>(a, r, p, flags);
+    }
     const bool report = blockIdx.y == 0 && plane0 == 0;
     if (report && lane == 0 && a.slots_out) a.slots_out[t] = slot;
     if (slot >= c.rows_per_layer) {
@@ -963,11 +976,15 @@ void launch_fused_shape(const MapArgs &a, const CopyArgs &c, unsigned groups, hi
 {
     const dim3 grid(grid_for(PLANES == 2 ? a.max_num_tokens : 2 * a.max_num_tokens, kFusedWaves), groups);
     const dim3 block(kFusedThreads);
+    if (c.num_layers == 0) {  // slots only: no row is read
+        hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 1, PLANES, false>), grid, block, 0, s, a, c);
+        return;
+    }
     switch (c.slices_per_row) {
-    case 1: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 1, PLANES>), grid, block, 0, s, a, c); break;
-    case 2: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 2, PLANES>), grid, block, 0, s, a, c); break;
-    case 3: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 3, PLANES>), grid, block, 0, s, a, c); break;
-    default: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, kMaxSlicesPerLane, PLANES>), grid, block, 0, s, a, c);
+    case 1: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 1, PLANES, true>), grid, block, 0, s, a, c); break;
+    case 2: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 2, PLANES, true>), grid, block, 0, s, a, c); break;
+    case 3: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, 3, PLANES, true>), grid, block, 0, s, a, c); break;
+    default: hipLaunchKernelGGL((kv_write_fused_kernel<MODE, kMaxSlicesPerLane, PLANES, true>), grid, block, 0, s, a, c);
     }
 }
 

@@ -180,11 +180,13 @@ __device__ __forceinline__ int32_t wave_uniform_upper_index(const int32_t *v, in
     int32_t lo = 0, len = n;
     const int64_t last = LAST ? static_cast<int64_t>(v[n - 1]) : INT64_MAX;
     bool first = true;
+    // loads are unconditional at clamped indices (see wave_samples)
     while (len > 2 * kWave) {
         const int32_t step = (len + 2 * kWave - 1) / (2 * kWave);
         const int32_t i0 = lane * step, i1 = (lane + kWave) * step;
-        const bool p0 = i0 < len && v[lo + i0] <= x;
-        const bool p1 = i1 < len && v[lo + i1] <= x;
+        const int64_t v0 = v[lo + min(i0, len - 1)], v1 = v[lo + min(i1, len - 1)];
+        const bool p0 = i0 < len && v0 <= x;
+        const bool p1 = i1 < len && v1 <= x;
         if (LAST && first && last <= x) return n - 1;
         first = false;
         const int32_t cnt = __builtin_amdgcn_readfirstlane(
@@ -193,11 +195,43 @@ __device__ __forceinline__ int32_t wave_uniform_upper_index(const int32_t *v, in
         lo += (cnt - 1) * step;
         len = min(step, len - (cnt - 1) * step);
     }
-    const bool p0 = lane < len && v[lo + lane] <= x;
-    const bool p1 = lane + kWave < len && v[lo + kWave + lane] <= x;
+    const int64_t v0 = v[lo + min(lane, len - 1)];
+    const int64_t v1 = len > kWave ? v[lo + min(lane + kWave, len - 1)] : INT64_MAX;  // uniform
+    const bool p0 = lane < len && v0 <= x;
+    const bool p1 = lane + kWave < len && v1 <= x;
     const int32_t cnt = __builtin_amdgcn_readfirstlane(
         static_cast<int32_t>(__popcll(__ballot(p0)) + __popcll(__ballot(p1))));
     return cnt == 0 ? -1 : lo + cnt - 1;
+}
+
+// The wave-uniform search of a sorted v with n <= 128 entries in two phases:
+// uniform_window issues its one vector load (two entries per lane, clamped
+// into v) and uniform_rank counts the entries <= x with ballots.  Issued
+// before other vector loads, the window can be waited on while those stay in
+// flight (vector loads complete in order).
+struct UniformWindow {
+    int32_t v0, v1;  // kept 32-bit: a widening right after the load would wait for it
+    int32_t n;
+};
+
+// Loads are unconditional (no branch to join) at indices clamped into v, which
+// must hold at least one entry; n <= 0 gives an empty window.
+__device__ __forceinline__ UniformWindow uniform_window(const int32_t *v, int32_t n)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int32_t last = n > 0 ? n - 1 : 0;
+    return UniformWindow{v[min(lane, last)], v[min(lane + kWave, last)], n};
+}
+
+// Largest i < n with v[i] <= x (x wave-uniform), or -1.
+__device__ __forceinline__ int32_t uniform_rank(const UniformWindow &w, int64_t x)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const bool p0 = lane < w.n && static_cast<int64_t>(w.v0) <= x;
+    const bool p1 = lane + kWave < w.n && static_cast<int64_t>(w.v1) <= x;
+    const int32_t cnt = __builtin_amdgcn_readfirstlane(
+        static_cast<int32_t>(__popcll(__ballot(p0)) + __popcll(__ballot(p1))));
+    return cnt == 0 ? -1 : cnt - 1;
 }
 
 // Logical block lb and in-block offset off of position p >= 0 on this rank.
