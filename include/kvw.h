@@ -320,8 +320,8 @@ size_t kvw_kv_write_args_size(void);
  * write always takes one kernel, which is slower than two on fragmented caches
  * and long multi-layer writes.  Measured on MI355X: 131,072 tokens of 2 KiB
  * rows, every 32-slot block its own run, one kernel at 70.0% (paged) and
- * 70.6% (ranges) of 8 TB/s against 73.4% and 72.7% for two kernels; 16,384
- * tokens x 32 layers, 74% against 79%.  Callers that write large batches
+ * 70.2% (ranges) of 8 TB/s against 73.7% and 73.1% for two kernels; 16,384
+ * tokens x 32 layers, 73-75% against 80%.  Callers that write large batches
  * should keep the slot mapping (the attention side needs it anyway).
  * Errors: KVW_ERR_INVALID_ARG for an unknown mode or schedule,
  * KVW_SCHEDULE_TWO_KERNELS without slot_mapping_out, NULL required

@@ -136,7 +136,10 @@ struct CopyArgs {
 // those loads (they may then be scalar loads for a wave-uniform token).
 __device__ __forceinline__ int64_t device_num_tokens(const MapArgs &a, uint32_t &flags)
 {
-    int64_t n = a.qsl[a.num_reqs];
+    // one uniform word: read through the constant address space, so it is a scalar
+    // load that does not queue behind the wave's vector loads
+    int64_t n = reinterpret_cast<const __attribute__((address_space(4))) int32_t *>(
+        reinterpret_cast<uintptr_t>(a.qsl))[a.num_reqs];
     if (n < 0) { n = 0; flags |= KVW_FLAG_NUM_TOKENS; }
     if (n > a.max_num_tokens) { n = a.max_num_tokens; flags |= KVW_FLAG_NUM_TOKENS; }
     return n;
@@ -162,14 +165,15 @@ __device__ __forceinline__ int64_t paged_block(const MapArgs &a, int32_t r, int6
     return b;
 }
 
-// Block of lb in the run (cum c, length l, start st), or -1.
+// Block of lb in the run (cum c, length l, start st), or -1.  Branch-free: a
+// field used only under a branch would be loaded there, after the others.
 __device__ __forceinline__ int64_t run_block(int64_t c, int64_t l, int64_t st, int64_t lb,
                                              uint32_t &flags)
 {
-    if (lb < c || lb >= c + l) return -1;
+    const bool in = lb >= c && lb < c + l;
     const int64_t b = st + (lb - c);
-    if (b < 0) { flags |= KVW_FLAG_BAD_BLOCK; return -1; }
-    return b;
+    flags |= in && b < 0 ? static_cast<uint32_t>(KVW_FLAG_BAD_BLOCK) : 0u;
+    return in && b >= 0 ? b : -1;
 }
 
 // Run of lb among runs [0, m) of a row whose next run starts at c_end > lb
@@ -201,10 +205,11 @@ __device__ __forceinline__ int32_t run_below(const int32_t *cum, int32_t m, int6
 
 // Slot of token t < num_tokens of request r (-1: none) at position p
 // (one-kernel path: t is the same on every lane of the wave), or the pad id.
-// All loads are wave-uniform.
+// All loads are wave-uniform.  Ranges: count_raw is num_ranges[r], found
+// together with r.
 template <int MODE>
 __device__ __forceinline__ int64_t resolve_slot(const MapArgs &a, int32_t r, int64_t p,
-                                                uint32_t &flags)
+                                                int32_t count_raw, uint32_t &flags)
 {
     if (r < 0 || p < 0) return KVW_PAD_ID;
     int64_t lb;
@@ -214,12 +219,16 @@ __device__ __forceinline__ int64_t resolve_slot(const MapArgs &a, int32_t r, int
     if (MODE == kPaged) {
         b = paged_block(a, r, lb, flags);
     } else {
-        const int32_t n = static_cast<int32_t>(clamp_count(a.num_ranges[r], a.range_stride, flags));
+        const int32_t n = static_cast<int32_t>(clamp_count(count_raw, a.range_stride, flags));
         if (n == 0) return KVW_PAD_ID;
         const int64_t row = static_cast<int64_t>(r) * a.range_stride;
         // the last run first, its three fields loaded together; then the runs below it
-        const int64_t c_last = a.range_cum[row + n - 1], l_last = a.range_len[row + n - 1],
-                      s_last = a.range_start[row + n - 1];
+        // the three fields loaded together and waited on once: a widening fused
+        // with each load would wait for it before the next load goes out
+        int32_t c32 = a.range_cum[row + n - 1], l32 = a.range_len[row + n - 1],
+                s32 = a.range_start[row + n - 1];
+        asm volatile("" : "+s"(c32), "+s"(l32), "+s"(s32));  // every use comes after all three
+        const int64_t c_last = c32, l_last = l32, s_last = s32;
         if (lb >= c_last) {
             b = run_block(c_last, l_last, s_last, lb, flags);
         } else {
@@ -279,6 +288,7 @@ __device__ __forceinline__ RunWindow run_window(const MapArgs &a, int64_t row, i
 // and the descriptor taken with readlane from the uniform index; otherwise
 // with a shuffle search per lane and shuffles from the lane holding the run.
 constexpr int32_t kNarrowKeys = 16;
+constexpr int32_t kFewStarts = 4;  // run starts inside a narrow key span taken without a loop
 
 struct RunProbe {
     int32_t lo, len;                 // the window [lo, lo + len) of the row
@@ -377,6 +387,44 @@ __device__ int32_t run_pick(const RunProbe &p, int64_t lb, bool part, int64_t &c
     }
     if (p.kmax - p.kmin < kNarrowKeys) {  // uniform
         const int32_t key = key32(lb);
+        // Runs c_lo - 1 .. c_hi - 1 of the window hold every lane's key; with few
+        // run starts between the smallest and the largest key, each lane counts
+        // the starts at or below its key (read once, uniform) and takes its run's
+        // descriptor from the lane that holds it.  Every read happens while all
+        // lanes are active: the lane read from need not take part.
+        const int32_t c_lo = ballot_rank(p.c0, p.c1, p.len, p.kmin);
+        const int32_t c_hi = ballot_rank(p.c0, p.c1, p.len, p.kmax);
+        if (c_hi == c_lo) {  // uniform: one run
+            if (c_lo == 0) return -1;  // every key before the first run
+            const int32_t idx = c_lo - 1, src = idx & (kWave - 1);
+            const bool hi = idx >= kWave;
+            const int32_t ck = __builtin_amdgcn_readlane(hi ? p.c1 : p.c0, src);
+            const int32_t lk = __builtin_amdgcn_readlane(hi ? p.l1 : p.l0, src);
+            const int32_t sk = __builtin_amdgcn_readlane(hi ? p.s1 : p.s0, src);
+            if (!part) return -1;
+            c = ck;
+            l = lk;
+            st = sk;
+            return p.lo + idx;
+        }
+        if (c_hi - c_lo <= kFewStarts) {  // uniform
+            int32_t idx = c_lo - 1;
+#pragma unroll
+            for (int32_t j = 0; j < kFewStarts; ++j) {
+                const int32_t e = min(c_lo + j, c_hi - 1);  // a run start inside the keys' span
+                const int32_t ce = __builtin_amdgcn_readlane(e >= kWave ? p.c1 : p.c0, e & (kWave - 1));
+                idx += c_lo + j < c_hi && ce <= key ? 1 : 0;
+            }
+            const int32_t src = max(idx, 0) & (kWave - 1);
+            const int32_t cl = __shfl(p.c0, src), ch = __shfl(p.c1, src);
+            const int32_t ll = __shfl(p.l0, src), lh = __shfl(p.l1, src);
+            const int32_t sl = __shfl(p.s0, src), sh = __shfl(p.s1, src);
+            if (!part || idx < 0) return -1;
+            c = idx < kWave ? cl : ch;
+            l = idx < kWave ? ll : lh;
+            st = idx < kWave ? sl : sh;
+            return p.lo + idx;
+        }
         int32_t found = -1;
         for (int32_t k = p.kmin; k <= p.kmax; ++k) {
             const int32_t cnt = ballot_rank(p.c0, p.c1, p.len, k);
@@ -501,28 +549,33 @@ __device__ __forceinline__ void table_role(const MapArgs &a, uint32_t tb)
 
 // One token per lane; the wave finds its tokens' requests (and, for ranges,
 // the runs of the tokens of its first request) with wavefront searches.
-template <int MODE>
-__global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
+// One token per lane; WIDE: more than 128 requests (two search levels).
+template <int MODE, bool WIDE>
+__device__ __forceinline__ void slot_mapping_tokens(const MapArgs &a)
 {
-    if (blockIdx.x >= a.slot_blocks) {  // uniform over the workgroup; no barriers below
-        table_role<MODE>(a, blockIdx.x - a.slot_blocks);
-        return;
-    }
     const int64_t t = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x;
     const bool in = t < a.max_num_tokens;  // every lane stays for the wave-wide searches
-    // Loads below are unconditional, at indices clamped into their arrays, and the
-    // values masked afterwards: a load under a per-lane branch makes the compiler
-    // wait for it before the branch joins, which would serialize the loads that are
-    // meant to be in flight together.  Branches around loads are uniform.
+    // Loads are unconditional, at indices clamped into their arrays, and the values
+    // masked at their use: the compiler moves a load under a branch to its use and
+    // waits there for it and every load before it, which would serialize loads meant
+    // to be in flight together.  The request search's first level and the token
+    // count (a scalar load) go out together, the positions as soon as the count is
+    // known (entries past it are not read).  Ranges: each lane's run count comes
+    // with its request, loaded beside the search's last level, so the request's
+    // runs are one load further, not two.
+    constexpr bool kCounts = MODE == kRanges;
+    const WaveSamples qs = wave_samples<kCounts, WIDE>(a.qsl, a.num_reqs, a.num_ranges);
     uint32_t nt_flag = 0, flags = 0;
     const int64_t num_tokens = device_num_tokens(a, nt_flag);
     const bool real = in && t < num_tokens;
     int64_t p = -1;
-    if (num_tokens > 0) {  // uniform; positions past num_tokens are not read
+    if (num_tokens > 0) {  // uniform
         const int64_t pv = a.positions[t < num_tokens ? t : num_tokens - 1];
-        if (real) p = pv;
+        const int64_t keep = real ? ~int64_t{0} : 0;  // -1 for padded tokens, without a select on the load
+        p = (pv & keep) | ~keep;
     }
-    const int32_t r = wave_upper_index(a.qsl, a.num_reqs, t, real);
+    int32_t r_count = 0;
+    const int32_t r = wave_search<kCounts, WIDE>(a.qsl, qs, t, real, a.num_ranges, &r_count);
     const int32_t bs = a.block_size;
     int64_t lb = 0;
     int32_t off = 0;
@@ -531,7 +584,7 @@ __global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
     const bool has_r = real && r >= 0;
     const uint64_t reals = __ballot(has_r);
     const int lane_a = reals ? __builtin_ctzll(reals) : 0;
-    const int32_t lead_a = reals ? __shfl(r, lane_a) : 0;
+    const int32_t lead_a = reals ? __builtin_amdgcn_readlane(r, lane_a) : 0;
     const int32_t r_safe = has_r ? r : lead_a;  // a real request of the wave for every lane
     int64_t b = -1;
     if (MODE == kPaged) {
@@ -564,13 +617,14 @@ __global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
         // last run (rare: a chunk that starts inside the wave) is settled by a
         // further cooperative search of its request's row.
         const int lane_b = 63 - __builtin_clzll(reals);
-        const int32_t lead_b = __shfl(r, lane_b);
+        const int32_t lead_b = __builtin_amdgcn_readlane(r, lane_b);
         uint32_t count_flags = 0;
+        const int32_t count_a = __builtin_amdgcn_readlane(r_count, lane_a);  // lanes without a request take lead_a's
         const int32_t n_all =
-            static_cast<int32_t>(clamp_count(a.num_ranges[r_safe], a.range_stride, count_flags));
+            static_cast<int32_t>(clamp_count(has_r ? r_count : count_a, a.range_stride, count_flags));
         if (ok) flags |= count_flags;  // the count's flag, per token that uses it
         const int32_t n = ok ? n_all : 0;
-        const int32_t n_a = __shfl(n_all, lane_a), n_b = __shfl(n_all, lane_b);
+        const int32_t n_a = __builtin_amdgcn_readlane(n_all, lane_a), n_b = __builtin_amdgcn_readlane(n_all, lane_b);
         if (a.range_stride > 0) {  // uniform; with no descriptor every slot is padding
             const bool two_a = __popcll(__ballot(has_r && r == lead_a)) >= 2;  // uniform
             const bool two_b = lead_b != lead_a && __popcll(__ballot(has_r && r == lead_b)) >= 2;
@@ -582,22 +636,30 @@ __global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
                           s_last = a.range_start[i_last];
             const RunWindow win_a = run_window(a, row_a, two_a ? n_a : 0);
             const RunWindow win_b = run_window(a, row_b, two_b ? n_b : 0);
-            const bool in_a = two_a && n > 0 && r == lead_a;
-            const bool in_b = two_b && n > 0 && r == lead_b;
-            RunProbe pa{}, pb{};
-            if (two_a) pa = run_probe(a, row_a, win_a, n_a, lb, in_a);
-            if (two_b) pb = run_probe(a, row_b, win_b, n_b, lb, in_b);
-            int64_t c = 0, l = 0, st = 0;
-            if (two_a && run_pick(pa, lb, in_a, c, l, st) >= 0 && in_a) b = run_block(c, l, st, lb, flags);
-            if (two_b && run_pick(pb, lb, in_b, c, l, st) >= 0 && in_b) b = run_block(c, l, st, lb, flags);
-            bool pending = false;
-            if (n > 0 && !in_a && !in_b) {
-                if (lb >= c_last) b = run_block(c_last, l_last, s_last, lb, flags);
-                else pending = true;
+            // positions in their request's last run are settled at once; the
+            // windows serve only the lanes left (none, for decode steps and for
+            // chunks that lie in one run)
+            asm volatile("" ::"v"(l_last), "v"(s_last));  // all three loaded here, together
+            bool pending = n > 0;
+            if (pending && lb >= c_last) {
+                b = run_block(c_last, l_last, s_last, lb, flags);
+                pending = false;
             }
+            const bool in_a = two_a && pending && r == lead_a;
+            const bool in_b = two_b && pending && r == lead_b;
+            int64_t c = 0, l = 0, st = 0;
+            if (__ballot(in_a)) {  // uniform
+                const RunProbe pa = run_probe(a, row_a, win_a, n_a, lb, in_a);
+                if (run_pick(pa, lb, in_a, c, l, st) >= 0 && in_a) b = run_block(c, l, st, lb, flags);
+            }
+            if (__ballot(in_b)) {  // uniform
+                const RunProbe pb = run_probe(a, row_b, win_b, n_b, lb, in_b);
+                if (run_pick(pb, lb, in_b, c, l, st) >= 0 && in_b) b = run_block(c, l, st, lb, flags);
+            }
+            if (in_a || in_b) pending = false;
             for (uint64_t left = __ballot(pending); left; left = __ballot(pending)) {  // uniform
                 const int lane_c = __builtin_ctzll(left);
-                const int32_t lead_c = __shfl(r, lane_c), n_c = __shfl(n_all, lane_c);
+                const int32_t lead_c = __builtin_amdgcn_readlane(r, lane_c), n_c = __builtin_amdgcn_readlane(n_all, lane_c);
                 const int64_t row_c = static_cast<int64_t>(lead_c) * a.range_stride;
                 const bool in_c = pending && r == lead_c;
                 const RunProbe pc = run_probe(a, row_c, run_window(a, row_c, n_c), n_c, lb, in_c);
@@ -608,6 +670,17 @@ __global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
     }
     if (in) a.slots_out[t] = b < 0 ? KVW_PAD_ID : b * bs + off;
     raise_flags(a.err_flag, flags | (t == 0 ? nt_flag : 0u));
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
+{
+    if (blockIdx.x >= a.slot_blocks) {  // uniform over the workgroup; no barriers below
+        table_role<MODE>(a, blockIdx.x - a.slot_blocks);
+        return;
+    }
+    if (a.num_reqs > 2 * kWave) slot_mapping_tokens<MODE, true>(a);  // uniform
+    else slot_mapping_tokens<MODE, false>(a);
 }
 
 
@@ -718,19 +791,17 @@ __global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a
     for (int q = 0; q < PLANES; ++q)
         src[q] = (plane0 + q ? c.value : c.key) + t * c.kv_token_stride + lane_off;
 
-    uint32_t flags = 0;
-    const int64_t num_tokens = device_num_tokens(a, flags);
-    if (t != 0) flags = 0;
-    const bool real = t < num_tokens;  // positions of padded tokens are not read
     // Vector loads complete in order, and a load under a branch is waited on
     // before the branch joins.  So the request search's one vector load goes out
-    // first (up to 128 requests: one level), then the rows' first loads, all
-    // unconditional: waiting for the search then leaves the rows in flight while
-    // the slot is resolved with scalar loads.  A padded token's rows are read too
-    // (they lie inside key/value) and never stored; lanes past a row's end read
-    // inside the row.
+    // first (up to 128 requests: one level; for ranges with the requests' run
+    // counts beside it), then the rows' first loads, all unconditional and
+    // independent of the token count: waiting for the search then leaves the
+    // rows in flight while the slot is resolved with scalar loads.  A padded
+    // token's rows are read too (they lie inside key/value) and never stored;
+    // lanes past a row's end read inside the row.
+    constexpr bool kCounts = MODE == kRanges;
     const bool one_level = a.num_reqs <= 2 * kWave;
-    const UniformWindow qw = uniform_window(a.qsl, real && one_level ? a.num_reqs : 0);
+    const UniformWindow qw = uniform_window<kCounts>(a.qsl, one_level ? a.num_reqs : 0, a.num_ranges);
     __builtin_amdgcn_sched_barrier(0);  // keep the search's load ahead of the rows'
     u32x4 row[PLANES][CH];
     if (ROWS) {  // launches with layers: l0 < l1
@@ -742,11 +813,21 @@ __global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a
                 row[q][ch] = load16<KVW_NT_LOADS>(src[q] + l0 * c.kv_layer_stride + off);
         }
     }
+    uint32_t flags = 0;
+    const int64_t num_tokens = device_num_tokens(a, flags);
+    if (t != 0) flags = 0;
+    const bool real = t < num_tokens;  // positions of padded tokens are not read
     const int64_t p = real ? a.positions[t] : -1;
     int64_t slot = KVW_PAD_ID;
     if (real) {
-        const int32_t r = one_level ? uniform_rank(qw, t) : wave_uniform_upper_index(a.qsl, a.num_reqs, t);
-        slot = resolve_slot<MODE>(a, r, p, flags);
+        int32_t r, count = 0;
+        if (one_level) {
+            r = uniform_rank(qw, t);
+            if (kCounts && r >= 0) count = uniform_entry(qw.c0, qw.c1, r);
+        } else {
+            r = wave_uniform_upper_index<kCounts>(a.qsl, a.num_reqs, t, a.num_ranges, &count);
+        }
+        slot = resolve_slot<MODE>(a, r, p, count, flags);
     }
     const bool report = blockIdx.y == 0 && plane0 == 0;
     if (report && lane == 0 && a.slots_out) a.slots_out[t] = slot;

@@ -71,19 +71,11 @@ __device__ __forceinline__ int wave_rank(int64_t sample, int64_t x)
     return all ? kWave : cnt;
 }
 
-__device__ __forceinline__ int32_t wave_min(int32_t v)
-{
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
-    return v;
-}
+// Minimum and maximum over the wave (every lane active), by the device
+// library's DPP reductions: row shifts within 16-lane rows, then across rows.
+__device__ __forceinline__ int32_t wave_min(int32_t v) { return __ockl_wfred_min_i32(v); }
 
-__device__ __forceinline__ int32_t wave_max(int32_t v)
-{
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
-    return v;
-}
+__device__ __forceinline__ int32_t wave_max(int32_t v) { return __ockl_wfred_max_i32(v); }
 
 // First level of a wavefront search of the sorted v[0, n): up to 128 entries
 // in registers, two per lane.  For n <= 128 these are all of v; otherwise 64
@@ -91,44 +83,85 @@ __device__ __forceinline__ int32_t wave_max(int32_t v)
 // the rest of the search so that a caller can issue these loads together with
 // other independent ones (the compiler keeps loads in flight across code that
 // does not use them).
+//
+// With COMP, a companion array c indexed like v (at least n entries) is loaded
+// beside the search's last level, and the search also returns c[i] for the i
+// it finds: a value keyed by the same index (a request's descriptor count,
+// found with the request) then costs no dependent load of its own.
 struct WaveSamples {
-    int64_t s0, s1;  // INT64_MAX where a lane holds no entry
+    int32_t r0, r1;  // raw entries (lane, lane + 64; or the lane's sample), clamped loads
     int32_t n, step; // step 0: the samples are v itself
+    int32_t c0, c1;  // COMP, step 0: c at the entries of r0 and r1
 };
 
-__device__ __forceinline__ WaveSamples wave_samples(const int32_t *v, int32_t n)
+// Entry v as a 64-bit key where the lane holds one, INT64_MAX where it holds
+// none.  A max, not a select: the compiler turns a select whose operand is a
+// load into a branch with the load moved under it, which then waits for the
+// load (and every load issued before it) at the branch.
+__device__ __forceinline__ int64_t entry_or_max(int32_t v, bool has)
 {
-    // loads are unconditional, at indices clamped into v, and masked afterwards: a load
-    // under a per-lane branch makes the compiler wait for it before the branch joins
+    return max(static_cast<int64_t>(v), has ? INT64_MIN : INT64_MAX);
+}
+
+// WIDE (n > 128: samples, then a window) or not (n <= 128: the whole of v) is
+// chosen by the caller, uniformly, before any load, so that each variant is
+// straight-line code from its loads to their use: the compiler moves a load
+// past a branch to the block that uses it, and there waits for it together
+// with every load issued before it.  The loads are at indices clamped into v
+// and masked at their use, so v must hold at least one entry even when n is 0
+// (query_start_loc always does; wave_upper_index checks n for other arrays).
+template <bool COMP = false, bool WIDE = false>
+__device__ __forceinline__ WaveSamples wave_samples(const int32_t *v, int32_t n,
+                                                    const int32_t *c = nullptr)
+{
     const int lane = threadIdx.x & (kWave - 1);
-    WaveSamples s{INT64_MAX, INT64_MAX, n, 0};
-    if (n <= 0) return s;  // uniform
-    if (n > 2 * kWave) {
-        s.step = (n + kWave - 1) / kWave;
-        const int32_t idx = lane * s.step;
-        const int64_t x = v[min(idx, n - 1)];
-        if (idx < n) s.s0 = x;
+    const int32_t last = max(n - 1, 0);
+    WaveSamples s{0, 0, n, 0, 0, 0};
+    if constexpr (WIDE) {
+        s.step = max((n + kWave - 1) / kWave, 1);
+        s.r0 = v[min(lane * s.step, last)];
     } else {
-        const int64_t x0 = v[min(lane, n - 1)], x1 = v[min(lane + kWave, n - 1)];
-        if (lane < n) s.s0 = x0;
-        if (lane + kWave < n) s.s1 = x1;
+        const int32_t i0 = min(lane, last), i1 = min(lane + kWave, last);
+        if (COMP) {
+            const int32_t *cc = n > 0 ? c : v;  // c may be absent when there is no entry
+            s.c0 = cc[i0];
+            s.c1 = cc[i1];
+        }
+        s.r0 = v[i0];
+        s.r1 = v[i1];
     }
     return s;
 }
 
+// Entry j (0 <= j < 128, per lane) of a 128-entry window held two per lane:
+// w0 holds entries 0..63, w1 entries 64..127.  Every lane runs both shuffles.
+__device__ __forceinline__ int32_t window_entry(int32_t w0, int32_t w1, int32_t j)
+{
+    const int32_t a = __shfl(w0, j & (kWave - 1)), b = __shfl(w1, j & (kWave - 1));
+    return j < kWave ? a : b;
+}
+
 // Largest i in [0, n) with v[i] <= x (this lane's key), or -1; v sorted, s
-// from wave_samples(v, n).  Every lane of the wave calls it with the same v
-// and samples; lanes with part == false get -1 and do not shape the search.
-// When the lanes' answers lie too far apart for one 128-entry window, each
-// lane finishes with a binary search inside its own 1/64 bucket.
-__device__ int32_t wave_search(const int32_t *v, const WaveSamples &s, int64_t x, bool part)
+// from wave_samples<COMP, WIDE>(v, n, c).  Every lane of the wave calls it with
+// the same v and samples; lanes with part == false get -1 and do not shape the
+// search.  WIDE: when the lanes' answers lie too far apart for one 128-entry
+// window, each lane finishes with a binary search inside its own 1/64 bucket.
+// With COMP, c_out receives c[i] (0 with no answer).
+template <bool COMP = false, bool WIDE = false>
+__device__ __forceinline__ int32_t wave_search(const int32_t *v, const WaveSamples &s, int64_t x,
+                                               bool part, const int32_t *c = nullptr,
+                                               int32_t *c_out = nullptr)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    if (s.n <= 0) return -1;
-    int32_t lo = 0, len = s.n;
-    int64_t s0 = s.s0, s1 = s.s1;
-    if (s.step > 0) {
-        const int cnt = wave_rank(s0, x);
+    int32_t lo = 0;
+    int64_t s0, s1;
+    int32_t w0 = s.c0, w1 = s.c1;
+    if constexpr (!WIDE) {  // n <= 128 (n <= 0: every entry masked, no answer)
+        s0 = entry_or_max(s.r0, lane < s.n);
+        s1 = entry_or_max(s.r1, lane + kWave < s.n);
+    } else {
+        if (COMP) *c_out = 0;
+        const int cnt = wave_rank(entry_or_max(s.r0, lane * s.step < s.n), x);
         int32_t b_lo = INT32_MAX, b_hi = INT32_MIN;  // this lane's bucket [b_lo, b_hi)
         if (part && cnt > 0) {
             b_lo = (cnt - 1) * s.step;
@@ -143,43 +176,69 @@ __device__ int32_t wave_search(const int32_t *v, const WaveSamples &s, int64_t x
                 const int32_t mid = (a + h) >> 1;
                 if (v[mid] <= x) a = mid; else h = mid;
             }
+            if (COMP) *c_out = c[a];
             return a;
         }
         // window of at most 128 entries: two per lane, loaded together (len >= 1)
         lo = u_lo;
-        len = u_hi - u_lo;
-        const int64_t x0 = v[lo + min(lane, len - 1)], x1 = v[lo + min(lane + kWave, len - 1)];
-        s0 = lane < len ? x0 : INT64_MAX;
-        s1 = lane + kWave < len ? x1 : INT64_MAX;
+        const int32_t len = u_hi - u_lo;
+        const int32_t i0 = lo + min(lane, len - 1), i1 = lo + min(lane + kWave, len - 1);
+        if (COMP) {
+            w0 = c[i0];
+            w1 = c[i1];
+        }
+        s0 = entry_or_max(v[i0], lane < len);
+        s1 = entry_or_max(v[i1], lane + kWave < len);
     }
     int cnt = wave_rank(s0, x);
     const int cnt1 = wave_rank(s1, x);
     if (cnt == kWave) cnt += cnt1;
-    return (part && cnt > 0) ? lo + cnt - 1 : -1;
+    const bool hit = part && cnt > 0;
+    if (COMP) {
+        const int32_t e = window_entry(w0, w1, hit ? cnt - 1 : 0);
+        *c_out = hit ? e : 0;
+    }
+    return hit ? lo + cnt - 1 : -1;
 }
 
 // Largest i in [0, n) with v[i] <= x (this lane's key), or -1; v sorted.
-// The two levels of wave_samples and wave_search in one call.
-__device__ __forceinline__ int32_t wave_upper_index(const int32_t *v, int32_t n, int64_t x, bool part)
+// Both levels in one call, the variant chosen from n; with COMP also c[i] in
+// c_out.
+template <bool COMP = false>
+__device__ __forceinline__ int32_t wave_upper_index(const int32_t *v, int32_t n, int64_t x, bool part,
+                                                    const int32_t *c = nullptr,
+                                                    int32_t *c_out = nullptr)
 {
-    return wave_search(v, wave_samples(v, n), x, part);
+    if (n <= 0) {  // uniform; v may hold no entry at all (a row of zero width)
+        if (COMP) *c_out = 0;
+        return -1;
+    }
+    if (n > 2 * kWave)
+        return wave_search<COMP, true>(v, wave_samples<COMP, true>(v, n, c), x, part, c, c_out);
+    return wave_search<COMP, false>(v, wave_samples<COMP, false>(v, n, c), x, part, c, c_out);
+}
+
+// Entry i (wave-uniform, 0 <= i < 128) of a window held two per lane.
+__device__ __forceinline__ int32_t uniform_entry(int32_t w0, int32_t w1, int32_t i)
+{
+    return i < kWave ? __builtin_amdgcn_readlane(w0, i) : __builtin_amdgcn_readlane(w1, i - kWave);
 }
 
 // The same search for a key x that is equal on every lane (one token per
 // wave): the entries <= x form a prefix of the sorted v, so a level is one
 // vector load of up to 128 entries (two per lane) and the popcount of a
 // ballot, with no shuffles.  One level covers n <= 128 and two n <= 16,384.
-// With LAST, v[n - 1] is loaded alongside the first level and, when <= x,
-// answers at once (a key in the last run skips the second level).  The
-// result is wave-uniform.
-template <bool LAST = false>
-__device__ __forceinline__ int32_t wave_uniform_upper_index(const int32_t *v, int32_t n, int64_t x)
+// The result is wave-uniform; with COMP, c_out receives c[i] (0 with none),
+// loaded beside the last level.
+template <bool COMP = false>
+__device__ __forceinline__ int32_t wave_uniform_upper_index(const int32_t *v, int32_t n, int64_t x,
+                                                            const int32_t *c = nullptr,
+                                                            int32_t *c_out = nullptr)
 {
     const int lane = threadIdx.x & (kWave - 1);
+    if (COMP) *c_out = 0;
     if (n <= 0) return -1;
     int32_t lo = 0, len = n;
-    const int64_t last = LAST ? static_cast<int64_t>(v[n - 1]) : INT64_MAX;
-    bool first = true;
     // loads are unconditional at clamped indices (see wave_samples)
     while (len > 2 * kWave) {
         const int32_t step = (len + 2 * kWave - 1) / (2 * kWave);
@@ -187,40 +246,61 @@ __device__ __forceinline__ int32_t wave_uniform_upper_index(const int32_t *v, in
         const int64_t v0 = v[lo + min(i0, len - 1)], v1 = v[lo + min(i1, len - 1)];
         const bool p0 = i0 < len && v0 <= x;
         const bool p1 = i1 < len && v1 <= x;
-        if (LAST && first && last <= x) return n - 1;
-        first = false;
         const int32_t cnt = __builtin_amdgcn_readfirstlane(
             static_cast<int32_t>(__popcll(__ballot(p0)) + __popcll(__ballot(p1))));
         if (cnt == 0) return -1;  // v[lo] > x: only possible at the first level
         lo += (cnt - 1) * step;
         len = min(step, len - (cnt - 1) * step);
     }
-    const int64_t v0 = v[lo + min(lane, len - 1)];
-    const int64_t v1 = len > kWave ? v[lo + min(lane + kWave, len - 1)] : INT64_MAX;  // uniform
+    const int32_t i0 = lo + min(lane, len - 1), i1 = lo + min(lane + kWave, len - 1);
+    int32_t w0 = 0, w1 = 0;
+    if (COMP) {
+        w0 = c[i0];
+        w1 = c[i1];
+    }
+    const int64_t v0 = v[i0];
+    const int64_t v1 = len > kWave ? v[i1] : INT64_MAX;  // uniform
     const bool p0 = lane < len && v0 <= x;
     const bool p1 = lane + kWave < len && v1 <= x;
     const int32_t cnt = __builtin_amdgcn_readfirstlane(
         static_cast<int32_t>(__popcll(__ballot(p0)) + __popcll(__ballot(p1))));
-    return cnt == 0 ? -1 : lo + cnt - 1;
+    if (cnt == 0) return -1;
+    if (COMP) *c_out = uniform_entry(w0, w1, cnt - 1);
+    return lo + cnt - 1;
 }
 
 // The wave-uniform search of a sorted v with n <= 128 entries in two phases:
 // uniform_window issues its one vector load (two entries per lane, clamped
 // into v) and uniform_rank counts the entries <= x with ballots.  Issued
 // before other vector loads, the window can be waited on while those stay in
-// flight (vector loads complete in order).
+// flight (vector loads complete in order).  With COMP the window also holds
+// the companion c at the same indices, and uniform_entry(w.c0, w.c1, i)
+// gives c[i].
 struct UniformWindow {
     int32_t v0, v1;  // kept 32-bit: a widening right after the load would wait for it
     int32_t n;
+    int32_t c0, c1;
 };
 
 // Loads are unconditional (no branch to join) at indices clamped into v, which
-// must hold at least one entry; n <= 0 gives an empty window.
-__device__ __forceinline__ UniformWindow uniform_window(const int32_t *v, int32_t n)
+// must hold at least one entry; n <= 0 gives an empty window.  The companion is
+// read only below n (with n <= 0 the loads go to v instead).
+template <bool COMP = false>
+__device__ __forceinline__ UniformWindow uniform_window(const int32_t *v, int32_t n,
+                                                        const int32_t *c = nullptr)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int32_t last = n > 0 ? n - 1 : 0;
-    return UniformWindow{v[min(lane, last)], v[min(lane + kWave, last)], n};
+    const int32_t i0 = min(lane, last), i1 = min(lane + kWave, last);
+    UniformWindow w{0, 0, n, 0, 0};
+    if (COMP) {
+        const int32_t *cc = n > 0 ? c : v;
+        w.c0 = cc[i0];
+        w.c1 = cc[i1];
+    }
+    w.v0 = v[i0];
+    w.v1 = v[i1];
+    return w;
 }
 
 // Largest i < n with v[i] <= x (x wave-uniform), or -1.
