@@ -120,7 +120,8 @@ const char *kvw_last_error(void);
  * [num_tokens, max_num_tokens) is KVW_PAD_ID.
  *
  *   query_start_loc    int32[num_reqs + 1]
- *   positions          int64[max_num_tokens]; entries past num_tokens unread
+ *   positions          int64[max_num_tokens], all of it readable; entries
+ *                      past num_tokens are ignored
  *   block_table        int32[max_num_reqs][block_table_stride], row-major;
  *                      row r holds request r's physical block ids in
  *                      logical order
@@ -319,9 +320,9 @@ size_t kvw_kv_write_args_size(void);
  * Results are identical either way.  Cost: without slot_mapping_out a large
  * write always takes one kernel, which is slower than two on fragmented caches
  * and long multi-layer writes.  Measured on MI355X: 131,072 tokens of 2 KiB
- * rows, every 32-slot block its own run, one kernel at 70.0% (paged) and
- * 70.2% (ranges) of 8 TB/s against 73.7% and 73.1% for two kernels; 16,384
- * tokens x 32 layers, 73-75% against 80%.  Callers that write large batches
+ * rows, every 32-slot block its own run, one kernel at 70-71% of 8 TB/s
+ * (paged and ranges) against 73-74% for two kernels; 16,384 tokens x 32
+ * layers, 74-76% against 80%.  Callers that write large batches
  * should keep the slot mapping (the attention side needs it anyway).
  * Errors: KVW_ERR_INVALID_ARG for an unknown mode or schedule,
  * KVW_SCHEDULE_TWO_KERNELS without slot_mapping_out, NULL required

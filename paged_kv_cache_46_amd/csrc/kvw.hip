@@ -558,22 +558,19 @@ __device__ __forceinline__ void slot_mapping_tokens(const MapArgs &a)
     // Loads are unconditional, at indices clamped into their arrays, and the values
     // masked at their use: the compiler moves a load under a branch to its use and
     // waits there for it and every load before it, which would serialize loads meant
-    // to be in flight together.  The request search's first level and the token
-    // count (a scalar load) go out together, the positions as soon as the count is
-    // known (entries past it are not read).  Ranges: each lane's run count comes
-    // with its request, loaded beside the search's last level, so the request's
-    // runs are one load further, not two.
+    // to be in flight together.  The request search's first level, the positions
+    // (all max_num_tokens of them are readable; a padded token's is ignored) and
+    // the token count (a scalar load) go out together.  Ranges: each lane's run
+    // count comes with its request, loaded beside the search's last level, so the
+    // request's runs are one load further, not two.
     constexpr bool kCounts = MODE == kRanges;
     const WaveSamples qs = wave_samples<kCounts, WIDE>(a.qsl, a.num_reqs, a.num_ranges);
+    const int64_t pv = a.positions[min(t, a.max_num_tokens - 1)];
     uint32_t nt_flag = 0, flags = 0;
     const int64_t num_tokens = device_num_tokens(a, nt_flag);
     const bool real = in && t < num_tokens;
-    int64_t p = -1;
-    if (num_tokens > 0) {  // uniform
-        const int64_t pv = a.positions[t < num_tokens ? t : num_tokens - 1];
-        const int64_t keep = real ? ~int64_t{0} : 0;  // -1 for padded tokens, without a select on the load
-        p = (pv & keep) | ~keep;
-    }
+    const int64_t keep = real ? ~int64_t{0} : 0;  // -1 for padded tokens, without a select on the load
+    const int64_t p = (pv & keep) | ~keep;
     int32_t r_count = 0;
     const int32_t r = wave_search<kCounts, WIDE>(a.qsl, qs, t, real, a.num_ranges, &r_count);
     const int32_t bs = a.block_size;
@@ -814,21 +811,25 @@ __global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a
         }
     }
     uint32_t flags = 0;
+    // the position and the token count go out together (scalar loads, after the
+    // rows': any wait for a scalar load waits for all of them); positions holds
+    // max_num_tokens entries, and a padded token's is read and ignored
+    const int64_t pv = a.positions[t];
     const int64_t num_tokens = device_num_tokens(a, flags);
     if (t != 0) flags = 0;
-    const bool real = t < num_tokens;  // positions of padded tokens are not read
-    const int64_t p = real ? a.positions[t] : -1;
-    int64_t slot = KVW_PAD_ID;
-    if (real) {
-        int32_t r, count = 0;
-        if (one_level) {
-            r = uniform_rank(qw, t);
-            if (kCounts && r >= 0) count = uniform_entry(qw.c0, qw.c1, r);
-        } else {
-            r = wave_uniform_upper_index<kCounts>(a.qsl, a.num_reqs, t, a.num_ranges, &count);
-        }
-        slot = resolve_slot<MODE>(a, r, p, count, flags);
+    const bool real = t < num_tokens;
+    const int64_t keep = real ? ~int64_t{0} : 0;  // -1 for padded tokens, without a select on the load
+    const int64_t p = (pv & keep) | ~keep;
+    // no branch on real before the position is used (a padded token has p = -1 and
+    // gets the pad id): the compiler would move the position's load under it
+    int32_t r, count = 0;
+    if (one_level) {
+        r = uniform_rank(qw, t);
+        if (kCounts && r >= 0) count = uniform_entry(qw.c0, qw.c1, r);
+    } else {
+        r = wave_uniform_upper_index<kCounts>(a.qsl, a.num_reqs, t, a.num_ranges, &count);
     }
+    int64_t slot = resolve_slot<MODE>(a, r, p, count, flags);
     const bool report = blockIdx.y == 0 && plane0 == 0;
     if (report && lane == 0 && a.slots_out) a.slots_out[t] = slot;
     if (slot >= c.rows_per_layer) {

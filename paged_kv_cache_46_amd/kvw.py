@@ -138,6 +138,16 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
+def _positions(positions, max_num_tokens) -> int:
+    """The positions pointer, after checking that all max_num_tokens entries exist (the
+    kernels read every one of them, padded tokens' included)."""
+    ptr = _dev(positions, torch.int64, "positions")
+    if positions.numel() < int(max_num_tokens):
+        raise ValueError(f"positions holds {positions.numel()} entries, fewer than max_num_tokens "
+                         f"({int(max_num_tokens)})")
+    return ptr
+
+
 def _stride(t: Optional[torch.Tensor]) -> int:
     return 0 if t is None else (int(t.shape[1]) if t.dim() == 2 else int(t.numel()))
 
@@ -149,7 +159,7 @@ def kvw_slot_mapping_paged(query_start_loc, num_reqs, positions, max_num_tokens,
     cp_world_size > 1 only this context-parallel rank's positions get slots."""
     _check(library().kvw_slot_mapping_paged(
         _dev(query_start_loc, torch.int32, "query_start_loc"), int(num_reqs),
-        _dev(positions, torch.int64, "positions"), int(max_num_tokens),
+        _positions(positions, max_num_tokens), int(max_num_tokens),
         _dev(block_table, torch.int32, "block_table", optional=True), _stride(block_table),
         _dev(num_blocks_per_req, torch.int32, "num_blocks_per_req", optional=True),
         int(block_size), int(cp_world_size), int(cp_rank), int(cp_interleave_size),
@@ -165,7 +175,7 @@ def kvw_slot_mapping_ranges(query_start_loc, num_reqs, positions, max_num_tokens
     cp_world_size > 1 only this context-parallel rank's positions get slots."""
     _check(library().kvw_slot_mapping_ranges(
         _dev(query_start_loc, torch.int32, "query_start_loc"), int(num_reqs),
-        _dev(positions, torch.int64, "positions"), int(max_num_tokens),
+        _positions(positions, max_num_tokens), int(max_num_tokens),
         _dev(range_start, torch.int32, "range_start"), _dev(range_len, torch.int32, "range_len"),
         _dev(range_cum, torch.int32, "range_cum"), _dev(num_ranges, torch.int32, "num_ranges"),
         _stride(range_start), int(block_size), int(cp_world_size), int(cp_rank),
@@ -273,7 +283,7 @@ def kvw_kv_write(*, mode, key, value, k_cache, v_cache, num_blocks, block_size,
         a.slot_mapping_in = _dev(slot_mapping_in, torch.int64, "slot_mapping_in")
     else:
         a.query_start_loc = _dev(query_start_loc, torch.int32, "query_start_loc")
-        a.positions = _dev(positions, torch.int64, "positions")
+        a.positions = _positions(positions, max_num_tokens)
         a.slot_mapping_out = _dev(slot_mapping_out, torch.int64, "slot_mapping_out", optional=True)
         if mode == KVW_SLOTS_PAGED:
             a.block_table = _dev(block_table, torch.int32, "block_table", optional=True)

@@ -303,7 +303,7 @@ def custom(name: str, seed: int, requests: Sequence[Request], *, block_size: int
     for rq in requests:
         pos[t:t + rq.n_new] = np.arange(rq.end - rq.n_new, rq.end, dtype=np.int64)
         t += rq.n_new
-    # positions past num_tokens are never to be read: fill with garbage
+    # positions past num_tokens are ignored: fill with garbage
     pos[n_tok:] = rng.integers(-(1 << 40), 1 << 40, size=m - n_tok, dtype=np.int64)
 
     return Workload(name=name, seed=seed, block_size=bs,
