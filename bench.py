@@ -143,6 +143,23 @@ def timed(fn, n_warm, n_steps):
     return wall * 1e3 / n_steps, [a.elapsed_time(b) for a, b in evs]
 
 
+def timed_block(fn, n_warm, n_steps):
+    """Average ms per call of n_steps back-to-back calls between one pair of HIP events on the
+    launch stream: a kernel's steady-state launch duration, without the cost of an event pair
+    around each call (a few microseconds)."""
+    import torch
+    for _ in range(n_warm):
+        fn(None)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(torch.cuda.current_stream())
+    for _ in range(n_steps):
+        fn(None)
+    e1.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n_steps
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -205,7 +222,7 @@ def main():
     scatter_bytes = real_tokens * base.num_layers * 4 * bpt + real_tokens * 8
 
     results = {}
-    scatter = contiguous_ms = None
+    scatter = scatter_pairs = contiguous_ms = None
     for name in variants:
         kind, _, r = name.partition("_r")
         if kind not in ("paged", "ranges") or not r.isdigit():
@@ -338,9 +355,11 @@ def main():
                 if ev is not None:
                     ev[1].record(stream)
             _, sc_ms = timed(scatter_only, args.warmup, args.steps)
-            scatter = statistics.fmean(sc_ms)
+            scatter_pairs = statistics.fmean(sc_ms)
+            scatter = timed_block(scatter_only, 2, args.steps)  # warm already
             log(f"[bench] kv_scatter_kernel alone ({name} slots): {scatter * 1e3:.1f} us = "
-                f"{scatter_bytes / (scatter * 1e-3) / 1e9:.0f} GB/s")
+                f"{scatter_bytes / (scatter * 1e-3) / 1e9:.0f} GB/s ({args.steps} launches back to "
+                f"back; {scatter_pairs * 1e3:.1f} us with an event pair around each)")
             # The same copy kernel with the destination made contiguous (slot t for token t):
             # the rate this 16-byte non-temporal copy reaches without the scattered blocks.
             ident = torch.arange(M, dtype=torch.int64, device=dev)
@@ -353,8 +372,7 @@ def main():
                                  block_size=w.block_size, slot_mapping_in=ident)
                 if ev is not None:
                     ev[1].record(stream)
-            _, ct_ms = timed(contiguous, args.warmup, args.steps)
-            contiguous_ms = statistics.fmean(ct_ms)
+            contiguous_ms = timed_block(contiguous, args.warmup, args.steps)
             log(f"[bench] the same copy to a contiguous destination: {contiguous_ms * 1e3:.1f} us = "
                 f"{scatter_bytes / (contiguous_ms * 1e-3) / 1e9:.0f} GB/s")
         del step, fused_call, single, write, expand, table_only, table_copy, table_dst
@@ -497,6 +515,9 @@ def main():
             "traffic": traffic,
             "kernel": "kv_scatter_kernel<1>",
             "launch_ms_avg": round(scatter, 5),
+            "launch_timing": (f"{args.steps} launches back to back between one pair of HIP events "
+                              "on the launch stream, after the step's own timing"),
+            "launch_ms_avg_event_pair_each": round(scatter_pairs, 5),
             "algorithmic_bytes_per_launch": scatter_bytes,
         }
     line = {
