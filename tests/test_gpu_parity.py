@@ -9,8 +9,8 @@ import pytest
 import torch
 
 import paged_kv_cache_46_amd as kvw
-from parity import (DEV, Caches, DeviceInputs, compare_caches, dev, gpu_slots, host, new_flag,
-                    oracle_slots, say)
+from parity import (DEV, Caches, DeviceInputs, compare_caches, dev, gpu_slots, host, kv_device,
+                    new_flag, oracle_slots, say)
 import oracle
 from workloads import config, custom, long_context, small_cases
 from workloads.gen import Request
@@ -505,3 +505,16 @@ def test_invalid_arguments_raise():
         kvw.kvw_slot_mapping_ranges(d.qsl, w.num_reqs, d.positions, w.max_num_tokens, big, big,
                                     big, d.nr, 16, out)
     assert e.value.status == 3
+    # positions must hold max_num_tokens entries (the kernels read a padded token's too): the
+    # binding refuses a shorter array before anything is launched
+    short = d.positions[:w.max_num_tokens - 1]
+    with pytest.raises(ValueError, match="fewer than max_num_tokens"):
+        kvw.kvw_slot_mapping_paged(d.qsl, w.num_reqs, short, w.max_num_tokens, d.block_table,
+                                   d.nbpr, w.block_size, out)
+    key, value = kv_device(w)
+    cache = torch.empty((w.num_blocks * w.block_size, w.row_elems), dtype=torch.int16, device=DEV)
+    with pytest.raises(ValueError, match="fewer than max_num_tokens"):
+        kvw.kvw_kv_write(mode=kvw.KVW_SLOTS_RANGES, key=key, value=value, k_cache=cache,
+                         v_cache=cache, num_blocks=w.num_blocks, block_size=w.block_size,
+                         query_start_loc=d.qsl, num_reqs=w.num_reqs, positions=short,
+                         range_start=d.rs, range_len=d.rl, range_cum=d.rc, num_ranges=d.nr)
