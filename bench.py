@@ -49,6 +49,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -60,7 +61,9 @@ METRIC = "tokens/s and HBM GB/s (% of peak) for fused slot-map+KV write, paged v
 # headline: paged gather over the fully fragmented layout (every manager block its own run)
 HEADLINE = "paged_r4096"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_46_amd", "csrc", "kvw.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_46_amd", "csrc", "kvw.hip"),
+                  os.path.join(ROOT, "paged_kv_cache_46_amd", "csrc", "kvw_device.h"),
+                  os.path.join(ROOT, "include", "kvw.h")]
 COUNTERS = os.path.join(ROOT, "profiles", "kv_scatter_kernel_long_context_counters.json")
 
 
@@ -104,8 +107,19 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 of the write path's device source (kvw.hip, kvw_device.h and kvw.h) with comments,
+    trailing blanks and empty lines removed: what the compiled kernels depend on, so that an
+    edited comment does not void counters taken on the same code."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines()]
+        h.update(os.path.basename(path).encode())
+        h.update("\n".join(ln for ln in lines if ln).encode())
+    return h.hexdigest()
 
 
 def counter_traffic():

@@ -222,9 +222,9 @@ __device__ __forceinline__ int64_t resolve_slot(const MapArgs &a, int32_t r, int
         const int32_t n = static_cast<int32_t>(clamp_count(count_raw, a.range_stride, flags));
         if (n == 0) return KVW_PAD_ID;
         const int64_t row = static_cast<int64_t>(r) * a.range_stride;
-        // the last run first, its three fields loaded together; then the runs below it
-        // the three fields loaded together and waited on once: a widening fused
-        // with each load would wait for it before the next load goes out
+        // the last run first, its three fields loaded together and waited on once (a
+        // widening fused with each load would wait for it before the next goes out);
+        // then the runs below it
         int32_t c32 = a.range_cum[row + n - 1], l32 = a.range_len[row + n - 1],
                 s32 = a.range_start[row + n - 1];
         asm volatile("" : "+s"(c32), "+s"(l32), "+s"(s32));  // every use comes after all three

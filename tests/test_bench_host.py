@@ -43,15 +43,18 @@ def test_counter_traffic_follows_the_kernel_source(tmp_path, monkeypatch):
     """The committed counter figure is reported only while the kernel source is the one the
     counters were taken on."""
     src = tmp_path / "kernel.hip"
-    src.write_text("// one version of the kernel\n")
+    src.write_text("// one version of the kernel\nint x = 1;\n")
     counters = tmp_path / "counters.json"
-    monkeypatch.setattr(bench, "KERNEL_SOURCE", str(src))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [str(src)])
     monkeypatch.setattr(bench, "COUNTERS", str(counters))
     assert bench.counter_traffic() is None  # no counter file
     counters.write_text(json.dumps({"kernel_source_sha256": bench.kernel_source_hash(),
                                     "traffic_bytes_per_launch": 1234}))
     assert bench.counter_traffic() == 1234
-    src.write_text("// the kernel changed since\n")
+    # comments, trailing blanks and empty lines do not change the compiled kernel
+    src.write_text("/* a comment\n   over lines */\n// another\nint x = 1;   // same code\n\n")
+    assert bench.counter_traffic() == 1234
+    src.write_text("// the kernel changed since\nint x = 2;\n")
     assert bench.counter_traffic() is None
     counters.write_text("not json")
     assert bench.counter_traffic() is None
