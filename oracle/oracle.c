@@ -210,6 +210,9 @@ int orc_slot_mapping_ranges(const int32_t *qsl, int32_t num_reqs, const int64_t 
  * A token of another rank is the pad id and reads nothing.  I must divide
  * block_size (so a rank's share of a virtual block is whole chunks and fits
  * its block); W = 1 is orc_slot_mapping_paged.  Other rules as there.
+ * Parity unpinned as to the reading: the pages print no values for this
+ * placement, so its pins check this code against a dealing simulation of the
+ * same reading, not against the pages.
  */
 static int cp_args_ok(int32_t block_size, int32_t world, int32_t rank, int32_t interleave)
 {
