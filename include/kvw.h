@@ -320,8 +320,8 @@ size_t kvw_kv_write_args_size(void);
  * Results are identical either way.  Cost: without slot_mapping_out a large
  * write always takes one kernel, which is slower than two on fragmented caches
  * and long multi-layer writes.  Measured on MI355X: 131,072 tokens of 2 KiB
- * rows, every 32-slot block its own run, one kernel at 70-71% of 8 TB/s
- * (paged and ranges) against 73-74% for two kernels; 16,384 tokens x 32
+ * rows, every 32-slot block its own run, one kernel at about 71% of 8 TB/s
+ * (paged and ranges) against 74-75% for two kernels; 16,384 tokens x 32
  * layers, 74-76% against 80%.  Callers that write large batches
  * should keep the slot mapping (the attention side needs it anyway).
  * Errors: KVW_ERR_INVALID_ARG for an unknown mode or schedule,

@@ -151,16 +151,26 @@ __device__ __forceinline__ bool locate(const MapArgs &a, int64_t p, int64_t &lb,
     return cp_locate(p, a.block_size, a.cp_world, a.cp_rank, a.cp_interleave, lb, off);
 }
 
-// Paged gather: one table load per position.  The entry is loaded together
-// with the row's count (lb < table_stride keeps it inside the row), so the two
-// loads cost one memory latency, not two.
+// Paged gather: one table load per position (wave-uniform: scalar loads).  The
+// entry and the row's count go out together, both unconditional at valid
+// addresses (the entry at a clamped index; without counts the "count" re-reads
+// the entry and is ignored), so the two cost one memory latency: a load under
+// the branch on the count pointer would go out only after the entry arrived.
 __device__ __forceinline__ int64_t paged_block(const MapArgs &a, int32_t r, int64_t lb,
                                                uint32_t &flags)
 {
-    const int32_t b = lb < a.table_stride ? a.block_table[static_cast<int64_t>(r) * a.table_stride + lb] : 0;
-    int64_t bound = a.table_stride;
-    if (a.num_blocks_per_req) bound = clamp_count(a.num_blocks_per_req[r], a.table_stride, flags);
-    if (lb >= bound) return -1;
+    const int32_t stride = a.table_stride;
+    const int32_t *counts = a.num_blocks_per_req;
+    if (stride <= 0 && !counts) return -1;  // uniform: no row, nothing to load
+    const int32_t *entry = stride > 0
+        ? a.block_table + static_cast<int64_t>(r) * stride + min(lb, static_cast<int64_t>(stride) - 1)
+        : counts + r;
+    const int32_t *count = counts ? counts + r : entry;
+    int32_t b = *entry, n = *count;
+    asm volatile("" : "+s"(b), "+s"(n));  // both issued before either is waited on
+    int64_t bound = stride;
+    if (counts) bound = clamp_count(n, stride, flags);
+    if (lb >= bound) return -1;  // with stride 0 every lb is out of the row
     if (b < 0) { flags |= KVW_FLAG_BAD_BLOCK; return -1; }
     return b;
 }
@@ -176,30 +186,41 @@ __device__ __forceinline__ int64_t run_block(int64_t c, int64_t l, int64_t st, i
     return in && b >= 0 ? b : -1;
 }
 
-// Run of lb among runs [0, m) of a row whose next run starts at c_end > lb
-// (cum[m] = c_end): the largest i < m with cum[i] <= lb, or -1.  Interpolation
-// first: with runs of equal length the run is i = lb * m / c_end, and with
-// unequal ones it lies near there, so one 64-entry window around that guess,
-// one vector load and a ballot, usually settles it; otherwise the full
-// wave-uniform search.  c_i receives cum[i].
-__device__ __forceinline__ int32_t run_below(const int32_t *cum, int32_t m, int64_t lb,
-                                             int64_t c_end, int64_t &c_i)
+// Run of lb among runs [0, m) of a row (fields cum, len, start) whose next
+// run starts at c_end > lb (cum[m] = c_end): the largest i < m with
+// cum[i] <= lb, or -1.  Interpolation first: with runs of equal length the run
+// is i = lb * m / c_end, and with unequal ones it lies near there, so one
+// 64-entry window around that guess, its three fields loaded together (one
+// memory latency) and a ballot, usually settles it; otherwise the full
+// wave-uniform search.  The run's fields go to c_i, l_i and s_i.
+__device__ __forceinline__ int32_t run_below(const int32_t *cum, const int32_t *len,
+                                             const int32_t *start, int32_t m, int64_t lb,
+                                             int64_t c_end, int64_t &c_i, int64_t &l_i,
+                                             int64_t &s_i)
 {
     const int lane = threadIdx.x & (kWave - 1);
     if (m <= 0) return -1;
     const int32_t g = static_cast<int32_t>(lb * m / c_end);  // 0 <= g < m: 0 <= lb < c_end
     const int32_t a = max(0, min(g - kWave / 2, m - kWave));
     const int32_t wlen = min(kWave, m - a);
-    const int32_t cw = cum[a + min(lane, wlen - 1)];  // unconditional at a clamped index
+    const int32_t w = a + min(lane, wlen - 1);  // unconditional loads at a clamped index
+    int32_t cw = cum[w], lw = len[w], sw = start[w];
+    asm volatile("" : "+v"(cw), "+v"(lw), "+v"(sw));  // all three out before any is waited on
     const int32_t cv = lane < wlen ? cw : INT32_MAX;
     const int32_t cnt = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(__popcll(__ballot(cv <= lb))));
     if (cnt > 0 && (cnt < wlen || a + wlen == m)) {
         c_i = __builtin_amdgcn_readlane(cv, cnt - 1);
+        l_i = __builtin_amdgcn_readlane(lw, cnt - 1);
+        s_i = __builtin_amdgcn_readlane(sw, cnt - 1);
         return a + cnt - 1;
     }
     if (cnt == 0 && a == 0) return -1;
     const int32_t i = wave_uniform_upper_index(cum, m, lb);
-    if (i >= 0) c_i = cum[i];
+    if (i >= 0) {
+        c_i = cum[i];
+        l_i = len[i];
+        s_i = start[i];
+    }
     return i;
 }
 
@@ -232,10 +253,11 @@ __device__ __forceinline__ int64_t resolve_slot(const MapArgs &a, int32_t r, int
         if (lb >= c_last) {
             b = run_block(c_last, l_last, s_last, lb, flags);
         } else {
-            int64_t c_i = 0;
-            const int32_t i = run_below(a.range_cum + row, n - 1, lb, c_last, c_i);
+            int64_t c_i = 0, l_i = 0, s_i = 0;
+            const int32_t i = run_below(a.range_cum + row, a.range_len + row, a.range_start + row,
+                                        n - 1, lb, c_last, c_i, l_i, s_i);
             if (i < 0) return KVW_PAD_ID;
-            b = run_block(c_i, a.range_len[row + i], a.range_start[row + i], lb, flags);
+            b = run_block(c_i, l_i, s_i, lb, flags);
         }
     }
     if (b < 0) return KVW_PAD_ID;
@@ -683,11 +705,15 @@ __global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
 
 
 // One wave per (layer, token, plane, 1 KiB slice) item.  The token is
-// wave-uniform; its slot is one scalar load, issued together with the
-// 16-byte data load of each lane; the store follows and the wave retires.
-// Items are ordered layer-major (blockIdx.y), then token, plane, slice, so
-// consecutive waves stream through consecutive K/V rows and, for tokens of
-// one block, consecutive cache slots.
+// wave-uniform; its slot is one scalar load, and the slice is read once the
+// slot is known.  (Issuing the read together with the slot load was measured
+// on 131,072 tokens of 2 KiB rows: 3% faster right after the slot-mapping
+// launch on a contiguous cache, 0.5% slower on a fully fragmented one, where
+// the scattered writes bound the kernel and earlier reads compete with them;
+// the fragmented case is the one kept.)  Items are ordered
+// layer-major (blockIdx.y), then token, plane, slice, so consecutive waves
+// stream through consecutive K/V rows and, for tokens of one block,
+// consecutive cache slots.
 // TPW > 1 (context parallelism, where most neighbouring tokens of a rank's
 // batch are another rank's): one wave takes the same slice of TPW consecutive
 // tokens and skips the padded ones, so far fewer waves start only to exit.
@@ -698,11 +724,13 @@ __global__ __launch_bounds__(kScatterThreads) void kv_scatter_kernel(const int64
     const int lane = threadIdx.x & (kWave - 1);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint64_t item = static_cast<uint64_t>(blockIdx.x) * kScatterWaves + wave;
+    int32_t items_log2 = c.items_log2;
+    asm("" : "+s"(items_log2) : "s"(slots));  // both argument lines in one round trip
     uint64_t g64;
     uint32_t r;
-    if (c.items_log2 >= 0) {
-        g64 = item >> c.items_log2;
-        r = static_cast<uint32_t>(item & ((1u << c.items_log2) - 1));
+    if (items_log2 >= 0) {
+        g64 = item >> items_log2;
+        r = static_cast<uint32_t>(item & ((1u << items_log2) - 1));
     } else {
         g64 = item / c.items_per_token;
         r = static_cast<uint32_t>(item - g64 * c.items_per_token);
@@ -733,7 +761,11 @@ __global__ __launch_bounds__(kScatterThreads) void kv_scatter_kernel(const int64
 // Rows shorter than a wave's 1 KiB: one wave copies one plane of up to
 // rows_per_wave consecutive tokens (lane group g of lanes_per_row lanes takes
 // token t0 + g), so a wave still moves up to 1 KiB; each lane reads its own
-// token's slot.
+// token's slot.  EAGER (no context parallelism): each lane's row load goes out
+// with its slot load, so the wave waits for the two together (2-3% faster at
+// 256 and 512 B rows); under context parallelism most rows are another
+// rank's, so a row is read only once its slot is known.
+template <bool EAGER>
 __global__ __launch_bounds__(kScatterThreads) void kv_scatter_small_kernel(const int64_t *slots,
                                                                            CopyArgs c,
                                                                            int32_t *err_flag)
@@ -742,21 +774,31 @@ __global__ __launch_bounds__(kScatterThreads) void kv_scatter_small_kernel(const
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint64_t item = static_cast<uint64_t>(blockIdx.x) * kScatterWaves + wave;
     const uint32_t plane = static_cast<uint32_t>(item & 1);
-    const uint32_t g = static_cast<uint32_t>(lane) / c.lanes_per_row;
+    uint32_t lanes_per_row = c.lanes_per_row;
+    asm("" : "+s"(lanes_per_row) : "s"(slots));  // both argument lines in one round trip
+    const uint32_t g = static_cast<uint32_t>(lane) / lanes_per_row;
     if (g >= c.rows_per_wave) return;
     const uint64_t t64 = (item >> 1) * c.rows_per_wave + g;
     if (t64 >= static_cast<uint64_t>(c.max_num_tokens)) return;
     const int64_t t = static_cast<int64_t>(t64);
-    const int64_t off = static_cast<int64_t>(static_cast<uint32_t>(lane) - g * c.lanes_per_row) * 16;
-    const int64_t slot = slots[t];
+    const int64_t off = static_cast<int64_t>(static_cast<uint32_t>(lane) - g * lanes_per_row) * 16;
+    const uint8_t *src = (plane ? c.value : c.key) + t * c.kv_token_stride + off;
+    const int64_t l0 = blockIdx.y;  // < num_layers: the grid has at most num_layers rows
+    int64_t slot = slots[t];
+    u32x4 first{};
+    if (EAGER) {  // the row's first layer goes out before the slot is waited on
+        first = load16<KVW_NT_LOADS>(src + l0 * c.kv_layer_stride);
+        asm("" : "+v"(slot), "+v"(first));
+    }
     if (slot >= c.rows_per_layer) {  // beyond the cache: skipped, reported once per token
-        if (blockIdx.y == 0 && plane == 0 && off == 0) raise_flags(err_flag, KVW_FLAG_SLOT_OOB);
+        if (l0 == 0 && plane == 0 && off == 0) raise_flags(err_flag, KVW_FLAG_SLOT_OOB);
         return;
     }
     if (slot < 0) return;
-    const uint8_t *src = (plane ? c.value : c.key) + t * c.kv_token_stride + off;
     uint8_t *dst = (plane ? c.v_cache : c.k_cache) + slot * c.bytes_per_token + off;
-    for (int64_t l = blockIdx.y; l < c.num_layers; l += gridDim.y)
+    if (!EAGER) first = load16<KVW_NT_LOADS>(src + l0 * c.kv_layer_stride);
+    store16<KVW_NT_STORES>(dst + l0 * c.rows_per_layer * c.bytes_per_token, first);
+    for (int64_t l = l0 + gridDim.y; l < c.num_layers; l += gridDim.y)
         store16<KVW_NT_STORES>(dst + l * c.rows_per_layer * c.bytes_per_token,
                                load16<KVW_NT_LOADS>(src + l * c.kv_layer_stride));
 }
@@ -778,7 +820,14 @@ __global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a
                          __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t t = PLANES == 2 ? item : item >> 1;
     const int plane0 = PLANES == 2 ? 0 : static_cast<int>(item & 1);  // first plane of the wave
-    if (t >= a.max_num_tokens) return;  // whole wave: this kernel has no barrier
+    // Kernel arguments are scalar loads, and a wave's first ones miss the scalar
+    // cache.  The compiler issues them where they are first used, so a prologue
+    // with a branch would wait for one 64-byte line of them before asking for the
+    // next.  Making the first branch's operand depend on a field of every line
+    // the prologue reads sends them out in one round trip.
+    int64_t max_tokens = a.max_num_tokens;
+    asm("" : "+s"(max_tokens) : "s"(a.qsl), "s"(c.key), "s"(c.kv_token_stride));
+    if (t >= max_tokens) return;  // whole wave: this kernel has no barrier
     const int l0 = blockIdx.y * c.layers_per_wave;
     const int l1 = min(c.num_layers, l0 + c.layers_per_wave);
     const int64_t bpt = c.bytes_per_token;
@@ -920,6 +969,7 @@ __global__ __launch_bounds__(kBlockThreads) void fill_table_kernel(
     int32_t *counts_out, int32_t *err_flag)
 {
     const int64_t q = static_cast<int64_t>(blockIdx.x) * kBlockThreads + threadIdx.x;
+    asm("" : "+s"(rows) : "s"(err_flag));  // both argument lines in one round trip
     for (int32_t r = blockIdx.y; r < rows; r += gridDim.y) {  // uniform over the workgroup
         uint32_t flags = 0;
         fill_table_row(start, len, cum, num_ranges, range_stride, k, out, out_stride, counts_out,
@@ -1416,9 +1466,12 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
         if (g.num_layers == 0) return KVW_OK;
         const int64_t *slots = fused ? g.slot_mapping_out : g.slot_mapping_in;
         const dim3 grid(static_cast<unsigned>(scatter_blocks), layer_grid);
-        if (small_rows)
-            hipLaunchKernelGGL(kv_scatter_small_kernel, grid, dim3(kScatterThreads), 0, s, slots, c,
-                               g.err_flag);
+        if (small_rows && cp > 1)
+            hipLaunchKernelGGL(kv_scatter_small_kernel<false>, grid, dim3(kScatterThreads), 0, s,
+                               slots, c, g.err_flag);
+        else if (small_rows)
+            hipLaunchKernelGGL(kv_scatter_small_kernel<true>, grid, dim3(kScatterThreads), 0, s,
+                               slots, c, g.err_flag);
         else if (tpw == 4)
             hipLaunchKernelGGL(kv_scatter_kernel<4>, grid, dim3(kScatterThreads), 0, s, slots, c,
                                g.err_flag);
