@@ -12,7 +12,7 @@ import paged_kv_cache_46_amd as kvw
 from parity import (DEV, Caches, DeviceInputs, compare_caches, dev, gpu_slots, host, kv_device,
                     new_flag, oracle_slots, say)
 import oracle
-from workloads import config, custom, long_context, small_cases
+from workloads import BF16_SENTINEL, config, custom, long_context, small_cases
 from workloads.gen import Request
 
 pytestmark = pytest.mark.gpu
@@ -406,10 +406,11 @@ def test_kv_write_32_layers(mode):
 # ---------------------------------------------------------------------------
 # flags, padding and degenerate sizes
 # ---------------------------------------------------------------------------
-def _flagged_workload():
+def _flagged_workload(heads=8, head_dim=128):
     reqs = [Request(100, 40), Request(70, 1), Request(300, 30), Request(20, 20)]
     w = custom("flagged", 4790, reqs, block_size=16, num_blocks=64, runs=("count", 1, 3),
-               max_num_tokens=120, table_stride=24, range_stride=6)
+               max_num_tokens=120, table_stride=24, range_stride=6, num_kv_heads=heads,
+               head_dim=head_dim)
     w.num_blocks_per_req[0] = 99      # above the row width: clamped
     w.num_blocks_per_req[3] = -3      # negative: clamped to 0
     w.block_table[1, 4] = -7          # negative physical block (request 1 writes logical block 4)
@@ -445,13 +446,20 @@ def test_flags_and_clamps(variant):
     assert np.array_equal(g, o) and gf == of and of & kvw.KVW_FLAG_NUM_TOKENS
 
 
+# 2 KiB rows (the slice-granular scatter), 256 B and 48 B rows (several tokens per wave, each
+# lane's row load issued with its slot load): padded, negative and out-of-pool slots alike
+FLAG_ROWS = [(8, 128), (1, 128), (1, 24)]
+
+
+@pytest.mark.parametrize("shape", FLAG_ROWS, ids=lambda s: f"{s[0] * s[1] * 2}B")
 @pytest.mark.parametrize("mode", WRITE_MODES[1:])
-def test_kv_write_flagged(mode):
-    check_kv_write(_flagged_workload(), mode)
+def test_kv_write_flagged(mode, shape):
+    check_kv_write(_flagged_workload(*shape), mode)
 
 
-def test_kv_write_out_of_pool_and_bad_slots():
-    w = _flagged_workload()
+@pytest.mark.parametrize("shape", FLAG_ROWS, ids=lambda s: f"{s[0] * s[1] * 2}B")
+def test_kv_write_out_of_pool_and_bad_slots(shape):
+    w = _flagged_workload(*shape)
     # precomputed slots beyond the cache and below the pad id write nothing
     key_h = w.kv_plane(0)
     rng = np.random.default_rng(4)
@@ -487,6 +495,31 @@ def test_zero_token_rows_and_zero_layers():
     torch.cuda.synchronize()
     assert np.array_equal(host(sm), o)
     assert (host(caches.t) == 0x7FC0).all()
+
+
+@pytest.mark.parametrize("counts", [True, False], ids=["counts", "nocounts"])
+@pytest.mark.parametrize("schedule", ["", "two", "one"])
+def test_zero_width_block_table(schedule, counts):
+    """A paged table of width 0 (no pointer): every token gets the pad id and nothing is
+    written; with counts, every request whose count exceeds the width raises KVW_FLAG_COUNT."""
+    w = config("tiny_prefill")
+    d = DeviceInputs(w)
+    table = torch.zeros((w.num_reqs, 0), dtype=torch.int32, device=DEV)
+    key, value = kv_device(w)
+    caches = Caches(w.num_layers, w.num_blocks, w.block_size, w.row_elems)
+    sm = torch.full((w.max_num_tokens,), 7, dtype=torch.int64, device=DEV)
+    flag = new_flag()
+    kvw.kvw_kv_write(mode=kvw.KVW_SLOTS_PAGED, key=key, value=value, k_cache=caches.k,
+                     v_cache=caches.v, num_blocks=w.num_blocks, block_size=w.block_size,
+                     query_start_loc=d.qsl, num_reqs=w.num_reqs, positions=d.positions,
+                     block_table=table, num_blocks_per_req=d.nbpr if counts else None,
+                     slot_mapping_out=sm, err_flag=flag, schedule=SCHEDULES[schedule])
+    o, of = oracle_slots(w, "paged", block_table=np.zeros((w.num_reqs, 0), np.int32),
+                         nbpr=w.num_blocks_per_req if counts else None)
+    torch.cuda.synchronize()
+    assert (o == -1).all() and np.array_equal(host(sm), o)
+    assert int(flag.item()) == of == (kvw.KVW_FLAG_COUNT if counts else 0)
+    assert (host(caches.t) == BF16_SENTINEL).all()
 
 
 def test_invalid_arguments_raise():
