@@ -379,7 +379,8 @@ def main():
                 f"{scatter_bytes / (scatter * 1e-3) / 1e9:.0f} GB/s ({args.steps} launches back to "
                 f"back; {scatter_pairs * 1e3:.1f} us with an event pair around each)")
             # The same copy kernel with the destination made contiguous (slot t for token t):
-            # the rate this 16-byte non-temporal copy reaches without the scattered blocks.
+            # the rate this 16-byte copy (non-temporal loads, write-through stores) reaches
+            # without the scattered blocks.
             ident = torch.arange(M, dtype=torch.int64, device=dev)
 
             def contiguous(ev, ident=ident, w=w):
@@ -506,9 +507,9 @@ def main():
     if contiguous_ms is not None:
         copy_ceiling = copy_ceiling or {}
         copy_ceiling.update({
-            "what": ("kv_scatter_kernel (16-byte non-temporal loads and stores, one 1 KiB slice per "
-                     "wave) on the headline batch with slot t for token t: the step's copy with a "
-                     "contiguous destination"),
+            "what": ("kv_scatter_kernel (16-byte non-temporal loads, non-temporal stores written "
+                     "through L2, one 1 KiB slice per wave) on the headline batch with slot t for "
+                     "token t: the step's copy with a contiguous destination"),
             "bytes_per_launch": scatter_bytes, "ms": round(contiguous_ms, 6),
             "gbps": round(scatter_bytes / (contiguous_ms * 1e-3) / 1e9, 1),
             "frac_of_peak": round(scatter_bytes / (contiguous_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),

@@ -272,7 +272,7 @@ typedef struct kvw_kv_write_args {
     int64_t kv_token_stride;
     void *k_cache;                     /* [L][B][T] rows of bytes_per_token bytes */
     void *v_cache;                     /* same layout as k_cache */
-    int64_t bytes_per_token;           /* multiple of 16 */
+    int64_t bytes_per_token;           /* multiple of 16, below 2^31 */
     int32_t *err_flag;                 /* device int32 or NULL */
     int32_t schedule;                  /* KVW_SCHEDULE_*; ignored in the precomputed mode */
     int32_t cp_world_size;             /* PAGED/RANGES: context parallelism (0 = none); the */
@@ -326,8 +326,9 @@ size_t kvw_kv_write_args_size(void);
  * should keep the slot mapping (the attention side needs it anyway).
  * Errors: KVW_ERR_INVALID_ARG for an unknown mode or schedule,
  * KVW_SCHEDULE_TWO_KERNELS without slot_mapping_out, NULL required
- * pointers, misalignment, negative sizes, bytes_per_token % 16 != 0, or a
- * cache size beyond int64; KVW_ERR_RANGE_CAP as kvw_slot_mapping_ranges.
+ * pointers, misalignment, negative sizes, bytes_per_token % 16 != 0 or
+ * >= 2^31, or a cache size beyond int64; KVW_ERR_RANGE_CAP as
+ * kvw_slot_mapping_ranges.
  */
 kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream);
 

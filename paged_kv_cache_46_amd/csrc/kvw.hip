@@ -750,11 +750,11 @@ __global__ __launch_bounds__(kScatterThreads) void kv_scatter_kernel(const int64
         }
         if (slot < 0 || off >= c.bytes_per_token) continue;
         const uint8_t *src = (plane ? c.value : c.key) + t * c.kv_token_stride + off;
-        uint8_t *dst = (plane ? c.v_cache : c.k_cache) + slot * c.bytes_per_token + off;
+        uint8_t *row = (plane ? c.v_cache : c.k_cache) + slot * c.bytes_per_token;  // wave-uniform
         // coordinate n = (l*B + slot/T)*T + slot%T = l*B*T + slot
         for (int64_t l = blockIdx.y; l < c.num_layers; l += gridDim.y)
-            store16<KVW_NT_STORES>(dst + l * c.rows_per_layer * c.bytes_per_token,
-                                   load16<KVW_NT_LOADS>(src + l * c.kv_layer_stride));
+            store16_through(row + l * c.rows_per_layer * c.bytes_per_token, static_cast<uint32_t>(off),
+                            load16<KVW_NT_LOADS>(src + l * c.kv_layer_stride));
     }
 }
 
@@ -888,9 +888,18 @@ __global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a
     if (report && lane == 0) raise_flags(a.err_flag, flags);
     if (slot < 0 || !real) return;
 
-    uint8_t *dst[PLANES];
+    uint8_t *dst[PLANES];  // wave-uniform rows; each lane stores at lane_off within them
 #pragma unroll
-    for (int q = 0; q < PLANES; ++q) dst[q] = (plane0 + q ? c.v_cache : c.k_cache) + slot * bpt + lane_off;
+    for (int q = 0; q < PLANES; ++q) dst[q] = (plane0 + q ? c.v_cache : c.k_cache) + slot * bpt;
+    // Large writes (one wave per token and plane) store through to memory, as the
+    // scatter does.  Small ones (one wave per token, a single round of waves on the
+    // GPU) keep the stores in L2: there the write-through traffic delayed the other
+    // waves' cold metadata loads (range lookup on the 8,192-token mixed batch: 13.2
+    // against 12.3 us of kernel time).
+    const auto store_row = [](uint8_t *base, uint32_t off, u32x4 v) {
+        if constexpr (PLANES == 1) store16_through(base, off, v);
+        else store16<KVW_NT_STORES>(base + off, v);
+    };
     for (int l = l0; l < l1; ++l) {
         const int64_t src_l = l * c.kv_layer_stride;
         const int64_t dst_l = static_cast<int64_t>(l) * c.rows_per_layer * bpt;  // l*B*T rows
@@ -908,7 +917,8 @@ __global__ __launch_bounds__(kFusedThreads) void kv_write_fused_kernel(MapArgs a
                 if (seg + lane_off + ch * kSliceBytes < bpt)
 #pragma unroll
                     for (int q = 0; q < PLANES; ++q)
-                        store16<KVW_NT_STORES>(dst[q] + dst_l + seg + ch * kSliceBytes, row[q][ch]);
+                        store_row(dst[q] + dst_l, static_cast<uint32_t>(lane_off + seg + ch * kSliceBytes),
+                                  row[q][ch]);
         }
     }
 }
@@ -1314,8 +1324,8 @@ kvw_status kvw_kv_write(const kvw_kv_write_args *args, void *stream)
     KVW_REQUIRE(g.num_layers >= 0, "%s: num_layers is negative", fn);
     KVW_REQUIRE(g.num_blocks >= 0, "%s: num_blocks is negative", fn);
     KVW_REQUIRE(g.block_size > 0, "%s: block_size %d must be positive", fn, g.block_size);
-    KVW_REQUIRE(g.bytes_per_token > 0 && g.bytes_per_token % 16 == 0,
-                "%s: bytes_per_token %lld must be a positive multiple of 16", fn,
+    KVW_REQUIRE(g.bytes_per_token > 0 && g.bytes_per_token % 16 == 0 && g.bytes_per_token <= INT32_MAX,
+                "%s: bytes_per_token %lld must be a positive multiple of 16 below 2^31", fn,
                 (long long)g.bytes_per_token);
     KVW_REQUIRE(g.num_blocks <= INT64_MAX / g.block_size, "%s: num_blocks*block_size overflows", fn);
     const int64_t rows_per_layer = g.num_blocks * g.block_size;

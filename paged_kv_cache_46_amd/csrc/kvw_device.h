@@ -46,6 +46,22 @@ __device__ __forceinline__ void store16(uint8_t *p, u32x4 v)
     else *reinterpret_cast<u32x4 *>(p) = v;
 }
 
+// 16 bytes to base + off for a wave-uniform base (off: the lane's offset, below
+// 2^31), stored at device scope and non-temporal: the line is written through
+// the XCD's L2 to memory rather than held there dirty, and streamed.  A buffer
+// store with the cache-policy bits (SC1 | NT), so the compiler sees the store.
+// Measured on the K/V scatter of 2 KiB rows, each call writing lines the call
+// before did not: 3-4% faster than a non-temporal store that L2 holds, at every
+// destination layout from contiguous to one 64 KiB block per run.
+constexpr int kCpolNt = 2, kCpolSc1 = 16;
+constexpr int kBufferRsrcWord3 = 0x00020000;  // raw (untyped) buffer access on gfx9-family parts
+
+__device__ __forceinline__ void store16_through(uint8_t *base, uint32_t off, u32x4 v)
+{
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, kBufferRsrcWord3);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(off), 0, kCpolSc1 | kCpolNt);
+}
+
 // ---- wavefront-level search -------------------------------------------------
 // The 64 lanes of a wave hold 64 evenly spaced entries of a sorted array (one
 // vector load) and each lane ranks its own key among them with a 6-step

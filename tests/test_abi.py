@@ -214,6 +214,7 @@ def test_kv_write_validation(lib):
     assert f(ctypes.byref(_args(mode=7)), None) == INVALID
     assert f(ctypes.byref(_args(bytes_per_token=24)), None) == INVALID
     assert f(ctypes.byref(_args(bytes_per_token=0)), None) == INVALID
+    assert f(ctypes.byref(_args(bytes_per_token=1 << 31)), None) == INVALID  # a row below 2 GiB
     assert f(ctypes.byref(_args(key=P + 8)), None) == INVALID
     assert f(ctypes.byref(_args(kv_token_stride=2056)), None) == INVALID
     assert f(ctypes.byref(_args(k_cache=None)), None) == INVALID
