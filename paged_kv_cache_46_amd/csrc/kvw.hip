@@ -60,7 +60,7 @@
 #define KVW_NT_STORES 1
 #endif
 #ifndef KVW_TOKEN_WAVE_MAX_ROWS
-#define KVW_TOKEN_WAVE_MAX_ROWS 32768
+#define KVW_TOKEN_WAVE_MAX_ROWS 8192
 #endif
 
 namespace {
