@@ -797,10 +797,10 @@ __global__ __launch_bounds__(kScatterThreads) void kv_scatter_small_kernel(const
     if (slot < 0) return;
     uint8_t *dst = (plane ? c.v_cache : c.k_cache) + slot * c.bytes_per_token + off;
     if (!EAGER) first = load16<KVW_NT_LOADS>(src + l0 * c.kv_layer_stride);
-    store16<KVW_NT_STORES>(dst + l0 * c.rows_per_layer * c.bytes_per_token, first);
+    store16_device(dst + l0 * c.rows_per_layer * c.bytes_per_token, first);
     for (int64_t l = l0 + gridDim.y; l < c.num_layers; l += gridDim.y)
-        store16<KVW_NT_STORES>(dst + l * c.rows_per_layer * c.bytes_per_token,
-                               load16<KVW_NT_LOADS>(src + l * c.kv_layer_stride));
+        store16_device(dst + l * c.rows_per_layer * c.bytes_per_token,
+                       load16<KVW_NT_LOADS>(src + l * c.kv_layer_stride));
 }
 
 // One wave per (token, plane) (PLANES = 1) or per token (PLANES = 2, both
