@@ -319,11 +319,12 @@ size_t kvw_kv_write_args_size(void);
  * KVW_TWO_KERNEL_MIN_ROWS (measured crossover on MI355X), one otherwise.
  * Results are identical either way.  Cost: without slot_mapping_out a large
  * write always takes one kernel, which is slower than two on fragmented caches
- * and long multi-layer writes.  Measured on MI355X: 131,072 tokens of 2 KiB
- * rows, every 32-slot block its own run, one kernel at about 71% of 8 TB/s
- * (paged and ranges) against 74-75% for two kernels; 16,384 tokens x 32
- * layers, 74-76% against 80%.  Callers that write large batches
- * should keep the slot mapping (the attention side needs it anyway).
+ * and long multi-layer writes (and 1-2% faster on contiguous ones).  Measured
+ * on MI355X: 131,072 tokens of 2 KiB rows, every 32-slot block its own run,
+ * one kernel at 73-74% of 8 TB/s (paged and ranges) against 77-78% for two
+ * kernels; 16,384 tokens x 32 layers, 77-79% against 81-82%.  Callers that
+ * write large fragmented batches should keep the slot mapping (the attention
+ * side needs it anyway).
  * Errors: KVW_ERR_INVALID_ARG for an unknown mode or schedule,
  * KVW_SCHEDULE_TWO_KERNELS without slot_mapping_out, NULL required
  * pointers, misalignment, negative sizes, bytes_per_token % 16 != 0 or
