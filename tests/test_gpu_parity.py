@@ -293,6 +293,29 @@ def test_kv_write_row_widths(shape, mode):
     check_kv_write(_row_width_workload(*shape), mode)
 
 
+def _wide_row_workload(heads, head_dim, layers):
+    r = np.random.default_rng(4760 + heads * 131 + head_dim + layers)
+    reqs = [Request(int(r.integers(1, 600)) + 700, int(r.integers(300, 700))) for _ in range(6)]
+    reqs += [Request(int(r.integers(1, 1200)), 1) for _ in range(24)]
+    n = sum(q.n_new for q in reqs)
+    return custom(f"wide_{heads * head_dim * 2}B_L{layers}", 4760 + heads, reqs, block_size=16,
+                  num_blocks=3000, runs=("count", 1, 5), num_kv_heads=heads, head_dim=head_dim,
+                  num_layers=layers, max_num_tokens=n + 29)
+
+
+# rows over 2 KiB: 2,064 B (a partial third slice), 3 KiB and 4 KiB (three and four slices per
+# lane in the one-kernel write), 6 KiB (copied in two segments); one layer keeps the one-kernel
+# write at one wave per token, four layers (over 8,192 token rows) at one wave per plane
+WIDE_ROWS = [(129, 8), (12, 128), (16, 128), (24, 128)]
+
+
+@pytest.mark.parametrize("layers", [1, 4])
+@pytest.mark.parametrize("mode", ["precomputed", "paged-two", "paged-one", "ranges-one"])
+@pytest.mark.parametrize("shape", WIDE_ROWS, ids=lambda s: f"{s[0] * s[1] * 2}B")
+def test_kv_write_wide_rows(shape, mode, layers):
+    check_kv_write(_wide_row_workload(*shape, layers), mode)
+
+
 @pytest.mark.parametrize("mode", WRITE_MODES[1:])
 @pytest.mark.parametrize("name", ["tiny_prefill", "decode_step", "mixed_chunked"])
 def test_kv_write_study(name, mode):
