@@ -707,10 +707,9 @@ __global__ __launch_bounds__(kBlockThreads) void slot_mapping_kernel(MapArgs a)
 // One wave per (layer, token, plane, 1 KiB slice) item.  The token is
 // wave-uniform; its slot is one scalar load, and the slice is read once the
 // slot is known.  (Issuing the read together with the slot load was measured
-// on 131,072 tokens of 2 KiB rows: 3% faster right after the slot-mapping
-// launch on a contiguous cache, 0.5% slower on a fully fragmented one, where
-// the scattered writes bound the kernel and earlier reads compete with them;
-// the fragmented case is the one kept.)  Items are ordered
+// on 131,072 tokens of 2 KiB rows: no faster on a contiguous cache and 0.5%
+// slower on a fully fragmented one, where the scattered writes bound the
+// kernel and earlier reads compete with them.)  Items are ordered
 // layer-major (blockIdx.y), then token, plane, slice, so consecutive waves
 // stream through consecutive K/V rows and, for tokens of one block,
 // consecutive cache slots.
